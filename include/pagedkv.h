@@ -1,0 +1,252 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X paged-KV decode library (libpagedkv.so).
+ *
+ * The library has two halves:
+ *   1. a host-side block allocator: a pool of fixed-size physical blocks,
+ *      per-sequence block tables, prefix sharing with reference counts and
+ *      copy-on-write, release and truncate. It owns host metadata only.
+ *   2. device operations on caller-owned GPU memory, issued asynchronously
+ *      on the caller's HIP stream: the slot-mapped cache write, the
+ *      copy-on-write block copy, and paged attention (decode, and causal
+ *      multi-query verify).
+ *
+ * Sources of the method (cited by section, as on the pages):
+ *   [vLLM]       PagedAttention / vLLM abstract, papers search page for
+ *                "external vector cache": attention over a KV cache kept in
+ *                fixed-size blocks like OS pages, with sharing of blocks
+ *                within and across requests.
+ *   [NeuralOps]  "NeuralOps v1.3.4: Serving Primitives & KV Cache
+ *                Optimization", Architectural Breakdown, 1. Paged KV Cache
+ *                Engine (16-token physical blocks, block table, growth one
+ *                block at a time) and Highlights (slot mapping, block
+ *                reclamation when generation ends).
+ *   [KVNB s5]    course page "Module 10. KV Caches and Efficient Inference",
+ *                notebook "KV cache and serving: bytes, pages, and
+ *                ceilings", section 5 "Page pool: prefix sharing and
+ *                copy-on-write" (allocation order, preflight, COW, release,
+ *                counters, invariants); section 2 (causal visibility: query
+ *                j of a suffix sees prefix + j + 1 keys); section 9
+ *                (negative tests: errors leave the pool unchanged).
+ *
+ * Conventions for every call:
+ *   - Return value: PKV_OK (0) or one of the PKV_E* codes below. On error a
+ *     human-readable message is available from paged_kv_last_error() (per
+ *     calling thread) and, for allocator calls, the pool is unchanged.
+ *   - All arguments are checked before anything is mutated or launched.
+ *   - Host pointers are plain host memory; "device" pointers are GPU memory
+ *     (for example torch tensors' data pointers). The caller owns all of it.
+ *   - A pool handle is not thread-safe: one thread at a time per pool.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device calls only enqueue work: no host synchronisation, no device
+ *     allocation.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+enum {
+  PKV_OK = 0,
+  PKV_EINVAL = 1,   /* bad size, pointer, dtype, count or unsupported shape */
+  PKV_ENOENT = 2,   /* unknown sequence id                                   */
+  PKV_EEXIST = 3,   /* sequence id already exists (create, fork target)      */
+  PKV_ENOMEM = 4,   /* not enough free blocks; the pool is unchanged         */
+  PKV_ECORRUPT = 5, /* paged_kv_validate found a broken invariant            */
+  PKV_EHIP = 6      /* a HIP runtime or launch error                         */
+};
+
+/* ---- element types of caches and queries ------------------------------ */
+enum { PKV_F32 = 0, PKV_BF16 = 1 };
+
+/* Thread-local text describing the last error of this thread's calls. */
+const char *paged_kv_last_error(void);
+
+/* ======================================================================
+ * Host allocator  ([KVNB s5], [NeuralOps], [vLLM] sharing)
+ * ====================================================================== */
+
+typedef struct pkv_pool pkv_pool; /* opaque */
+
+/* A device block copy the caller must perform (paged_kv_copy_blocks) before
+ * writing the new tokens: physical block `src` -> `dst`, K and V. */
+typedef struct {
+  int32_t src;
+  int32_t dst;
+} pkv_cow_t;
+
+/* The counters of [KVNB s5]. A block's fill is the most tokens any live
+ * sequence keeps in it; payload sums fills once per physical block. */
+typedef struct {
+  int64_t allocated_blocks;         /* blocks with at least one reference  */
+  int64_t free_blocks;              /* blocks on the free stack            */
+  int64_t physical_capacity_tokens; /* allocated_blocks * block_size       */
+  int64_t physical_payload_tokens;  /* sum of fills of allocated blocks    */
+  int64_t logical_tokens;           /* sum of sequence lengths             */
+  int64_t internal_waste_tokens;    /* capacity - payload                  */
+  int64_t sharing_savings_tokens;   /* logical - payload                   */
+} pkv_stats_t;
+
+/* Create a pool of `total_blocks` blocks of `block_size` token slots.
+ * initial_free_stack: NULL for the order N-1, ..., 0 (block 0 is handed out
+ * first), or a permutation of 0..N-1 (host array of N ints) whose LAST entry
+ * is handed out first. Requires total_blocks * block_size <= INT32_MAX so
+ * every slot fits an int32. *out receives the handle. */
+int paged_kv_pool_create(int32_t total_blocks, int32_t block_size,
+                         const int32_t *initial_free_stack, pkv_pool **out);
+void paged_kv_pool_destroy(pkv_pool *pool);
+
+/* Register an empty sequence. EEXIST if the id is taken. */
+int paged_kv_seq_create(pkv_pool *pool, int64_t seq_id);
+
+/* Append `n_tokens` logical tokens to a sequence ([KVNB s5] append).
+ * Order: preflight the blocks needed (one extra when the last block is
+ * partial and shared with another sequence) -> ENOMEM with no change if too
+ * few are free; then, if the last block is partial and shared, take a
+ * replacement block and report the pair (old, new) in cow_out; fill the last
+ * block's free slots; then take new blocks from the free stack.
+ * slot_mapping_out: host array of n_tokens ints; token k of this append gets
+ *   slot = block * block_size + offset (block id from the sequence's table).
+ * cow_out: host array of at least 1 pair; *n_cow_out gets 0 or 1.
+ * n_tokens == 0 is a no-op that succeeds. */
+int paged_kv_alloc(pkv_pool *pool, int64_t seq_id, int32_t n_tokens,
+                   int32_t *slot_mapping_out, pkv_cow_t *cow_out,
+                   int32_t *n_cow_out);
+
+/* paged_kv_alloc for n_seqs sequences in order, as separate calls would.
+ * Slots are written back to back into slot_mapping_out (sum of n_tokens
+ * entries); copy pairs back to back into cow_out (capacity n_seqs);
+ * *n_cow_out gets their count and *n_done the number of sequences handled.
+ * Stops at the first failing sequence (earlier ones stay applied) and
+ * returns its code. */
+int paged_kv_alloc_batch(pkv_pool *pool, const int64_t *seq_ids,
+                         const int32_t *n_tokens, int32_t n_seqs,
+                         int32_t *slot_mapping_out, pkv_cow_t *cow_out,
+                         int32_t *n_cow_out, int32_t *n_done);
+
+/* Create `child` sharing the first ceil(prefix_tokens / block_size) blocks
+ * of `parent` (each gains a reference); child length = prefix_tokens
+ * ([KVNB s5] share_prefix). EINVAL if prefix_tokens > parent length,
+ * EEXIST if child exists, ENOENT if parent does not. */
+int paged_kv_fork(pkv_pool *pool, int64_t parent, int64_t child,
+                  int32_t prefix_tokens);
+
+/* Release a sequence: drop one reference per table entry in table order;
+ * blocks reaching zero go on top of the free stack ([KVNB s5] release). */
+int paged_kv_free(pkv_pool *pool, int64_t seq_id);
+
+/* Shorten a sequence to new_length (0 <= new_length <= length): table
+ * entries past ceil(new_length / block_size) are released in table order; a
+ * kept partial block that is shared stays shared, so the next append copies
+ * it. (Rollback of rejected speculative tokens.) */
+int paged_kv_truncate(pkv_pool *pool, int64_t seq_id, int32_t new_length);
+
+int paged_kv_seq_length(const pkv_pool *pool, int64_t seq_id, int32_t *len);
+
+/* Number of live sequences in *n_out, and (when ids_out is not NULL) their
+ * ids in ascending order in ids_out[capacity]; EINVAL if capacity is too
+ * small. */
+int paged_kv_seq_ids(const pkv_pool *pool, int64_t *ids_out, int32_t capacity,
+                     int32_t *n_out);
+
+/* One sequence's block table (host array of `capacity` ints). */
+int paged_kv_page_table(const pkv_pool *pool, int64_t seq_id,
+                        int32_t *blocks_out, int32_t capacity, int32_t *n_out);
+
+/* The free stack bottom to top (the top is handed out next). */
+int paged_kv_free_stack(const pkv_pool *pool, int32_t *out, int32_t capacity,
+                        int32_t *n_out);
+
+/* Row-major block tables for n_seqs sequences into host memory:
+ * tables_out[n_seqs * max_blocks], each row padded with -1, and
+ * context_lens_out[n_seqs]. EINVAL if a table is longer than max_blocks. */
+int paged_kv_block_tables(const pkv_pool *pool, const int64_t *seq_ids,
+                          int32_t n_seqs, int32_t max_blocks,
+                          int32_t *tables_out, int32_t *context_lens_out);
+
+int paged_kv_stats(const pkv_pool *pool, pkv_stats_t *out);
+
+/* Check the invariants of [KVNB s5] validate: no duplicate or out-of-range
+ * id on the free stack; table length = ceil(length / block_size); no block
+ * twice in one table; reference count = number of table entries naming the
+ * block; referenced <=> not free; 1 <= fill <= block_size for referenced
+ * blocks; logical >= payload. ECORRUPT with the broken rule as message. */
+int paged_kv_validate(const pkv_pool *pool);
+
+/* ======================================================================
+ * Device operations (gfx950)
+ *
+ * Cache layout ([NeuralOps] blocks; layout chosen here): K and V pools are
+ * separate row-major arrays [num_blocks, Hkv, block_size, D] of the cache
+ * dtype, so one (block, KV head) is a contiguous block_size * D run.
+ * Supported on the device: D in {64, 128, 256}; block_size a multiple of 16
+ * for attention (any positive size for the cache write and block copy).
+ * ====================================================================== */
+
+/* Slot-mapped cache write ([NeuralOps] slot mapping): for every t < T with
+ * s = slot_mapping[t] in [0, num_blocks * block_size):
+ *   k_cache[s / bs, h, s % bs, :] = k_new[t, h, :]   (and V), all h < Hkv.
+ * Bit-exact copy. Slots < 0 or >= num_blocks * block_size are skipped.
+ * k_new, v_new: device [T, Hkv, D]; slot_mapping: device int32 [T].
+ * Two tokens must not name the same slot (the allocator never does). */
+int paged_cache_write(const void *k_new, const void *v_new, void *k_cache,
+                      void *v_cache, const int32_t *slot_mapping, int32_t T,
+                      int32_t num_blocks, int32_t Hkv, int32_t D,
+                      int32_t block_size, int dtype, void *stream);
+
+/* Copy-on-write device copy: for each of the n pairs (device array), copy
+ * block src -> dst in both pools (all Hkv * block_size * D elements). Pairs
+ * with an id outside [0, num_blocks) are skipped. Must run before the cache
+ * write of the same step, on the same stream. */
+int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_t *pairs,
+                         int32_t n, int32_t num_blocks, int32_t Hkv, int32_t D,
+                         int32_t block_size, int dtype, void *stream);
+
+/* Workspace bytes paged_attention_decode needs for these sizes (0 when the
+ * chosen partitioning keeps everything on chip). partition_tokens: 0 lets
+ * the library choose; otherwise a positive multiple of 16. */
+int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int32_t max_blocks,
+                                   int32_t block_size,
+                                   int32_t partition_tokens, size_t *bytes);
+
+/* Paged attention ([vLLM]; causal rule of [KVNB s2]).
+ * For sequence b, query i < nq, query head h (KV head g = h / (Hq / Hkv)):
+ * the query sees its first n = context_lens[b] - nq + i + 1 tokens, token t
+ * being slot t % bs of block block_tables[b * max_blocks + t / bs];
+ *   out = softmax(scale * q . K^T) V   over those n tokens,
+ *   lse = log(sum exp(scale * q . k))  (natural log; optional).
+ * context_lens includes this step's tokens (write them first).
+ *   out:          device float32 [B, nq, Hq, D]
+ *   q:            device `dtype` [B, nq, Hq, D]
+ *   k_cache/v_cache: device `dtype` [num_blocks, Hkv, block_size, D]
+ *   block_tables: device int32 [B, max_blocks]; entries past the used ones
+ *                 are ignored
+ *   context_lens: device int32 [B]
+ *   lse_out:      device float32 [B, nq, Hq] or NULL
+ *   workspace:    device buffer of paged_attention_workspace_size() bytes
+ *                 (may be NULL when that size is 0)
+ * Accumulation is float32. Rows that see no token (n <= 0), rows of a
+ * sequence with context_lens[b] > max_blocks * block_size, and rows whose
+ * visible tokens meet a table entry outside [0, num_blocks) produce NaN in
+ * out and lse instead of reading out of bounds.
+ * Host-checked: sizes, Hq % Hkv == 0, D and block_size supported, nq <= 16,
+ * scale finite, workspace large enough -> EINVAL. */
+int paged_attention_decode(float *out, const void *q, const void *k_cache,
+                           const void *v_cache, const int32_t *block_tables,
+                           int32_t max_blocks, const int32_t *context_lens,
+                           int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t num_blocks,
+                           float scale, int dtype, int32_t partition_tokens,
+                           void *workspace, size_t workspace_bytes,
+                           float *lse_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

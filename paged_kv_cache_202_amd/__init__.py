@@ -1,0 +1,218 @@
+"""Paged-KV decode for MI355X: Python binding of libpagedkv.so.
+
+The binding only marshals arguments: every step runs in the C++ allocator or
+in the HIP kernels of the shared library (see include/pagedkv.h). Names match
+the C ABI. Device buffers are torch tensors on the GPU; PyTorch is used for
+device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    Corrupt, HipError, InvalidArgument, OutOfBlocks, PagedKVError, SequenceExists,
+    UnknownSequence, PKV_BF16, PKV_F32, check, load)
+
+__all__ = [
+    "PagedKVPool", "paged_cache_write", "paged_kv_copy_blocks",
+    "paged_attention_workspace_size", "paged_attention_decode", "dtype_code",
+]
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(_lib.P_i32)
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(_lib.P_i64)
+
+
+class PagedKVPool:
+    """Host block allocator (paged_kv_pool_* / paged_kv_* calls)."""
+
+    def __init__(self, total_blocks: int, block_size: int = 16, initial_free_stack=None):
+        lib = load()
+        self._lib = lib
+        self.total_blocks = int(total_blocks)
+        self.block_size = int(block_size)
+        handle = ctypes.c_void_p()
+        stack = None
+        if initial_free_stack is not None:
+            stack = np.ascontiguousarray(initial_free_stack, dtype=np.int32)
+            if stack.shape != (self.total_blocks,):
+                raise InvalidArgument(_lib.PKV_EINVAL, "initial free stack needs N entries")
+        check(lib.paged_kv_pool_create(self.total_blocks, self.block_size,
+                                       None if stack is None else _i32p(stack),
+                                       ctypes.byref(handle)))
+        self._h = handle
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.paged_kv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def seq_create(self, seq_id: int) -> None:
+        check(self._lib.paged_kv_seq_create(self._h, seq_id))
+
+    def alloc(self, seq_id: int, n_tokens: int):
+        """Returns (slots int32 array, list of (src, dst) copy pairs)."""
+        slots = np.empty(max(n_tokens, 1), dtype=np.int32)
+        cow = (_lib.CowPair * 1)()
+        n_cow = ctypes.c_int32()
+        check(self._lib.paged_kv_alloc(self._h, seq_id, n_tokens, _i32p(slots), cow,
+                                       ctypes.byref(n_cow)))
+        return slots[:n_tokens], [(cow[i].src, cow[i].dst) for i in range(n_cow.value)]
+
+    def alloc_batch(self, seq_ids, n_tokens):
+        """Returns (slots, copy pairs [n, 2] int32, n_done); raises on failure."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        ns = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        slots = np.empty(max(int(ns.sum()), 1), dtype=np.int32)
+        cow = (_lib.CowPair * max(len(ids), 1))()
+        n_cow, n_done = ctypes.c_int32(), ctypes.c_int32()
+        rc = self._lib.paged_kv_alloc_batch(self._h, _i64p(ids), _i32p(ns), len(ids),
+                                            _i32p(slots), cow, ctypes.byref(n_cow),
+                                            ctypes.byref(n_done))
+        self.last_batch_done = n_done.value
+        check(rc)
+        pairs = np.array([(cow[i].src, cow[i].dst) for i in range(n_cow.value)],
+                         dtype=np.int32).reshape(-1, 2)
+        return slots[:int(ns.sum())], pairs
+
+    def fork(self, parent: int, child: int, prefix_tokens: int) -> None:
+        check(self._lib.paged_kv_fork(self._h, parent, child, prefix_tokens))
+
+    def free(self, seq_id: int) -> None:
+        check(self._lib.paged_kv_free(self._h, seq_id))
+
+    def truncate(self, seq_id: int, new_length: int) -> None:
+        check(self._lib.paged_kv_truncate(self._h, seq_id, new_length))
+
+    def seq_length(self, seq_id: int) -> int:
+        n = ctypes.c_int32()
+        check(self._lib.paged_kv_seq_length(self._h, seq_id, ctypes.byref(n)))
+        return n.value
+
+    def seq_ids(self) -> list[int]:
+        n = ctypes.c_int32()
+        check(self._lib.paged_kv_seq_ids(self._h, None, 0, ctypes.byref(n)))
+        out = np.empty(max(n.value, 1), dtype=np.int64)
+        check(self._lib.paged_kv_seq_ids(self._h, _i64p(out), len(out), ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def page_table(self, seq_id: int) -> tuple[int, ...]:
+        n = ctypes.c_int32()
+        cap = -(-self.seq_length(seq_id) // self.block_size)
+        out = np.empty(max(cap, 1), dtype=np.int32)
+        check(self._lib.paged_kv_page_table(self._h, seq_id, _i32p(out), len(out),
+                                            ctypes.byref(n)))
+        return tuple(out[:n.value].tolist())
+
+    def free_stack(self) -> list[int]:
+        n = ctypes.c_int32()
+        out = np.empty(self.total_blocks, dtype=np.int32)
+        check(self._lib.paged_kv_free_stack(self._h, _i32p(out), len(out), ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def block_tables(self, seq_ids, max_blocks: int):
+        """Returns (tables [n, max_blocks] int32 padded with -1, lens [n] int32)."""
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        check(self._lib.paged_kv_block_tables(self._h, _i64p(ids), len(ids), max_blocks,
+                                               _i32p(tables), _i32p(lens)))
+        return tables, lens
+
+    def stats(self) -> dict:
+        st = _lib.Stats()
+        check(self._lib.paged_kv_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in _lib.Stats._fields_}
+
+    def validate(self) -> None:
+        check(self._lib.paged_kv_validate(self._h))
+
+
+# ---------------------------------------------------------------- device ops
+
+def dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise InvalidArgument(_lib.PKV_EINVAL, f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise InvalidArgument(_lib.PKV_EINVAL, "device tensors must be contiguous on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def paged_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """k_new, v_new [T, Hkv, D]; caches [NB, Hkv, bs, D]; slot_mapping int32 [T]."""
+    NB, Hkv, bs, D = k_cache.shape
+    T = k_new.shape[0]
+    if (tuple(k_new.shape) != (T, Hkv, D) or v_new.shape != k_new.shape
+            or v_cache.shape != k_cache.shape or tuple(slot_mapping.shape) != (T,)
+            or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype):
+        raise InvalidArgument(_lib.PKV_EINVAL, "paged_cache_write: shape or dtype mismatch")
+    check(load().paged_cache_write(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
+                                   _dev(slot_mapping), T, NB, Hkv, D, bs,
+                                   dtype_code(k_cache), _stream(stream)))
+
+
+def paged_kv_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """pairs: device int32 [n, 2] of (src, dst)."""
+    NB, Hkv, bs, D = k_cache.shape
+    n = pairs.shape[0]
+    check(load().paged_kv_copy_blocks(_dev(k_cache), _dev(v_cache), _dev(pairs), n, NB, Hkv,
+                                      D, bs, dtype_code(k_cache), _stream(stream)))
+
+
+def paged_attention_workspace_size(B, nq, Hq, Hkv, D, max_blocks, block_size,
+                                   partition_tokens=0) -> int:
+    out = ctypes.c_size_t()
+    check(load().paged_attention_workspace_size(B, nq, Hq, Hkv, D, max_blocks, block_size,
+                                                partition_tokens, ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           partition_tokens=0, workspace=None, lse=None, stream=None) -> None:
+    """out fp32 [B, nq, Hq, D]; q [B, nq, Hq, D]; tables int32 [B, max_blocks]."""
+    B, nq, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    max_blocks = block_tables.shape[1]
+    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
+            or tuple(context_lens.shape) != (B,) or q.dtype != k_cache.dtype
+            or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype):
+        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode: shape mismatch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().paged_attention_decode(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,
+        _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB, float(scale), dtype_code(k_cache),
+        int(partition_tokens), _dev(workspace), ws_bytes, _dev(lse), _stream(stream)))
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)

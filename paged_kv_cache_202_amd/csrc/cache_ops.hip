@@ -1,0 +1,119 @@
+// Device cache maintenance for gfx950: the slot-mapped cache write and the
+// copy-on-write block copy.
+//
+// Cache write: "NeuralOps v1.3.4: Serving Primitives & KV Cache Optimization"
+// (Highlights: slot mapping; Architectural Breakdown 1: block table). The
+// copy: course page "Module 10. KV Caches and Efficient Inference", notebook
+// section 5 "Page pool: prefix sharing and copy-on-write" (a writer into a
+// shared partial block first gets a private copy).
+//
+// Both are pure byte movement, bound by HBM bandwidth. Every (token, KV head)
+// row of D elements is contiguous in the source and in the destination pool
+// ([num_blocks, Hkv, block_size, D]), and a whole block is contiguous too, so
+// each thread moves 16-byte vectors and consecutive lanes touch consecutive
+// addresses on both sides.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pagedkv.h"
+#include "status.h"
+
+namespace {
+
+// One thread per 16-byte vector of the new rows; grid-stride.
+__global__ void __launch_bounds__(256)
+cache_write_kernel(const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_new,
+                   uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
+                   const int32_t *__restrict__ slots, int64_t total_vec, int32_t vec_per_row,
+                   int32_t Hkv, int32_t bs, int64_t num_slots) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_vec; i += stride) {
+    const int64_t row = i / vec_per_row;  // t * Hkv + h
+    const int32_t v = (int32_t)(i - row * vec_per_row);
+    const int64_t t = row / Hkv;
+    const int32_t h = (int32_t)(row - t * Hkv);
+    const int64_t s = slots[t];
+    if (s < 0 || s >= num_slots) continue;
+    const int64_t blk = s / bs, off = s - blk * bs;
+    const int64_t dst = ((blk * Hkv + h) * bs + off) * vec_per_row + v;
+    k_cache[dst] = k_new[i];
+    v_cache[dst] = v_new[i];
+  }
+}
+
+// blockIdx.y = pair index; threads stride over the block's 16-byte vectors.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
+                   const pkv_cow_t *__restrict__ pairs, int64_t vec_per_block,
+                   int32_t num_blocks) {
+  const pkv_cow_t pr = pairs[blockIdx.y];
+  if (pr.src < 0 || pr.src >= num_blocks || pr.dst < 0 || pr.dst >= num_blocks) return;
+  const uint4 *ks = k_cache + (int64_t)pr.src * vec_per_block;
+  const uint4 *vs = v_cache + (int64_t)pr.src * vec_per_block;
+  uint4 *kd = k_cache + (int64_t)pr.dst * vec_per_block;
+  uint4 *vd = v_cache + (int64_t)pr.dst * vec_per_block;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vec_per_block;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 0; }
+
+}  // namespace
+
+using pkv::fail;
+
+extern "C" int paged_cache_write(const void *k_new, const void *v_new, void *k_cache,
+                                 void *v_cache, const int32_t *slot_mapping, int32_t T,
+                                 int32_t num_blocks, int32_t Hkv, int32_t D,
+                                 int32_t block_size, int dtype, void *stream) {
+  const int es = elem_bytes(dtype);
+  if (!es) return fail(PKV_EINVAL, "unsupported dtype %d", dtype);
+  if (T < 0 || num_blocks <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "sizes must be positive (T >= 0)");
+  if ((D * es) % 16)
+    return fail(PKV_EINVAL, "a row of D=%d elements must be a multiple of 16 bytes", D);
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_EINVAL, "NULL pointer");
+  for (const void *p : {k_new, v_new, (const void *)k_cache, (const void *)v_cache})
+    if ((uintptr_t)p % 16) return fail(PKV_EINVAL, "K/V pointers must be 16-byte aligned");
+  const int32_t vpr = D * es / 16;
+  const int64_t total = (int64_t)T * Hkv * vpr;
+  const int64_t want = (total + 255) / 256;
+  const int grid = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(cache_write_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4 *)k_new, (const uint4 *)v_new, (uint4 *)k_cache,
+                     (uint4 *)v_cache, slot_mapping, total, vpr, Hkv, block_size,
+                     (int64_t)num_blocks * block_size);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "cache write launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_t *pairs,
+                                    int32_t n, int32_t num_blocks, int32_t Hkv, int32_t D,
+                                    int32_t block_size, int dtype, void *stream) {
+  const int es = elem_bytes(dtype);
+  if (!es) return fail(PKV_EINVAL, "unsupported dtype %d", dtype);
+  if (n < 0 || num_blocks <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "sizes must be positive (n >= 0)");
+  if (n > 65535) return fail(PKV_EINVAL, "at most 65535 pairs per call");
+  const int64_t block_bytes = (int64_t)Hkv * block_size * D * es;
+  if (block_bytes % 16) return fail(PKV_EINVAL, "block bytes must be a multiple of 16");
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !pairs) return fail(PKV_EINVAL, "NULL pointer");
+  if ((uintptr_t)k_cache % 16 || (uintptr_t)v_cache % 16)
+    return fail(PKV_EINVAL, "K/V pools must be 16-byte aligned");
+  const int64_t vpb = block_bytes / 16;
+  int gx = (int)((vpb + 255) / 256);
+  if (gx > 64) gx = 64;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, n), dim3(256), 0, (hipStream_t)stream,
+                     (uint4 *)k_cache, (uint4 *)v_cache, pairs, vpb, num_blocks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "block copy launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}

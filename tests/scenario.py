@@ -1,0 +1,146 @@
+"""Build the same paged-attention case on both sides: oracle (host) and library (GPU).
+
+Both sides receive only what ``synth`` generates (logical per-sequence K/V,
+queries, lengths, the initial free-stack permutation). The oracle builds its
+pool with ``oracle.pool`` and ``oracle.attention.cache_write``; the GPU side
+builds its own with the C-ABI allocator and the ``paged_cache_write`` kernel.
+Nothing computed by the GPU path is ever fed to the oracle.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import paged_kv_cache_202_amd as pkv
+from oracle import attention as oatt
+from oracle import native
+from oracle.pool import PagedPool
+from synth import workloads as wl
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def storage(t: torch.Tensor) -> np.ndarray:
+    """Host storage view: float32 array, or uint16 bit patterns for bf16."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def nan_fill(shape, dtype, device):
+    t = torch.empty(shape, dtype=TORCH_DT[dtype], device=device)
+    if dtype == "bf16":
+        t.view(torch.int16).fill_(-1)  # 0xFFFF: a NaN pattern
+    else:
+        t.fill_(float("nan"))
+    return t
+
+
+class Case:
+    """One paged-attention batch, built independently by oracle and library."""
+
+    def __init__(self, lens, Hq, Hkv, D, bs, dtype, nq=1, num_blocks=None, seed=0,
+                 stack_seed=None, device="cuda:0", partition_tokens=0, scale=None,
+                 stack=None, root=None):
+        self.lens = [int(n) for n in lens]
+        self.Hq, self.Hkv, self.D, self.bs, self.dtype, self.nq = Hq, Hkv, D, bs, dtype, nq
+        self.B = len(self.lens)
+        self.num_blocks = num_blocks or sum(-(-n // bs) for n in self.lens) + 5
+        self.partition_tokens = partition_tokens
+        self.scale = scale if scale is not None else 1.0 / math.sqrt(D)
+        self.device = device
+        rng = np.random.default_rng(seed)
+        if stack is None and stack_seed is not None:
+            stack = np.random.default_rng(stack_seed).permutation(self.num_blocks)
+        if stack is not None:
+            stack = np.asarray(stack, dtype=np.int32)
+        if root is None:
+            root = wl.root_seed(rng)
+        T = sum(self.lens)
+        self.k_new = wl.cast(wl.normal_array(root, 0, (T, Hkv, D)), dtype)
+        self.v_new = wl.cast(wl.normal_array(root, 1, (T, Hkv, D)), dtype)
+        self.q = wl.cast(wl.normal_array(root, 2, (self.B, nq, Hq, D)), dtype)
+        self.max_blocks = max(1, max(-(-n // bs) for n in self.lens))
+
+        # ---- oracle side -------------------------------------------------
+        opool = PagedPool(self.num_blocks, bs, None if stack is None else stack.tolist())
+        o_slots = []
+        for b, n in enumerate(self.lens):
+            opool.create(b)
+            s, cow = opool.append(b, n)
+            assert not cow
+            o_slots += s
+        self.o_slots = np.array(o_slots, dtype=np.int32)
+        tables, lens_ = opool.block_tables(range(self.B), self.max_blocks)
+        self.o_tables = np.array(tables, dtype=np.int32)
+        self.o_lens = np.array(lens_, dtype=np.int32)
+        shape = (self.num_blocks, Hkv, bs, D)
+        npdt = np.float32 if dtype == "f32" else np.uint16
+        self.o_kpool = np.zeros(shape, dtype=npdt)
+        self.o_vpool = np.zeros(shape, dtype=npdt)
+        oatt.cache_write(self.o_kpool, self.o_vpool, storage(self.k_new), storage(self.v_new),
+                         self.o_slots, bs)
+        self.opool = opool
+
+        # ---- library side --------------------------------------------------
+        self.pool = pkv.PagedKVPool(self.num_blocks, bs, stack)
+        for b in range(self.B):
+            self.pool.seq_create(b)
+        slots, pairs = self.pool.alloc_batch(list(range(self.B)), self.lens)
+        assert pairs.shape[0] == 0
+        self.slots = slots
+        t, l = self.pool.block_tables(list(range(self.B)), self.max_blocks)
+        self.tables_host, self.lens_host = t, l
+        dev = device
+        self.k_cache = nan_fill(shape, dtype, dev)
+        self.v_cache = nan_fill(shape, dtype, dev)
+        self.d_slots = torch.from_numpy(slots.copy()).to(dev)
+        self.d_tables = torch.from_numpy(t.copy()).to(dev)
+        self.d_lens = torch.from_numpy(l.copy()).to(dev)
+        self.d_q = self.q.to(dev)
+        if T:
+            pkv.paged_cache_write(self.k_new.to(dev), self.v_new.to(dev), self.k_cache,
+                                  self.v_cache, self.d_slots)
+
+    # ------------------------------------------------------------------
+    def run_gpu(self, partition_tokens=None, with_lse=True):
+        part = self.partition_tokens if partition_tokens is None else partition_tokens
+        out = torch.full((self.B, self.nq, self.Hq, self.D), float("nan"),
+                         dtype=torch.float32, device=self.device)
+        lse = torch.full((self.B, self.nq, self.Hq), float("nan"), dtype=torch.float32,
+                         device=self.device) if with_lse else None
+        ws_bytes = pkv.paged_attention_workspace_size(self.B, self.nq, self.Hq, self.Hkv,
+                                                      self.D, self.max_blocks, self.bs, part)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=self.device) \
+            if ws_bytes else None
+        pkv.paged_attention_decode(out, self.d_q, self.k_cache, self.v_cache, self.d_tables,
+                                   self.d_lens, self.scale, partition_tokens=part,
+                                   workspace=ws, lse=lse)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), (lse.cpu().numpy() if lse is not None else None)
+
+    def run_oracle(self, rows=None, use_c=True):
+        q = storage(self.q)
+        if use_c:
+            return native.attention(q, self.dtype, self.o_kpool, self.o_vpool, self.dtype,
+                                    self.o_tables, self.o_lens, self.scale, self.bs, rows=rows)
+        assert rows is None
+        return oatt.attention(q, self.dtype, self.o_kpool, self.o_vpool, self.dtype,
+                              self.o_tables, self.o_lens, self.scale, self.bs)
+
+    def live_slot_mask(self):
+        """Bool [num_blocks, bs]: slots some sequence reads (the oracle's view)."""
+        live = np.zeros((self.num_blocks, self.bs), dtype=bool)
+        for b, n in enumerate(self.lens):
+            for t in range(n):
+                live[self.o_tables[b][t // self.bs], t % self.bs] = True
+        return live
+
+
+def tolerance(dtype: str) -> float:
+    """Max-abs bound on the output: 1e-5 for fp32 caches, 1e-2 for bf16 caches."""
+    return 1e-5 if dtype == "f32" else 1e-2

@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path against the float64 oracle (run on an MI355X).
+
+Every case is built on both sides from the same seeded synthetic inputs
+(tests/scenario.py). Slots, block tables and cache contents must match bit
+for bit; attention output must be within max-abs 1e-5 (fp32 caches) or 1e-2
+(bf16 caches) of the float64 oracle, which is the target stated for this
+library. Unwritten cache slots start as NaN so that any read of a slot past a
+sequence's end shows up.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_202_amd as pkv
+from scenario import Case, storage, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_case(case: Case, partition_tokens=None, use_c=True):
+    say(f"case lens={case.lens[:8]} Hq={case.Hq} Hkv={case.Hkv} D={case.D} "
+        f"dtype={case.dtype} nq={case.nq} part={partition_tokens}")
+    # indexing: bit-exact
+    assert np.array_equal(case.slots, case.o_slots)
+    assert np.array_equal(case.tables_host, case.o_tables)
+    assert np.array_equal(case.lens_host, case.o_lens)
+    out, lse = case.run_gpu(partition_tokens)
+    ref, ref_lse = case.run_oracle(use_c=use_c)
+    err = np.abs(out - ref).max()
+    lerr = np.abs(lse - ref_lse).max()
+    say(f"  max-abs out err {err:.3e}, lse err {lerr:.3e}")
+    assert np.isfinite(out).all()
+    assert err <= tolerance(case.dtype)
+    assert lerr <= tolerance(case.dtype)
+    return out, lse
+
+
+def test_tiny_fp32_workload(device):
+    """Tiny fp32 workload: lengths 6/9/17/33, Hq 4, Hkv 2, D 64, shuffled 16-block pool."""
+    from synth.workloads import WORKLOADS, free_stack_permutation, root_seed
+
+    w = WORKLOADS["tiny_f32"]
+    rng = np.random.default_rng(w.rng_seed)
+    stack = free_stack_permutation(rng, w.num_blocks)
+    case = Case(w.lengths, w.q_heads, w.kv_heads, w.head_dim, w.block_size, w.dtype,
+                num_blocks=w.num_blocks, stack=stack, root=root_seed(rng))
+    out, _ = check_case(case, use_c=False)
+    # cache contents: bit-exact on live slots
+    live = case.live_slot_mask()
+    for gpu_pool, o_pool in ((case.k_cache, case.o_kpool), (case.v_cache, case.o_vpool)):
+        g = storage(gpu_pool)
+        for h in range(case.Hkv):
+            assert np.array_equal(g[:, h][live].view(np.uint32), o_pool[:, h][live].view(np.uint32))
+
+
+CASES = [
+    # lens, Hq, Hkv, D, dtype, nq, partition
+    ((1, 15, 16, 17, 100, 333), 8, 8, 128, "bf16", 1, 0),
+    ((5, 64, 129, 700, 1025), 32, 8, 128, "bf16", 1, 0),
+    ((5, 64, 129, 700, 1025), 32, 8, 128, "bf16", 1, 64),
+    ((2049, 77, 1), 64, 8, 128, "bf16", 1, 256),
+    ((31, 480, 1000), 16, 8, 64, "bf16", 1, 128),
+    ((31, 480, 1000), 8, 2, 256, "bf16", 1, 0),
+    ((31, 480, 1000), 8, 2, 256, "bf16", 1, 64),
+    ((6, 9, 17, 33, 300), 4, 2, 64, "f32", 1, 0),
+    ((6, 9, 17, 33, 300), 4, 2, 64, "f32", 1, 32),
+    ((40, 515), 16, 2, 128, "f32", 1, 64),
+    ((40, 515), 4, 4, 256, "f32", 1, 0),
+    ((18, 200, 64), 8, 4, 128, "bf16", 2, 0),
+    ((18, 200, 64), 8, 4, 128, "bf16", 4, 48),
+    ((18, 200, 64), 8, 8, 128, "bf16", 3, 0),
+    ((18, 200, 64), 8, 8, 64, "f32", 8, 32),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_decode_matches_oracle(device, ci):
+    lens, Hq, Hkv, D, dtype, nq, part = CASES[ci]
+    case = Case(lens, Hq, Hkv, D, 16, dtype, nq=nq, seed=500 + ci, stack_seed=ci,
+                partition_tokens=part)
+    check_case(case, part)
+
+
+def test_partition_sizes_agree(device):
+    case = Case((3000, 1234), 32, 8, 128, 16, "bf16", seed=77, stack_seed=4)
+    outs = [case.run_gpu(p)[0] for p in (0, 512, 256, 128, 64, 16, 3008)]
+    ref, _ = case.run_oracle()
+    for o in outs:
+        assert np.abs(o - ref).max() <= 1e-2
+    for o in outs[1:]:
+        assert np.abs(o - outs[0]).max() <= 1e-5  # fp32 rounding order only
+
+
+def test_placement_invariance_is_bitwise(device):
+    a = Case((700, 33, 1500), 32, 8, 128, 16, "bf16", seed=9, stack_seed=1, num_blocks=300)
+    b = Case((700, 33, 1500), 32, 8, 128, 16, "bf16", seed=9, stack_seed=2, num_blocks=300)
+    assert not np.array_equal(a.tables_host, b.tables_host)
+    oa, la = a.run_gpu()
+    ob, lb = b.run_gpu()
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
+def test_single_token_context_returns_its_value(device):
+    case = Case((1, 1, 1), 8, 2, 128, 16, "bf16", seed=3, stack_seed=3)
+    out, _ = case.run_gpu()
+    v = case.v_new.float().numpy()  # [T, Hkv, D]
+    for b in range(3):
+        for h in range(8):
+            assert np.array_equal(out[b, 0, h], v[b, h // 4])
+
+
+def test_invalid_rows_are_nan_not_faults(device):
+    """Zero length, a table entry out of range, or a length past the table -> NaN rows."""
+    case = Case((40, 40, 40, 40), 8, 2, 128, 16, "bf16", seed=5, stack_seed=5,
+                num_blocks=20)
+    lens = case.lens_host.copy()
+    tables = case.tables_host.copy()
+    lens[0] = 0
+    tables[1, 1] = 10_000  # second block of sequence 1
+    lens[2] = case.max_blocks * 16 + 1
+    case.d_lens = torch.from_numpy(lens).to(device)
+    case.d_tables = torch.from_numpy(tables).to(device)
+    for part in (0, 16):
+        out, lse = case.run_gpu(part)
+        for b in (0, 1, 2):
+            assert np.isnan(out[b]).all() and np.isnan(lse[b]).all()
+        assert np.isfinite(out[3]).all()
+        ref, _ = case.run_oracle(rows=np.arange(3 * 8, 4 * 8))
+        assert np.abs(out[3, 0] - ref).max() <= 1e-2
+
+
+def test_cache_write_skips_negative_and_out_of_range_slots(device):
+    T, Hkv, D, bs, NB = 6, 2, 64, 16, 2
+    k = torch.randn(T, Hkv, D, device=device).to(torch.bfloat16)
+    v = torch.randn(T, Hkv, D, device=device).to(torch.bfloat16)
+    kc = torch.zeros(NB, Hkv, bs, D, dtype=torch.bfloat16, device=device)
+    vc = torch.zeros_like(kc)
+    slots = torch.tensor([0, -1, 17, NB * bs, 31, -5], dtype=torch.int32, device=device)
+    pkv.paged_cache_write(k, v, kc, vc, slots)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[0, :, 0], k[0]) and torch.equal(vc[1, :, 1], v[2])
+    assert torch.equal(kc[1, :, 15], k[4])
+    written = torch.zeros(NB, bs, dtype=torch.bool)
+    written[0, 0] = written[1, 1] = written[1, 15] = True
+    assert (kc.cpu()[~written[:, None, :].expand(NB, Hkv, bs)] == 0).all()
+
+
+def test_copy_on_write_step_bit_exact(device):
+    """Fork + appends that copy shared partial blocks, then decode; vs the oracle."""
+    from oracle import attention as oatt
+    from oracle import native
+    from oracle.pool import PagedPool
+    from synth import workloads as wl
+
+    Hq, Hkv, D, bs, NB, dtype = 8, 2, 128, 16, 64, "bf16"
+    stack = np.random.default_rng(12).permutation(NB).astype(np.int32)
+    lib = pkv.PagedKVPool(NB, bs, stack)
+    ora = PagedPool(NB, bs, stack.tolist())
+    shape = (NB, Hkv, bs, D)
+    kc = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+    vc = torch.zeros_like(kc)
+    okp = np.zeros(shape, np.uint16)
+    ovp = np.zeros(shape, np.uint16)
+    root = 4242
+    stream_id = [10]
+
+    def step(seq_ids, counts):
+        slots, pairs = lib.alloc_batch(seq_ids, counts)
+        o_slots, o_pairs = [], []
+        for s, n in zip(seq_ids, counts):
+            sl, cw = ora.append(s, n)
+            o_slots += sl
+            o_pairs += cw
+        assert slots.tolist() == o_slots and [tuple(p) for p in pairs.tolist()] == o_pairs
+        T = sum(counts)
+        kn = wl.cast(wl.normal_array(root, stream_id[0], (T, Hkv, D)), dtype)
+        vn = wl.cast(wl.normal_array(root, stream_id[0] + 1, (T, Hkv, D)), dtype)
+        stream_id[0] += 2
+        if len(pairs):
+            pkv.paged_kv_copy_blocks(kc, vc, torch.from_numpy(pairs).to(device))
+            for src, dst in o_pairs:  # oracle: the whole block is copied
+                okp[dst] = okp[src]
+                ovp[dst] = ovp[src]
+        pkv.paged_cache_write(kn.to(device), vn.to(device), kc, vc,
+                              torch.from_numpy(slots).to(device))
+        oatt.cache_write(okp, ovp, storage(kn), storage(vn), o_slots, bs)
+
+    lib.seq_create(0)
+    ora.create(0)
+    step([0], [40])  # parent: 2 full blocks + 8 tokens
+    for c in (1, 2, 3):
+        lib.fork(0, c, 40)
+        ora.share_prefix(0, c, 40)
+    step([0, 1, 2, 3], [3, 5, 20, 1])  # 3 copies (parent first), last writer in place
+    ids = [0, 1, 2, 3]
+    maxb = max(len(ora.page_table(s)) for s in ids)
+    tables, lens = lib.block_tables(ids, maxb)
+    ot, ol = ora.block_tables(ids, maxb)
+    assert tables.tolist() == ot and lens.tolist() == ol
+    torch.cuda.synchronize()
+    live = np.zeros((NB, bs), bool)
+    for s in ids:
+        for t in range(ora.sequence_length(s)):
+            live[ot[s][t // bs], t % bs] = True
+    g = storage(kc)
+    for h in range(Hkv):
+        assert np.array_equal(g[:, h][live], okp[:, h][live])
+    q = wl.cast(wl.normal_array(root, 99, (4, 1, Hq, D)), dtype)
+    out = torch.empty(4, 1, Hq, D, device=device)
+    pkv.paged_attention_decode(out, q.to(device), kc, vc, torch.from_numpy(tables).to(device),
+                               torch.from_numpy(lens).to(device), 1 / math.sqrt(D))
+    ref, _ = native.attention(storage(q), dtype, okp, ovp, dtype, np.array(ot, np.int32),
+                              np.array(ol, np.int32), 1 / math.sqrt(D), bs)
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-2
