@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Paged-attention decode benchmark on one MI355X.
+
+Default workload: one attention layer of Llama-3-8B geometry (32 query heads,
+8 KV heads, head dim 128, bf16 K/V, 16-token blocks), 32 sequences at context
+8192, one decode token each, physical blocks placed by a seeded permutation of
+a 16384-block pool.
+
+A step is the whole hot path for one batch: the slot-mapped cache write of
+each sequence's new K/V token, then paged attention over all 8192 tokens
+(partition kernel + log-sum-exp reduce). The host allocator ran before the
+timed region (its cost is reported separately) and the block tables are
+already resident in HBM.
+
+Prints ONE JSON line. ``value`` is decode tokens/s (one token per sequence
+per step) for the one GPU; ``roofline`` reports the attention call's achieved
+HBM bandwidth from its algorithmic bytes and its event-timed duration;
+``cpu_baseline`` times the float64 C oracle on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, decimal GB/s
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(B, nq, Hq, Hkv, D, es, lens, max_blocks, with_lse=False):
+    """Bytes the attention call must move at minimum: every visible K and V
+    element once per KV head, q read, fp32 out written, block-table entries
+    and context lengths read."""
+    kv = 2 * Hkv * D * es * int(np.sum(lens))
+    q = B * nq * Hq * D * es
+    out = B * nq * Hq * D * 4 + (B * nq * Hq * 4 if with_lse else 0)
+    tables = 4 * int(np.sum(-(-np.asarray(lens) // 16)))
+    return kv + q + out + tables + 4 * B
+
+
+class Workload:
+    """Device state for one workload, built through the library only."""
+
+    def __init__(self, name: str, rotate: int, device):
+        import torch
+
+        import paged_kv_cache_202_amd as pkv
+        from synth import workloads as wl
+
+        self.w = w = wl.WORKLOADS[name]
+        self.torch, self.pkv = torch, pkv
+        rng = np.random.default_rng(w.rng_seed)
+        stack = wl.free_stack_permutation(rng, w.num_blocks)
+        lens = wl.draw_lengths(rng, w)
+        root = wl.root_seed(rng)
+        self.stack, self.lens, self.root = stack, lens, root
+        B, Hq, Hkv, D, bs, nq = w.batch, w.q_heads, w.kv_heads, w.head_dim, w.block_size, \
+            w.queries_per_seq
+        self.B, self.Hq, self.Hkv, self.D, self.bs, self.nq = B, Hq, Hkv, D, bs, nq
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.es = w.esize
+        # context tokens cached before the step, then nq new tokens per sequence
+        pre = lens - nq
+        t0 = time.perf_counter()
+        T = int(lens.sum())
+        k_all = wl.cast(wl.normal_array(root, 0, (T, Hkv, D)), w.dtype)
+        v_all = wl.cast(wl.normal_array(root, 1, (T, Hkv, D)), w.dtype)
+        q = wl.cast(wl.normal_array(root, 2, (B, nq, Hq, D)), w.dtype)
+        log(f"[bench] generated {T} tokens of K/V in {time.perf_counter() - t0:.1f}s")
+        self.host_k, self.host_v, self.host_q = k_all, v_all, q
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        pre_idx = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, pre)])
+        new_idx = np.concatenate([np.arange(s + n, s + n + nq) for s, n in zip(starts, pre)])
+
+        pool = pkv.PagedKVPool(w.num_blocks, bs, stack)
+        ids = list(range(B))
+        for b in ids:
+            pool.seq_create(b)
+        t0 = time.perf_counter()
+        pre_slots, cow = pool.alloc_batch(ids, pre.tolist())
+        self.alloc_prefill_s = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        step_slots, cow2 = pool.alloc_batch(ids, [nq] * B)
+        self.alloc_step_s = time.perf_counter() - t0
+        assert cow.shape[0] == 0 and cow2.shape[0] == 0
+        self.max_blocks = int(max(-(-lens // bs)))
+        tables, clens = pool.block_tables(ids, self.max_blocks)
+        assert np.array_equal(clens, lens)
+        self.pool = pool
+        dev = device
+        shape = (w.num_blocks, Hkv, bs, D)
+        self.kc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
+        self.vc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
+        kpre = k_all[torch.from_numpy(pre_idx)].to(dev)
+        vpre = v_all[torch.from_numpy(pre_idx)].to(dev)
+        d_pre_slots = torch.from_numpy(pre_slots).to(dev)
+        for i in range(rotate):
+            pkv.paged_cache_write(kpre, vpre, self.kc[i], self.vc[i], d_pre_slots)
+        del kpre, vpre
+        self.k_step = k_all[torch.from_numpy(new_idx)].to(dev)
+        self.v_step = v_all[torch.from_numpy(new_idx)].to(dev)
+        self.d_step_slots = torch.from_numpy(step_slots).to(dev)
+        self.d_tables = torch.from_numpy(tables).to(dev)
+        self.d_lens = torch.from_numpy(clens).to(dev)
+        self.d_q = q.to(dev)
+        self.tables_host = tables
+        self.out = torch.empty((B, nq, Hq, D), dtype=torch.float32, device=dev)
+        self.scale = 1.0 / math.sqrt(D)
+        self.part = w.partition_tokens
+        ws = pkv.paged_attention_workspace_size(B, nq, Hq, Hkv, D, self.max_blocks, bs,
+                                                self.part)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
+        self.rotate = rotate
+        torch.cuda.synchronize()
+
+    def cache_write(self, i: int) -> None:
+        r = i % self.rotate
+        self.pkv.paged_cache_write(self.k_step, self.v_step, self.kc[r], self.vc[r],
+                                   self.d_step_slots)
+
+    def attend(self, i: int) -> None:
+        r = i % self.rotate
+        self.pkv.paged_attention_decode(self.out, self.d_q, self.kc[r], self.vc[r],
+                                        self.d_tables, self.d_lens, self.scale,
+                                        partition_tokens=self.part, workspace=self.ws)
+
+    def step(self, i: int) -> None:
+        self.cache_write(i)
+        self.attend(i)
+
+    def attention_bytes(self) -> int:
+        return algorithmic_bytes(self.B, self.nq, self.Hq, self.Hkv, self.D, self.es,
+                                 self.lens, self.max_blocks)
+
+    def cache_write_bytes(self) -> int:
+        return 2 * 2 * self.B * self.nq * self.Hkv * self.D * self.es + 4 * self.B * self.nq
+
+
+def cpu_baseline(wk: Workload, budget_s: float = 20.0) -> dict:
+    """The float64 C oracle on the host cores, on its own allocator and pool."""
+    from oracle import attention as oatt
+    from oracle import native
+    from oracle.pool import PagedPool
+
+    w = wk.w
+    threads = len(os.sched_getaffinity(0))
+    native.build(force=False)
+    t0 = time.perf_counter()
+    opool = PagedPool(w.num_blocks, wk.bs, wk.stack.tolist())
+    slots = []
+    for b, n in enumerate(wk.lens.tolist()):
+        opool.create(b)
+        slots += opool.append(b, n)[0]
+    tables, lens = opool.block_tables(range(wk.B), wk.max_blocks)
+    npdt = np.uint16 if w.dtype == "bf16" else np.float32
+    shape = (w.num_blocks, wk.Hkv, wk.bs, wk.D)
+    kp = np.zeros(shape, npdt)
+    vp = np.zeros(shape, npdt)
+
+    def st(t):
+        t = t.contiguous()
+        return t.view(wk.torch.int16).numpy().view(np.uint16) if w.dtype == "bf16" else t.numpy()
+
+    oatt.cache_write(kp, vp, st(wk.host_k), st(wk.host_v), slots, wk.bs)
+    q = st(wk.host_q)
+    log(f"[bench] oracle pool built in {time.perf_counter() - t0:.1f}s")
+    tables = np.array(tables, np.int32)
+    lens = np.array(lens, np.int32)
+    rows_total = wk.B * wk.nq * wk.Hq
+    # time one sequence's rows first, then size the sample to the budget
+    probe = np.arange(wk.nq * wk.Hq, dtype=np.int64)
+    t0 = time.perf_counter()
+    native.attention(q, w.dtype, kp, vp, w.dtype, tables, lens, wk.scale, wk.bs, rows=probe,
+                     threads=threads)
+    t_seq = time.perf_counter() - t0
+    n_seq = int(max(1, min(wk.B, budget_s / 3 / max(t_seq, 1e-6))))
+    rows = np.arange(n_seq * wk.nq * wk.Hq, dtype=np.int64)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        native.attention(q, w.dtype, kp, vp, w.dtype, tables, lens, wk.scale, wk.bs, rows=rows,
+                         threads=threads)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    tok_s = n_seq * wk.nq / med
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"float64 C oracle walking block tables token by token, OpenMP over "
+                      f"rows; {n_seq} of {wk.B} sequences (all {wk.Hq} heads, full context), "
+                      f"median of 3 runs of {med:.2f}s; rows {len(rows)} of {rows_total}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b_b32_8k")
+    ap.add_argument("--rotate", type=int, default=2,
+                    help="pool copies used in turn so repeats cannot hit the 256 MB cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own pool and sequences with no exchange).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    wk = Workload(args.workload, args.rotate, dev)
+    log(f"[bench] workload {args.workload} ready; max_blocks {wk.max_blocks}")
+
+    for i in range(args.warmup):
+        wk.step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        wk.step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step")
+
+    # per-call durations with events on the launch stream (same steps again)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        a, b, c = ev[i]
+        a.record()
+        wk.cache_write(i)
+        b.record()
+        wk.attend(i)
+        c.record()
+    torch.cuda.synchronize()
+    attn_ms = statistics.mean(b.elapsed_time(c) for a, b, c in ev)
+    write_ms = statistics.mean(a.elapsed_time(b) for a, b, c in ev)
+    attn_bytes = wk.attention_bytes()
+    achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    log(f"[bench] attention {attn_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; cache write "
+        f"{write_ms * 1e3:.1f} us")
+
+    result = {
+        "metric": "paged-attn decode tokens/s + achieved HBM GB/s (% of peak), 1 MI355X",
+        "value": wk.B * wk.nq / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wk.w.dtype,
+        "data": "synthetic",
+        "config": {"workload": wk.w.name, "batch": wk.B, "context": int(wk.lens.max()),
+                   "q_heads": wk.Hq, "kv_heads": wk.Hkv, "head_dim": wk.D,
+                   "block_size": wk.bs, "queries_per_seq": wk.nq,
+                   "kv_dtype": wk.w.dtype, "pool_blocks": wk.w.num_blocks,
+                   "placement": "seeded permutation", "pool_rotation": args.rotate},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "paged_attention_decode (partition + reduce launches)",
+                     "algorithmic_bytes": attn_bytes, "avg_duration_us": attn_ms * 1e3},
+        "step_breakdown_us": {"cache_write": write_ms * 1e3, "attention": attn_ms * 1e3},
+        "host_alloc_us": {"step_alloc": wk.alloc_step_s * 1e6},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wk)
+        log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-SOURCES = ["pool.cpp", "cache_ops.hip", "decode.hip"]
+SOURCES = ["pool.cpp", "cache_ops.hip", "decode.hip"] + [
+    f"decode_inst_{dt}_d{d}.hip" for dt in ("f32", "bf16") for d in (64, 128, 256)]
 ARCH = "gfx950"
 
 
@@ -52,7 +53,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
