@@ -65,38 +65,52 @@ int next_pow2(int x) {
   return p;
 }
 
-// Launch plan: wavefronts per workgroup, partition size in tokens, and the
-// number of partitions. The chip holds about kResidentWaves of these
-// wavefronts at once (256 CUs x 4 SIMDs x 2 wavefronts at ~190 VGPRs); the
-// plan aims for one such round of long-running wavefronts, each streaming
-// many tiles, and only splits a context into partitions when there are too
-// few (sequence, KV head) pairs to fill the chip.
+// Launch plan. The chip holds about kResidentWaves decode wavefronts at once
+// (256 CUs x 4 SIMDs x 2 wavefronts at ~190-230 VGPRs each).
+//  * Workgroup-split (waves = 4 or 8): one partition per (sequence, KV head)
+//    when those pairs alone fill a round of long-running wavefronts; no
+//    workspace, no reduce launch.
+//  * Work items (waves = 0): contexts split into partitions of P tokens;
+//    kResidentWaves persistent wavefronts stream the (sequence, KV head,
+//    partition) items back to back and a reduce launch merges the partials.
+//    Used when a partition size is requested or the pairs are too few.
 constexpr int64_t kResidentWaves = 2048;
+constexpr int64_t kMaxItemSeqs = 16000;  // LDS holds the per-sequence prefix
 
 struct Plan {
-  int waves;
+  int waves;  // 4 or 8: workgroup-split kernel; 0: work-item kernel
   int32_t part_tokens;
   int32_t num_parts;
+  int32_t grid_x;  // work items: persistent workgroups
 };
 
-Plan plan_launch(int64_t units, int64_t max_ctx, int32_t req) {
+Plan plan_launch(int64_t B, int64_t Hkv, int64_t max_ctx, int32_t req) {
   Plan pl{};
-  const int64_t tiles = (max_ctx + kTile - 1) / kTile;
+  const int64_t units = B * Hkv;
   int64_t P;
   if (req > 0) {
     P = req;
+  } else if (units * 8 >= kResidentWaves || B > kMaxItemSeqs) {
+    P = (max_ctx + kTile - 1) / kTile * kTile;  // one partition per pair
   } else {
-    int64_t np = kResidentWaves / (units * 8);
-    const int64_t cap = tiles / 64;  // at least 64 tiles per partition
-    if (np > cap) np = cap;
-    if (np < 1) np = 1;
+    // about two items per resident wavefront, at least 256 tokens each
+    int64_t np = (2 * kResidentWaves + units - 1) / units;
     P = ((max_ctx + np - 1) / np + kTile - 1) / kTile * kTile;
+    if (P < 256) P = 256;
   }
   pl.part_tokens = (int32_t)P;
   pl.num_parts = (int32_t)((max_ctx + P - 1) / P);
   if (pl.num_parts < 1) pl.num_parts = 1;
-  const int64_t tiles_per_part = (P + kTile - 1) / kTile;
-  pl.waves = (tiles_per_part >= 64 && units * pl.num_parts * 8 <= 2 * kResidentWaves) ? 8 : 4;
+  if (pl.num_parts > 1 && B <= kMaxItemSeqs) {
+    pl.waves = 0;
+    int64_t waves = units * pl.num_parts;
+    if (waves > kResidentWaves) waves = kResidentWaves;
+    pl.grid_x = (int32_t)((waves + kItemWaves - 1) / kItemWaves);
+  } else {
+    const int64_t tiles_per_part = (P + kTile - 1) / kTile;
+    pl.waves = (tiles_per_part >= 64 && units * pl.num_parts * 8 <= 2 * kResidentWaves) ? 8 : 4;
+    pl.grid_x = pl.num_parts;
+  }
   return pl;
 }
 
@@ -160,7 +174,7 @@ extern "C" int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
                                               int32_t part, size_t *bytes) {
   if (!bytes) return fail(PKV_EINVAL, "bytes is NULL");
   if (int rc = check_sizes(B, nq, Hq, Hkv, D, max_blocks, bs, part)) return rc;
-  const Plan pl = plan_launch((int64_t)B * Hkv, (int64_t)max_blocks * bs, part);
+  const Plan pl = plan_launch(B, Hkv, (int64_t)max_blocks * bs, part);
   *bytes = pl.num_parts == 1 ? 0 : partial_bytes((int64_t)B * nq * Hq, pl.num_parts, D);
   return PKV_OK;
 }
@@ -181,7 +195,7 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   for (const void *p : {(const void *)out, q, k_cache, v_cache})
     if ((uintptr_t)p % 16) return fail(PKV_EINVAL, "out, q, K and V must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
-  const Plan pl = plan_launch((int64_t)B * Hkv, (int64_t)max_blocks * bs, part);
+  const Plan pl = plan_launch(B, Hkv, (int64_t)max_blocks * bs, part);
   const int32_t P = pl.part_tokens, NP = pl.num_parts;
   const int G = Hq / Hkv;
   const int RP = G * next_pow2(nq);
@@ -195,6 +209,7 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   a.vc = v_cache;
   a.tables = block_tables;
   a.lens = context_lens;
+  a.B = B;
   a.max_blocks = max_blocks;
   a.nq = nq;
   a.Hq = Hq;
@@ -219,7 +234,7 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
     a.part_l = (float *)w;
   }
   hipStream_t s = (hipStream_t)stream;
-  launch(a, dim3(NP, Hkv, B), s);
+  launch(a, pl.waves ? dim3(NP, Hkv, B) : dim3(pl.grid_x), s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (NP > 1) {

@@ -9,7 +9,9 @@ Launcher pick_rows<PKV_F32, 128>(int G, int RP, int W) {
   constexpr int DT = PKV_F32, D = 128;
 #define PKV_CASE(g, rp)                                                  \
   if (G == g && RP == rp)                                                \
-    return W == 8 ? &launch_decode<DT, D, g, rp, 8> : &launch_decode<DT, D, g, rp, 4>;
+    return W == 8   ? &launch_decode<DT, D, g, rp, 8>                   \
+           : W == 4 ? &launch_decode<DT, D, g, rp, 4>                   \
+                    : &launch_decode<DT, D, g, rp, 0>;
   PKV_CASE(1, 1) PKV_CASE(1, 2) PKV_CASE(1, 4) PKV_CASE(1, 8)
   PKV_CASE(2, 2) PKV_CASE(2, 4) PKV_CASE(2, 8)
   PKV_CASE(4, 4) PKV_CASE(4, 8)

@@ -40,6 +40,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <type_traits>
 
 #include "pagedkv.h"
 
@@ -71,6 +72,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
 }
 
 template <int M>
@@ -168,7 +178,7 @@ struct DecodeArgs {
   const void *vc;
   const int32_t *tables;
   const int32_t *lens;
-  int32_t max_blocks, nq, Hq, Hkv, bs, num_blocks, part_tokens, num_parts;
+  int32_t B, max_blocks, nq, Hq, Hkv, bs, num_blocks, part_tokens, num_parts;
   float scale_log2;
 };
 
@@ -201,18 +211,6 @@ __device__ __forceinline__ void reduce_scatter(float (&x)[V], int jl) {
   }
 }
 
-// Broadcast of the V weights of a token group to all its lanes: weight v
-// lives in lane v / C (component v % C), or lane v * DUP when lanes
-// duplicate a weight.
-template <int LPT, int V, int C, int DUP, int v = 0>
-__device__ __forceinline__ void gather_weights(float (&pa)[V], const float (&pw)[C], int lane) {
-  if constexpr (v < V) {
-    constexpr int src = V >= LPT ? v / C : v * DUP;
-    pa[v] = group_bcast<LPT, src>(pw[v % C], lane);
-    gather_weights<LPT, V, C, DUP, v + 1>(pa, pw, lane);
-  }
-}
-
 template <int M, int LPT, int RP, int EPL>
 __device__ __forceinline__ void sum_over_groups(float (&acc)[RP][EPL]) {
   if constexpr (M < 64) {
@@ -242,111 +240,80 @@ __device__ __forceinline__ void load_tile(uint4 (&kr)[NL], uint4 (&vr)[NL], cons
   for (int i = 0; i < NL; ++i) vr[i] = stream_load(vp + i * 1024);
 }
 
-template <int DT, int D, int G, int RP, int kWaves>
-__global__ void __launch_bounds__(kWaves * 64)
-decode_partition_kernel(const DecodeArgs a) {
+// ---------------------------------------------------------------------------
+// One wavefront's attention state for RP query rows of one KV head:
+// queries, running max / sum and fp32 accumulators, and the per-tile math.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G, int RP>
+struct DecodeWave {
   using Gm = Geo<DT, D>;
-  constexpr int LPT = Gm::LPT, TPL = Gm::TPL, NL = Gm::NL, EPL = Gm::EPL;
-  constexpr int V = RP * NL;                    // partial sums per lane per tile
-  constexpr int C = V >= LPT ? V / LPT : 1;     // whole scores per lane
-  constexpr int DUP = V >= LPT ? 1 : LPT / V;   // lanes holding the same score
-  constexpr float kNegInf = -std::numeric_limits<float>::infinity();
-  constexpr int kStride = kWaves * kTile;       // tokens between a wavefront's tiles
+  static constexpr int LPT = Gm::LPT, TPL = Gm::TPL, NL = Gm::NL, EPL = Gm::EPL;
+  static constexpr int V = RP * NL;                   // partial sums per lane per tile
+  static constexpr int C = V >= LPT ? V / LPT : 1;    // whole scores per lane
+  static constexpr int DUP = V >= LPT ? 1 : LPT / V;  // lanes holding the same score
+  static constexpr float kNegInf = -std::numeric_limits<float>::infinity();
 
-  __shared__ float sm_acc[kWaves][RP][D];
-  __shared__ float sm_m[kWaves][RP];
-  __shared__ float sm_l[kWaves][RP];
-  __shared__ int sm_bad[kWaves];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = lane / LPT, jl = lane % LPT;
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int nq = a.nq;
-  const int L = a.lens[b];
-  const int max_ctx = a.max_blocks * a.bs;
-
-  if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
-    if (a.num_parts == 1 && p == 0) {
-      const float nan = __builtin_nanf("");
-      for (int idx = threadIdx.x; idx < RP * D; idx += kWaves * 64) {
-        const int r = idx / D, d = idx % D, qi = r / G;
-        if (qi >= nq) continue;
-        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
-        a.out[row * D + d] = nan;
-        if (d == 0 && a.lse) a.lse[row] = nan;
-      }
-    }
-    return;  // with partitions, the reduce kernel writes the NaN rows
-  }
-  const int t_begin = p * a.part_tokens;
-  if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
-  const int t_end = min(L, t_begin + a.part_tokens);
-
-  // ---- query rows: r = qi * G + gj, head g * G + gj ----------------------
-  const int d0 = jl * EPL;
-  uint32_t qw[RP][EPL / 2 > 0 ? EPL / 2 : 1];  // bf16 pairs
-  float qf[RP][EPL];                           // fp32
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    const int qi = r / G;
-    const size_t row = ((size_t)b * nq + (qi < nq ? qi : 0)) * a.Hq + g * G + (r % G);
-    if constexpr (DT == PKV_BF16) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (qi < nq) w = *reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
-      qw[r][0] = w.x; qw[r][1] = w.y; qw[r][2] = w.z; qw[r][3] = w.w;
-    } else {
-      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (qi < nq) w = *reinterpret_cast<const float4 *>((const float *)a.q + row * D + d0);
-      qf[r][0] = w.x; qf[r][1] = w.y; qf[r][2] = w.z; qf[r][3] = w.w;
-    }
-  }
-
-  // ---- scores this lane owns after the reduce-scatter --------------------
-  const int own = jl * V / LPT;
+  int lane, grp, jl, d0;
+  uint32_t qw[RP][4];  // bf16 query slices, two per word
+  float qf[RP][4];     // fp32 query slices
   int own_row[C], own_tok[C], own_lim[C];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int v = own + c;
-    own_row[c] = v / NL;
-    own_tok[c] = (v % NL) * TPL + grp;       // token offset inside the tile
-    const int qi = own_row[c] / G;
-    own_lim[c] = qi < nq ? L - nq + qi + 1 : 0;  // visible keys of that row
-  }
-
   float acc[RP][EPL];
   float m_run[RP];
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    m_run[r] = kNegInf;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
-  }
   float m_own[C], l_own[C];
+  int L, min_lim;
+  int bad;
+
+  __device__ __forceinline__ void init(int lane_) {
+    lane = lane_;
+    grp = lane / LPT;
+    jl = lane % LPT;
+    d0 = jl * EPL;
+    const int own = jl * V / LPT;
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    m_own[c] = kNegInf;
-    l_own[c] = 0.f;
+    for (int c = 0; c < C; ++c) {
+      const int v = own + c;
+      own_row[c] = v / NL;
+      own_tok[c] = (v % NL) * TPL + grp;  // token offset inside the tile
+    }
   }
 
-  const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
-  int bad = 0;
-  const int min_lim = L - nq + 1;
-  const size_t head_off = (size_t)g * a.bs * Gm::TB + (size_t)lane * 16;
-  const size_t block_bytes = (size_t)a.Hkv * a.bs * Gm::TB;
-  // Byte offset of tile t0 for this lane; bad table entries read block 0.
-  auto tile_offset = [&](int t0, int blk) -> size_t {
-    if (blk < 0 || blk >= a.num_blocks) {
-      bad = 1;
-      blk = 0;
+  // Start a (sequence b, KV head g) item of context length L_: load the
+  // query rows r = qi * G + gj (head g * G + gj) and reset the statistics.
+  __device__ __forceinline__ void begin(const DecodeArgs &a, int b, int g, int L_) {
+    const int nq = a.nq;
+    L = L_;
+    min_lim = L - nq + 1;
+    bad = 0;
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      const int qi = r / G;
+      const size_t row = ((size_t)b * nq + (qi < nq ? qi : 0)) * a.Hq + g * G + (r % G);
+      if constexpr (DT == PKV_BF16) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (qi < nq) w = *reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
+        qw[r][0] = w.x; qw[r][1] = w.y; qw[r][2] = w.z; qw[r][3] = w.w;
+      } else {
+        float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (qi < nq) w = *reinterpret_cast<const float4 *>((const float *)a.q + row * D + d0);
+        qf[r][0] = w.x; qf[r][1] = w.y; qf[r][2] = w.z; qf[r][3] = w.w;
+      }
+      m_run[r] = kNegInf;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
     }
-    return (size_t)blk * block_bytes + head_off + (size_t)(t0 % a.bs) * Gm::TB;
-  };
-  const char *kbase = (const char *)a.kc;
-  const char *vbase = (const char *)a.vc;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int qi = own_row[c] / G;
+      own_lim[c] = qi < nq ? L - nq + qi + 1 : 0;  // visible keys of that row
+      m_own[c] = kNegInf;
+      l_own[c] = 0.f;
+    }
+  }
 
-  // Consume one tile whose K/V rows are in kr / vr.
-  auto process = [&](const uint4 (&kr)[NL], const uint4 (&vr)[NL], int t0) {
+  // Consume one 16-token tile starting at logical token t0 whose K/V rows
+  // are in kr / vr.
+  __device__ __forceinline__ void process(const uint4 (&kr)[NL], const uint4 (&vr)[NL], int t0,
+                                          float scale_log2) {
     // partial q.k over this lane's EPL dims: x[r * NL + i]
     float x[V];
 #pragma unroll
@@ -375,7 +342,7 @@ decode_partition_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool vis = t0 + own_tok[c] < own_lim[c];
-      sc[c] = vis ? x[c] * a.scale_log2 : kNegInf;
+      sc[c] = vis ? x[c] * scale_log2 : kNegInf;
       need |= sc[c] > m_own[c] + kLazyLog2;
     }
     if (__any(need)) {
@@ -412,14 +379,13 @@ decode_partition_kernel(const DecodeArgs a) {
       pw[c] = sc[c] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[c] - m_own[c]);
       l_own[c] += pw[c];
     }
-    // every lane of the group needs all V weights of its tokens
-    float pa[V];
-    gather_weights<LPT, V, C, DUP>(pa, pw, lane);
+    // every lane of the group needs all V weights of its tokens: each is
+    // broadcast from its owner lane right before its FMAs
     // in a tail tile, slots past the context may hold stale bits (even NaN):
     // their V is zeroed so that 0 * NaN cannot reach acc
     const bool tail = t0 + kTile > min_lim;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    static_for<NL>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
       float vv[EPL];
       if constexpr (DT == PKV_BF16) {
         vv[0] = bf16_lo(vr[i].x); vv[1] = bf16_hi(vr[i].x);
@@ -434,13 +400,99 @@ decode_partition_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) vv[e] = 0.f;
       }
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        const float w = pa[r * NL + i];
+      static_for<RP>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        constexpr int v = r * NL + i;
+        constexpr int src = V >= LPT ? v / C : v * DUP;
+        const float w = group_bcast<LPT, src>(pw[v % C], lane);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(w, vv[e], acc[r][e]);
+      });
+    });
+  }
+
+  // Sum acc over the token groups (every lane then holds the totals of its
+  // dims) and return each row's sum of weights.
+  __device__ __forceinline__ void totals(float (&l_row)[RP]) {
+    sum_over_groups<LPT, LPT, RP, EPL>(acc);
+    const bool counted = (jl % DUP) == 0;
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      float xs = 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (own_row[c] == r && counted) xs += l_own[c];
+      l_row[r] = wave_sum(xs);
+    }
+  }
+};
+
+// Byte offset of the 16-token tile at logical token t0 of KV head g in
+// block blk, for this lane.
+template <int TB>
+__device__ __forceinline__ size_t tile_bytes_offset(const DecodeArgs &a, int g, int t0, int blk,
+                                                    int lane) {
+  return ((size_t)blk * a.Hkv + g) * ((size_t)a.bs * TB) + (size_t)(t0 % a.bs) * TB +
+         (size_t)lane * 16;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup-split kernel: one workgroup of kWaves wavefronts per (partition,
+// KV head, sequence); the wavefronts take interleaved tiles and are merged
+// in LDS. Used when there are enough (sequence, KV head) pairs to fill the
+// chip with one partition each.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G, int RP, int kWaves>
+__global__ void __launch_bounds__(kWaves * 64)
+decode_partition_kernel(const DecodeArgs a) {
+  using W = DecodeWave<DT, D, G, RP>;
+  using Gm = Geo<DT, D>;
+  constexpr int NL = Gm::NL, EPL = Gm::EPL;
+  constexpr float kNegInf = -std::numeric_limits<float>::infinity();
+  constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
+
+  __shared__ float sm_acc[kWaves][RP][D];
+  __shared__ float sm_m[kWaves][RP];
+  __shared__ float sm_l[kWaves][RP];
+  __shared__ int sm_bad[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nq = a.nq;
+  const int L = a.lens[b];
+  const int max_ctx = a.max_blocks * a.bs;
+
+  if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
+    if (a.num_parts == 1 && p == 0) {
+      const float nan = __builtin_nanf("");
+      for (int idx = threadIdx.x; idx < RP * D; idx += kWaves * 64) {
+        const int r = idx / D, d = idx % D, qi = r / G;
+        if (qi >= nq) continue;
+        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
+        a.out[row * D + d] = nan;
+        if (d == 0 && a.lse) a.lse[row] = nan;
       }
     }
+    return;  // with partitions, the reduce kernel writes the NaN rows
+  }
+  const int t_begin = p * a.part_tokens;
+  if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
+  const int t_end = min(L, t_begin + a.part_tokens);
+
+  W st;
+  st.init(lane);
+  st.begin(a, b, g, L);
+
+  const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
+  const char *kbase = (const char *)a.kc;
+  const char *vbase = (const char *)a.vc;
+  auto tile_offset = [&](int t0, int blk) -> size_t {
+    if (blk < 0 || blk >= a.num_blocks) {  // bad table entry: read block 0, poison later
+      st.bad = 1;
+      blk = 0;
+    }
+    return tile_bytes_offset<Gm::TB>(a, g, t0, blk, lane);
   };
 
   // Software pipeline: the next tile's K/V loads are in flight while the
@@ -467,54 +519,44 @@ decode_partition_kernel(const DecodeArgs a) {
         const size_t off = tile_offset(tile_t0(k + 1), blk1);
         load_tile<NL>(kb, vb, kbase + off, vbase + off);
       }
-      process(ka, va, tile_t0(k));
+      st.process(ka, va, tile_t0(k), a.scale_log2);
       {
         const size_t off = tile_offset(tile_t0(k + 2), blk2);
         load_tile<NL>(ka, va, kbase + off, vbase + off);
       }
-      process(kb, vb, tile_t0(k + 1));
+      st.process(kb, vb, tile_t0(k + 1), a.scale_log2);
       blk1 = nb1;
       blk2 = nb2;
     }
     if (k + 1 < n_tiles) {
       const size_t off = tile_offset(tile_t0(k + 1), blk1);
       load_tile<NL>(kb, vb, kbase + off, vbase + off);
-      process(ka, va, tile_t0(k));
-      process(kb, vb, tile_t0(k + 1));
+      st.process(ka, va, tile_t0(k), a.scale_log2);
+      st.process(kb, vb, tile_t0(k + 1), a.scale_log2);
     } else {
-      process(ka, va, tile_t0(k));
+      st.process(ka, va, tile_t0(k), a.scale_log2);
     }
   }
 
-  // ---- wavefront totals ---------------------------------------------------
-  sum_over_groups<LPT, LPT, RP, EPL>(acc);
-  const bool counted = (jl % DUP) == 0;
+  // ---- wavefront totals, then merge the wavefronts in LDS ------------------
   float l_row[RP];
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-    float xs = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-      if (own_row[c] == r && counted) xs += l_own[c];
-    l_row[r] = wave_sum(xs);
-  }
-  if (lane < LPT) {
+  st.totals(l_row);
+  if (lane < W::LPT) {
 #pragma unroll
     for (int r = 0; r < RP; ++r)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][r][d0 + e] = acc[r][e];
+      for (int e = 0; e < EPL; ++e) sm_acc[wave][r][st.d0 + e] = st.acc[r][e];
   }
   if (lane == 0) {  // bad is wavefront-uniform: it comes from scalar table reads
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      sm_m[wave][r] = m_run[r];
+      sm_m[wave][r] = st.m_run[r];
       sm_l[wave][r] = l_row[r];
     }
-    sm_bad[wave] = bad;
+    sm_bad[wave] = st.bad;
   }
   __syncthreads();
 
-  // ---- merge the wavefronts; write output or partials ----------------------
   int any_bad = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) any_bad |= sm_bad[w];
@@ -548,15 +590,202 @@ decode_partition_kernel(const DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Work-item kernel for split contexts: persistent wavefronts, each taking
+// (sequence, KV head, partition) items in round robin from a dense list
+// (partitions past a sequence's end are not items). A wavefront streams the
+// tiles of its items back to back -- the software pipeline runs across item
+// boundaries -- and writes unnormalised partials per item; the reduce kernel
+// merges them. No LDS merge, no barriers after the item list is built.
+// ---------------------------------------------------------------------------
+constexpr int kItemWaves = 4;  // wavefronts per workgroup (independent)
+
+template <int DT, int D, int G, int RP>
+__global__ void __launch_bounds__(kItemWaves * 64)
+decode_items_kernel(const DecodeArgs a) {
+  using W = DecodeWave<DT, D, G, RP>;
+  using Gm = Geo<DT, D>;
+  constexpr int NL = Gm::NL, EPL = Gm::EPL;
+  constexpr int kThreads = kItemWaves * 64;
+  extern __shared__ int sm_pre[];  // [B + 1]: partitions before sequence b
+  __shared__ int sm_scan[kThreads];
+
+  const int B = a.B, P = a.part_tokens, nq = a.nq, Hkv = a.Hkv;
+  const int max_ctx = a.max_blocks * a.bs;
+
+  // ---- dense item list: prefix sums of partitions per sequence ------------
+  {
+    const int per = (B + kThreads - 1) / kThreads;
+    const int lo = min(B, (int)threadIdx.x * per), hi = min(B, lo + per);
+    int sum = 0;
+    for (int b = lo; b < hi; ++b) {
+      const int L = a.lens[b];
+      sum += (L >= nq && L <= max_ctx) ? (L + P - 1) / P : 0;
+    }
+    sm_scan[threadIdx.x] = sum;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
+      const int v = threadIdx.x >= off ? sm_scan[threadIdx.x - off] : 0;
+      __syncthreads();
+      sm_scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    int run = sm_scan[threadIdx.x] - sum;  // exclusive prefix of this chunk
+    for (int b = lo; b < hi; ++b) {
+      sm_pre[b] = run;
+      const int L = a.lens[b];
+      run += (L >= nq && L <= max_ctx) ? (L + P - 1) / P : 0;
+    }
+    if (threadIdx.x == kThreads - 1) sm_pre[B] = sm_scan[kThreads - 1];
+    __syncthreads();
+  }
+  const int total = __builtin_amdgcn_readfirstlane(sm_pre[B]) * Hkv;
+
+  const int lane = threadIdx.x & 63;
+  const int n_waves = gridDim.x * kItemWaves;
+  const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kItemWaves + (threadIdx.x >> 6));
+  if (first >= total) return;
+
+  // item id -> (b, g, token range); ids of one sequence are contiguous
+  struct Cursor {
+    int id, b, g, t, t_end;
+  };
+  auto locate = [&](Cursor &c) {
+    int lo = 0, hi = B;  // sm_pre[lo] * Hkv <= id < sm_pre[hi] * Hkv
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(sm_pre[mid]) * Hkv <= c.id) lo = mid; else hi = mid;
+    }
+    const int p0 = __builtin_amdgcn_readfirstlane(sm_pre[lo]);
+    const int np = __builtin_amdgcn_readfirstlane(sm_pre[lo + 1]) - p0;
+    const int local = c.id - p0 * Hkv;
+    c.b = lo;
+    c.g = local / np;
+    const int p = local - c.g * np;
+    c.t = p * P;
+    c.t_end = min(a.lens[lo], c.t + P);
+  };
+  auto advance = [&](Cursor &c) {  // next tile of this wavefront's stream
+    if (c.id >= total) return;
+    c.t += kTile;
+    if (c.t >= c.t_end) {
+      c.id += n_waves;
+      if (c.id < total) locate(c);
+    }
+  };
+  auto table_entry = [&](const Cursor &c) {
+    return a.tables[(size_t)c.b * a.max_blocks + c.t / a.bs];
+  };
+
+  W st;
+  st.init(lane);
+  const char *kbase = (const char *)a.kc;
+  const char *vbase = (const char *)a.vc;
+  // Offset of a tile; a bad table entry reads block 0 and flags the tile so
+  // that its item's partials are poisoned when the tile is consumed.
+  auto offset = [&](const Cursor &c, int blk, int &tile_bad) -> size_t {
+    tile_bad = blk < 0 || blk >= a.num_blocks;
+    return tile_bytes_offset<Gm::TB>(a, c.g, c.t, tile_bad ? 0 : blk, lane);
+  };
+
+  // Tiles in this wavefront's stream (all tiles of its items, in order).
+  int n_tiles = 0;
+  for (Cursor c{first, 0, 0, 0, 0}; c.id < total; c.id += n_waves) {
+    locate(c);
+    n_tiles += (c.t_end - c.t + kTile - 1) / kTile;
+  }
+
+  // Cursors: cur = tile being consumed, iss = next tile to load, pre = the
+  // one after (its block id is read a step ahead). The steady-state loop
+  // has the same shape as the workgroup-split kernel's: two tiles per trip,
+  // alternating register sets, loads issued unconditionally, the last one or
+  // two tiles peeled.
+  Cursor cur{first, 0, 0, 0, 0};
+  locate(cur);
+  st.begin(a, cur.b, cur.g, a.lens[cur.b]);
+  Cursor iss = cur;
+  advance(iss);
+  Cursor pre = iss;
+  advance(pre);
+  int bad_a = 0, bad_b = 0;
+  const size_t off0 = offset(cur, table_entry(cur), bad_a);
+  int blk_iss = iss.id < total ? table_entry(iss) : 0;
+  int blk_pre = pre.id < total ? table_entry(pre) : 0;
+
+  // Load the tile at `iss`, then move the cursors on.
+  auto issue = [&](uint4 (&kr)[NL], uint4 (&vr)[NL], int &tile_bad) {
+    const size_t off = offset(iss, blk_iss, tile_bad);
+    load_tile<NL>(kr, vr, kbase + off, vbase + off);
+    iss = pre;
+    blk_iss = blk_pre;
+    advance(pre);
+    blk_pre = pre.id < total ? table_entry(pre) : 0;
+  };
+  // Consume the tile in kr / vr at cursor `cur`; at an item's last tile,
+  // write the item's partials and start the next item.
+  auto consume = [&](const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tile_bad) {
+    st.bad |= tile_bad;
+    st.process(kr, vr, cur.t, a.scale_log2);
+    if (cur.t + kTile < cur.t_end) {
+      cur.t += kTile;
+      return;
+    }
+    float l_row[RP];
+    st.totals(l_row);
+    const int p = cur.t / P;
+    const float nan = __builtin_nanf("");
+    if (lane < W::LPT) {
+#pragma unroll
+      for (int r = 0; r < RP; ++r) {
+        const int qi = r / G;
+        if (qi >= nq) continue;
+        const size_t row = ((size_t)cur.b * nq + qi) * a.Hq + cur.g * G + (r % G);
+        float *dst = a.part_acc + (row * a.num_parts + p) * D + st.d0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dst[e] = st.acc[r][e];
+        if (lane == 0) {
+          a.part_m[row * a.num_parts + p] = st.bad ? nan : st.m_run[r];
+          a.part_l[row * a.num_parts + p] = l_row[r];
+        }
+      }
+    }
+    advance(cur);
+    if (cur.id < total) st.begin(a, cur.b, cur.g, a.lens[cur.b]);
+  };
+
+  uint4 ka[NL], va[NL], kb[NL], vb[NL];
+  load_tile<NL>(ka, va, kbase + off0, vbase + off0);
+  int k = 0;
+  for (; k + 2 < n_tiles; k += 2) {
+    issue(kb, vb, bad_b);
+    consume(ka, va, bad_a);
+    issue(ka, va, bad_a);
+    consume(kb, vb, bad_b);
+  }
+  if (k + 1 < n_tiles) {
+    issue(kb, vb, bad_b);
+    consume(ka, va, bad_a);
+    consume(kb, vb, bad_b);
+  } else {
+    consume(ka, va, bad_a);
+  }
+}
+
 using Launcher = void (*)(const DecodeArgs &, dim3, hipStream_t);
 
 template <int DT, int D, int G, int RP, int W>
 void launch_decode(const DecodeArgs &a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, W>), grid, dim3(W * 64), 0, s, a);
+  if constexpr (W == 0) {  // work-item kernel; grid.x persistent workgroups
+    hipLaunchKernelGGL((decode_items_kernel<DT, D, G, RP>), grid, dim3(kItemWaves * 64),
+                       (a.B + 1) * sizeof(int), s, a);
+  } else {
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, W>), grid, dim3(W * 64), 0, s, a);
+  }
 }
 
 // Launcher for (dtype, D) and rows per wavefront RP = G * (query tokens
-// rounded up to a power of two), W wavefronts per workgroup; nullptr if no
+// rounded up to a power of two): W = 4 or 8 wavefronts per workgroup of the
+// workgroup-split kernel, or W = 0 for the work-item kernel; nullptr if no
 // such kernel is built. Defined in decode_inst_<dtype>_d<D>.hip.
 template <int DT, int D>
 Launcher pick_rows(int G, int RP, int W);
