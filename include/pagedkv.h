@@ -235,8 +235,13 @@ int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
  * sequence with context_lens[b] > max_blocks * block_size, and rows whose
  * visible tokens meet a table entry outside [0, num_blocks) produce NaN in
  * out and lse instead of reading out of bounds.
- * Host-checked: sizes, Hq % Hkv == 0, D and block_size supported, nq <= 16,
- * scale finite, workspace large enough -> EINVAL. */
+ * Kernels: single query rows (nq = 1) and fp32 caches run on VALU kernels
+ * (up to 8 rows per KV head: G * nq rounded up to a power of two); bf16
+ * caches with nq > 1 run on an MFMA tile of 16 query rows per KV head
+ * (G * nq <= 16), e.g. 4 query heads x 4 draft tokens for verification.
+ * Host-checked: sizes, Hq % Hkv == 0, D and block_size supported, rows per
+ * KV head within those limits, scale finite, workspace large enough ->
+ * EINVAL. */
 int paged_attention_decode(float *out, const void *q, const void *k_cache,
                            const void *v_cache, const int32_t *block_tables,
                            int32_t max_blocks, const int32_t *context_lens,

@@ -10,6 +10,7 @@
 #include <limits>
 
 #include "decode_kernel.h"
+#include "verify_mfma.h"
 #include "pagedkv.h"
 #include "status.h"
 
@@ -163,9 +164,19 @@ static int check_sizes(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t D
   if ((int64_t)max_blocks * bs > INT32_MAX) return fail(PKV_EINVAL, "table too wide");
   if (part < 0 || part % kTile) return fail(PKV_EINVAL, "partition_tokens must be 0 or k*16");
   if (B > 65535 || Hkv > 65535) return fail(PKV_EINVAL, "B and Hkv must be <= 65535");
-  const int G = Hq / Hkv;
+  return PKV_OK;
+}
+
+// The kernel family for a launch: the MFMA tile for bf16 multi-query rows
+// (up to 16 rows per KV head), else the VALU kernels (up to kMaxRows rows).
+static bool use_mfma(int dtype, int32_t nq, int32_t G) {
+  return dtype == PKV_BF16 && nq > 1 && G * nq <= kVerifyRows;
+}
+
+static int check_rows(int dtype, int32_t nq, int32_t G) {
+  if (use_mfma(dtype, nq, G)) return PKV_OK;
   if (G * next_pow2(nq) > kMaxRows)
-    return fail(PKV_EINVAL, "G * nq = %d * %d exceeds %d rows per wavefront", G, nq, kMaxRows);
+    return fail(PKV_EINVAL, "G * nq = %d * %d exceeds the supported rows per KV head", G, nq);
   return PKV_OK;
 }
 
@@ -195,12 +206,16 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   for (const void *p : {(const void *)out, q, k_cache, v_cache})
     if ((uintptr_t)p % 16) return fail(PKV_EINVAL, "out, q, K and V must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  const int G = Hq / Hkv;
+  if (int rc = check_rows(dtype, nq, G)) return rc;
   const Plan pl = plan_launch(B, Hkv, (int64_t)max_blocks * bs, part);
   const int32_t P = pl.part_tokens, NP = pl.num_parts;
-  const int G = Hq / Hkv;
+  const bool mfma = use_mfma(dtype, nq, G);
   const int RP = G * next_pow2(nq);
-  Launcher launch = pick_launcher(dtype, D, G, RP, pl.waves);
+  Launcher launch = mfma ? pick_verify(D) : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
+  // the MFMA tile always uses the workgroup-split grid
+  const dim3 grid = (pl.waves || mfma) ? dim3(NP, Hkv, B) : dim3(pl.grid_x);
   DecodeArgs a{};
   a.out = out;
   a.lse = lse_out;
@@ -234,7 +249,7 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
     a.part_l = (float *)w;
   }
   hipStream_t s = (hipStream_t)stream;
-  launch(a, pl.waves ? dim3(NP, Hkv, B) : dim3(pl.grid_x), s);
+  launch(a, grid, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, "decode launch: %s", hipGetErrorString(e));
   if (NP > 1) {
