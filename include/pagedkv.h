@@ -207,9 +207,17 @@ int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_t *pairs,
                          int32_t n, int32_t num_blocks, int32_t Hkv, int32_t D,
                          int32_t block_size, int dtype, void *stream);
 
-/* Workspace bytes paged_attention_decode needs for these sizes (0 when the
- * chosen partitioning keeps everything on chip). partition_tokens: 0 lets
- * the library choose; otherwise a positive multiple of 16. */
+/* Workspace bytes paged_attention_decode needs for these sizes and
+ * partition_tokens (0 when the chosen launch keeps everything on chip).
+ * partition_tokens:
+ *    0  the library chooses (one workgroup per (sequence, KV head) when
+ *       those pairs fill the GPU, else a balanced stream);
+ *   -1  balanced stream: all sequences' tiles are shared equally among the
+ *       wavefronts whatever their lengths (for batches of mixed lengths);
+ *   >0  split every context into partitions of that many tokens (a multiple
+ *       of 16), merged by a log-sum-exp reduce launch.
+ * The workspace holds partial results only for the duration of one call;
+ * it need not be initialised. */
 int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
                                    int32_t Hkv, int32_t D, int32_t max_blocks,
                                    int32_t block_size,

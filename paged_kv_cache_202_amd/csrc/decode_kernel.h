@@ -179,6 +179,10 @@ struct DecodeArgs {
   const int32_t *tables;
   const int32_t *lens;
   int32_t B, max_blocks, nq, Hq, Hkv, bs, num_blocks, part_tokens, num_parts;
+  // Query rows of a KV head are r = qi * G + gj (query token qi, head gj of
+  // the group); a wavefront holds RP of them and `slices` wavefronts share
+  // a KV head's rows: slice s holds rows s * RP .. s * RP + RP - 1.
+  int32_t slices;
   float scale_log2;
 };
 
@@ -220,6 +224,15 @@ __device__ __forceinline__ void sum_over_groups(float (&acc)[RP][EPL]) {
       for (int e = 0; e < EPL; ++e) acc[r][e] += exact_xor<M>(acc[r][e]);
     sum_over_groups<M * 2, LPT, RP, EPL>(acc);
   }
+}
+
+// Read-only metadata (block tables, context lengths) read at a
+// wavefront-uniform address: through the constant address space the load is
+// a scalar load, even in loops that also store to global memory, so it never
+// waits on the vector-memory counter that tracks the K/V stream.
+template <class T>
+__device__ __forceinline__ T load_const(const T *p) {
+  return *(const __attribute__((address_space(4))) T *)(p);
 }
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -277,17 +290,18 @@ struct DecodeWave {
     }
   }
 
-  // Start a (sequence b, KV head g) item of context length L_: load the
-  // query rows r = qi * G + gj (head g * G + gj) and reset the statistics.
-  __device__ __forceinline__ void begin(const DecodeArgs &a, int b, int g, int L_) {
+  // Start a (sequence b, KV head g) item of context length L_ for rows
+  // row0 .. row0 + RP - 1: load those query rows and reset the statistics.
+  __device__ __forceinline__ void begin(const DecodeArgs &a, int b, int g, int L_, int row0) {
     const int nq = a.nq;
     L = L_;
     min_lim = L - nq + 1;
     bad = 0;
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-      const int qi = r / G;
-      const size_t row = ((size_t)b * nq + (qi < nq ? qi : 0)) * a.Hq + g * G + (r % G);
+      const int rr = row0 + r;
+      const int qi = rr / G;
+      const size_t row = ((size_t)b * nq + (qi < nq ? qi : 0)) * a.Hq + g * G + (rr % G);
       if constexpr (DT == PKV_BF16) {
         uint4 w = make_uint4(0, 0, 0, 0);
         if (qi < nq) w = *reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
@@ -303,8 +317,24 @@ struct DecodeWave {
     }
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-      const int qi = own_row[c] / G;
+      const int qi = (row0 + own_row[c]) / G;
       own_lim[c] = qi < nq ? L - nq + qi + 1 : 0;  // visible keys of that row
+      m_own[c] = kNegInf;
+      l_own[c] = 0.f;
+    }
+  }
+
+  // Fresh statistics for a new partition of the same (b, g): queries kept.
+  __device__ __forceinline__ void restart() {
+    bad = 0;
+#pragma unroll
+    for (int r = 0; r < RP; ++r) {
+      m_run[r] = kNegInf;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
       m_own[c] = kNegInf;
       l_own[c] = 0.f;
     }
@@ -427,6 +457,50 @@ struct DecodeWave {
   }
 };
 
+// NS row sets of RP rows each in one wavefront (RW = NS * RP rows): every
+// loaded K/V tile feeds all of them, so a KV head's rows need not be split
+// over wavefronts that would each stream the same bytes.
+template <int DT, int D, int G, int RP, int NS>
+struct DecodeWaveSet {
+  using One = DecodeWave<DT, D, G, RP>;
+  static constexpr int LPT = One::LPT, EPL = One::EPL, RW = RP * NS;
+  One w[NS];
+  int bad;  // a tile of the current item came from a bad table entry
+  int d0;
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) w[j].init(lane);
+    d0 = w[0].d0;
+  }
+  __device__ __forceinline__ void begin(const DecodeArgs &a, int b, int g, int L, int row0) {
+    bad = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) w[j].begin(a, b, g, L, row0 + j * RP);
+  }
+  __device__ __forceinline__ void restart() {
+    bad = 0;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) w[j].restart();
+  }
+  __device__ __forceinline__ void process(const uint4 (&kr)[One::NL], const uint4 (&vr)[One::NL],
+                                          int t0, float scale_log2) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) w[j].process(kr, vr, t0, scale_log2);
+  }
+  __device__ __forceinline__ void totals(float (&l_row)[RW]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float l[RP];
+      w[j].totals(l);
+#pragma unroll
+      for (int r = 0; r < RP; ++r) l_row[j * RP + r] = l[r];
+    }
+  }
+  __device__ __forceinline__ float acc(int r, int e) const { return w[r / RP].acc[r % RP][e]; }
+  __device__ __forceinline__ float m(int r) const { return w[r / RP].m_run[r % RP]; }
+};
+
 // Byte offset of the 16-token tile at logical token t0 of KV head g in
 // block blk, for this lane.
 template <int TB>
@@ -442,32 +516,36 @@ __device__ __forceinline__ size_t tile_bytes_offset(const DecodeArgs &a, int g, 
 // in LDS. Used when there are enough (sequence, KV head) pairs to fill the
 // chip with one partition each.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int G, int RP, int kWaves>
+template <int DT, int D, int G, int RP, int NS, int kWaves>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_partition_kernel(const DecodeArgs a) {
-  using W = DecodeWave<DT, D, G, RP>;
+  using W = DecodeWaveSet<DT, D, G, RP, NS>;
+  constexpr int RW = W::RW;  // query rows of this wavefront
   using Gm = Geo<DT, D>;
   constexpr int NL = Gm::NL, EPL = Gm::EPL;
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
 
-  __shared__ float sm_acc[kWaves][RP][D];
-  __shared__ float sm_m[kWaves][RP];
-  __shared__ float sm_l[kWaves][RP];
+  __shared__ float sm_acc[kWaves][RW][D];
+  __shared__ float sm_m[kWaves][RW];
+  __shared__ float sm_l[kWaves][RW];
   __shared__ int sm_bad[kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // blockIdx.y = slice * Hkv + KV head: the slices of one KV head are Hkv
+  // workgroups apart, so they run on the same XCD and share its L2
+  const int p = blockIdx.x, b = blockIdx.z;
+  const int g = blockIdx.y % a.Hkv, row0 = (blockIdx.y / a.Hkv) * RW;
   const int nq = a.nq;
-  const int L = a.lens[b];
+  const int L = load_const(a.lens + b);
   const int max_ctx = a.max_blocks * a.bs;
 
   if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
     if (a.num_parts == 1 && p == 0) {
       const float nan = __builtin_nanf("");
-      for (int idx = threadIdx.x; idx < RP * D; idx += kWaves * 64) {
-        const int r = idx / D, d = idx % D, qi = r / G;
+      for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+        const int r = row0 + idx / D, d = idx % D, qi = r / G;
         if (qi >= nq) continue;
         const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
         a.out[row * D + d] = nan;
@@ -482,7 +560,7 @@ decode_partition_kernel(const DecodeArgs a) {
 
   W st;
   st.init(lane);
-  st.begin(a, b, g, L);
+  st.begin(a, b, g, L, row0);
 
   const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
   const char *kbase = (const char *)a.kc;
@@ -504,7 +582,9 @@ decode_partition_kernel(const DecodeArgs a) {
                           ? (t_end - (t_begin + wave * kTile) + kStride - 1) / kStride
                           : 0;
   auto tile_t0 = [&](int k) { return t_begin + wave * kTile + k * kStride; };
-  auto table_at = [&](int k) { return trow[tile_t0(k < n_tiles ? k : n_tiles - 1) / a.bs]; };
+  auto table_at = [&](int k) {
+    return load_const(trow + tile_t0(k < n_tiles ? k : n_tiles - 1) / a.bs);
+  };
   if (n_tiles > 0) {
     uint4 ka[NL], va[NL], kb[NL], vb[NL];
     {
@@ -539,18 +619,18 @@ decode_partition_kernel(const DecodeArgs a) {
   }
 
   // ---- wavefront totals, then merge the wavefronts in LDS ------------------
-  float l_row[RP];
+  float l_row[RW];
   st.totals(l_row);
   if (lane < W::LPT) {
 #pragma unroll
-    for (int r = 0; r < RP; ++r)
+    for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][r][st.d0 + e] = st.acc[r][e];
+      for (int e = 0; e < EPL; ++e) sm_acc[wave][r][st.d0 + e] = st.acc(r, e);
   }
   if (lane == 0) {  // bad is wavefront-uniform: it comes from scalar table reads
 #pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      sm_m[wave][r] = st.m_run[r];
+    for (int r = 0; r < RW; ++r) {
+      sm_m[wave][r] = st.m(r);
       sm_l[wave][r] = l_row[r];
     }
     sm_bad[wave] = st.bad;
@@ -561,8 +641,8 @@ decode_partition_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) any_bad |= sm_bad[w];
   const float nan = __builtin_nanf("");
-  for (int idx = threadIdx.x; idx < RP * D; idx += kWaves * 64) {
-    const int r = idx / D, d = idx % D, qi = r / G;
+  for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+    const int r = idx / D, d = idx % D, rr = row0 + r, qi = rr / G;
     if (qi >= nq) continue;
     float M = kNegInf;
 #pragma unroll
@@ -575,7 +655,7 @@ decode_partition_kernel(const DecodeArgs a) {
       num = fmaf(f, sm_acc[w][r][d], num);
       den = fmaf(f, sm_l[w][r], den);
     }
-    const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
+    const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
     if (a.num_parts == 1) {
       a.out[row * D + d] = any_bad || den == 0.f ? nan : num / den;
       if (d == 0 && a.lse) a.lse[row] = any_bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
@@ -591,166 +671,216 @@ decode_partition_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Work-item kernel for split contexts: persistent wavefronts, each taking
-// (sequence, KV head, partition) items in round robin from a dense list
-// (partitions past a sequence's end are not items). A wavefront streams the
-// tiles of its items back to back -- the software pipeline runs across item
-// boundaries -- and writes unnormalised partials per item; the reduce kernel
-// merges them. No LDS merge, no barriers after the item list is built.
+// Stream kernel (stream-K decomposition) for mixed lengths and split
+// contexts. All (sequence, KV head) units are laid end to end as one stream
+// of 16-token tiles -- unit u = b * Hkv + g holds ceil(L_b / 16) tiles -- and
+// persistent wavefront w takes tiles [w T / N, (w + 1) T / N) of it: every
+// wavefront gets the same number of tiles, whatever the lengths. A
+// wavefront's range is cut into segments at unit boundaries, at multiples of
+// the requested partition size, and at its own ends; each segment leaves
+// unnormalised partials (m, l, acc) under the id w + (global index of its
+// partition), unique because both terms only grow along the stream. The
+// reduce kernel finds a row's segments from the same arithmetic. No atomics,
+// no LDS merge, no barriers after the prefix sums are built.
 // ---------------------------------------------------------------------------
-constexpr int kItemWaves = 4;  // wavefronts per workgroup (independent)
+constexpr int kStreamWaves = 4;  // wavefronts per workgroup (independent)
 
-template <int DT, int D, int G, int RP>
-__global__ void __launch_bounds__(kItemWaves * 64)
-decode_items_kernel(const DecodeArgs a) {
-  using W = DecodeWave<DT, D, G, RP>;
+// Stream geometry shared by the stream kernel and its reduce kernel.
+struct StreamArgs {
+  int32_t *tile_pre;  // [B + 1] tiles per unit, prefix over sequences
+  int32_t *part_pre;  // [B + 1] partitions per unit, prefix over sequences
+  int32_t n_waves;    // N
+};
+
+__device__ __forceinline__ int seq_tiles(int L, int nq, int max_ctx) {
+  return (L >= nq && L <= max_ctx) ? (L + kTile - 1) / kTile : 0;
+}
+__device__ __forceinline__ int seq_parts(int L, int nq, int max_ctx, int P) {
+  return (L >= nq && L <= max_ctx) ? (P > 0 ? (L + P - 1) / P : 1) : 0;
+}
+// Wavefront whose range holds stream tile `pos`: the largest w with
+// floor(w T / N) <= pos.
+__device__ __forceinline__ int64_t stream_wave(int64_t pos, int64_t T, int64_t N) {
+  return ((pos + 1) * N + T - 1) / T - 1;
+}
+
+template <int DT, int D, int G, int RP, int NS>
+__global__ void __launch_bounds__(kStreamWaves * 64)
+decode_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
+  using W = DecodeWaveSet<DT, D, G, RP, NS>;
+  constexpr int RW = W::RW;  // query rows of this wavefront
   using Gm = Geo<DT, D>;
   constexpr int NL = Gm::NL, EPL = Gm::EPL;
-  constexpr int kThreads = kItemWaves * 64;
-  extern __shared__ int sm_pre[];  // [B + 1]: partitions before sequence b
-  __shared__ int sm_scan[kThreads];
+  constexpr int kThreads = kStreamWaves * 64;
+  extern __shared__ int sm_dyn[];  // tile prefix [B + 1], then partition prefix [B + 1]
+  __shared__ int sm_scan[2][kThreads];
 
-  const int B = a.B, P = a.part_tokens, nq = a.nq, Hkv = a.Hkv;
+  // Units: each sequence contributes HU = Hkv * slices of them, unit vg of
+  // a sequence being KV head vg / slices, row slice vg % slices.
+  const int B = a.B, P = a.part_tokens, nq = a.nq, S = a.slices, HU = a.Hkv * a.slices;
   const int max_ctx = a.max_blocks * a.bs;
+  int *sm_tp = sm_dyn;
+  int *sm_pp = sm_dyn + B + 1;
 
-  // ---- dense item list: prefix sums of partitions per sequence ------------
+  // ---- prefix sums over sequences (every workgroup; workgroup 0 also
+  //      leaves them in the workspace for the reduce kernel) ---------------
   {
     const int per = (B + kThreads - 1) / kThreads;
     const int lo = min(B, (int)threadIdx.x * per), hi = min(B, lo + per);
-    int sum = 0;
+    int st_ = 0, sp_ = 0;
     for (int b = lo; b < hi; ++b) {
-      const int L = a.lens[b];
-      sum += (L >= nq && L <= max_ctx) ? (L + P - 1) / P : 0;
+      const int L = load_const(a.lens + b);
+      st_ += seq_tiles(L, nq, max_ctx);
+      sp_ += seq_parts(L, nq, max_ctx, P);
     }
-    sm_scan[threadIdx.x] = sum;
+    sm_scan[0][threadIdx.x] = st_;
+    sm_scan[1][threadIdx.x] = sp_;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
-      const int v = threadIdx.x >= off ? sm_scan[threadIdx.x - off] : 0;
+    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scans
+      const int v0 = threadIdx.x >= off ? sm_scan[0][threadIdx.x - off] : 0;
+      const int v1 = threadIdx.x >= off ? sm_scan[1][threadIdx.x - off] : 0;
       __syncthreads();
-      sm_scan[threadIdx.x] += v;
+      sm_scan[0][threadIdx.x] += v0;
+      sm_scan[1][threadIdx.x] += v1;
       __syncthreads();
     }
-    int run = sm_scan[threadIdx.x] - sum;  // exclusive prefix of this chunk
+    int rt = sm_scan[0][threadIdx.x] - st_, rp = sm_scan[1][threadIdx.x] - sp_;
     for (int b = lo; b < hi; ++b) {
-      sm_pre[b] = run;
-      const int L = a.lens[b];
-      run += (L >= nq && L <= max_ctx) ? (L + P - 1) / P : 0;
+      sm_tp[b] = rt;
+      sm_pp[b] = rp;
+      const int L = load_const(a.lens + b);
+      rt += seq_tiles(L, nq, max_ctx);
+      rp += seq_parts(L, nq, max_ctx, P);
     }
-    if (threadIdx.x == kThreads - 1) sm_pre[B] = sm_scan[kThreads - 1];
+    if (threadIdx.x == kThreads - 1) {
+      sm_tp[B] = sm_scan[0][kThreads - 1];
+      sm_pp[B] = sm_scan[1][kThreads - 1];
+    }
     __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i <= B; i += kThreads) {
+        sa.tile_pre[i] = sm_tp[i];
+        sa.part_pre[i] = sm_pp[i];
+      }
   }
-  const int total = __builtin_amdgcn_readfirstlane(sm_pre[B]) * Hkv;
 
+  const int64_t T = (int64_t)__builtin_amdgcn_readfirstlane(sm_tp[B]) * HU;
+  const int64_t N = sa.n_waves;
+  const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kStreamWaves + (threadIdx.x >> 6));
+  const int64_t pos0 = (int64_t)w * T / N, pos1 = (int64_t)(w + 1) * T / N;
+  const int n_tiles = (int)(pos1 - pos0);
+  if (n_tiles <= 0) return;
   const int lane = threadIdx.x & 63;
-  const int n_waves = gridDim.x * kItemWaves;
-  const int first = __builtin_amdgcn_readfirstlane(blockIdx.x * kItemWaves + (threadIdx.x >> 6));
-  if (first >= total) return;
+  const int ptiles = P > 0 ? P / kTile : 0;  // tiles per partition (0: unbounded)
 
-  // item id -> (b, g, token range); ids of one sequence are contiguous
+  // A cursor is a tile of the stream: sequence b, unit g of the sequence
+  // (KV head g / S, row slice g % S), tile k of the unit, plus the unit's
+  // tile count and the sequence's length.
   struct Cursor {
-    int id, b, g, t, t_end;
+    int b, g, k, nt, L;
   };
-  auto locate = [&](Cursor &c) {
-    int lo = 0, hi = B;  // sm_pre[lo] * Hkv <= id < sm_pre[hi] * Hkv
+  auto locate = [&](int64_t pos) {
+    int lo = 0, hi = B;  // HU * sm_tp[lo] <= pos < HU * sm_tp[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (__builtin_amdgcn_readfirstlane(sm_pre[mid]) * Hkv <= c.id) lo = mid; else hi = mid;
+      if ((int64_t)__builtin_amdgcn_readfirstlane(sm_tp[mid]) * HU <= pos) lo = mid; else hi = mid;
     }
-    const int p0 = __builtin_amdgcn_readfirstlane(sm_pre[lo]);
-    const int np = __builtin_amdgcn_readfirstlane(sm_pre[lo + 1]) - p0;
-    const int local = c.id - p0 * Hkv;
+    Cursor c;
     c.b = lo;
-    c.g = local / np;
-    const int p = local - c.g * np;
-    c.t = p * P;
-    c.t_end = min(a.lens[lo], c.t + P);
+    c.nt = __builtin_amdgcn_readfirstlane(sm_tp[lo + 1]) - __builtin_amdgcn_readfirstlane(sm_tp[lo]);
+    const int local = (int)(pos - (int64_t)__builtin_amdgcn_readfirstlane(sm_tp[lo]) * HU);
+    c.g = local / c.nt;
+    c.k = local - c.g * c.nt;
+    c.L = load_const(a.lens + lo);
+    return c;
   };
-  auto advance = [&](Cursor &c) {  // next tile of this wavefront's stream
-    if (c.id >= total) return;
-    c.t += kTile;
-    if (c.t >= c.t_end) {
-      c.id += n_waves;
-      if (c.id < total) locate(c);
-    }
+  auto step = [&](Cursor &c) {  // the next tile of the stream
+    if (++c.k < c.nt) return;
+    c.k = 0;
+    if (++c.g < HU) return;
+    c.g = 0;
+    do {  // next sequence that has tiles
+      ++c.b;
+      c.L = c.b < B ? load_const(a.lens + c.b) : 0;
+      c.nt = c.b < B ? seq_tiles(c.L, nq, max_ctx) : 1;
+    } while (c.nt == 0);
   };
   auto table_entry = [&](const Cursor &c) {
-    return a.tables[(size_t)c.b * a.max_blocks + c.t / a.bs];
+    return load_const(a.tables + (size_t)c.b * a.max_blocks + (c.k * kTile) / a.bs);
   };
 
   W st;
   st.init(lane);
   const char *kbase = (const char *)a.kc;
   const char *vbase = (const char *)a.vc;
-  // Offset of a tile; a bad table entry reads block 0 and flags the tile so
-  // that its item's partials are poisoned when the tile is consumed.
   auto offset = [&](const Cursor &c, int blk, int &tile_bad) -> size_t {
     tile_bad = blk < 0 || blk >= a.num_blocks;
-    return tile_bytes_offset<Gm::TB>(a, c.g, c.t, tile_bad ? 0 : blk, lane);
+    return tile_bytes_offset<Gm::TB>(a, c.g / S, c.k * kTile, tile_bad ? 0 : blk, lane);
   };
 
-  // Tiles in this wavefront's stream (all tiles of its items, in order).
-  int n_tiles = 0;
-  for (Cursor c{first, 0, 0, 0, 0}; c.id < total; c.id += n_waves) {
-    locate(c);
-    n_tiles += (c.t_end - c.t + kTile - 1) / kTile;
-  }
-
-  // Cursors: cur = tile being consumed, iss = next tile to load, pre = the
-  // one after (its block id is read a step ahead). The steady-state loop
-  // has the same shape as the workgroup-split kernel's: two tiles per trip,
-  // alternating register sets, loads issued unconditionally, the last one or
-  // two tiles peeled.
-  Cursor cur{first, 0, 0, 0, 0};
-  locate(cur);
-  st.begin(a, cur.b, cur.g, a.lens[cur.b]);
+  Cursor cur = locate(pos0);
+  st.begin(a, cur.b, cur.g / S, cur.L, (cur.g % S) * RW);
+  int left = n_tiles;  // tiles of this wavefront not yet consumed
   Cursor iss = cur;
-  advance(iss);
+  if (n_tiles > 1) step(iss);
   Cursor pre = iss;
-  advance(pre);
+  if (n_tiles > 2) step(pre);
+  int issued = 1;  // tiles whose loads have been issued
   int bad_a = 0, bad_b = 0;
   const size_t off0 = offset(cur, table_entry(cur), bad_a);
-  int blk_iss = iss.id < total ? table_entry(iss) : 0;
-  int blk_pre = pre.id < total ? table_entry(pre) : 0;
+  int blk_iss = n_tiles > 1 ? table_entry(iss) : 0;
+  int blk_pre = n_tiles > 2 ? table_entry(pre) : 0;
 
-  // Load the tile at `iss`, then move the cursors on.
   auto issue = [&](uint4 (&kr)[NL], uint4 (&vr)[NL], int &tile_bad) {
     const size_t off = offset(iss, blk_iss, tile_bad);
     load_tile<NL>(kr, vr, kbase + off, vbase + off);
+    ++issued;
     iss = pre;
     blk_iss = blk_pre;
-    advance(pre);
-    blk_pre = pre.id < total ? table_entry(pre) : 0;
+    if (issued + 1 < n_tiles) {
+      step(pre);
+      blk_pre = table_entry(pre);
+    }
   };
-  // Consume the tile in kr / vr at cursor `cur`; at an item's last tile,
-  // write the item's partials and start the next item.
+  // Consume the tile at `cur`; close the segment when the tile ends the
+  // unit, a partition, or this wavefront's range.
   auto consume = [&](const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tile_bad) {
     st.bad |= tile_bad;
-    st.process(kr, vr, cur.t, a.scale_log2);
-    if (cur.t + kTile < cur.t_end) {
-      cur.t += kTile;
+    st.process(kr, vr, cur.k * kTile, a.scale_log2);
+    --left;
+    const bool unit_end = cur.k + 1 == cur.nt;
+    const bool part_end = ptiles > 0 && (cur.k + 1) % ptiles == 0;
+    if (!(unit_end || part_end || left == 0)) {
+      ++cur.k;
       return;
     }
-    float l_row[RP];
+    float l_row[RW];
     st.totals(l_row);
-    const int p = cur.t / P;
+    const int p = ptiles > 0 ? cur.k / ptiles : 0;
+    const int64_t gp = (int64_t)__builtin_amdgcn_readfirstlane(sm_pp[cur.b]) * HU +
+                       (int64_t)cur.g * (sm_pp[cur.b + 1] - sm_pp[cur.b]) + p;
+    const int64_t sid = w + gp;
     const float nan = __builtin_nanf("");
     if (lane < W::LPT) {
+      float *dst = a.part_acc + (size_t)sid * RW * D + st.d0;
 #pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        const int qi = r / G;
-        if (qi >= nq) continue;
-        const size_t row = ((size_t)cur.b * nq + qi) * a.Hq + cur.g * G + (r % G);
-        float *dst = a.part_acc + (row * a.num_parts + p) * D + st.d0;
+      for (int r = 0; r < RW; ++r)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dst[e] = st.acc[r][e];
-        if (lane == 0) {
-          a.part_m[row * a.num_parts + p] = st.bad ? nan : st.m_run[r];
-          a.part_l[row * a.num_parts + p] = l_row[r];
+        for (int e = 0; e < EPL; ++e) dst[r * D + e] = st.acc(r, e);
+      if (lane == 0)
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+          a.part_m[(size_t)sid * RW + r] = st.bad ? nan : st.m(r);
+          a.part_l[(size_t)sid * RW + r] = l_row[r];
         }
-      }
     }
-    advance(cur);
-    if (cur.id < total) st.begin(a, cur.b, cur.g, a.lens[cur.b]);
+    if (left == 0) return;
+    const int b0 = cur.b, g0 = cur.g;
+    step(cur);
+    if (cur.b != b0 || cur.g != g0)
+      st.begin(a, cur.b, cur.g / S, cur.L, (cur.g % S) * RW);
+    else  // a new partition of the same unit: same queries, fresh statistics
+      st.restart();
   };
 
   uint4 ka[NL], va[NL], kb[NL], vb[NL];
@@ -771,27 +901,95 @@ decode_items_kernel(const DecodeArgs a) {
   }
 }
 
-using Launcher = void (*)(const DecodeArgs &, dim3, hipStream_t);
+// Merge of the stream kernel's segments: one workgroup per (query row,
+// sequence), thread d owns output element d.
+template <int D, int RW, int G>
+__global__ void __launch_bounds__(D)
+reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
+  constexpr float kNegInf = -std::numeric_limits<float>::infinity();
+  const int rowq = blockIdx.x;  // qi * Hq + h
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const int nq = a.nq, P = a.part_tokens, HU = a.Hkv * a.slices;
+  const int qi = rowq / a.Hq, h = rowq % a.Hq;
+  const int rr = qi * G + (h % G);             // row within the KV head
+  const int vg = (h / G) * a.slices + rr / RW;  // its unit within the sequence
+  const int r = rr % RW;                        // its row within the unit
+  const size_t row = (size_t)b * nq * a.Hq + rowq;
+  const float nan = __builtin_nanf("");
+  const int L = load_const(a.lens + b);
+  if (L < nq || L > a.max_blocks * a.bs) {
+    a.out[row * D + d] = nan;
+    if (d == 0 && a.lse) a.lse[row] = nan;
+    return;
+  }
+  const int64_t T = (int64_t)sa.tile_pre[a.B] * HU;
+  const int64_t N = sa.n_waves;
+  const int nt = sa.tile_pre[b + 1] - sa.tile_pre[b];
+  const int np = sa.part_pre[b + 1] - sa.part_pre[b];
+  const int64_t u0 = (int64_t)sa.tile_pre[b] * HU + (int64_t)vg * nt;  // first tile of the unit
+  const int64_t gp0 = (int64_t)sa.part_pre[b] * HU + (int64_t)vg * np;
+  const int ptiles = P > 0 ? P / kTile : nt;
+  // pass 1: maximum
+  float M = kNegInf;
+  bool bad = false;
+  // the wavefronts holding a partition's tiles, in order: from the one that
+  // holds its first tile, hop to the one holding the tile after each range
+  // (wavefronts with empty ranges hold no segment)
+  for (int p = 0; p < np; ++p) {
+    const int64_t first = u0 + (int64_t)p * ptiles;
+    const int64_t last = u0 + min(nt, (p + 1) * ptiles) - 1;
+    for (int64_t pos = first; pos <= last;) {
+      const int64_t ww = stream_wave(pos, T, N);
+      pos = (ww + 1) * T / N;
+      const float m = a.part_m[(size_t)(ww + gp0 + p) * RW + r];
+      bad |= m != m;
+      M = fmaxf(M, m);
+    }
+  }
+  float num = 0.f, den = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const int64_t first = u0 + (int64_t)p * ptiles;
+    const int64_t last = u0 + min(nt, (p + 1) * ptiles) - 1;
+    for (int64_t pos = first; pos <= last;) {
+      const int64_t ww = stream_wave(pos, T, N);
+      pos = (ww + 1) * T / N;
+      const size_t sid = (size_t)(ww + gp0 + p);
+      const float m = a.part_m[sid * RW + r];
+      const float f = m == kNegInf ? 0.f : exp2f(m - M);
+      num = fmaf(f, a.part_acc[(sid * RW + r) * D + d], num);
+      den = fmaf(f, a.part_l[sid * RW + r], den);
+    }
+  }
+  a.out[row * D + d] = bad || den == 0.f ? nan : num / den;
+  if (d == 0 && a.lse) a.lse[row] = bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
+}
 
-template <int DT, int D, int G, int RP, int W>
-void launch_decode(const DecodeArgs &a, dim3 grid, hipStream_t s) {
-  if constexpr (W == 0) {  // work-item kernel; grid.x persistent workgroups
-    hipLaunchKernelGGL((decode_items_kernel<DT, D, G, RP>), grid, dim3(kItemWaves * 64),
-                       (a.B + 1) * sizeof(int), s, a);
+using Launcher = void (*)(const DecodeArgs &, const StreamArgs &, dim3, hipStream_t);
+
+template <int DT, int D, int G, int RP, int NS, int W>
+void launch_decode(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
+  if constexpr (W == 0) {  // stream kernel + its reduce; grid.x persistent workgroups
+    hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, RP, NS>), grid, dim3(kStreamWaves * 64),
+                       2 * (a.B + 1) * sizeof(int), s, a, sa);
+    hipLaunchKernelGGL((reduce_stream_kernel<D, RP * NS, G>), dim3(a.nq * a.Hq, a.B), dim3(D),
+                       0, s, a, sa);
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, W>), grid, dim3(W * 64), 0, s, a);
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, NS, W>), grid, dim3(W * 64), 0, s,
+                       a);
   }
 }
 
 // Launcher for (dtype, D) and rows per wavefront RP = G * (query tokens
 // rounded up to a power of two): W = 4 or 8 wavefronts per workgroup of the
-// workgroup-split kernel, or W = 0 for the work-item kernel; nullptr if no
-// such kernel is built. Defined in decode_inst_<dtype>_d<D>.hip.
+// workgroup-split kernel, or W = 0 for the stream kernel (which also
+// launches its reduce); nullptr if no such kernel is built. Defined in
+// decode_inst_<dtype>_d<D>.hip.
 template <int DT, int D>
-Launcher pick_rows(int G, int RP, int W);
+Launcher pick_rows(int G, int RP, int NS, int W);
 
-// Largest RP with a kernel.
-constexpr int kMaxRows = 8;
+// Most query rows per KV head on the VALU kernels (as up to 4 slices of 4).
+constexpr int kMaxRows = 16;
 
 }  // namespace decode
 }  // namespace pkv

@@ -6,7 +6,7 @@ namespace pkv {
 namespace decode {
 
 template <int D>
-static void launch_verify(const DecodeArgs &a, dim3 grid, hipStream_t s) {
+static void launch_verify(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
   hipLaunchKernelGGL((verify_mfma_kernel<D, kVerifyWaves>), grid, dim3(kVerifyWaves * 64), 0, s,
                      a);
 }

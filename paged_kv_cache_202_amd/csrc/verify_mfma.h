@@ -81,7 +81,7 @@ verify_mfma_kernel(const DecodeArgs a) {
   const int ln = lane & 15, lg = lane >> 4;
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int nq = a.nq, G = a.Hq / a.Hkv, R = G * nq;
-  const int L = a.lens[b];
+  const int L = load_const(a.lens + b);
   const int max_ctx = a.max_blocks * a.bs;
   const float nan = __builtin_nanf("");
 
@@ -217,7 +217,9 @@ verify_mfma_kernel(const DecodeArgs a) {
                           ? (t_end - (t_begin + wave * kTile) + kStride - 1) / kStride
                           : 0;
   auto tile_t0 = [&](int k) { return t_begin + wave * kTile + k * kStride; };
-  auto table_at = [&](int k) { return trow[tile_t0(k < n_tiles ? k : n_tiles - 1) / a.bs]; };
+  auto table_at = [&](int k) {
+    return load_const(trow + tile_t0(k < n_tiles ? k : n_tiles - 1) / a.bs);
+  };
   if (n_tiles > 0) {
     uint4 ka[NC], va[NC], kb[NC], vb[NC];
     load(ka, va, tile_offset(tile_t0(0), table_at(0)));

@@ -51,7 +51,7 @@ class Workload:
     lognormal_median: float | None = None  # variable-length workload
     lognormal_sigma: float | None = None
     length_clip: tuple[int, int] | None = None
-    partition_tokens: int = 0  # 0 = library's choice
+    partition_tokens: int = 0  # 0 = library's choice; -1 = balanced stream
     shared_prefix: int = 0  # prefix-sharing workload: tokens shared by all
     unique_suffix: int = 0  # prefix-sharing workload: private tokens per seq
     cache_write_in_step: bool = True
@@ -81,7 +81,8 @@ WORKLOADS = {
     "llama3_8b_varlen_b256": Workload(
         index=3, name="llama3_8b_varlen_b256", dtype="bf16", q_heads=32,
         kv_heads=8, head_dim=128, block_size=16, batch=256, num_blocks=32768,
-        lognormal_median=1024.0, lognormal_sigma=1.0, length_clip=(16, 8192)),
+        lognormal_median=1024.0, lognormal_sigma=1.0, length_clip=(16, 8192),
+        partition_tokens=-1),
     "llama33_70b_b4_128k": Workload(
         index=4, name="llama33_70b_b4_128k", dtype="bf16", q_heads=64,
         kv_heads=8, head_dim=128, block_size=16, batch=4, num_blocks=32768,

@@ -69,4 +69,12 @@ def test_workspace_grows_with_partitions():
     s1 = pkv.paged_attention_workspace_size(4, 1, 64, 8, 128, 8192, 16, 512)
     rows, parts = 4 * 64, 131072 // 512
     assert s1 >= rows * parts * (128 + 2) * 4
+    # enough (sequence, KV head) pairs, one partition each: no workspace
+    assert pkv.paged_attention_workspace_size(64, 1, 32, 8, 128, 512, 16, 0) == 0
+    # short contexts: one partition each, whatever the pair count
     assert pkv.paged_attention_workspace_size(4, 1, 4, 2, 64, 3, 16, 0) == 0
+    # few pairs of long contexts, or balanced scheduling: a stream launch
+    assert pkv.paged_attention_workspace_size(4, 1, 64, 8, 128, 8192, 16, 0) > 0
+    assert pkv.paged_attention_workspace_size(64, 1, 32, 8, 128, 512, 16, -1) > 0
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.paged_attention_workspace_size(64, 1, 32, 8, 128, 512, 16, -2)

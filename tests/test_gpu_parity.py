@@ -79,6 +79,15 @@ CASES = [
     ((18, 200, 64), 8, 4, 128, "bf16", 4, 48),
     ((18, 200, 64), 8, 8, 128, "bf16", 3, 0),
     ((18, 200, 64), 8, 8, 64, "f32", 8, 32),
+    # balanced stream over mixed lengths (partition_tokens = -1)
+    ((1, 15, 16, 17, 100, 333, 2049, 700), 32, 8, 128, "bf16", 1, -1),
+    ((6, 9, 17, 33, 300, 1000), 4, 2, 64, "f32", 1, -1),
+    ((2049, 77, 1, 512), 64, 8, 128, "bf16", 1, -1),
+    ((31, 480, 1000), 8, 2, 256, "bf16", 1, -1),
+    # fp32 verify with 16 query rows per KV head: four row slices on VALU
+    ((30, 100, 517), 16, 4, 64, "f32", 4, 0),
+    ((30, 100, 517), 16, 4, 64, "f32", 4, -1),
+    ((30, 100, 517), 16, 4, 128, "f32", 3, 64),
 ]
 
 
@@ -92,7 +101,7 @@ def test_decode_matches_oracle(device, ci):
 
 def test_partition_sizes_agree(device):
     case = Case((3000, 1234), 32, 8, 128, 16, "bf16", seed=77, stack_seed=4)
-    outs = [case.run_gpu(p)[0] for p in (0, 512, 256, 128, 64, 16, 3008)]
+    outs = [case.run_gpu(p)[0] for p in (0, 512, 256, 128, 64, 16, 3008, -1)]
     ref, _ = case.run_oracle()
     for o in outs:
         assert np.abs(o - ref).max() <= 1e-2
@@ -216,8 +225,11 @@ def test_copy_on_write_step_bit_exact(device):
         assert np.array_equal(g[:, h][live], okp[:, h][live])
     q = wl.cast(wl.normal_array(root, 99, (4, 1, Hq, D)), dtype)
     out = torch.empty(4, 1, Hq, D, device=device)
+    ws_bytes = pkv.paged_attention_workspace_size(4, 1, Hq, Hkv, D, maxb, bs, 0)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=device)
     pkv.paged_attention_decode(out, q.to(device), kc, vc, torch.from_numpy(tables).to(device),
-                               torch.from_numpy(lens).to(device), 1 / math.sqrt(D))
+                               torch.from_numpy(lens).to(device), 1 / math.sqrt(D),
+                               workspace=ws)
     ref, _ = native.attention(storage(q), dtype, okp, ovp, dtype, np.array(ot, np.int32),
                               np.array(ol, np.int32), 1 / math.sqrt(D), bs)
     assert np.abs(out.cpu().numpy() - ref).max() <= 1e-2
