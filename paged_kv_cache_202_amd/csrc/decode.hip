@@ -18,44 +18,98 @@ namespace pkv {
 namespace decode {
 namespace {
 
-// One workgroup per (query row, sequence); thread d owns output element d.
+// Split-K merge: one workgroup of 256 threads per (query row, sequence).
+// D / 4 threads own four output elements each; the 1024 / D groups of them
+// take every (1024 / D)-th partition with a running maximum, and the groups
+// are merged in LDS: M = max m_p, out = sum 2^(m_p-M) acc_p / sum 2^(m_p-M) l_p.
+constexpr int kReduceThreads = 256;
+
 template <int D>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kReduceThreads)
 reduce_partitions_kernel(const DecodeArgs a) {
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
+  constexpr int TPG = D / 4;                    // threads per group
+  constexpr int NG = kReduceThreads / TPG;      // groups
+  __shared__ float sm_m[NG], sm_den[NG];
+  __shared__ float4 sm_num[NG][TPG];
   const int rowq = blockIdx.x;  // qi * Hq + h
   const int b = blockIdx.y;
-  const int d = threadIdx.x;
+  const int grp = threadIdx.x / TPG, t = threadIdx.x % TPG;
   const int L = load_const(a.lens + b);
-  const int qi = rowq / a.Hq;
   const size_t row = (size_t)b * a.nq * a.Hq + rowq;
   const float nan = __builtin_nanf("");
   if (L < a.nq || L > a.max_blocks * a.bs) {
-    a.out[row * D + d] = nan;
-    if (d == 0 && a.lse) a.lse[row] = nan;
+    if (grp == 0) {
+      a.out[row * D + 4 * t + 0] = nan;
+      a.out[row * D + 4 * t + 1] = nan;
+      a.out[row * D + 4 * t + 2] = nan;
+      a.out[row * D + 4 * t + 3] = nan;
+      if (t == 0 && a.lse) a.lse[row] = nan;
+    }
     return;
   }
-  (void)qi;
   const int np = (L + a.part_tokens - 1) / a.part_tokens;
   const float *pm = a.part_m + row * a.num_parts;
   const float *pl = a.part_l + row * a.num_parts;
-  const float *pacc = a.part_acc + row * a.num_parts * D;
-  float M = kNegInf;
+  const float4 *pacc = reinterpret_cast<const float4 *>(a.part_acc + row * a.num_parts * D);
+  float M = kNegInf, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   bool bad = false;
-  for (int p = 0; p < np; ++p) {
+#pragma unroll 4
+  for (int p = grp; p < np; p += NG) {
     const float m = pm[p];
+    const float l = pl[p];
+    const float4 v = pacc[(size_t)p * TPG + t];
     bad |= m != m;
-    M = fmaxf(M, m);
+    if (m == kNegInf) continue;  // no visible key in the partition
+    if (m > M) {
+      const float c = exp2f(M - m);  // 0 while M is still -inf
+      num.x *= c; num.y *= c; num.z *= c; num.w *= c;
+      den *= c;
+      M = m;
+    }
+    const float f = exp2f(m - M);
+    num.x = fmaf(f, v.x, num.x);
+    num.y = fmaf(f, v.y, num.y);
+    num.z = fmaf(f, v.z, num.z);
+    num.w = fmaf(f, v.w, num.w);
+    den = fmaf(f, l, den);
   }
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const float m = pm[p];
-    const float f = m == kNegInf ? 0.f : exp2f(m - M);
-    num = fmaf(f, pacc[(size_t)p * D + d], num);
-    den = fmaf(f, pl[p], den);
+  // a group's bad flag is the same in all its threads: fold it into M
+  if (t == 0) {
+    sm_m[grp] = bad ? nan : M;
+    sm_den[grp] = den;
   }
-  a.out[row * D + d] = bad || den == 0.f ? nan : num / den;
-  if (d == 0 && a.lse) a.lse[row] = bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
+  sm_num[grp][t] = num;
+  __syncthreads();
+  if (grp != 0) return;
+  float Mt = kNegInf;
+  bool any_bad = false;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    any_bad |= sm_m[g] != sm_m[g];
+    Mt = fmaxf(Mt, sm_m[g]);
+  }
+  float dt = 0.f;
+  float4 nt = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const float mg = sm_m[g];
+    const float f = mg == kNegInf || mg != mg ? 0.f : exp2f(mg - Mt);
+    const float4 v = sm_num[g][t];
+    nt.x = fmaf(f, v.x, nt.x);
+    nt.y = fmaf(f, v.y, nt.y);
+    nt.z = fmaf(f, v.z, nt.z);
+    nt.w = fmaf(f, v.w, nt.w);
+    dt = fmaf(f, sm_den[g], dt);
+  }
+  const bool nan_out = any_bad || dt == 0.f;
+  float *o = a.out + row * D + 4 * t;
+  o[0] = nan_out ? nan : nt.x / dt;
+  o[1] = nan_out ? nan : nt.y / dt;
+  o[2] = nan_out ? nan : nt.z / dt;
+  o[3] = nan_out ? nan : nt.w / dt;
+  if (t == 0 && a.lse) a.lse[row] = nan_out ? nan : (Mt + log2f(dt)) * kLn2;
 }
 
 int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 0; }
@@ -67,21 +121,34 @@ int next_pow2(int x) {
 }
 
 // Launch plan. The chip holds about kResidentWaves decode wavefronts at once
-// (256 CUs x 4 SIMDs x 2 wavefronts at ~190-230 VGPRs each).
-//  * Workgroup-split (waves = 4 or 8): one workgroup per (partition, KV
-//    head, sequence). With one partition it needs no workspace and no
-//    reduce launch: the choice when the (sequence, KV head) pairs alone
-//    fill a round of long-running wavefronts and lengths are alike.
+// (256 CUs x 4 SIMDs x 2 wavefronts of up to 256 VGPRs).
+//  * Workgroup-split (waves = 1, 4 or 8): one workgroup per (partition, KV
+//    head, sequence); its wavefronts take interleaved tiles of the
+//    partition and merge in LDS. With one partition it needs no workspace
+//    and no reduce launch. Short partitions (under 128 tiles) get one
+//    wavefront, long ones four or eight. Used for a requested partition
+//    size, and by default: one partition per context when the (sequence,
+//    KV head) pairs fill a round of wavefronts, else as many equal
+//    partitions as fill one.
 //  * Stream (waves = 0): kResidentWaves persistent wavefronts share the
-//    stream of all tiles equally, cut at requested partition boundaries;
-//    a reduce launch merges the segments. The choice for a requested
-//    partition size, for balanced scheduling of mixed lengths
-//    (partition_tokens = -1), and when the pairs are too few.
+//    stream of all tiles equally; a reduce launch merges their segments.
+//    Used for balanced scheduling of mixed lengths (partition_tokens = -1).
 constexpr int64_t kResidentWaves = 2048;
-constexpr int64_t kMaxStreamSeqs = 8000;  // LDS holds two per-sequence prefixes
+
+// Whether the stream kernel's LDS (tile rings plus two per-sequence
+// prefixes) fits one workgroup for B sequences.
+bool stream_fits(int dtype, int32_t D, int64_t B) {
+  int64_t bytes = 0;
+#define PKV_LDS_CASE(dt, d) \
+  if (dtype == dt && D == d) bytes = stream_lds_bytes<dt, d>(B);
+  PKV_LDS_CASE(PKV_F32, 64) PKV_LDS_CASE(PKV_F32, 128) PKV_LDS_CASE(PKV_F32, 256)
+  PKV_LDS_CASE(PKV_BF16, 64) PKV_LDS_CASE(PKV_BF16, 128) PKV_LDS_CASE(PKV_BF16, 256)
+#undef PKV_LDS_CASE
+  return bytes > 0 && bytes <= kLdsLimit;
+}
 
 struct Plan {
-  int waves;          // 4 or 8: workgroup-split kernel; 0: stream kernel
+  int waves;            // 1, 4 or 8: workgroup-split kernel; 0: stream kernel
   int32_t part_tokens;  // stream: 0 = no partition cuts
   int32_t num_parts;    // workgroup-split: partitions per context
   int32_t grid_x;
@@ -90,39 +157,38 @@ struct Plan {
 Plan plan_launch(int64_t B, int64_t Hkv, int64_t max_ctx, int32_t req, bool stream_ok) {
   Plan pl{};
   const int64_t units = B * Hkv;
-  const int64_t whole = (max_ctx + kTile - 1) / kTile * kTile;  // one partition
-  bool stream;
-  int64_t P;
-  if (req == -1) {
-    stream = true;
-    P = 0;
-  } else if (req > 0) {
-    P = req;
-    stream = (max_ctx + P - 1) / P > 1;
-  } else {  // stream only long contexts of too few pairs
-    stream = units * 8 < kResidentWaves && max_ctx >= 1024;
-    P = stream ? 0 : whole;
-  }
-  if (stream && stream_ok && B <= kMaxStreamSeqs) {
+  if (req == -1 && stream_ok) {
     pl.waves = 0;
-    pl.part_tokens = (int32_t)P;
-    pl.num_parts = P > 0 ? (int32_t)((max_ctx + P - 1) / P) : 1;
+    pl.part_tokens = 0;
+    pl.num_parts = 1;
     pl.grid_x = (int32_t)(kResidentWaves / kStreamWaves);
     return pl;
   }
-  if (P <= 0) P = whole;
+  const int64_t whole = (max_ctx + kTile - 1) / kTile * kTile;  // one partition
+  int64_t P = req > 0 ? req : whole;
+  if (req == 0 && units * 8 < kResidentWaves && max_ctx >= 1024) {
+    // too few pairs: split every context into enough partitions of eight
+    // wavefronts to fill a round
+    const int64_t np = (kResidentWaves + units * 8 - 1) / (units * 8);
+    P = ((max_ctx + np - 1) / np + kTile - 1) / kTile * kTile;
+  }
   pl.part_tokens = (int32_t)P;
   pl.num_parts = (int32_t)((max_ctx + P - 1) / P);
   if (pl.num_parts < 1) pl.num_parts = 1;
   const int64_t tiles_per_part = (P + kTile - 1) / kTile;
-  pl.waves = (tiles_per_part >= 64 && units * pl.num_parts * 8 <= 2 * kResidentWaves) ? 8 : 4;
   pl.grid_x = pl.num_parts;
+  if (tiles_per_part < 128)
+    pl.waves = 1;
+  else if (tiles_per_part >= 256 && units * pl.num_parts * 8 <= 2 * kResidentWaves)
+    pl.waves = 8;
+  else
+    pl.waves = 4;
   return pl;
 }
 
 template <int D>
 void launch_reduce(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((reduce_partitions_kernel<D>), grid, dim3(D), 0, s, a);
+  hipLaunchKernelGGL((reduce_partitions_kernel<D>), grid, dim3(kReduceThreads), 0, s, a);
 }
 
 Launcher pick_reduce(int D) {
@@ -140,24 +206,25 @@ size_t partial_bytes(int64_t rows, int32_t NP, int32_t D) {
   return align_up((size_t)rows * NP * D * 4, 256) + 2 * align_up((size_t)rows * NP * 4, 256);
 }
 
-// Stream launch workspace: the two per-sequence prefixes, then segment
-// partials acc [S, RP, D], m, l [S, RP] with S = N + units * NP segment ids.
-size_t stream_segments(int64_t units, int32_t NP) { return kResidentWaves + units * NP; }
-size_t stream_bytes(int64_t B, int64_t units, int32_t NP, int32_t RP, int32_t D) {
-  const size_t S = stream_segments(units, NP);
-  return 2 * align_up((size_t)(B + 1) * 4, 256) + align_up(S * RP * D * 4, 256) +
+// Stream launch workspace: the per-sequence tile prefix, then segment
+// partials acc [S, RP, D], m, l [S, RP] with S = N + units segment ids
+// (segment id w + u: wavefront w < N, unit u < units).
+size_t stream_segments(int64_t units) { return kResidentWaves + units; }
+size_t stream_bytes(int64_t B, int64_t units, int32_t RP, int32_t D) {
+  const size_t S = stream_segments(units);
+  return align_up((size_t)(B + 1) * 4, 256) + align_up(S * RP * D * 4, 256) +
          2 * align_up(S * RP * 4, 256);
 }
 
-Launcher pick_launcher(int dtype, int D, int G, int RP, int NS, int W) {
+Launcher pick_launcher(int dtype, int D, int G, int RP, int W) {
   if (dtype == PKV_F32) {
-    if (D == 64) return pick_rows<PKV_F32, 64>(G, RP, NS, W);
-    if (D == 128) return pick_rows<PKV_F32, 128>(G, RP, NS, W);
-    if (D == 256) return pick_rows<PKV_F32, 256>(G, RP, NS, W);
+    if (D == 64) return pick_rows<PKV_F32, 64>(G, RP, W);
+    if (D == 128) return pick_rows<PKV_F32, 128>(G, RP, W);
+    if (D == 256) return pick_rows<PKV_F32, 256>(G, RP, W);
   } else if (dtype == PKV_BF16) {
-    if (D == 64) return pick_rows<PKV_BF16, 64>(G, RP, NS, W);
-    if (D == 128) return pick_rows<PKV_BF16, 128>(G, RP, NS, W);
-    if (D == 256) return pick_rows<PKV_BF16, 256>(G, RP, NS, W);
+    if (D == 64) return pick_rows<PKV_BF16, 64>(G, RP, W);
+    if (D == 128) return pick_rows<PKV_BF16, 128>(G, RP, W);
+    if (D == 256) return pick_rows<PKV_BF16, 256>(G, RP, W);
   }
   return nullptr;
 }
@@ -199,28 +266,27 @@ static int check_rows(int dtype, int32_t nq, int32_t G) {
 // Workspace a launch needs, for either kernel family (the larger of the two
 // possibilities, so the size does not depend on the dtype).
 // How the VALU kernels hold the G * nq query rows of a KV head (rounded up
-// to a power of two): sets of RP <= 4 rows, NS <= 2 sets per wavefront
-// sharing every loaded tile, and S wavefront slices when more rows remain
-// (a slice streams the KV head's bytes again, so it is the last resort).
-static void row_split(int32_t G, int32_t nq, int32_t *RP, int32_t *NS, int32_t *S) {
+// to a power of two): up to RP = 8 rows per wavefront, all fed by every
+// tile the wavefront loads, and S wavefront slices when more rows remain (a
+// slice streams the KV head's bytes again, so it is the last resort).
+static void row_split(int32_t G, int32_t nq, int32_t *RP, int32_t *S) {
   const int32_t all = G * next_pow2(nq);
-  *RP = all < 4 ? all : 4;
-  *NS = all / *RP < 2 ? all / *RP : 2;
-  *S = all / (*RP * *NS);
+  *RP = all < 8 ? all : 8;
+  *S = all / *RP;
 }
 
 static size_t workspace_need(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t D,
                              int64_t max_ctx, int32_t part) {
-  int32_t RP, NS, S;
-  row_split(Hq / Hkv, nq, &RP, &NS, &S);
+  int32_t RP, S;
+  row_split(Hq / Hkv, nq, &RP, &S);
   const int64_t units = (int64_t)B * Hkv * S;
-  const int32_t RW = RP * NS;
+  const int32_t RW = RP;
   size_t need = 0;
   for (bool stream_ok : {true, false}) {
     const Plan pl = plan_launch(B, Hkv, max_ctx, part, stream_ok);
     size_t n = 0;
     if (pl.waves == 0)
-      n = stream_bytes(B, units, pl.num_parts, RW, D);
+      n = stream_bytes(B, units, RW, D);
     else if (pl.num_parts > 1)
       n = partial_bytes((int64_t)B * nq * Hq, pl.num_parts, D);
     if (n > need) need = n;
@@ -256,13 +322,14 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   const int G = Hq / Hkv;
   if (int rc = check_rows(dtype, nq, G)) return rc;
   const bool mfma = use_mfma(dtype, nq, G);
-  const Plan pl = plan_launch(B, Hkv, (int64_t)max_blocks * bs, part, !mfma);
+  const Plan pl =
+      plan_launch(B, Hkv, (int64_t)max_blocks * bs, part, !mfma && stream_fits(dtype, D, B));
   const int32_t P = pl.part_tokens, NP = pl.num_parts;
-  int32_t RP, NS, S;
-  row_split(G, nq, &RP, &NS, &S);
+  int32_t RP, S;
+  row_split(G, nq, &RP, &S);
   if (mfma) S = 1;
-  const int32_t RW = RP * NS;
-  Launcher launch = mfma ? pick_verify(D) : pick_launcher(dtype, D, G, RP, NS, pl.waves);
+  const int32_t RW = RP;
+  Launcher launch = mfma ? pick_verify(D) : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
   const bool streamed = pl.waves == 0 && !mfma;
   const dim3 grid = streamed ? dim3(pl.grid_x) : dim3(NP, Hkv * S, B);
@@ -288,7 +355,7 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   StreamArgs sa{};
   size_t need = 0;
   if (streamed)
-    need = stream_bytes(B, (int64_t)B * Hkv * S, NP, RW, D);
+    need = stream_bytes(B, (int64_t)B * Hkv * S, RW, D);
   else if (NP > 1)
     need = partial_bytes((int64_t)B * nq * Hq, NP, D);
   if (need) {
@@ -298,10 +365,8 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
     if ((uintptr_t)workspace % 256) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
     char *w = (char *)workspace;
     if (streamed) {
-      const size_t nseg = stream_segments((int64_t)B * Hkv * S, NP);
+      const size_t nseg = stream_segments((int64_t)B * Hkv * S);
       sa.tile_pre = (int32_t *)w;
-      w += align_up((size_t)(B + 1) * 4, 256);
-      sa.part_pre = (int32_t *)w;
       w += align_up((size_t)(B + 1) * 4, 256);
       sa.n_waves = (int32_t)(pl.grid_x * kStreamWaves);
       a.part_acc = (float *)w;

@@ -5,17 +5,18 @@ namespace pkv {
 namespace decode {
 
 template <>
-Launcher pick_rows<PKV_BF16, 256>(int G, int RP, int NS, int W) {
+Launcher pick_rows<PKV_BF16, 256>(int G, int RP, int W) {
   constexpr int DT = PKV_BF16, D = 256;
-#define PKV_CASE(g, rp, ns)                                              \
-  if (G == g && RP == rp && NS == ns)                                    \
-    return W == 8   ? &launch_decode<DT, D, g, rp, ns, 8>               \
-           : W == 4 ? &launch_decode<DT, D, g, rp, ns, 4>               \
-                    : &launch_decode<DT, D, g, rp, ns, 0>;
-  PKV_CASE(1, 1, 1) PKV_CASE(1, 2, 1) PKV_CASE(1, 4, 1) PKV_CASE(1, 4, 2)
-  PKV_CASE(2, 2, 1) PKV_CASE(2, 4, 1) PKV_CASE(2, 4, 2)
-  PKV_CASE(4, 4, 1) PKV_CASE(4, 4, 2)
-  PKV_CASE(8, 4, 2)
+#define PKV_CASE(g, rp)                                                  \
+  if (G == g && RP == rp)                                                \
+    return W == 8   ? &launch_decode<DT, D, g, rp, 8>                   \
+           : W == 4 ? &launch_decode<DT, D, g, rp, 4>                   \
+           : W == 1 ? &launch_decode<DT, D, g, rp, 1>                   \
+                    : &launch_decode<DT, D, g, rp, 0>;
+  PKV_CASE(1, 1) PKV_CASE(1, 2) PKV_CASE(1, 4) PKV_CASE(1, 8)
+  PKV_CASE(2, 2) PKV_CASE(2, 4) PKV_CASE(2, 8)
+  PKV_CASE(4, 4) PKV_CASE(4, 8)
+  PKV_CASE(8, 8)
 #undef PKV_CASE
   return nullptr;
 }

@@ -17,10 +17,12 @@
 //     query heads of a KV head (times the query tokens) are handled by the
 //     same wavefront, so every K/V byte loaded from HBM feeds all of them.
 //   * a wavefront consumes one 16-token tile per step. The tile of one KV
-//     head is a contiguous 16 * D-element run of one block, read with one
-//     16-byte load per lane per 1 KiB, fully coalesced; lanes own a slice of
-//     D for a few tokens, so the loads feed the arithmetic directly from
-//     registers with no LDS staging.
+//     head is a contiguous 16 * D-element run of one block, gathered with
+//     one 16-byte direct-to-LDS load per lane per 1 KiB (fully coalesced)
+//     into a per-wavefront ring of LDS slots: tiles in flight hold no
+//     registers, so two (16 KiB) stay in flight per wavefront even with
+//     eight query rows. Each lane reads back the 16 bytes it gathered --
+//     its slice of D for a few tokens -- just before the tile is used.
 //   * q.k partial sums are reduced across the lanes that share a token with
 //     a reduce-scatter (each step halves the values a lane carries), so
 //     every lane ends with whole scores; exponentials are taken once per
@@ -71,7 +73,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // needs.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+  // every lane reads a valid source lane for the patterns used here, so the
+  // previous value of the destination is never kept and needs no set-up
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
 }
 
 // Compile-time loop: f(integral_constant<int, I>) for I = 0 .. N-1.
@@ -237,21 +241,133 @@ __device__ __forceinline__ T load_const(const T *p) {
 
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-// K/V rows are read once per step: non-temporal loads keep them from
-// displacing reusable lines (tables, queries) and measured faster on MI355X.
+#define PKV_LDS __attribute__((address_space(3)))
+
+// Cache policy of the K/V gathers: non-temporal. Every K/V byte is read once
+// per call, so the rows should not displace reusable lines (tables, queries).
+constexpr int kKvNonTemporal = 2;
+
+// The same policy for a gather into registers.
 __device__ __forceinline__ uint4 stream_load(const char *p) {
   const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
-template <int NL>
-__device__ __forceinline__ void load_tile(uint4 (&kr)[NL], uint4 (&vr)[NL], const char *kp,
-                                          const char *vp) {
-#pragma unroll
-  for (int i = 0; i < NL; ++i) kr[i] = stream_load(kp + i * 1024);
-#pragma unroll
-  for (int i = 0; i < NL; ++i) vr[i] = stream_load(vp + i * 1024);
+// N (2, 4 or 8) 16-byte LDS reads at p, p + 1 KiB, ..., and a wait for
+// them, in one statement so that no use of a result can be scheduled before
+// the wait.
+template <int N>
+__device__ __forceinline__ void lds_rows(u32x4_t *t, const PKV_LDS char *p) {
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1])
+        : "v"(p)
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(p)
+        : "memory");
+  } else {
+    static_assert(N == 8, "2, 4 or 8 rows per read");
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+          "=&v"(t[6]), "=&v"(t[7])
+        : "v"(p)
+        : "memory");
+  }
 }
+
+// Wait until at most VM vector-memory operations of this wavefront are
+// pending.
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt is six bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"i"(VM) : "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Per-wavefront ring of LDS slots that K/V tiles are gathered into with
+// direct-to-LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at
+// slot + 16 i). A tile in flight holds no VGPRs; it is read back into
+// registers, one 16-byte row piece per lane, just before it is consumed.
+// Slot layout: K rows 0 .. NL-1 (1 KiB each, one per load), then V rows.
+// The wavefront waits for its own loads only (vmcnt), so the ring needs no
+// barrier; the compiler cannot track which LDS bytes a pending DMA writes,
+// so the read-back and its waits are written out here.
+// ---------------------------------------------------------------------------
+template <int NL>
+struct TileRing {
+  static constexpr int kTileBytes = 2 * NL * 1024;
+  // at least one tile, else as many as fit 16 KiB: two tiles of a
+  // D = 128 bf16 head, four of a D = 64 one
+  static constexpr int kSlots = kTileBytes >= 16384 ? 1 : 16384 / kTileBytes;
+  static constexpr int kBytes = kSlots * kTileBytes;  // per wavefront
+  static constexpr int kLoads = 2 * NL;               // DMA instructions per tile
+  static_assert((kSlots & (kSlots - 1)) == 0, "slot count must be a power of two");
+
+  PKV_LDS char *base;  // this wavefront's ring (wavefront-uniform)
+  const PKV_LDS char *mine;  // base + 16 * lane
+
+  __device__ __forceinline__ void init(PKV_LDS char *ring, int lane) {
+    base = ring;
+    mine = ring + lane * 16;
+  }
+
+  // Gather one tile into `slot`: kp / vp already include this lane's 16 B.
+  __device__ __forceinline__ void stage(int slot, const char *kp, const char *vp) {
+    PKV_LDS char *dst = base + slot * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_global_load_lds(kp + i * 1024, dst + i * 1024, 16, 0, kKvNonTemporal);
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_global_load_lds(vp + i * 1024, dst + (NL + i) * 1024, 16, 0,
+                                       kKvNonTemporal);
+  }
+
+  // Read back the K half (HALF = 0) or the V half (HALF = 1) of the tile in
+  // `slot` once its gathers have landed. `ahead` (wavefront-uniform, below
+  // kSlots) whole tiles were staged after it and stay in flight:
+  // vector-memory loads complete in issue order, so the wait leaves exactly
+  // those (and, for K, this tile's V rows) pending. Other loads or stores
+  // issued later only make the wait stricter. Only the wait depends on
+  // `ahead`, so the reads themselves are not duplicated per case.
+  template <int HALF>
+  __device__ __forceinline__ void fetch(int slot, int ahead, uint4 (&r)[NL]) const {
+    static_for<kSlots>([&](auto ac) {
+      constexpr int A = decltype(ac)::value;
+      if (ahead == A) wait_vmcnt<A * kLoads + (HALF == 0 ? NL : 0)>();
+    });
+    const PKV_LDS char *p = mine + slot * kTileBytes + HALF * NL * 1024;
+    u32x4_t t[NL];
+    if constexpr (NL <= 8) {
+      lds_rows<NL>(t, p);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NL / 8; ++c) lds_rows<8>(t + 8 * c, p + c * 8192);
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) r[i] = make_uint4(t[i].x, t[i].y, t[i].z, t[i].w);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // One wavefront's attention state for RP query rows of one KV head:
@@ -340,9 +456,11 @@ struct DecodeWave {
     }
   }
 
-  // Consume one 16-token tile starting at logical token t0 whose K/V rows
-  // are in kr / vr.
-  __device__ __forceinline__ void process(const uint4 (&kr)[NL], const uint4 (&vr)[NL], int t0,
+  // Consume one 16-token tile starting at logical token t0: its K rows are
+  // in kr, and get_v(vr) supplies its V rows once the weights are known (so
+  // the V half of a gather may still be landing during the q.k work).
+  template <class GetV>
+  __device__ __forceinline__ void process(const uint4 (&kr)[NL], GetV &&get_v, int t0,
                                           float scale_log2) {
     // partial q.k over this lane's EPL dims: x[r * NL + i]
     float x[V];
@@ -412,8 +530,14 @@ struct DecodeWave {
     // every lane of the group needs all V weights of its tokens: each is
     // broadcast from its owner lane right before its FMAs
     // in a tail tile, slots past the context may hold stale bits (even NaN):
-    // their V is zeroed so that 0 * NaN cannot reach acc
-    const bool tail = t0 + kTile > min_lim;
+    // their V is zeroed (before widening) so that 0 * NaN cannot reach acc
+    uint4 vr[NL];
+    get_v(vr);
+    if (t0 + kTile > min_lim) {  // wavefront-uniform: only a context's last tile
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        if (t0 + i * TPL + grp >= L) vr[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     static_for<NL>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       float vv[EPL];
@@ -425,10 +549,6 @@ struct DecodeWave {
       } else {
         vv[0] = __uint_as_float(vr[i].x); vv[1] = __uint_as_float(vr[i].y);
         vv[2] = __uint_as_float(vr[i].z); vv[3] = __uint_as_float(vr[i].w);
-      }
-      if (tail && t0 + i * TPL + grp >= L) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) vv[e] = 0.f;
       }
       static_for<RP>([&](auto rc) {
         constexpr int r = decltype(rc)::value;
@@ -457,50 +577,6 @@ struct DecodeWave {
   }
 };
 
-// NS row sets of RP rows each in one wavefront (RW = NS * RP rows): every
-// loaded K/V tile feeds all of them, so a KV head's rows need not be split
-// over wavefronts that would each stream the same bytes.
-template <int DT, int D, int G, int RP, int NS>
-struct DecodeWaveSet {
-  using One = DecodeWave<DT, D, G, RP>;
-  static constexpr int LPT = One::LPT, EPL = One::EPL, RW = RP * NS;
-  One w[NS];
-  int bad;  // a tile of the current item came from a bad table entry
-  int d0;
-
-  __device__ __forceinline__ void init(int lane) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) w[j].init(lane);
-    d0 = w[0].d0;
-  }
-  __device__ __forceinline__ void begin(const DecodeArgs &a, int b, int g, int L, int row0) {
-    bad = 0;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) w[j].begin(a, b, g, L, row0 + j * RP);
-  }
-  __device__ __forceinline__ void restart() {
-    bad = 0;
-#pragma unroll
-    for (int j = 0; j < NS; ++j) w[j].restart();
-  }
-  __device__ __forceinline__ void process(const uint4 (&kr)[One::NL], const uint4 (&vr)[One::NL],
-                                          int t0, float scale_log2) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) w[j].process(kr, vr, t0, scale_log2);
-  }
-  __device__ __forceinline__ void totals(float (&l_row)[RW]) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      float l[RP];
-      w[j].totals(l);
-#pragma unroll
-      for (int r = 0; r < RP; ++r) l_row[j * RP + r] = l[r];
-    }
-  }
-  __device__ __forceinline__ float acc(int r, int e) const { return w[r / RP].acc[r % RP][e]; }
-  __device__ __forceinline__ float m(int r) const { return w[r / RP].m_run[r % RP]; }
-};
-
 // Byte offset of the 16-token tile at logical token t0 of KV head g in
 // block blk, for this lane.
 template <int TB>
@@ -516,20 +592,33 @@ __device__ __forceinline__ size_t tile_bytes_offset(const DecodeArgs &a, int g, 
 // in LDS. Used when there are enough (sequence, KV head) pairs to fill the
 // chip with one partition each.
 // ---------------------------------------------------------------------------
-template <int DT, int D, int G, int RP, int NS, int kWaves>
+template <int DT, int D, int G, int RP, int kWaves>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_partition_kernel(const DecodeArgs a) {
-  using W = DecodeWaveSet<DT, D, G, RP, NS>;
-  constexpr int RW = W::RW;  // query rows of this wavefront
+  using W = DecodeWave<DT, D, G, RP>;
+  constexpr int RW = RP;  // query rows of this wavefront
   using Gm = Geo<DT, D>;
   constexpr int NL = Gm::NL, EPL = Gm::EPL;
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
+  using Ring = TileRing<NL>;
+  constexpr int kSlots = Ring::kSlots;
 
-  __shared__ float sm_acc[kWaves][RW][D];
-  __shared__ float sm_m[kWaves][RW];
-  __shared__ float sm_l[kWaves][RW];
-  __shared__ int sm_bad[kWaves];
+  // the tile rings while streaming; the wavefronts' partials once done
+  struct Merge {
+    float acc[kWaves][RW][D];
+    float m[kWaves][RW];
+    float l[kWaves][RW];
+    int bad[kWaves];
+  };
+  __shared__ union {
+    u32x4_t ring[kWaves * Ring::kBytes / 16];
+    Merge mg;
+  } sm;
+  auto &sm_acc = sm.mg.acc;
+  auto &sm_m = sm.mg.m;
+  auto &sm_l = sm.mg.l;
+  auto &sm_bad = sm.mg.bad;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -573,11 +662,9 @@ decode_partition_kernel(const DecodeArgs a) {
     return tile_bytes_offset<Gm::TB>(a, g, t0, blk, lane);
   };
 
-  // Software pipeline: the next tile's K/V loads are in flight while the
-  // current tile is consumed. The steady-state loop issues its loads
-  // unconditionally (two tiles per trip, alternating register sets) so the
-  // compiler's wait counts leave the prefetched loads outstanding; the last
-  // one or two tiles are peeled. Block ids are read one trip ahead.
+  // Pipeline: up to kSlots tiles are gathered into the wavefront's LDS ring
+  // ahead of the one being consumed; a slot is refilled as soon as its tile
+  // has been read back. Block ids are read one tile before their gather.
   const int n_tiles = t_begin + wave * kTile < t_end
                           ? (t_end - (t_begin + wave * kTile) + kStride - 1) / kStride
                           : 0;
@@ -586,51 +673,52 @@ decode_partition_kernel(const DecodeArgs a) {
     return load_const(trow + tile_t0(k < n_tiles ? k : n_tiles - 1) / a.bs);
   };
   if (n_tiles > 0) {
-    uint4 ka[NL], va[NL], kb[NL], vb[NL];
-    {
-      const size_t off = tile_offset(tile_t0(0), table_at(0));
-      load_tile<NL>(ka, va, kbase + off, vbase + off);
-    }
-    int blk1 = table_at(1), blk2 = table_at(2);
-    int k = 0;
-    for (; k + 2 < n_tiles; k += 2) {
-      const int nb1 = table_at(k + 3), nb2 = table_at(k + 4);
-      {
-        const size_t off = tile_offset(tile_t0(k + 1), blk1);
-        load_tile<NL>(kb, vb, kbase + off, vbase + off);
+    Ring ring;
+    ring.init((PKV_LDS char *)&sm.ring[0] + wave * Ring::kBytes, lane);
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k)
+      if (k < n_tiles) {
+        const size_t off = tile_offset(tile_t0(k), table_at(k));
+        ring.stage(k, kbase + off, vbase + off);
       }
-      st.process(ka, va, tile_t0(k), a.scale_log2);
-      {
-        const size_t off = tile_offset(tile_t0(k + 2), blk2);
-        load_tile<NL>(ka, va, kbase + off, vbase + off);
-      }
-      st.process(kb, vb, tile_t0(k + 1), a.scale_log2);
-      blk1 = nb1;
-      blk2 = nb2;
-    }
-    if (k + 1 < n_tiles) {
-      const size_t off = tile_offset(tile_t0(k + 1), blk1);
-      load_tile<NL>(kb, vb, kbase + off, vbase + off);
-      st.process(ka, va, tile_t0(k), a.scale_log2);
-      st.process(kb, vb, tile_t0(k + 1), a.scale_log2);
-    } else {
-      st.process(ka, va, tile_t0(k), a.scale_log2);
+    int blk_next = table_at(kSlots);
+    // the scale is waited for here, not at its first use inside the loop,
+    // where the wait would also catch each step's block-id read
+    float scale_log2 = a.scale_log2;
+    asm volatile("" : "+s"(scale_log2));
+    for (int k = 0; k < n_tiles; ++k) {
+      const int slot = k & (kSlots - 1);
+      const int ahead = min(n_tiles - 1 - k, kSlots - 1);
+      uint4 kr[NL];
+      ring.template fetch<0>(slot, ahead, kr);
+      st.process(
+          kr,
+          [&](uint4 (&vr)[NL]) {
+            ring.template fetch<1>(slot, ahead, vr);
+            if (k + kSlots < n_tiles) {  // the slot is free again: refill it
+              const size_t off = tile_offset(tile_t0(k + kSlots), blk_next);
+              ring.stage(slot, kbase + off, vbase + off);
+              blk_next = table_at(k + kSlots + 1);
+            }
+          },
+          tile_t0(k), scale_log2);
     }
   }
 
   // ---- wavefront totals, then merge the wavefronts in LDS ------------------
   float l_row[RW];
   st.totals(l_row);
+  __syncthreads();  // the partials overwrite the other wavefronts' rings
   if (lane < W::LPT) {
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) sm_acc[wave][r][st.d0 + e] = st.acc(r, e);
+      for (int e = 0; e < EPL; ++e) sm_acc[wave][r][st.d0 + e] = st.acc[r][e];
   }
   if (lane == 0) {  // bad is wavefront-uniform: it comes from scalar table reads
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
-      sm_m[wave][r] = st.m(r);
+      sm_m[wave][r] = st.m_run[r];
       sm_l[wave][r] = l_row[r];
     }
     sm_bad[wave] = st.bad;
@@ -671,16 +759,16 @@ decode_partition_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Stream kernel (stream-K decomposition) for mixed lengths and split
-// contexts. All (sequence, KV head) units are laid end to end as one stream
-// of 16-token tiles -- unit u = b * Hkv + g holds ceil(L_b / 16) tiles -- and
+// Stream kernel (stream-K decomposition) for batches of mixed lengths. All
+// (sequence, KV head slice) units are laid end to end as one stream of
+// 16-token tiles -- unit u = b * HU + g holds ceil(L_b / 16) tiles -- and
 // persistent wavefront w takes tiles [w T / N, (w + 1) T / N) of it: every
 // wavefront gets the same number of tiles, whatever the lengths. A
-// wavefront's range is cut into segments at unit boundaries, at multiples of
-// the requested partition size, and at its own ends; each segment leaves
-// unnormalised partials (m, l, acc) under the id w + (global index of its
-// partition), unique because both terms only grow along the stream. The
-// reduce kernel finds a row's segments from the same arithmetic. No atomics,
+// wavefront's range is cut into segments at unit boundaries and at its own
+// ends; each segment leaves unnormalised partials (m, l, acc) under the id
+// w + u, unique because both terms only grow along the stream. The
+// wavefronts holding a unit's tiles are consecutive, so the reduce kernel
+// finds a unit's segments from its first and last tile alone. No atomics,
 // no LDS merge, no barriers after the prefix sums are built.
 // ---------------------------------------------------------------------------
 constexpr int kStreamWaves = 4;  // wavefronts per workgroup (independent)
@@ -688,15 +776,11 @@ constexpr int kStreamWaves = 4;  // wavefronts per workgroup (independent)
 // Stream geometry shared by the stream kernel and its reduce kernel.
 struct StreamArgs {
   int32_t *tile_pre;  // [B + 1] tiles per unit, prefix over sequences
-  int32_t *part_pre;  // [B + 1] partitions per unit, prefix over sequences
   int32_t n_waves;    // N
 };
 
 __device__ __forceinline__ int seq_tiles(int L, int nq, int max_ctx) {
   return (L >= nq && L <= max_ctx) ? (L + kTile - 1) / kTile : 0;
-}
-__device__ __forceinline__ int seq_parts(int L, int nq, int max_ctx, int P) {
-  return (L >= nq && L <= max_ctx) ? (P > 0 ? (L + P - 1) / P : 1) : 0;
 }
 // Wavefront whose range holds stream tile `pos`: the largest w with
 // floor(w T / N) <= pos.
@@ -704,64 +788,49 @@ __device__ __forceinline__ int64_t stream_wave(int64_t pos, int64_t T, int64_t N
   return ((pos + 1) * N + T - 1) / T - 1;
 }
 
-template <int DT, int D, int G, int RP, int NS>
+template <int DT, int D, int G, int RP>
 __global__ void __launch_bounds__(kStreamWaves * 64)
 decode_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
-  using W = DecodeWaveSet<DT, D, G, RP, NS>;
-  constexpr int RW = W::RW;  // query rows of this wavefront
+  using W = DecodeWave<DT, D, G, RP>;
+  constexpr int RW = RP;  // query rows of this wavefront
   using Gm = Geo<DT, D>;
   constexpr int NL = Gm::NL, EPL = Gm::EPL;
   constexpr int kThreads = kStreamWaves * 64;
-  extern __shared__ int sm_dyn[];  // tile prefix [B + 1], then partition prefix [B + 1]
-  __shared__ int sm_scan[2][kThreads];
+  using Ring = TileRing<NL>;
+  constexpr int kSlots = Ring::kSlots;
+  extern __shared__ int sm_tp[];  // tile prefix [B + 1]
+  __shared__ int sm_scan[kThreads];
+  __shared__ u32x4_t sm_ring[kStreamWaves * Ring::kBytes / 16];
 
   // Units: each sequence contributes HU = Hkv * slices of them, unit vg of
   // a sequence being KV head vg / slices, row slice vg % slices.
-  const int B = a.B, P = a.part_tokens, nq = a.nq, S = a.slices, HU = a.Hkv * a.slices;
+  const int B = a.B, nq = a.nq, S = a.slices, HU = a.Hkv * a.slices;
   const int max_ctx = a.max_blocks * a.bs;
-  int *sm_tp = sm_dyn;
-  int *sm_pp = sm_dyn + B + 1;
 
-  // ---- prefix sums over sequences (every workgroup; workgroup 0 also
-  //      leaves them in the workspace for the reduce kernel) ---------------
+  // ---- prefix sum of tiles over sequences (every workgroup; workgroup 0
+  //      also leaves it in the workspace for the reduce kernel) ------------
   {
     const int per = (B + kThreads - 1) / kThreads;
     const int lo = min(B, (int)threadIdx.x * per), hi = min(B, lo + per);
-    int st_ = 0, sp_ = 0;
-    for (int b = lo; b < hi; ++b) {
-      const int L = load_const(a.lens + b);
-      st_ += seq_tiles(L, nq, max_ctx);
-      sp_ += seq_parts(L, nq, max_ctx, P);
-    }
-    sm_scan[0][threadIdx.x] = st_;
-    sm_scan[1][threadIdx.x] = sp_;
+    int st_ = 0;
+    for (int b = lo; b < hi; ++b) st_ += seq_tiles(load_const(a.lens + b), nq, max_ctx);
+    sm_scan[threadIdx.x] = st_;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scans
-      const int v0 = threadIdx.x >= off ? sm_scan[0][threadIdx.x - off] : 0;
-      const int v1 = threadIdx.x >= off ? sm_scan[1][threadIdx.x - off] : 0;
+    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
+      const int v = threadIdx.x >= off ? sm_scan[threadIdx.x - off] : 0;
       __syncthreads();
-      sm_scan[0][threadIdx.x] += v0;
-      sm_scan[1][threadIdx.x] += v1;
+      sm_scan[threadIdx.x] += v;
       __syncthreads();
     }
-    int rt = sm_scan[0][threadIdx.x] - st_, rp = sm_scan[1][threadIdx.x] - sp_;
+    int rt = sm_scan[threadIdx.x] - st_;
     for (int b = lo; b < hi; ++b) {
       sm_tp[b] = rt;
-      sm_pp[b] = rp;
-      const int L = load_const(a.lens + b);
-      rt += seq_tiles(L, nq, max_ctx);
-      rp += seq_parts(L, nq, max_ctx, P);
+      rt += seq_tiles(load_const(a.lens + b), nq, max_ctx);
     }
-    if (threadIdx.x == kThreads - 1) {
-      sm_tp[B] = sm_scan[0][kThreads - 1];
-      sm_pp[B] = sm_scan[1][kThreads - 1];
-    }
+    if (threadIdx.x == kThreads - 1) sm_tp[B] = sm_scan[kThreads - 1];
     __syncthreads();
     if (blockIdx.x == 0)
-      for (int i = threadIdx.x; i <= B; i += kThreads) {
-        sa.tile_pre[i] = sm_tp[i];
-        sa.part_pre[i] = sm_pp[i];
-      }
+      for (int i = threadIdx.x; i <= B; i += kThreads) sa.tile_pre[i] = sm_tp[i];
   }
 
   const int64_t T = (int64_t)__builtin_amdgcn_readfirstlane(sm_tp[B]) * HU;
@@ -771,11 +840,11 @@ decode_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
   const int n_tiles = (int)(pos1 - pos0);
   if (n_tiles <= 0) return;
   const int lane = threadIdx.x & 63;
-  const int ptiles = P > 0 ? P / kTile : 0;  // tiles per partition (0: unbounded)
 
   // A cursor is a tile of the stream: sequence b, unit g of the sequence
   // (KV head g / S, row slice g % S), tile k of the unit, plus the unit's
-  // tile count and the sequence's length.
+  // tile count and the sequence's length (kept in registers: once gathers
+  // are in flight, no LDS reads but the ring's).
   struct Cursor {
     int b, g, k, nt, L;
   };
@@ -818,91 +887,86 @@ decode_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
     return tile_bytes_offset<Gm::TB>(a, c.g / S, c.k * kTile, tile_bad ? 0 : blk, lane);
   };
 
-  Cursor cur = locate(pos0);
-  st.begin(a, cur.b, cur.g / S, cur.L, (cur.g % S) * RW);
-  int left = n_tiles;  // tiles of this wavefront not yet consumed
-  Cursor iss = cur;
-  if (n_tiles > 1) step(iss);
-  Cursor pre = iss;
-  if (n_tiles > 2) step(pre);
-  int issued = 1;  // tiles whose loads have been issued
-  int bad_a = 0, bad_b = 0;
-  const size_t off0 = offset(cur, table_entry(cur), bad_a);
-  int blk_iss = n_tiles > 1 ? table_entry(iss) : 0;
-  int blk_pre = n_tiles > 2 ? table_entry(pre) : 0;
+  Ring ring;
+  ring.init((PKV_LDS char *)&sm_ring[0] + (threadIdx.x >> 6) * Ring::kBytes, lane);
 
-  auto issue = [&](uint4 (&kr)[NL], uint4 (&vr)[NL], int &tile_bad) {
+  Cursor cur = locate(pos0);  // the tile to consume next
+  st.begin(a, cur.b, cur.g / S, cur.L, (cur.g % S) * RW);
+  Cursor iss = cur;    // the tile to gather next
+  int blk_iss = table_entry(iss);
+  int issued = 0;     // tiles whose gathers have been issued
+  int bad_slots = 0;  // bit s: the tile in slot s came from a bad table entry
+
+  auto issue = [&](int slot) {
+    int tile_bad;
     const size_t off = offset(iss, blk_iss, tile_bad);
-    load_tile<NL>(kr, vr, kbase + off, vbase + off);
-    ++issued;
-    iss = pre;
-    blk_iss = blk_pre;
-    if (issued + 1 < n_tiles) {
-      step(pre);
-      blk_pre = table_entry(pre);
+    ring.stage(slot, kbase + off, vbase + off);
+    bad_slots = (bad_slots & ~(1 << slot)) | (tile_bad << slot);
+    if (++issued < n_tiles) {  // block id of the next gather, read ahead
+      step(iss);
+      blk_iss = table_entry(iss);
     }
   };
-  // Consume the tile at `cur`; close the segment when the tile ends the
-  // unit, a partition, or this wavefront's range.
-  auto consume = [&](const uint4 (&kr)[NL], const uint4 (&vr)[NL], int tile_bad) {
-    st.bad |= tile_bad;
-    st.process(kr, vr, cur.k * kTile, a.scale_log2);
-    --left;
-    const bool unit_end = cur.k + 1 == cur.nt;
-    const bool part_end = ptiles > 0 && (cur.k + 1) % ptiles == 0;
-    if (!(unit_end || part_end || left == 0)) {
-      ++cur.k;
-      return;
+  float scale_log2 = a.scale_log2;  // waited for here (see the other kernel)
+  asm volatile("" : "+s"(scale_log2));
+
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s)
+    if (s < n_tiles) issue(s);
+  // Segments: runs of tiles of one unit that end at the unit's end or at
+  // this wavefront's end. The per-tile loop stays free of the segment
+  // bookkeeping; gathers run ahead across segments.
+  int i = 0;  // tiles consumed
+  for (;;) {
+    const int n_seg = min(cur.nt - cur.k, n_tiles - i);
+    const int k0 = cur.k;
+    for (int j = 0; j < n_seg; ++j, ++i) {
+      const int slot = i & (kSlots - 1);
+      const int ahead = min(n_tiles - 1 - i, kSlots - 1);
+      uint4 kr[NL];
+      ring.template fetch<0>(slot, ahead, kr);
+      st.bad |= (bad_slots >> slot) & 1;
+      st.process(
+          kr,
+          [&](uint4 (&vr)[NL]) {
+            ring.template fetch<1>(slot, ahead, vr);
+            if (issued < n_tiles) issue(slot);  // the slot is free again
+          },
+          (k0 + j) * kTile, scale_log2);
     }
+    cur.k = k0 + n_seg - 1;  // the segment's last tile
+
+    // close the segment: unnormalised partials under its id
     float l_row[RW];
     st.totals(l_row);
-    const int p = ptiles > 0 ? cur.k / ptiles : 0;
-    const int64_t gp = (int64_t)__builtin_amdgcn_readfirstlane(sm_pp[cur.b]) * HU +
-                       (int64_t)cur.g * (sm_pp[cur.b + 1] - sm_pp[cur.b]) + p;
-    const int64_t sid = w + gp;
+    const int64_t sid = w + (int64_t)cur.b * HU + cur.g;
     const float nan = __builtin_nanf("");
     if (lane < W::LPT) {
       float *dst = a.part_acc + (size_t)sid * RW * D + st.d0;
 #pragma unroll
       for (int r = 0; r < RW; ++r)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dst[r * D + e] = st.acc(r, e);
+        for (int e = 0; e < EPL; ++e) dst[r * D + e] = st.acc[r][e];
       if (lane == 0)
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
-          a.part_m[(size_t)sid * RW + r] = st.bad ? nan : st.m(r);
+          a.part_m[(size_t)sid * RW + r] = st.bad ? nan : st.m_run[r];
           a.part_l[(size_t)sid * RW + r] = l_row[r];
         }
     }
-    if (left == 0) return;
+    if (i == n_tiles) break;
     const int b0 = cur.b, g0 = cur.g;
     step(cur);
     if (cur.b != b0 || cur.g != g0)
       st.begin(a, cur.b, cur.g / S, cur.L, (cur.g % S) * RW);
     else  // a new partition of the same unit: same queries, fresh statistics
       st.restart();
-  };
-
-  uint4 ka[NL], va[NL], kb[NL], vb[NL];
-  load_tile<NL>(ka, va, kbase + off0, vbase + off0);
-  int k = 0;
-  for (; k + 2 < n_tiles; k += 2) {
-    issue(kb, vb, bad_b);
-    consume(ka, va, bad_a);
-    issue(ka, va, bad_a);
-    consume(kb, vb, bad_b);
-  }
-  if (k + 1 < n_tiles) {
-    issue(kb, vb, bad_b);
-    consume(ka, va, bad_a);
-    consume(kb, vb, bad_b);
-  } else {
-    consume(ka, va, bad_a);
   }
 }
 
 // Merge of the stream kernel's segments: one workgroup per (query row,
-// sequence), thread d owns output element d.
+// sequence), thread d owns output element d; one pass with a running
+// maximum over the unit's segments w + u, w = w0 .. w1.
 template <int D, int RW, int G>
 __global__ void __launch_bounds__(D)
 reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
@@ -910,7 +974,7 @@ reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
   const int rowq = blockIdx.x;  // qi * Hq + h
   const int b = blockIdx.y;
   const int d = threadIdx.x;
-  const int nq = a.nq, P = a.part_tokens, HU = a.Hkv * a.slices;
+  const int nq = a.nq, HU = a.Hkv * a.slices;
   const int qi = rowq / a.Hq, h = rowq % a.Hq;
   const int rr = qi * G + (h % G);             // row within the KV head
   const int vg = (h / G) * a.slices + rr / RW;  // its unit within the sequence
@@ -923,43 +987,30 @@ reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
     if (d == 0 && a.lse) a.lse[row] = nan;
     return;
   }
-  const int64_t T = (int64_t)sa.tile_pre[a.B] * HU;
+  const int64_t T = (int64_t)load_const(sa.tile_pre + a.B) * HU;
   const int64_t N = sa.n_waves;
-  const int nt = sa.tile_pre[b + 1] - sa.tile_pre[b];
-  const int np = sa.part_pre[b + 1] - sa.part_pre[b];
-  const int64_t u0 = (int64_t)sa.tile_pre[b] * HU + (int64_t)vg * nt;  // first tile of the unit
-  const int64_t gp0 = (int64_t)sa.part_pre[b] * HU + (int64_t)vg * np;
-  const int ptiles = P > 0 ? P / kTile : nt;
-  // pass 1: maximum
-  float M = kNegInf;
+  const int nt = load_const(sa.tile_pre + b + 1) - load_const(sa.tile_pre + b);
+  const int64_t first = (int64_t)load_const(sa.tile_pre + b) * HU + (int64_t)vg * nt;
+  const int64_t w0 = stream_wave(first, T, N), w1 = stream_wave(first + nt - 1, T, N);
+  const int64_t u = (int64_t)b * HU + vg;
+  float M = kNegInf, num = 0.f, den = 0.f;
   bool bad = false;
-  // the wavefronts holding a partition's tiles, in order: from the one that
-  // holds its first tile, hop to the one holding the tile after each range
-  // (wavefronts with empty ranges hold no segment)
-  for (int p = 0; p < np; ++p) {
-    const int64_t first = u0 + (int64_t)p * ptiles;
-    const int64_t last = u0 + min(nt, (p + 1) * ptiles) - 1;
-    for (int64_t pos = first; pos <= last;) {
-      const int64_t ww = stream_wave(pos, T, N);
-      pos = (ww + 1) * T / N;
-      const float m = a.part_m[(size_t)(ww + gp0 + p) * RW + r];
-      bad |= m != m;
-      M = fmaxf(M, m);
+  for (int64_t w = w0; w <= w1; ++w) {
+    // with fewer tiles than wavefronts, some wavefronts hold none
+    if (T < N && w * T / N == (w + 1) * T / N) continue;
+    const size_t sid = (size_t)(w + u);
+    const float m = a.part_m[sid * RW + r];
+    bad |= m != m;
+    if (m == kNegInf) continue;  // no visible key in the segment
+    if (m > M) {
+      const float c = exp2f(M - m);  // 0 while M is still -inf
+      num *= c;
+      den *= c;
+      M = m;
     }
-  }
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < np; ++p) {
-    const int64_t first = u0 + (int64_t)p * ptiles;
-    const int64_t last = u0 + min(nt, (p + 1) * ptiles) - 1;
-    for (int64_t pos = first; pos <= last;) {
-      const int64_t ww = stream_wave(pos, T, N);
-      pos = (ww + 1) * T / N;
-      const size_t sid = (size_t)(ww + gp0 + p);
-      const float m = a.part_m[sid * RW + r];
-      const float f = m == kNegInf ? 0.f : exp2f(m - M);
-      num = fmaf(f, a.part_acc[(sid * RW + r) * D + d], num);
-      den = fmaf(f, a.part_l[sid * RW + r], den);
-    }
+    const float f = exp2f(m - M);
+    num = fmaf(f, a.part_acc[(sid * RW + r) * D + d], num);
+    den = fmaf(f, a.part_l[sid * RW + r], den);
   }
   a.out[row * D + d] = bad || den == 0.f ? nan : num / den;
   if (d == 0 && a.lse) a.lse[row] = bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
@@ -967,26 +1018,41 @@ reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
 
 using Launcher = void (*)(const DecodeArgs &, const StreamArgs &, dim3, hipStream_t);
 
-template <int DT, int D, int G, int RP, int NS, int W>
+// Bytes of LDS one workgroup may allocate on gfx950.
+constexpr int kLdsLimit = 163840;
+
+// LDS of the stream kernel for B sequences: the tile rings and the scan
+// array, plus the per-sequence tile prefix.
+template <int DT, int D>
+constexpr int64_t stream_lds_bytes(int64_t B) {
+  return (int64_t)kStreamWaves * TileRing<Geo<DT, D>::NL>::kBytes +
+         kStreamWaves * 64 * (int64_t)sizeof(int) + (B + 1) * (int64_t)sizeof(int);
+}
+
+template <int DT, int D, int G, int RP, int W>
 void launch_decode(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
-  if constexpr (W == 0) {  // stream kernel + its reduce; grid.x persistent workgroups
-    hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, RP, NS>), grid, dim3(kStreamWaves * 64),
-                       2 * (a.B + 1) * sizeof(int), s, a, sa);
-    hipLaunchKernelGGL((reduce_stream_kernel<D, RP * NS, G>), dim3(a.nq * a.Hq, a.B), dim3(D),
+  // eight wavefronts' tile rings must fit the workgroup's LDS
+  constexpr int kRing = TileRing<Geo<DT, D>::NL>::kBytes;
+  if constexpr (W == 8 && 8 * kRing > kLdsLimit) {
+    launch_decode<DT, D, G, RP, 4>(a, sa, grid, s);
+  } else if constexpr (W == 0) {  // stream kernel + its reduce; grid.x persistent workgroups
+    hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, RP>), grid, dim3(kStreamWaves * 64),
+                       (a.B + 1) * sizeof(int), s, a, sa);
+    hipLaunchKernelGGL((reduce_stream_kernel<D, RP, G>), dim3(a.nq * a.Hq, a.B), dim3(D),
                        0, s, a, sa);
   } else {
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, NS, W>), grid, dim3(W * 64), 0, s,
+    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, W>), grid, dim3(W * 64), 0, s,
                        a);
   }
 }
 
 // Launcher for (dtype, D) and rows per wavefront RP = G * (query tokens
 // rounded up to a power of two): W = 4 or 8 wavefronts per workgroup of the
-// workgroup-split kernel, or W = 0 for the stream kernel (which also
-// launches its reduce); nullptr if no such kernel is built. Defined in
-// decode_inst_<dtype>_d<D>.hip.
+// workgroup-split kernel (W = 1: one wavefront per partition), or W = 0 for
+// the stream kernel (which also launches its reduce); nullptr if no such
+// kernel is built. Defined in decode_inst_<dtype>_d<D>.hip.
 template <int DT, int D>
-Launcher pick_rows(int G, int RP, int NS, int W);
+Launcher pick_rows(int G, int RP, int W);
 
 // Most query rows per KV head on the VALU kernels (as up to 4 slices of 4).
 constexpr int kMaxRows = 16;
