@@ -25,6 +25,7 @@ import argparse
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -349,6 +350,84 @@ def copy_probe(mib: int, dev) -> int:
     return 0
 
 
+def _csv_rows(d: str, suffix: str):
+    import csv
+    import glob
+
+    files = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def _counter_per_dispatch(d: str, counter: str, kernel_re: str):
+    """Mean over dispatches of a kernel of one rocprofv3 --pmc counter."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] == counter and re.search(kernel_re, r["Kernel_Name"]):
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for /{kernel_re}/ under {d}")
+    return statistics.mean(per.values()), len(per)
+
+
+def summarize_profile(args) -> int:
+    """Condense rocprofv3 output into profiles/decode_<workload>.json: the
+    kernel's average duration (--kernel-trace --stats), its HBM bytes per
+    dispatch (--pmc FETCH_SIZE, WRITE_SIZE) scaled by what the same counters
+    read for a plain copy of known size (--copy-probe), and a hash of the
+    kernel sources they were taken on."""
+    import hashlib
+
+    kre = args.kernel_regex
+    stats = [r for r in _csv_rows(args.trace_dir, "kernel_stats.csv") if re.search(kre, r["Name"])]
+    if len(stats) != 1:
+        raise SystemExit(f"/{kre}/ matches {len(stats)} kernels in the trace")
+    st = stats[0]
+    fetch, nd = _counter_per_dispatch(args.fetch_dir, "FETCH_SIZE", kre)
+    write, _ = _counter_per_dispatch(args.write_dir, "WRITE_SIZE", kre)
+    cfetch, _ = _counter_per_dispatch(args.copy_fetch_dir, "FETCH_SIZE", "copy_blocks")
+    cwrite, _ = _counter_per_dispatch(args.copy_write_dir, "WRITE_SIZE", "copy_blocks")
+    moved = 2 * args.copy_mib * 2**20  # K and V, read once and written once
+    ffac, wfac = moved / (cfetch * 1024), moved / (cwrite * 1024)
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    from synth.workloads import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    if w.context is None:
+        raise SystemExit("profile summaries cover equal-length workloads")
+    lens = np.full(w.batch, w.context, dtype=np.int64)
+    out = {
+        "kernel": st["Name"],
+        "workload": args.workload,
+        "kernel_sources_sha256": h.hexdigest(),
+        "trace": {"calls": int(st["Calls"]), "avg_ns": float(st["AverageNs"]),
+                  "min_ns": float(st["MinNs"]), "max_ns": float(st["MaxNs"])},
+        "pmc": {"FETCH_SIZE_kib_per_dispatch": fetch, "WRITE_SIZE_kib_per_dispatch": write,
+                "dispatches": nd},
+        "calibration": {"probe": f"paged_kv_copy_blocks copying {args.copy_mib} MiB of K and "
+                                 f"{args.copy_mib} MiB of V",
+                        "bytes_read": moved, "bytes_written": moved,
+                        "FETCH_SIZE_kib": cfetch, "WRITE_SIZE_kib": cwrite,
+                        "fetch_factor": ffac, "write_factor": wfac},
+        "fetch_bytes_per_launch": fetch * 1024 * ffac,
+        "write_bytes_per_launch": write * 1024 * wfac,
+        "traffic_bytes_per_launch": fetch * 1024 * ffac + write * 1024 * wfac,
+        "algorithmic_bytes_per_launch": algorithmic_bytes(
+            w.batch, w.queries_per_seq, w.q_heads, w.kv_heads, w.head_dim, w.esize, lens,
+            -(-int(lens.max()) // w.block_size)),
+    }
+    path = os.path.join(ROOT, "profiles", f"decode_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,7 +440,19 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run paged_kv_copy_blocks over MIB MiB of K and of V (a plain "
                          "copy of known size, to calibrate HBM byte counters), then exit")
+    ap.add_argument("--summarize-profile", action="store_true",
+                    help="no GPU work: condense rocprofv3 output (the --*-dir options) into "
+                         "profiles/decode_<workload>.json")
+    ap.add_argument("--kernel-regex", default="decode_partition_kernel")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--copy-fetch-dir")
+    ap.add_argument("--copy-write-dir")
+    ap.add_argument("--copy-mib", type=int, default=512)
     args = ap.parse_args()
+    if args.summarize_profile:
+        return summarize_profile(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each GPU would run its own pool and sequences with no exchange).",

@@ -61,6 +61,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
+// The same with a zero accumulator, in the three-operand form that takes
+// the zero as an inline constant (the two-operand form the compiler picks
+// for chains would first need a register cleared).
+__device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -470,7 +478,7 @@ struct DecodeWave {
       for (int i = 0; i < NL; ++i) {
         float s = 0.f;
         if constexpr (DT == PKV_BF16) {
-          s = dot2_bf16(qw[r][0], kr[i].x, s);
+          s = dot2_bf16_first(qw[r][0], kr[i].x);
           s = dot2_bf16(qw[r][1], kr[i].y, s);
           s = dot2_bf16(qw[r][2], kr[i].z, s);
           s = dot2_bf16(qw[r][3], kr[i].w, s);
