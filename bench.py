@@ -75,6 +75,16 @@ def algorithmic_bytes(B, nq, Hq, Hkv, D, es, lens, max_blocks, with_lse=False):
     return kv + q + out + tables + 4 * B
 
 
+def kernel_label(wk) -> str:
+    """Which launches one attention call makes, as the library plans them."""
+    mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16
+    if wk.part == -1 and not mfma:
+        return "decode_stream_kernel + reduce_stream_kernel"
+    main = "verify_mfma_kernel" if mfma else "decode_partition_kernel"
+    return main + (" + reduce_partitions_kernel" if wk.ws is not None else
+                   " (one launch per attention call)")
+
+
 class Workload:
     """Device state for one workload, built through the library only."""
 
@@ -525,9 +535,7 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": profiled_traffic(wk.w.name),
-                     "kernel": ("decode_partition_kernel (one launch per attention call)"
-                                if wk.ws is None else
-                                "paged_attention_decode (partition + reduce launches)"),
+                     "kernel": kernel_label(wk),
                      "algorithmic_bytes": attn_bytes, "avg_duration_us": attn_ms * 1e3},
         "step_breakdown_us": {"cache_write": write_ms * 1e3, "attention": attn_ms * 1e3},
         "host_alloc_us": {"step_alloc": wk.alloc_step_s * 1e6},
