@@ -255,11 +255,6 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 // per call, so the rows should not displace reusable lines (tables, queries).
 constexpr int kKvNonTemporal = 2;
 
-// The same policy for a gather into registers.
-__device__ __forceinline__ uint4 stream_load(const char *p) {
-  const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return make_uint4(t.x, t.y, t.z, t.w);
-}
 
 // N (2, 4 or 8) 16-byte LDS reads at p, p + 1 KiB, ..., and a wait for
 // them, in one statement so that no use of a result can be scheduled before
