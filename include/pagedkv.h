@@ -210,8 +210,9 @@ int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_t *pairs,
 /* Workspace bytes paged_attention_decode needs for these sizes and
  * partition_tokens (0 when the chosen launch keeps everything on chip).
  * partition_tokens:
- *    0  the library chooses (one workgroup per (sequence, KV head) when
- *       those pairs fill the GPU, else a balanced stream);
+ *    0  the library chooses (one partition per (sequence, KV head) when
+ *       those pairs fill the GPU, else as many equal partitions per
+ *       context as fill it);
  *   -1  balanced stream: all sequences' tiles are shared equally among the
  *       wavefronts whatever their lengths (for batches of mixed lengths);
  *   >0  split every context into partitions of that many tokens (a multiple
@@ -244,9 +245,10 @@ int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
  * visible tokens meet a table entry outside [0, num_blocks) produce NaN in
  * out and lse instead of reading out of bounds.
  * Kernels: single query rows (nq = 1) and fp32 caches run on VALU kernels
- * (up to 8 rows per KV head: G * nq rounded up to a power of two); bf16
- * caches with nq > 1 run on an MFMA tile of 16 query rows per KV head
- * (G * nq <= 16), e.g. 4 query heads x 4 draft tokens for verification.
+ * (up to 16 rows per KV head: G * nq rounded up to a power of two, 8 per
+ * wavefront); bf16 caches with nq > 1 run on an MFMA tile of 16 query rows
+ * per KV head (G * nq <= 16), e.g. 4 query heads x 4 draft tokens for
+ * verification.
  * Host-checked: sizes, Hq % Hkv == 0, D and block_size supported, rows per
  * KV head within those limits, scale finite, workspace large enough ->
  * EINVAL. */
@@ -258,6 +260,73 @@ int paged_attention_decode(float *out, const void *q, const void *k_cache,
                            float scale, int dtype, int32_t partition_tokens,
                            void *workspace, size_t workspace_bytes,
                            float *lse_out, void *stream);
+
+/* ----------------------------------------------------------------------
+ * Shared prefixes ([vLLM]: blocks shared within and across requests;
+ * [KVNB s5] share_prefix forks a parent's leading blocks).
+ * ---------------------------------------------------------------------- */
+
+/* Groups of a batch that share leading physical blocks, from host copies of
+ * the block tables [B, max_blocks] and context_lens [B]. Sequences are
+ * grouped by their first block id; a group's prefix is the longest run of
+ * leading block ids common to all its members, capped so that every query
+ * row of every member sees all of it (prefix <= context_lens[b] - nq + 1)
+ * and rounded down to a multiple of 16 tokens. Groups with fewer than
+ * min_members members (>= 2) or a prefix under min_tokens (>= 16) are
+ * dropped. Host outputs, caller-allocated:
+ *   seq_prefix[B]       tokens of sequence b in its group's prefix (0: none)
+ *   group_start[B + 1]  members of group i are members[group_start[i] ..
+ *                       group_start[i + 1])
+ *   members[B]          sequence indices, grouped, in ascending order
+ *   group_tokens[B]     prefix tokens of group i (first *n_groups entries)
+ *   *n_groups, *max_members (largest group), *max_prefix (longest prefix)
+ * EINVAL on NULL pointers or bad sizes; nothing is allocated. */
+int paged_kv_prefix_groups(const int32_t *block_tables, int32_t max_blocks,
+                           const int32_t *context_lens, int32_t B, int32_t nq,
+                           int32_t block_size, int32_t min_members,
+                           int32_t min_tokens, int32_t *seq_prefix,
+                           int32_t *group_start, int32_t *members,
+                           int32_t *group_tokens, int32_t *n_groups,
+                           int32_t *max_members, int32_t *max_prefix);
+
+/* Workspace bytes paged_attention_decode_shared needs (the larger of what
+ * it and paged_attention_decode need for these sizes). */
+int paged_attention_shared_workspace_size(int32_t B, int32_t nq, int32_t Hq,
+                                          int32_t Hkv, int32_t D,
+                                          int32_t max_blocks,
+                                          int32_t block_size,
+                                          int32_t partition_tokens,
+                                          int32_t n_groups, int32_t max_members,
+                                          int32_t max_prefix, size_t *bytes);
+
+/* paged_attention_decode with each group's shared prefix read once per KV
+ * head for all its members: the query rows of a group's members are
+ * stacked into 16-row MFMA tiles that stream the prefix blocks together,
+ * the rest of every context (from seq_prefix[b] on) runs on the ordinary
+ * kernels, and a log-sum-exp merge joins the parts. Same results as
+ * paged_attention_decode (up to float32 rounding order and, in the prefix
+ * part, weights rounded to bf16 for the MFMA product, as in its nq > 1
+ * path). bf16 caches only; G * nq rounded up to a power of two <= 16.
+ *   seq_prefix, group_start, members, group_tokens: device int32 copies of
+ *     paged_kv_prefix_groups' outputs (members' tables must hold the same
+ *     block ids over the group's prefix, and seq_prefix[b] must be the
+ *     group's prefix for members and 0 otherwise);
+ *   n_groups, n_members = group_start[n_groups], max_members, max_prefix:
+ *     the host-side values of the same call (they size the launch).
+ * Inconsistent group arrays give wrong or NaN results but no access
+ * outside the arrays. With n_groups = 0 this is paged_attention_decode.
+ * Host-checked: as paged_attention_decode, plus dtype bf16, the group
+ * sizes, and a workspace of paged_attention_shared_workspace_size(). */
+int paged_attention_decode_shared(
+    float *out, const void *q, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks,
+    const int32_t *context_lens, int32_t B, int32_t nq, int32_t Hq,
+    int32_t Hkv, int32_t D, int32_t block_size, int32_t num_blocks,
+    float scale, int dtype, int32_t partition_tokens,
+    const int32_t *seq_prefix, const int32_t *group_start,
+    const int32_t *members, const int32_t *group_tokens, int32_t n_groups,
+    int32_t n_members, int32_t max_members, int32_t max_prefix,
+    void *workspace, size_t workspace_bytes, float *lse_out, void *stream);
 
 #ifdef __cplusplus
 }

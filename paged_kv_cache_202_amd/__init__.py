@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "PagedKVPool", "paged_cache_write", "paged_kv_copy_blocks",
     "paged_attention_workspace_size", "paged_attention_decode", "dtype_code",
+    "PrefixGroups", "paged_kv_prefix_groups", "paged_attention_shared_workspace_size",
+    "paged_attention_decode_shared",
 ]
 
 
@@ -212,6 +214,84 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,
         _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB, float(scale), dtype_code(k_cache),
         int(partition_tokens), _dev(workspace), ws_bytes, _dev(lse), _stream(stream)))
+
+
+# ---------------------------------------------------------------- shared prefixes
+
+class PrefixGroups:
+    """Host outputs of paged_kv_prefix_groups (numpy int32 arrays and ints)."""
+
+    def __init__(self, seq_prefix, group_start, members, group_tokens, n_groups, max_members,
+                 max_prefix):
+        self.seq_prefix, self.group_start = seq_prefix, group_start
+        self.members, self.group_tokens = members, group_tokens
+        self.n_groups, self.max_members, self.max_prefix = n_groups, max_members, max_prefix
+        self.n_members = int(group_start[n_groups])
+
+    def to_device(self, device):
+        """The four arrays as device int32 tensors (for paged_attention_decode_shared)."""
+        import torch
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+        return (dev(self.seq_prefix), dev(self.group_start[:self.n_groups + 1]),
+                dev(self.members[:max(self.n_members, 1)]),
+                dev(self.group_tokens[:max(self.n_groups, 1)]))
+
+
+def paged_kv_prefix_groups(block_tables, context_lens, nq, block_size, min_members=2,
+                           min_tokens=256) -> PrefixGroups:
+    """Groups that share leading blocks, from host tables [B, max_blocks] and lengths [B]."""
+    tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    lens = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B, max_blocks = tables.shape
+    if lens.shape != (B,):
+        raise InvalidArgument(_lib.PKV_EINVAL, "paged_kv_prefix_groups: shape mismatch")
+    seq_prefix = np.zeros(B, dtype=np.int32)
+    group_start = np.zeros(B + 1, dtype=np.int32)
+    members = np.zeros(B, dtype=np.int32)
+    group_tokens = np.zeros(B, dtype=np.int32)
+    ng, mm, mp = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    check(load().paged_kv_prefix_groups(
+        _i32p(tables), max_blocks, _i32p(lens), B, int(nq), int(block_size), int(min_members),
+        int(min_tokens), _i32p(seq_prefix), _i32p(group_start), _i32p(members),
+        _i32p(group_tokens), ctypes.byref(ng), ctypes.byref(mm), ctypes.byref(mp)))
+    return PrefixGroups(seq_prefix, group_start, members, group_tokens, ng.value, mm.value,
+                        mp.value)
+
+
+def paged_attention_shared_workspace_size(B, nq, Hq, Hkv, D, max_blocks, block_size,
+                                          groups: PrefixGroups, partition_tokens=0) -> int:
+    out = ctypes.c_size_t()
+    check(load().paged_attention_shared_workspace_size(
+        B, nq, Hq, Hkv, D, max_blocks, block_size, partition_tokens, groups.n_groups,
+        groups.max_members, groups.max_prefix, ctypes.byref(out)))
+    return out.value
+
+
+def paged_attention_decode_shared(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                  groups: PrefixGroups, device_groups, partition_tokens=0,
+                                  workspace=None, lse=None, stream=None) -> None:
+    """paged_attention_decode with shared prefixes read once per group and KV head.
+
+    device_groups: groups.to_device(...) (seq_prefix, group_start, members,
+    group_tokens as device int32 tensors)."""
+    B, nq, Hq, D = q.shape
+    NB, Hkv, bs, Dk = k_cache.shape
+    max_blocks = block_tables.shape[1]
+    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
+            or tuple(context_lens.shape) != (B,) or q.dtype != k_cache.dtype
+            or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype):
+        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode_shared: shape mismatch")
+    seq_prefix, group_start, members, group_tokens = device_groups
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().paged_attention_decode_shared(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,
+        _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB, float(scale), dtype_code(k_cache),
+        int(partition_tokens), _dev(seq_prefix), _dev(group_start), _dev(members),
+        _dev(group_tokens), groups.n_groups, groups.n_members, groups.max_members,
+        groups.max_prefix, _dev(workspace), ws_bytes, _dev(lse), _stream(stream)))
 
 
 def default_scale(head_dim: int) -> float:

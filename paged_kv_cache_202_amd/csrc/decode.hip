@@ -11,6 +11,7 @@
 
 #include "decode_kernel.h"
 #include "verify_mfma.h"
+#include "shared_prefix.h"
 #include "pagedkv.h"
 #include "status.h"
 
@@ -18,37 +19,49 @@ namespace pkv {
 namespace decode {
 namespace {
 
-// Split-K merge: one workgroup of 256 threads per (query row, sequence).
-// D / 4 threads own four output elements each; the 1024 / D groups of them
-// take every (1024 / D)-th partition with a running maximum, and the groups
-// are merged in LDS: M = max m_p, out = sum 2^(m_p-M) acc_p / sum 2^(m_p-M) l_p.
+// Split-K merge: workgroups of 256 threads, D / 4 threads per group owning
+// four output elements each. With many partitions per row (GPR = 1024 / D
+// groups per row), the groups of a workgroup take every GPR-th partition of
+// one row with a running maximum and are merged in LDS; with few (GPR = 1),
+// each group merges one row alone. M = max m_p,
+// out = sum 2^(m_p-M) acc_p / sum 2^(m_p-M) l_p.
 constexpr int kReduceThreads = 256;
 
-template <int D>
+template <int D, int GPR>
 __global__ void __launch_bounds__(kReduceThreads)
 reduce_partitions_kernel(const DecodeArgs a) {
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
-  constexpr int TPG = D / 4;                    // threads per group
-  constexpr int NG = kReduceThreads / TPG;      // groups
+  constexpr int TPG = D / 4;                // threads per group
+  constexpr int NG = kReduceThreads / TPG;  // groups per workgroup
+  constexpr int RPW = NG / GPR;             // rows per workgroup
   __shared__ float sm_m[NG], sm_den[NG];
   __shared__ float4 sm_num[NG][TPG];
-  const int rowq = blockIdx.x;  // qi * Hq + h
-  const int b = blockIdx.y;
   const int grp = threadIdx.x / TPG, t = threadIdx.x % TPG;
+  const int sub = grp % GPR;                          // this group's share of its row
+  const int rowq = blockIdx.x * RPW + grp / GPR;      // qi * Hq + h
+  const int b = blockIdx.y;
+  const bool row_ok = rowq < a.nq * a.Hq;             // workgroup-uniform when GPR > 1
   const int L = load_const(a.lens + b);
-  const size_t row = (size_t)b * a.nq * a.Hq + rowq;
+  const size_t row = (size_t)b * a.nq * a.Hq + (row_ok ? rowq : 0);
   const float nan = __builtin_nanf("");
+  float *o = a.out + row * D + 4 * t;
   if (L < a.nq || L > a.max_blocks * a.bs) {
-    if (grp == 0) {
-      a.out[row * D + 4 * t + 0] = nan;
-      a.out[row * D + 4 * t + 1] = nan;
-      a.out[row * D + 4 * t + 2] = nan;
-      a.out[row * D + 4 * t + 3] = nan;
+    if (row_ok && sub == 0) {
+      o[0] = nan;
+      o[1] = nan;
+      o[2] = nan;
+      o[3] = nan;
       if (t == 0 && a.lse) a.lse[row] = nan;
     }
     return;
   }
-  const int np = (L + a.part_tokens - 1) / a.part_tokens;
+  // slots written for this row: partitions [0, ceil(L / P)); with a shared
+  // prefix, prefix pieces [0, ceil(start / PP)) and then the suffix's
+  // partitions from slot part_base on
+  const int start = a.starts ? min(max(load_const(a.starts + b), 0), L) : 0;
+  const int np_pre = a.starts ? (start + a.prefix_part - 1) / a.prefix_part : 0;
+  const int np_suf = (L - start + a.part_tokens - 1) / a.part_tokens;
+  const int np = row_ok ? min(a.num_parts, a.part_base + np_suf) : 0;
   const float *pm = a.part_m + row * a.num_parts;
   const float *pl = a.part_l + row * a.num_parts;
   const float4 *pacc = reinterpret_cast<const float4 *>(a.part_acc + row * a.num_parts * D);
@@ -56,7 +69,8 @@ reduce_partitions_kernel(const DecodeArgs a) {
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   bool bad = false;
 #pragma unroll 4
-  for (int p = grp; p < np; p += NG) {
+  for (int p = sub; p < np; p += GPR) {
+    if (p >= np_pre && p < a.part_base) continue;  // prefix pieces past this row's prefix
     const float m = pm[p];
     const float l = pl[p];
     const float4 v = pacc[(size_t)p * TPG + t];
@@ -75,41 +89,47 @@ reduce_partitions_kernel(const DecodeArgs a) {
     num.w = fmaf(f, v.w, num.w);
     den = fmaf(f, l, den);
   }
-  // a group's bad flag is the same in all its threads: fold it into M
-  if (t == 0) {
-    sm_m[grp] = bad ? nan : M;
-    sm_den[grp] = den;
-  }
-  sm_num[grp][t] = num;
-  __syncthreads();
-  if (grp != 0) return;
-  float Mt = kNegInf;
-  bool any_bad = false;
+  if constexpr (GPR > 1) {
+    // a group's bad flag is the same in all its threads: fold it into M
+    if (t == 0) {
+      sm_m[grp] = bad ? nan : M;
+      sm_den[grp] = den;
+    }
+    sm_num[grp][t] = num;
+    __syncthreads();
+    if (sub != 0) return;
+    float Mt = kNegInf;
+    bool any_bad = false;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    any_bad |= sm_m[g] != sm_m[g];
-    Mt = fmaxf(Mt, sm_m[g]);
-  }
-  float dt = 0.f;
-  float4 nt = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int g = 0; g < GPR; ++g) {
+      any_bad |= sm_m[grp + g] != sm_m[grp + g];
+      Mt = fmaxf(Mt, sm_m[grp + g]);
+    }
+    float dt = 0.f;
+    float4 nt = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const float mg = sm_m[g];
-    const float f = mg == kNegInf || mg != mg ? 0.f : exp2f(mg - Mt);
-    const float4 v = sm_num[g][t];
-    nt.x = fmaf(f, v.x, nt.x);
-    nt.y = fmaf(f, v.y, nt.y);
-    nt.z = fmaf(f, v.z, nt.z);
-    nt.w = fmaf(f, v.w, nt.w);
-    dt = fmaf(f, sm_den[g], dt);
+    for (int g = 0; g < GPR; ++g) {
+      const float mg = sm_m[grp + g];
+      const float f = mg == kNegInf || mg != mg ? 0.f : exp2f(mg - Mt);
+      const float4 v = sm_num[grp + g][t];
+      nt.x = fmaf(f, v.x, nt.x);
+      nt.y = fmaf(f, v.y, nt.y);
+      nt.z = fmaf(f, v.z, nt.z);
+      nt.w = fmaf(f, v.w, nt.w);
+      dt = fmaf(f, sm_den[grp + g], dt);
+    }
+    M = Mt;
+    den = dt;
+    num = nt;
+    bad = any_bad;
   }
-  const bool nan_out = any_bad || dt == 0.f;
-  float *o = a.out + row * D + 4 * t;
-  o[0] = nan_out ? nan : nt.x / dt;
-  o[1] = nan_out ? nan : nt.y / dt;
-  o[2] = nan_out ? nan : nt.z / dt;
-  o[3] = nan_out ? nan : nt.w / dt;
-  if (t == 0 && a.lse) a.lse[row] = nan_out ? nan : (Mt + log2f(dt)) * kLn2;
+  if (!row_ok) return;
+  const bool nan_out = bad || den == 0.f;
+  o[0] = nan_out ? nan : num.x / den;
+  o[1] = nan_out ? nan : num.y / den;
+  o[2] = nan_out ? nan : num.z / den;
+  o[3] = nan_out ? nan : num.w / den;
+  if (t == 0 && a.lse) a.lse[row] = nan_out ? nan : (M + log2f(den)) * kLn2;
 }
 
 int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 0; }
@@ -188,7 +208,14 @@ Plan plan_launch(int64_t B, int64_t Hkv, int64_t max_ctx, int32_t req, bool stre
 
 template <int D>
 void launch_reduce(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((reduce_partitions_kernel<D>), grid, dim3(kReduceThreads), 0, s, a);
+  // grid.x = query rows per sequence; few slots per row: one group per row
+  constexpr int NG = kReduceThreads / (D / 4);
+  if (a.num_parts <= 8) {
+    grid.x = (grid.x + NG - 1) / NG;
+    hipLaunchKernelGGL((reduce_partitions_kernel<D, 1>), grid, dim3(kReduceThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((reduce_partitions_kernel<D, NG>), grid, dim3(kReduceThreads), 0, s, a);
+  }
 }
 
 Launcher pick_reduce(int D) {
@@ -392,5 +419,175 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch: %s", hipGetErrorString(e));
   }
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Shared prefixes: the prefix kernel over each group's stacked query rows,
+// then the ordinary kernels from seq_prefix[b] on, then the merge.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct SharePlan {
+  int32_t W;       // wavefronts per prefix workgroup
+  int32_t RT;      // row tiles per wavefront
+  int32_t chunks;  // prefix workgroups per group along grid.z
+  int32_t rpm;     // rows per member, padded to a power of two
+  int32_t npp;     // prefix partitions (slots 0 .. npp - 1)
+  int32_t pp;      // tokens per prefix partition
+};
+
+int share_plan(int32_t G, int32_t nq, int32_t Hkv, int32_t D, int32_t n_groups,
+               int32_t max_members, int32_t max_prefix, SharePlan *sp) {
+  sp->rpm = next_pow2(G * nq);
+  if (sp->rpm > kVerifyRows)
+    return fail(PKV_EINVAL, "G * nq = %d * %d rows per member exceed one 16-row tile", G, nq);
+  if (n_groups <= 0 || max_members < 1 || max_prefix < kTile || max_prefix % kTile)
+    return fail(PKV_EINVAL, "group sizes: n_groups %d, max_members %d, max_prefix %d", n_groups,
+                max_members, max_prefix);
+  const int32_t mpt = kVerifyRows / sp->rpm;                 // members per row tile
+  const int32_t tiles = (max_members + mpt - 1) / mpt;       // row tiles of the largest group
+  sp->W = tiles >= 8 ? 8 : next_pow2(tiles);
+  // two row tiles per wavefront share each K/V read where both accumulators
+  // fit in registers
+  sp->RT = tiles >= 16 && D <= 128 ? 2 : 1;
+  sp->chunks = (tiles + sp->W * sp->RT - 1) / (sp->W * sp->RT);
+  // enough prefix partitions that the prefix workgroups fill a round
+  const int64_t per_part = (int64_t)n_groups * Hkv * sp->chunks * sp->W;
+  int64_t npp = (kResidentWaves + per_part - 1) / per_part;
+  if (npp > max_prefix / kTile) npp = max_prefix / kTile;
+  if (npp < 1) npp = 1;
+  sp->pp = (int32_t)(((max_prefix + npp - 1) / npp + kTile - 1) / kTile * kTile);
+  sp->npp = (max_prefix + sp->pp - 1) / sp->pp;
+  if ((int64_t)n_groups * sp->chunks > 65535)
+    return fail(PKV_EINVAL, "too many groups for one launch");
+  return PKV_OK;
+}
+
+}  // namespace
+
+static size_t shared_workspace_need(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t D,
+                                    int64_t max_ctx, int32_t part, const SharePlan &sp) {
+  const Plan pl = plan_launch(B, Hkv, max_ctx, part, false);
+  return partial_bytes((int64_t)B * nq * Hq, sp.npp + pl.num_parts, D);
+}
+
+extern "C" int paged_attention_shared_workspace_size(int32_t B, int32_t nq, int32_t Hq,
+                                                     int32_t Hkv, int32_t D, int32_t max_blocks,
+                                                     int32_t bs, int32_t part, int32_t n_groups,
+                                                     int32_t max_members, int32_t max_prefix,
+                                                     size_t *bytes) {
+  if (!bytes) return fail(PKV_EINVAL, "bytes is NULL");
+  if (int rc = check_sizes(B, nq, Hq, Hkv, D, max_blocks, bs, part)) return rc;
+  const int64_t max_ctx = (int64_t)max_blocks * bs;
+  size_t need = workspace_need(B, nq, Hq, Hkv, D, max_ctx, part);
+  if (n_groups > 0) {
+    SharePlan sp;
+    if (int rc = share_plan(Hq / Hkv, nq, Hkv, D, n_groups, max_members, max_prefix, &sp)) return rc;
+    const size_t n = shared_workspace_need(B, nq, Hq, Hkv, D, max_ctx, part, sp);
+    if (n > need) need = n;
+  }
+  *bytes = need;
+  return PKV_OK;
+}
+
+extern "C" int paged_attention_decode_shared(
+    float *out, const void *q, const void *k_cache, const void *v_cache,
+    const int32_t *block_tables, int32_t max_blocks, const int32_t *context_lens, int32_t B,
+    int32_t nq, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t num_blocks, float scale,
+    int dtype, int32_t part, const int32_t *seq_prefix, const int32_t *group_start,
+    const int32_t *members, const int32_t *group_tokens, int32_t n_groups, int32_t n_members,
+    int32_t max_members, int32_t max_prefix, void *workspace, size_t workspace_bytes,
+    float *lse_out, void *stream) {
+  if (n_groups == 0)
+    return paged_attention_decode(out, q, k_cache, v_cache, block_tables, max_blocks,
+                                  context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype,
+                                  part, workspace, workspace_bytes, lse_out, stream);
+  if (dtype != PKV_BF16) return fail(PKV_EINVAL, "shared prefixes need a bf16 cache");
+  if (int rc = check_sizes(B, nq, Hq, Hkv, D, max_blocks, bs, part)) return rc;
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "num_blocks must be positive");
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !seq_prefix ||
+      !group_start || !members || !group_tokens)
+    return fail(PKV_EINVAL, "NULL pointer");
+  for (const void *p : {(const void *)out, q, k_cache, v_cache})
+    if ((uintptr_t)p % 16) return fail(PKV_EINVAL, "out, q, K and V must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
+  if (n_groups < 0 || n_members < 2 * n_groups || n_members > B || max_members > B ||
+      max_prefix > max_blocks * bs)
+    return fail(PKV_EINVAL, "group sizes out of range");
+  const int G = Hq / Hkv;
+  if (int rc = check_rows(dtype, nq, G)) return rc;
+  SharePlan sp;
+  if (int rc = share_plan(G, nq, Hkv, D, n_groups, max_members, max_prefix, &sp)) return rc;
+  const int64_t max_ctx = (int64_t)max_blocks * bs;
+
+  // the rest of every context: the ordinary kernels, never the stream
+  const bool mfma = use_mfma(dtype, nq, G);
+  const Plan pl = plan_launch(B, Hkv, max_ctx, part, false);
+  int32_t RP, S;
+  row_split(G, nq, &RP, &S);
+  if (mfma) S = 1;
+  Launcher launch = mfma ? pick_verify(D) : pick_launcher(dtype, D, G, RP, pl.waves);
+  PrefixLauncher prefix = pick_prefix(D, sp.W, sp.RT);
+  if (!launch || !prefix) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
+
+  const int32_t slots = sp.npp + pl.num_parts;
+  const size_t need = partial_bytes((int64_t)B * nq * Hq, slots, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EINVAL, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((uintptr_t)workspace % 256) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+
+  DecodeArgs a{};
+  a.out = out;
+  a.lse = lse_out;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.B = B;
+  a.max_blocks = max_blocks;
+  a.nq = nq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.bs = bs;
+  a.num_blocks = num_blocks;
+  a.part_tokens = pl.part_tokens;
+  a.num_parts = slots;
+  a.slices = S;
+  a.scale_log2 = scale * kLog2e;
+  a.starts = seq_prefix;
+  a.part_base = sp.npp;
+  a.prefix_part = sp.pp;
+  const int64_t rows = (int64_t)B * nq * Hq;
+  char *w = (char *)workspace;
+  a.part_acc = (float *)w;
+  w += align_up((size_t)rows * slots * D * 4, 256);
+  a.part_m = (float *)w;
+  w += align_up((size_t)rows * slots * 4, 256);
+  a.part_l = (float *)w;
+
+  ShareArgs sh{};
+  sh.group_start = group_start;
+  sh.members = members;
+  sh.group_tokens = group_tokens;
+  sh.n_groups = n_groups;
+  sh.n_members = n_members;
+  sh.chunks = sp.chunks;
+  sh.rpm = sp.rpm;
+  sh.prefix_part = sp.pp;
+
+  hipStream_t s = (hipStream_t)stream;
+  StreamArgs sa{};
+  prefix(a, sh, dim3(sp.npp, Hkv, n_groups * sp.chunks), s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "prefix launch: %s", hipGetErrorString(e));
+  launch(a, sa, dim3(pl.num_parts, Hkv * S, B), s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "decode launch: %s", hipGetErrorString(e));
+  pick_reduce(D)(a, sa, dim3(nq * Hq, B), s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }

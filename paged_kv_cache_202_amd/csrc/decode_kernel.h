@@ -196,6 +196,13 @@ struct DecodeArgs {
   // a KV head's rows: slice s holds rows s * RP .. s * RP + RP - 1.
   int32_t slices;
   float scale_log2;
+  // Shared-prefix launches only (else nullptr / 0): starts[b] tokens of
+  // sequence b are covered by its group's prefix phase, which writes
+  // partition slots [0, part_base) in prefix_part-token pieces; the
+  // ordinary kernels cover [starts[b], L) from slot part_base on.
+  const int32_t *starts;
+  int32_t part_base;
+  int32_t prefix_part;
 };
 
 // One step of the reduce-scatter over lane bit M with `cnt` live values:
@@ -298,6 +305,24 @@ __device__ __forceinline__ void lds_rows(u32x4_t *t, const PKV_LDS char *p) {
   }
 }
 
+// One 1 KiB direct-to-LDS gather: lane i's 16 bytes from src (per lane)
+// land at dst + 16 i (dst wavefront-uniform). AUX is the cache policy.
+template <int AUX>
+__device__ __forceinline__ void gather_lds16(const char *src, PKV_LDS char *dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, AUX);
+}
+
+// A value a loop reads, waited for here and kept in a register from here
+// on: if its load were first used inside the loop, the compiler's wait for
+// it would sit in every trip and also wait for the gathers in flight.
+// (Device functions: AMDGPU register constraints cannot appear in a kernel
+// body, which the host compiler also checks.)
+__device__ __forceinline__ void settle_s(float &x) { asm volatile("" : "+s"(x)); }
+__device__ __forceinline__ void settle_v(int &x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle_v(uint4 &x) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+}
+
 // Wait until at most VM vector-memory operations of this wavefront are
 // pending.
 template <int VM>
@@ -338,12 +363,10 @@ struct TileRing {
   __device__ __forceinline__ void stage(int slot, const char *kp, const char *vp) {
     PKV_LDS char *dst = base + slot * kTileBytes;
 #pragma unroll
-    for (int i = 0; i < NL; ++i)
-      __builtin_amdgcn_global_load_lds(kp + i * 1024, dst + i * 1024, 16, 0, kKvNonTemporal);
+    for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(kp + i * 1024, dst + i * 1024);
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      __builtin_amdgcn_global_load_lds(vp + i * 1024, dst + (NL + i) * 1024, 16, 0,
-                                       kKvNonTemporal);
+      gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
   }
 
   // Read back the K half (HALF = 0) or the V half (HALF = 1) of the tile in
@@ -646,7 +669,10 @@ decode_partition_kernel(const DecodeArgs a) {
     }
     return;  // with partitions, the reduce kernel writes the NaN rows
   }
-  const int t_begin = p * a.part_tokens;
+  // earlier tokens belong to the prefix phase (clamped: bad values cannot
+  // send reads outside the table)
+  const int start = a.starts ? min(max(load_const(a.starts + b), 0), L) : 0;
+  const int t_begin = start + p * a.part_tokens;
   if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
   const int t_end = min(L, t_begin + a.part_tokens);
 
@@ -688,7 +714,7 @@ decode_partition_kernel(const DecodeArgs a) {
     // the scale is waited for here, not at its first use inside the loop,
     // where the wait would also catch each step's block-id read
     float scale_log2 = a.scale_log2;
-    asm volatile("" : "+s"(scale_log2));
+    settle_s(scale_log2);
     for (int k = 0; k < n_tiles; ++k) {
       const int slot = k & (kSlots - 1);
       const int ahead = min(n_tiles - 1 - k, kSlots - 1);
@@ -751,7 +777,7 @@ decode_partition_kernel(const DecodeArgs a) {
       a.out[row * D + d] = any_bad || den == 0.f ? nan : num / den;
       if (d == 0 && a.lse) a.lse[row] = any_bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
     } else {
-      const size_t pi = row * a.num_parts + p;
+      const size_t pi = row * a.num_parts + a.part_base + p;
       a.part_acc[pi * D + d] = num;
       if (d == 0) {
         a.part_m[pi] = any_bad ? nan : M;
@@ -911,7 +937,7 @@ decode_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
     }
   };
   float scale_log2 = a.scale_log2;  // waited for here (see the other kernel)
-  asm volatile("" : "+s"(scale_log2));
+  settle_s(scale_log2);
 
 #pragma unroll
   for (int s = 0; s < kSlots; ++s)

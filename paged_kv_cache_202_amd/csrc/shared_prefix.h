@@ -1,0 +1,361 @@
+// Shared-prefix attention on MFMA for gfx950 (MI355X): the prefix phase of
+// paged attention for groups of sequences whose block tables begin with the
+// same physical blocks. Sharing blocks within and across requests is the
+// point of PagedAttention (vLLM abstract on the papers page "external
+// vector cache"); forking a prefix by reference counts is the page pool of
+// the course page "Module 10. KV Caches and Efficient Inference", notebook
+// section 5. The arithmetic is the decode kernels' -- each query row's
+// max-subtracted softmax over the keys it sees (that page's project demo,
+// Demo 2), computed online -- restricted to the shared tokens; the private
+// rest of every context is handled by the ordinary kernels from the
+// group's prefix length on, and a log-sum-exp merge joins the two.
+//
+// Design (this build's, for CDNA4):
+//   * the query rows of all members of a group are stacked: a 16-row MFMA
+//     tile holds 16 / RPM members' rows (RPM = G x query tokens, padded to a
+//     power of two). One workgroup = W wavefronts = W row tiles of the same
+//     (group, KV head, prefix partition), RT = 1 or 2 tiles per wavefront
+//     sharing each K/V read; every prefix tile is gathered once
+//     into the workgroup's LDS ring by direct-to-LDS loads and read by all W
+//     wavefronts, so each shared K/V byte leaves L2 once per W row tiles
+//     instead of once per member;
+//   * the gathers place bytes so that the reads are conflict-free: K in the
+//     order its MFMA A operand is read (lane l's c-th 16 bytes at
+//     (c * 64 + l) * 16), V in token rows whose 16-byte chunks are
+//     XOR-swizzled by token, read back with the transposing LDS read as the
+//     B operand of the P V product;
+//   * per tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online softmax
+//     with a lazily raised maximum, P rounded to bf16, O += P V with
+//     v_mfma_f32_16x16x16_bf16 -- the verify kernel's arithmetic;
+//   * a ring of 4 or 8 tile slots and one workgroup barrier per tile: a slot
+//     is refilled right after the barrier that follows the last reads of it,
+//     so all but one slot are in flight;
+//   * each wavefront writes its rows' unnormalised partials (m, l, acc) for
+//     its prefix partition; the merge kernel joins them with the suffix's.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "decode_kernel.h"
+#include "verify_mfma.h"
+
+namespace pkv {
+namespace decode {
+
+// Sharing groups as the prefix kernel sees them (all device arrays).
+struct ShareArgs {
+  const int32_t *group_start;   // [n_groups + 1] offsets into members
+  const int32_t *members;       // sequence indices, grouped
+  const int32_t *group_tokens;  // [n_groups] shared prefix tokens (multiple of 16)
+  int32_t n_groups;
+  int32_t n_members;    // length of members (= group_start[n_groups])
+  int32_t chunks;       // workgroups (of W row tiles) per group along grid.z
+  int32_t rpm;          // query rows per member, padded to a power of two
+  int32_t prefix_part;  // tokens per prefix partition (multiple of 16)
+};
+
+template <int D>
+struct PrefixGeo {
+  static constexpr int NC = D / 32;                // A-operand chunks per lane (16 B each)
+  static constexpr int NCB = D / 16;               // column blocks of P V
+  static constexpr int kHalf = kTile * D * 2;      // bytes of a K (or V) tile
+  static constexpr int kTileBytes = 2 * kHalf;     // K then V
+  static constexpr int kLoads = kTileBytes / 1024; // 1 KiB gathers per tile
+  static constexpr int kRowChunks = D / 8;         // 16-byte chunks per V token row
+  // tiles in the ring (64 KiB at most): all but one are in flight while the
+  // oldest is read, so the workgroup keeps up to 56 KiB of gathers going
+  static constexpr int kSlots = kTileBytes <= 8192 ? 8 : 65536 / kTileBytes;
+  static_assert(kSlots >= 3 && (kSlots & (kSlots - 1)) == 0, "ring of 4 or 8 slots");
+};
+
+// XOR swizzle of the 16-byte chunks of V token row t: the sixteen rows of a
+// tile put any given chunk in different bank groups.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int t) {
+  return t & (PrefixGeo<D>::kRowChunks - 1);
+}
+
+// B operands of the P V product for four column blocks with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane s names 8 bytes holding elements 4 s' .. 4 s' + 3 of a 64-element
+// window and lane i receives window elements i, i + 16, i + 32, i + 48. So
+// if lane s of group lg names dims cb * 16 + 4 (s % 4) .. + 3 of token
+// 4 lg + s / 4, lane i receives V[4 lg + u][cb * 16 + i], u = 0..3: the B
+// operand. addr[j] is this lane's address for block j; one wait for all.
+__device__ __forceinline__ void read_vtr4(uint2 (&vb)[4], const PKV_LDS char *a0,
+                                          const PKV_LDS char *a1, const PKV_LDS char *a2,
+                                          const PKV_LDS char *a3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vb[0]), "=&v"(vb[1]), "=&v"(vb[2]), "=&v"(vb[3])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+template <int D, int W, int RT>
+__global__ void __launch_bounds__(W * 64)
+prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
+  using Gp = PrefixGeo<D>;
+  constexpr int NC = Gp::NC, NCB = Gp::NCB, kSlots = Gp::kSlots;
+  constexpr float kNegInf = -std::numeric_limits<float>::infinity();
+  __shared__ u32x4_t sm_ring[kSlots * Gp::kTileBytes / 16];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15, lg = lane >> 4;
+  const int p = blockIdx.x, h = blockIdx.y;
+  const int grp = blockIdx.z / s.chunks, chunk = blockIdx.z % s.chunks;
+  if (grp >= s.n_groups) return;
+  // group bounds are clamped to the members array, so that inconsistent
+  // arrays cannot send reads out of it
+  const int ms = max(0, min(s.n_members, load_const(s.group_start + grp)));
+  const int me = max(ms, min(s.n_members, load_const(s.group_start + grp + 1)));
+  const int prefix_req = load_const(s.group_tokens + grp);
+  const int max_ctx = a.max_blocks * a.bs;
+  // a prefix that is not whole tiles or runs past the table poisons the group
+  const int prefix = max(0, min(prefix_req, max_ctx)) & ~(kTile - 1);
+  const int t_begin = p * s.prefix_part;
+  const int mpt = kVerifyRows / s.rpm;  // members per row tile
+  const int tile0 = chunk * W * RT;     // first row tile of this workgroup
+  // workgroup-uniform exits: no tokens in this partition, no rows in this chunk
+  if (t_begin >= prefix || ms + tile0 * mpt >= me) return;
+  const int t_end = min(prefix, t_begin + s.prefix_part);
+  const int n_tiles = (t_end - t_begin) / kTile;  // prefix is a multiple of 16
+  const int nq = a.nq, G = a.Hq / a.Hkv;
+  const float nan = __builtin_nanf("");
+
+  // ---- this lane's query rows: row ln of each of the wavefront's RT tiles ---
+  const int rr = ln % s.rpm;  // row within the member
+  const int qi = rr / G;
+  uint4 qb[RT][NC];
+  int lim_r[RT];  // visible keys of row ln of tile r
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int mem_idx = ms + (tile0 + wave * RT + r) * mpt + ln / s.rpm;  // member of the row
+    const bool row_ok = mem_idx < me && qi < nq;
+    const int b_raw = row_ok ? s.members[mem_idx] : -1;
+    const bool b_ok = b_raw >= 0 && b_raw < a.B;
+    const int b = b_ok ? b_raw : 0;
+    const int L = b_ok ? a.lens[b] : 0;
+    // a member whose length is out of range is left to the merge kernel (NaN)
+    const bool live = row_ok && b_ok && L >= nq && L <= max_ctx;
+    lim_r[r] = live ? L - nq + qi + 1 : 0;
+    const size_t row = ((size_t)b * nq + (live ? qi : 0)) * a.Hq + h * G + rr % G;
+    const uint16_t *qp = (const uint16_t *)a.q + row * D + lg * (D / 4);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qb[r][c] = live ? *reinterpret_cast<const uint4 *>(qp + c * 8) : make_uint4(0, 0, 0, 0);
+  }
+  // the query rows and lengths are waited for before the tile loop
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) settle_v(qb[r][c]);
+    settle_v(lim_r[r]);
+  }
+
+  // ---- gathers: the leader's table holds the shared blocks -------------------
+  const int leader_raw = load_const(s.members + ms);
+  const int leader = leader_raw >= 0 && leader_raw < a.B ? leader_raw : 0;
+  const int32_t *trow = a.tables + (size_t)leader * a.max_blocks;
+  const char *kbase = (const char *)a.kc;
+  const char *vbase = (const char *)a.vc;
+  PKV_LDS char *ring = (PKV_LDS char *)&sm_ring[0];
+  // a prefix tile came from a bad table entry, or the group's description
+  // was unusable (workgroup-uniform): the group's partials become NaN
+  int bad = leader != leader_raw || prefix != prefix_req;
+  // global byte offsets, inside a tile, of the 16 bytes lane l moves in
+  // gather j: K in A-operand read order, V in swizzled token rows
+  const int k_src = ln * (D * 2) + lg * (D / 2);  // + 16 j
+  auto v_src = [&](int j) {
+    const int pos = j * 1024 + lane * 16;  // destination byte in the V half
+    const int t = pos / (D * 2), cp = (pos % (D * 2)) / 16;
+    return t * (D * 2) + (cp ^ v_swizzle<D>(t)) * 16;
+  };
+  auto table_at = [&](int k) {  // block id of tile k (clamped to the last tile)
+    return load_const(trow + (t_begin + min(k, n_tiles - 1) * kTile) / a.bs);
+  };
+  auto stage = [&](int slot, int k, int blk) {
+    const int t0 = t_begin + k * kTile;
+    if (blk < 0 || blk >= a.num_blocks) {
+      bad = 1;
+      blk = 0;
+    }
+    const size_t tile = (((size_t)blk * a.Hkv + h) * a.bs + (size_t)(t0 % a.bs)) * (D * 2);
+    PKV_LDS char *dst = ring + slot * Gp::kTileBytes;
+#pragma unroll
+    for (int i = 0; i < (Gp::kLoads + W - 1) / W; ++i) {
+      const int j = wave + i * W;  // this wavefront's gathers of the tile
+      if (j < Gp::kLoads / 2)
+        gather_lds16<0>(kbase + tile + k_src + j * 16, dst + j * 1024);
+      else if (j < Gp::kLoads)
+        gather_lds16<0>(vbase + tile + v_src(j - Gp::kLoads / 2), dst + j * 1024);
+    }
+  };
+  constexpr int kPerWave = (Gp::kLoads + W - 1) / W;  // gathers per wavefront per tile
+
+  // this lane's transposing-read addresses, relative to the V half of a
+  // slot: dims cb * 16 + 4 (ln % 4) .. + 3 of token 4 lg + ln / 4, whose
+  // 16-byte chunk sits at position chunk ^ swizzle(token)
+  int v_addr[NCB];
+  {
+    const int t = 4 * lg + (ln >> 2);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int c = 2 * cb + ((ln >> 1) & 1);
+      v_addr[cb] = t * (D * 2) + ((c ^ v_swizzle<D>(t)) << 4) + (ln & 1) * 8;
+    }
+  }
+
+  f32x4_t o[RT][NCB];
+#pragma unroll
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[r][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_row[RT], l_part[RT];  // running max (log2 units) and weight-sum share of row ln
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    m_row[r] = kNegInf;
+    l_part[r] = 0.f;
+  }
+  float scale_log2 = a.scale_log2;  // waited for here, not inside the loop
+  settle_s(scale_log2);
+
+  // prologue: tiles 0 .. kSlots - 2 in flight
+#pragma unroll
+  for (int k = 0; k < kSlots - 1; ++k)
+    if (k < n_tiles) stage(k, k, table_at(k));
+  int blk_next = table_at(kSlots - 1);  // read one trip ahead of its gather
+  for (int k = 0; k < n_tiles; ++k) {
+    // this wavefront's gathers of tile k have landed (the later ones, up to
+    // kSlots - 2 tiles, may not)
+    const int ahead = min(n_tiles - 1 - k, kSlots - 2);
+    static_for<kSlots - 1>([&](auto ac) {
+      constexpr int A = decltype(ac)::value;
+      if (ahead == A) wait_vmcnt<A * kPerWave>();
+    });
+    // ... and so have everyone's; everyone is done reading tile k - 1, whose
+    // slot takes tile k + kSlots - 1
+    __builtin_amdgcn_s_barrier();
+    if (k + kSlots - 1 < n_tiles) {
+      stage((k + kSlots - 1) % kSlots, k + kSlots - 1, blk_next);
+      blk_next = table_at(k + kSlots);
+    }
+    const PKV_LDS char *kt = ring + (k % kSlots) * Gp::kTileBytes;
+    const PKV_LDS char *vt = kt + Gp::kHalf;
+    const int t0 = t_begin + k * kTile;
+
+    // S^T = K Q^T per row tile: sv[r][e] = score of row ln with token t0 + 4 lg + e
+    u32x4_t kr[NC];
+    if constexpr (NC == 2) {
+      lds_rows<2>(kr, kt + lane * 16);
+    } else if constexpr (NC == 4) {
+      lds_rows<4>(kr, kt + lane * 16);
+    } else {
+      lds_rows<8>(kr, kt + lane * 16);
+    }
+    uint2 pa[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
+                                                     __builtin_bit_cast(bf16x8_t, qb[r][c]), sv,
+                                                     0, 0, 0);
+      float sc[4];
+      bool need = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool vis = t0 + 4 * lg + e < lim_r[r];
+        sc[e] = vis ? sv[e] * scale_log2 : kNegInf;
+        need |= sc[e] > m_row[r] + kLazyLog2;
+      }
+      if (__any(need)) {
+        float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        tmax = fmaxf(tmax, exact_xor<16>(tmax));
+        tmax = fmaxf(tmax, exact_xor<32>(tmax));
+        const float mn = fmaxf(m_row[r], tmax);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row[r] - mn);
+        m_row[r] = mn;
+        l_part[r] *= alpha;
+        // O holds rows 4 lg + e: their factors live in lanes 4 lg + e
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float al = __shfl(alpha, 4 * lg + e, 64);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) o[r][cb][e] *= al;
+        }
+      }
+      float pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[e] = sc[e] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[e] - m_row[r]);
+        l_part[r] += pw[e];
+      }
+      pa[r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
+    }
+
+    // O += P V: B operand V[token 4 lg + u][dim cb * 16 + ln], u = 0..3,
+    // read once for all row tiles
+    static_for<NCB / 4>([&](auto gc) {
+      constexpr int CB = 4 * decltype(gc)::value;
+      uint2 vb[4];
+      read_vtr4(vb, vt + v_addr[CB], vt + v_addr[CB + 1], vt + v_addr[CB + 2],
+                vt + v_addr[CB + 3]);
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[r][CB + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(i16x4_t, pa[r]), __builtin_bit_cast(i16x4_t, vb[j]),
+              o[r][CB + j], 0, 0, 0);
+    });
+  }
+
+  // ---- this wavefront's partials for prefix partition p ---------------------
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float l_row = l_part[r];
+    l_row += exact_xor<16>(l_row);
+    l_row += exact_xor<32>(l_row);
+    // output rows 4 lg + e of the tile: their statistics live in lanes 4 lg + e
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rt = 4 * lg + e;  // tile row
+      const int r_mem = ms + (tile0 + wave * RT + r) * mpt + rt / s.rpm;
+      const int r_rr = rt % s.rpm, r_qi = r_rr / G;
+      const float mr = __shfl(m_row[r], rt, 64);
+      const float lr = __shfl(l_row, rt, 64);
+      if (r_mem >= me || r_qi >= nq) continue;
+      const int rb = load_const(s.members + r_mem);
+      if (rb < 0 || rb >= a.B) continue;
+      const size_t row = ((size_t)rb * nq + r_qi) * a.Hq + h * G + r_rr % G;
+      const size_t pi = row * a.num_parts + p;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) a.part_acc[pi * D + cb * 16 + ln] = o[r][cb][e];
+      if (ln == 0) {
+        a.part_m[pi] = bad ? nan : mr;
+        a.part_l[pi] = lr;
+      }
+    }
+  }
+}
+
+using PrefixLauncher = void (*)(const DecodeArgs &, const ShareArgs &, dim3, hipStream_t);
+
+// Launcher of the prefix kernel for a head dim, W wavefronts per workgroup
+// (1, 2, 4 or 8) and RT row tiles per wavefront (1 or 2); nullptr if none.
+// Defined in shared_inst.hip.
+PrefixLauncher pick_prefix(int D, int W, int RT);
+
+}  // namespace decode
+}  // namespace pkv

@@ -96,7 +96,10 @@ verify_mfma_kernel(const DecodeArgs a) {
     }
     return;
   }
-  const int t_begin = p * a.part_tokens;
+  // earlier tokens belong to the prefix phase (clamped: bad values cannot
+  // send reads outside the table)
+  const int start = a.starts ? min(max(load_const(a.starts + b), 0), L) : 0;
+  const int t_begin = start + p * a.part_tokens;
   if (t_begin >= L) return;
   const int t_end = min(L, t_begin + a.part_tokens);
 
@@ -287,7 +290,7 @@ verify_mfma_kernel(const DecodeArgs a) {
       a.out[row * D + d] = any_bad || den == 0.f ? nan : num / den;
       if (d == 0 && a.lse) a.lse[row] = any_bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
     } else {
-      const size_t pi = row * a.num_parts + p;
+      const size_t pi = row * a.num_parts + a.part_base + p;
       a.part_acc[pi * D + d] = num;
       if (d == 0) {
         a.part_m[pi] = any_bad ? nan : M;

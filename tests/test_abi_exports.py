@@ -3,6 +3,8 @@
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -78,3 +80,15 @@ def test_workspace_grows_with_partitions():
     assert pkv.paged_attention_workspace_size(64, 1, 32, 8, 128, 512, 16, -1) > 0
     with pytest.raises(pkv.InvalidArgument):
         pkv.paged_attention_workspace_size(64, 1, 32, 8, 128, 512, 16, -2)
+
+
+def test_every_kernel_launch_has_its_kernel():
+    """A kernel template whose host-side check fails is dropped without an
+    error, leaving its launch stub undefined; the library must have none."""
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    lib = os.path.join(os.path.dirname(pkv.__file__), "libpagedkv.so")
+    syms = subprocess.run([nm, "-D", lib], capture_output=True, text=True, check=True).stdout
+    undefined = [l for l in syms.splitlines() if " U " in l and "__device_stub__" in l]
+    assert not undefined, undefined

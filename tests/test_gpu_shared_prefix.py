@@ -1,0 +1,252 @@
+"""GPU parity of shared-prefix attention (paged_attention_decode_shared).
+
+Batches of forked sequences are built twice from the same synthetic inputs:
+by the oracle's page pool with its cache writes and copies, and by the
+library's allocator, block copy and cache-write kernels. The shared path's
+output is compared with the float64 oracle walk, and with the library's
+ordinary decode on the same device state.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import bench
+import paged_kv_cache_202_amd as pkv
+from oracle import attention as oatt
+from oracle import native
+from oracle.pool import PagedPool
+from synth import workloads as wl
+from scenario import nan_fill, storage, tolerance
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
+class ShareCase:
+    """Fork families (parent prefix + per-member suffixes) and loners, bf16."""
+
+    def __init__(self, families, loners, Hq, Hkv, D, nq, bs=16, seed=0, device="cuda:0"):
+        self.Hq, self.Hkv, self.D, self.nq, self.bs = Hq, Hkv, D, nq, bs
+        rng = np.random.default_rng(seed)
+        root = wl.root_seed(rng)
+        # sequence ids: each family's parent, then its children, then loners
+        plan = []  # (seq, parent or None, prefix, suffix)
+        sid = 0
+        for prefix, suffixes in families:
+            parent = sid
+            for j, suf in enumerate(suffixes):
+                plan.append((sid, None if j == 0 else parent, prefix, suf))
+                sid += 1
+        for n in loners:
+            plan.append((sid, None, 0, n))
+            sid += 1
+        self.B = sid
+        self.lens = [p + s for _, _, p, s in plan]
+        need = sum(-(-p // bs) + 1 for p, _ in families) + sum(-(-n // bs) + 1 for n in self.lens)
+        self.num_blocks = need + 8
+        stack = np.random.default_rng(seed + 1).permutation(self.num_blocks).astype(np.int32)
+        self.max_blocks = max(-(-n // bs) for n in self.lens)
+        stream = iter(range(3, 10**6))
+        pre = {s: (wl.cast(wl.normal_array(root, next(stream), (p, Hkv, D)), "bf16"),
+                   wl.cast(wl.normal_array(root, next(stream), (p, Hkv, D)), "bf16"))
+               for s, par, p, _ in plan if par is None and p}
+        suf = {s: (wl.cast(wl.normal_array(root, next(stream), (n, Hkv, D)), "bf16"),
+                   wl.cast(wl.normal_array(root, next(stream), (n, Hkv, D)), "bf16"))
+               for s, _, _, n in plan}
+        self.q = wl.cast(wl.normal_array(root, 2, (self.B, nq, Hq, D)), "bf16")
+        self.scale = 1.0 / np.sqrt(D)
+
+        # ---- oracle side ----------------------------------------------------
+        op = PagedPool(self.num_blocks, bs, stack.tolist())
+        o_pre, o_suf, o_pairs = {}, {}, []
+        for s, par, p, _ in plan:
+            if par is None:
+                op.create(s)
+                if p:
+                    o_pre[s] = op.append(s, p)[0]
+            else:
+                op.share_prefix(par, s, p)
+        for s, _, _, n in plan:
+            sl, cw = op.append(s, n)
+            o_suf[s] = sl
+            o_pairs += cw
+        tables, lens = op.block_tables(range(self.B), self.max_blocks)
+        self.o_tables = np.array(tables, np.int32)
+        self.o_lens = np.array(lens, np.int32)
+        shape = (self.num_blocks, Hkv, bs, D)
+        self.o_k = np.zeros(shape, np.uint16)
+        self.o_v = np.zeros(shape, np.uint16)
+        for s, (k, v) in pre.items():
+            oatt.cache_write(self.o_k, self.o_v, storage(k), storage(v), o_pre[s], bs)
+        for src, dst in o_pairs:
+            self.o_k[dst] = self.o_k[src]
+            self.o_v[dst] = self.o_v[src]
+        for s, (k, v) in suf.items():
+            oatt.cache_write(self.o_k, self.o_v, storage(k), storage(v), o_suf[s], bs)
+
+        # ---- library side ---------------------------------------------------
+        pool = pkv.PagedKVPool(self.num_blocks, bs, stack)
+        self.kc = nan_fill(shape, "bf16", device)
+        self.vc = nan_fill(shape, "bf16", device)
+        for s, par, p, _ in plan:
+            if par is None:
+                pool.seq_create(s)
+                if p:
+                    sl, cw = pool.alloc(s, p)
+                    assert len(cw) == 0
+                    k, v = pre[s]
+                    pkv.paged_cache_write(k.to(device), v.to(device), self.kc, self.vc,
+                                          torch.from_numpy(np.asarray(sl, np.int32)).to(device))
+            else:
+                pool.fork(par, s, p)
+        pairs, writes = [], []
+        for s, _, _, n in plan:
+            sl, cw = pool.alloc(s, n)
+            pairs += [tuple(x) for x in np.asarray(cw).reshape(-1, 2).tolist()]
+            writes.append((s, sl))
+        assert pairs == [tuple(x) for x in o_pairs]
+        if pairs:
+            pkv.paged_kv_copy_blocks(self.kc, self.vc, torch.tensor(pairs, dtype=torch.int32,
+                                                                   device=device))
+        for s, sl in writes:
+            k, v = suf[s]
+            assert list(sl) == list(o_suf[s])
+            if len(sl):
+                pkv.paged_cache_write(k.to(device), v.to(device), self.kc, self.vc,
+                                      torch.from_numpy(np.asarray(sl, np.int32)).to(device))
+        t, l = pool.block_tables(list(range(self.B)), self.max_blocks)
+        assert np.array_equal(t, self.o_tables) and np.array_equal(l, self.o_lens)
+        self.tables_host, self.lens_host = t, l
+        self.d_tables = torch.from_numpy(t.copy()).to(device)
+        self.d_lens = torch.from_numpy(l.copy()).to(device)
+        self.d_q = self.q.to(device)
+        self.device = device
+        self.pool = pool
+
+    def oracle(self):
+        out, lse = native.attention(storage(self.q), "bf16", self.o_k, self.o_v, "bf16",
+                                    self.o_tables, self.o_lens, self.scale, self.bs,
+                                    threads=THREADS)
+        return out, lse
+
+    def run(self, shared=True, partition_tokens=0, min_tokens=16):
+        B, nq, Hq, D = self.B, self.nq, self.Hq, self.D
+        out = torch.full((B, nq, Hq, D), float("nan"), dtype=torch.float32, device=self.device)
+        lse = torch.full((B, nq, Hq), float("nan"), dtype=torch.float32, device=self.device)
+        if shared:
+            g = pkv.paged_kv_prefix_groups(self.tables_host, self.lens_host, nq, self.bs,
+                                           min_members=2, min_tokens=min_tokens)
+            n = pkv.paged_attention_shared_workspace_size(B, nq, Hq, self.Hkv, D,
+                                                          self.max_blocks, self.bs, g,
+                                                          partition_tokens)
+            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+            pkv.paged_attention_decode_shared(out, self.d_q, self.kc, self.vc, self.d_tables,
+                                              self.d_lens, self.scale, g,
+                                              g.to_device(self.device),
+                                              partition_tokens=partition_tokens,
+                                              workspace=ws, lse=lse)
+            self.groups = g
+        else:
+            n = pkv.paged_attention_workspace_size(B, nq, Hq, self.Hkv, D, self.max_blocks,
+                                                   self.bs, partition_tokens)
+            ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+            pkv.paged_attention_decode(out, self.d_q, self.kc, self.vc, self.d_tables,
+                                       self.d_lens, self.scale, partition_tokens=partition_tokens,
+                                       workspace=ws, lse=lse)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy()
+
+
+CASES = [
+    # (families [(prefix, [suffix per member])], loners, Hq, Hkv, D, nq, partition)
+    ([(320, [20, 35, 70, 1, 48, 16]), (264, [9, 40, 33])], [100, 17], 32, 8, 128, 4, 0),
+    ([(256, [5, 60, 31, 90, 2]), (512, [30, 47])], [75], 32, 8, 128, 1, 0),
+    ([(400, [33] * 11)], [50, 81], 64, 8, 64, 1, 0),
+    ([(192, [40, 3, 77, 12, 19, 64, 5, 8, 100])], [], 8, 8, 256, 2, 0),
+    ([(272, [4, 30, 18])], [64], 4, 2, 128, 8, 0),
+    ([(640, [12 + 7 * i for i in range(40)])], [333], 32, 8, 128, 4, 0),
+    ([(384, [50, 130, 77, 260])], [400], 32, 8, 128, 1, 64),
+    ([(384, [50, 130, 77, 260])], [400], 32, 8, 128, 4, 96),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(CASES)))
+def test_shared_prefix_matches_oracle(ci, device):
+    fam, lon, Hq, Hkv, D, nq, part = CASES[ci]
+    print(f"shared prefix case {ci}: families {[(p, len(s)) for p, s in fam]} loners {lon} "
+          f"Hq {Hq} Hkv {Hkv} D {D} nq {nq} partition {part}", flush=True)
+    c = ShareCase(fam, lon, Hq, Hkv, D, nq, seed=ci, device=device)
+    out, lse = c.run(shared=True, partition_tokens=part)
+    assert c.groups.n_groups == len(fam)
+    ref, ref_lse = c.oracle()
+    err = np.abs(out - ref).max()
+    err_lse = np.abs(lse - ref_lse).max()
+    print(f"  groups {c.groups.n_groups}, prefix {c.groups.group_tokens[:c.groups.n_groups]}; "
+          f"max-abs {err:.3e}, lse {err_lse:.3e}", flush=True)
+    assert np.isfinite(out).all() and err <= tolerance("bf16")
+    assert np.isfinite(lse).all() and err_lse <= tolerance("bf16")
+    plain, _ = c.run(shared=False, partition_tokens=part)
+    assert np.abs(out - plain).max() <= tolerance("bf16")
+
+
+def test_no_groups_is_plain_decode(device):
+    c = ShareCase([(256, [10, 20])], [30], 32, 8, 128, 4, seed=11, device=device)
+    out, _ = c.run(shared=True, min_tokens=10**6)  # no group qualifies
+    assert c.groups.n_groups == 0
+    plain, _ = c.run(shared=False)
+    assert np.array_equal(out, plain)
+
+
+@pytest.mark.parametrize("prefix", [2048, 2056])
+def test_prefix_share_verify_full_size(prefix, device):
+    """64 sequences forking a 2048-token (or 2056-token) prefix, 512 private
+    tokens each and K = 4 drafts: the shared path against the float64 C
+    oracle, all rows."""
+    print(f"prefix-share verify (shared path): prefix {prefix}", flush=True)
+    wk = bench.PrefixVerifyWorkload("prefix_share_verify_k4", device, prefix=prefix)
+    B, K, bs = wk.B, wk.nq, wk.bs
+    opool = PagedPool(wk.w.num_blocks, bs, wk.stack.tolist())
+    opool.create(0)
+    pre_slots, _ = opool.append(0, prefix)
+    for s in range(1, B):
+        opool.share_prefix(0, s, prefix)
+    suf_slots, pairs = [], []
+    for s in range(B):
+        sl, cw = opool.append(s, wk.suffix)
+        suf_slots += sl
+        pairs += cw
+    dft_slots = []
+    for s in range(B):
+        dft_slots += opool.append(s, K)[0]
+    tables, lens = opool.block_tables(range(B), wk.max_blocks)
+    assert wk.tables_host.tolist() == tables
+    shape = (wk.w.num_blocks, wk.Hkv, bs, wk.D)
+    kp = np.zeros(shape, np.uint16)
+    vp = np.zeros(shape, np.uint16)
+    oatt.cache_write(kp, vp, storage(wk.k_pre), storage(wk.v_pre), pre_slots, bs)
+    for src, dst in pairs:
+        kp[dst] = kp[src]
+        vp[dst] = vp[src]
+    oatt.cache_write(kp, vp, storage(wk.k_suf), storage(wk.v_suf), suf_slots, bs)
+    oatt.cache_write(kp, vp, storage(wk.k_dft), storage(wk.v_dft), dft_slots, bs)
+    wk.cache_write(0)
+    g = pkv.paged_kv_prefix_groups(wk.tables_host, np.asarray(lens, np.int32), K, bs)
+    assert g.n_groups == 1 and g.max_members == B and g.max_prefix == 2048
+    n = pkv.paged_attention_shared_workspace_size(B, K, wk.Hq, wk.Hkv, wk.D, wk.max_blocks, bs,
+                                                  g)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    out = torch.full_like(wk.out, float("nan"))
+    pkv.paged_attention_decode_shared(out, wk.d_q, wk.kc, wk.vc, wk.d_tables, wk.d_lens,
+                                      wk.scale, g, g.to_device(device), workspace=ws)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    ref, _ = native.attention(storage(wk.host_q), "bf16", kp, vp, "bf16",
+                              np.array(tables, np.int32), np.array(lens, np.int32), wk.scale, bs,
+                              threads=THREADS)
+    err = np.abs(out - ref).max()
+    print(f"  max-abs error {err:.3e} over {out.size} outputs", flush=True)
+    assert np.isfinite(out).all() and err <= tolerance("bf16")
