@@ -23,10 +23,12 @@
 //     order its MFMA A operand is read (lane l's c-th 16 bytes at
 //     (c * 64 + l) * 16), V in token rows whose 16-byte chunks are
 //     XOR-swizzled by token, read back with the transposing LDS read as the
-//     B operand of the P V product;
+//     A operand of the transposed product O^T += V^T P^T;
 //   * per tile: S^T = K Q^T with v_mfma_f32_16x16x32_bf16, online softmax
-//     with a lazily raised maximum, P rounded to bf16, O += P V with
-//     v_mfma_f32_16x16x16_bf16 -- the verify kernel's arithmetic;
+//     with a lazily raised maximum, P rounded to bf16, O^T += V^T P^T with
+//     v_mfma_f32_16x16x16_bf16 -- the verify kernel's arithmetic. Computing
+//     O transposed leaves each row's outputs in the lane that holds its
+//     softmax statistics, so rescaling needs no cross-lane moves;
 //   * a ring of 4 or 8 tile slots and one workgroup barrier per tile: a slot
 //     is refilled right after the barrier that follows the last reads of it,
 //     so all but one slot are in flight;
@@ -79,24 +81,93 @@ __device__ __forceinline__ int v_swizzle(int t) {
   return t & (PrefixGeo<D>::kRowChunks - 1);
 }
 
-// B operands of the P V product for four column blocks with the gfx950
-// transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane s names 8 bytes holding elements 4 s' .. 4 s' + 3 of a 64-element
-// window and lane i receives window elements i, i + 16, i + 32, i + 48. So
-// if lane s of group lg names dims cb * 16 + 4 (s % 4) .. + 3 of token
-// 4 lg + s / 4, lane i receives V[4 lg + u][cb * 16 + i], u = 0..3: the B
-// operand. addr[j] is this lane's address for block j; one wait for all.
-__device__ __forceinline__ void read_vtr4(uint2 (&vb)[4], const PKV_LDS char *a0,
-                                          const PKV_LDS char *a1, const PKV_LDS char *a2,
-                                          const PKV_LDS char *a3) {
+// One tile's MFMA operands from an LDS slot, with one wait for all of them.
+// K: this lane's NC 16-byte A-operand chunks at kp + c * 1024 (the gathers
+// put them there). V: the A operand of O^T += V^T P^T for each 16-dim column
+// block, read with the gfx950 transposing LDS read (ds_read_b64_tr_b16):
+// within each group of 16 lanes, lane s names 8 bytes holding elements
+// 4 s' .. 4 s' + 3 of a 64-element window and lane i receives window elements
+// i, i + 16, i + 32, i + 48. So if lane s of group lg names dims
+// cb * 16 + 4 (s % 4) .. + 3 of token 4 lg + s / 4, lane i receives
+// V[4 lg + u][cb * 16 + i], u = 0..3. va[cb] is this lane's address for
+// column block cb.
+template <int D>
+__device__ __forceinline__ void read_kv(u32x4_t (&k)[D / 32], uint2 (&v)[D / 16],
+                                        const PKV_LDS char *kp,
+                                        const PKV_LDS char *const (&va)[D / 16]);
+
+template <>
+__device__ __forceinline__ void read_kv<64>(u32x4_t (&k)[2], uint2 (&v)[4],
+                                           const PKV_LDS char *kp,
+                                           const PKV_LDS char *const (&va)[4]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %6 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %7\n\t"
+      "ds_read_b64_tr_b16 %3, %8\n\t"
+      "ds_read_b64_tr_b16 %4, %9\n\t"
+      "ds_read_b64_tr_b16 %5, %10\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(vb[0]), "=&v"(vb[1]), "=&v"(vb[2]), "=&v"(vb[3])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(kp), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_kv<128>(u32x4_t (&k)[4], uint2 (&v)[8],
+                                           const PKV_LDS char *kp,
+                                           const PKV_LDS char *const (&va)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %12 offset:1024\n\t"
+      "ds_read_b128 %2, %12 offset:2048\n\t"
+      "ds_read_b128 %3, %12 offset:3072\n\t"
+      "ds_read_b64_tr_b16 %4, %13\n\t"
+      "ds_read_b64_tr_b16 %5, %14\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %16\n\t"
+      "ds_read_b64_tr_b16 %8, %17\n\t"
+      "ds_read_b64_tr_b16 %9, %18\n\t"
+      "ds_read_b64_tr_b16 %10, %19\n\t"
+      "ds_read_b64_tr_b16 %11, %20\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(kp), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_kv<256>(u32x4_t (&k)[8], uint2 (&v)[16],
+                                           const PKV_LDS char *kp,
+                                           const PKV_LDS char *const (&va)[16]) {
+  asm volatile(
+      "ds_read_b128 %0, %24\n\t"
+      "ds_read_b128 %1, %24 offset:1024\n\t"
+      "ds_read_b128 %2, %24 offset:2048\n\t"
+      "ds_read_b128 %3, %24 offset:3072\n\t"
+      "ds_read_b128 %4, %24 offset:4096\n\t"
+      "ds_read_b128 %5, %24 offset:5120\n\t"
+      "ds_read_b128 %6, %24 offset:6144\n\t"
+      "ds_read_b128 %7, %24 offset:7168\n\t"
+      "ds_read_b64_tr_b16 %8, %25\n\t"
+      "ds_read_b64_tr_b16 %9, %26\n\t"
+      "ds_read_b64_tr_b16 %10, %27\n\t"
+      "ds_read_b64_tr_b16 %11, %28\n\t"
+      "ds_read_b64_tr_b16 %12, %29\n\t"
+      "ds_read_b64_tr_b16 %13, %30\n\t"
+      "ds_read_b64_tr_b16 %14, %31\n\t"
+      "ds_read_b64_tr_b16 %15, %32\n\t"
+      "ds_read_b64_tr_b16 %16, %33\n\t"
+      "ds_read_b64_tr_b16 %17, %34\n\t"
+      "ds_read_b64_tr_b16 %18, %35\n\t"
+      "ds_read_b64_tr_b16 %19, %36\n\t"
+      "ds_read_b64_tr_b16 %20, %37\n\t"
+      "ds_read_b64_tr_b16 %21, %38\n\t"
+      "ds_read_b64_tr_b16 %22, %39\n\t"
+      "ds_read_b64_tr_b16 %23, %40\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(kp), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), "v"(va[8]), "v"(va[9]), "v"(va[10]), "v"(va[11]), "v"(va[12]), "v"(va[13]), "v"(va[14]), "v"(va[15])
       : "memory");
 }
 
@@ -132,29 +203,46 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   const int nq = a.nq, G = a.Hq / a.Hkv;
   const float nan = __builtin_nanf("");
 
-  // ---- this lane's query rows: row ln of each of the wavefront's RT tiles ---
+  // ---- set-up: two short chains of dependent loads, issued side by side ----
+  // (1) the leader's table row, whose entries address the shared tiles;
+  // (2) this lane's query rows: row ln of each of the wavefront's RT tiles.
+  const int leader_raw = load_const(s.members + ms);
   const int rr = ln % s.rpm;  // row within the member
   const int qi = rr / G;
-  uint4 qb[RT][NC];
-  int lim_r[RT];  // visible keys of row ln of tile r
+  int b_row[RT];              // sequence of row ln of tile r (-1: none)
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int mem_idx = ms + (tile0 + wave * RT + r) * mpt + ln / s.rpm;  // member of the row
-    const bool row_ok = mem_idx < me && qi < nq;
-    const int b_raw = row_ok ? s.members[mem_idx] : -1;
-    const bool b_ok = b_raw >= 0 && b_raw < a.B;
-    const int b = b_ok ? b_raw : 0;
-    const int L = b_ok ? a.lens[b] : 0;
+    const int mem_idx = ms + (tile0 + wave * RT + r) * mpt + ln / s.rpm;
+    const int b_raw = mem_idx < me && qi < nq ? s.members[mem_idx] : -1;
+    b_row[r] = b_raw >= 0 && b_raw < a.B ? b_raw : -1;
+  }
+  const int leader = leader_raw >= 0 && leader_raw < a.B ? leader_raw : 0;
+  const int32_t *trow = a.tables + (size_t)leader * a.max_blocks;
+  // lane i holds the block id of tile 64 w + i of the current window w
+  // (clamped to the partition's last tile)
+  auto table_window = [&](int w) {
+    return trow[(t_begin + min(64 * w + lane, n_tiles - 1) * kTile) / a.bs];
+  };
+  int tblv = table_window(0);
+  uint4 qb[RT][NC];
+  int lim_r[RT];  // keys visible to row ln of tile r
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int b = max(b_row[r], 0);
+    const int L = a.lens[b];
     // a member whose length is out of range is left to the merge kernel (NaN)
-    const bool live = row_ok && b_ok && L >= nq && L <= max_ctx;
+    const bool live = b_row[r] >= 0 && L >= nq && L <= max_ctx;
     lim_r[r] = live ? L - nq + qi + 1 : 0;
-    const size_t row = ((size_t)b * nq + (live ? qi : 0)) * a.Hq + h * G + rr % G;
+    const size_t row = ((size_t)b * nq + min(qi, nq - 1)) * a.Hq + h * G + rr % G;
     const uint16_t *qp = (const uint16_t *)a.q + row * D + lg * (D / 4);
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qb[r][c] = live ? *reinterpret_cast<const uint4 *>(qp + c * 8) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < NC; ++c) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(qp + c * 8);
+      qb[r][c] = live ? v : make_uint4(0, 0, 0, 0);
+    }
   }
-  // the query rows and lengths are waited for before the tile loop
+  // all of it is waited for here, once, before the first gather
+  settle_v(tblv);
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
 #pragma unroll
@@ -162,10 +250,6 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
     settle_v(lim_r[r]);
   }
 
-  // ---- gathers: the leader's table holds the shared blocks -------------------
-  const int leader_raw = load_const(s.members + ms);
-  const int leader = leader_raw >= 0 && leader_raw < a.B ? leader_raw : 0;
-  const int32_t *trow = a.tables + (size_t)leader * a.max_blocks;
   const char *kbase = (const char *)a.kc;
   const char *vbase = (const char *)a.vc;
   PKV_LDS char *ring = (PKV_LDS char *)&sm_ring[0];
@@ -179,9 +263,6 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
     const int pos = j * 1024 + lane * 16;  // destination byte in the V half
     const int t = pos / (D * 2), cp = (pos % (D * 2)) / 16;
     return t * (D * 2) + (cp ^ v_swizzle<D>(t)) * 16;
-  };
-  auto table_at = [&](int k) {  // block id of tile k (clamped to the last tile)
-    return load_const(trow + (t_begin + min(k, n_tiles - 1) * kTile) / a.bs);
   };
   auto stage = [&](int slot, int k, int blk) {
     const int t0 = t_begin + k * kTile;
@@ -211,10 +292,12 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int c = 2 * cb + ((ln >> 1) & 1);
-      v_addr[cb] = t * (D * 2) + ((c ^ v_swizzle<D>(t)) << 4) + (ln & 1) * 8;
+      v_addr[cb] = Gp::kHalf + t * (D * 2) + ((c ^ v_swizzle<D>(t)) << 4) + (ln & 1) * 8;
     }
   }
 
+  // O^T accumulators: o[r][cb][e] = O[row ln][dim cb * 16 + 4 lg + e], so
+  // a row's statistics and its outputs live in the same lane
   f32x4_t o[RT][NCB];
 #pragma unroll
   for (int r = 0; r < RT; ++r)
@@ -232,8 +315,7 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   // prologue: tiles 0 .. kSlots - 2 in flight
 #pragma unroll
   for (int k = 0; k < kSlots - 1; ++k)
-    if (k < n_tiles) stage(k, k, table_at(k));
-  int blk_next = table_at(kSlots - 1);  // read one trip ahead of its gather
+    if (k < n_tiles) stage(k, k, __builtin_amdgcn_readlane(tblv, k));
   for (int k = 0; k < n_tiles; ++k) {
     // this wavefront's gathers of tile k have landed (the later ones, up to
     // kSlots - 2 tiles, may not)
@@ -245,41 +327,50 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
     // ... and so have everyone's; everyone is done reading tile k - 1, whose
     // slot takes tile k + kSlots - 1
     __builtin_amdgcn_s_barrier();
-    if (k + kSlots - 1 < n_tiles) {
-      stage((k + kSlots - 1) % kSlots, k + kSlots - 1, blk_next);
-      blk_next = table_at(k + kSlots);
+    const int kn = k + kSlots - 1;
+    if (kn < n_tiles) {
+      if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
+        tblv = table_window(kn >> 6);
+        settle_v(tblv);
+      }
+      stage(kn % kSlots, kn, __builtin_amdgcn_readlane(tblv, kn & 63));
     }
     const PKV_LDS char *kt = ring + (k % kSlots) * Gp::kTileBytes;
-    const PKV_LDS char *vt = kt + Gp::kHalf;
     const int t0 = t_begin + k * kTile;
 
-    // S^T = K Q^T per row tile: sv[r][e] = score of row ln with token t0 + 4 lg + e
     u32x4_t kr[NC];
-    if constexpr (NC == 2) {
-      lds_rows<2>(kr, kt + lane * 16);
-    } else if constexpr (NC == 4) {
-      lds_rows<4>(kr, kt + lane * 16);
-    } else {
-      lds_rows<8>(kr, kt + lane * 16);
+    uint2 vb[NCB];
+    {
+      const PKV_LDS char *va[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) va[cb] = kt + v_addr[cb];
+      read_kv<D>(kr, vb, kt + lane * 16, va);
     }
+
+    // S^T = K Q^T per row tile: sv[r][e] = score of row ln with token t0 + 4 lg + e
+    f32x4_t sv[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        sv[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
+                                                        __builtin_bit_cast(bf16x8_t, qb[r][c]),
+                                                        sv[r], 0, 0, 0);
     uint2 pa[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      f32x4_t sv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        sv = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
-                                                     __builtin_bit_cast(bf16x8_t, qb[r][c]), sv,
-                                                     0, 0, 0);
       float sc[4];
       bool need = false;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool vis = t0 + 4 * lg + e < lim_r[r];
-        sc[e] = vis ? sv[e] * scale_log2 : kNegInf;
+        sc[e] = vis ? sv[r][e] * scale_log2 : kNegInf;
         need |= sc[e] > m_row[r] + kLazyLog2;
       }
       if (__any(need)) {
+        // row ln's scores are spread over the four lane groups
         float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         tmax = fmaxf(tmax, exact_xor<16>(tmax));
         tmax = fmaxf(tmax, exact_xor<32>(tmax));
@@ -287,13 +378,8 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
         const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row[r] - mn);
         m_row[r] = mn;
         l_part[r] *= alpha;
-        // O holds rows 4 lg + e: their factors live in lanes 4 lg + e
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float al = __shfl(alpha, 4 * lg + e, 64);
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) o[r][cb][e] *= al;
-        }
+        for (int cb = 0; cb < NCB; ++cb) o[r][cb] *= alpha;
       }
       float pw[4];
 #pragma unroll
@@ -304,48 +390,34 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
       pa[r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
     }
 
-    // O += P V: B operand V[token 4 lg + u][dim cb * 16 + ln], u = 0..3,
-    // read once for all row tiles
-    static_for<NCB / 4>([&](auto gc) {
-      constexpr int CB = 4 * decltype(gc)::value;
-      uint2 vb[4];
-      read_vtr4(vb, vt + v_addr[CB], vt + v_addr[CB + 1], vt + v_addr[CB + 2],
-                vt + v_addr[CB + 3]);
+    // O^T += V^T P^T: A operand V[token 4 lg + u][dim cb * 16 + ln], B operand
+    // P[row ln][token 4 lg + u], u = 0..3; the V read serves all row tiles
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[r][CB + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(i16x4_t, pa[r]), __builtin_bit_cast(i16x4_t, vb[j]),
-              o[r][CB + j], 0, 0, 0);
-    });
+        o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(i16x4_t, vb[cb]), __builtin_bit_cast(i16x4_t, pa[r]), o[r][cb],
+            0, 0, 0);
   }
 
-  // ---- this wavefront's partials for prefix partition p ---------------------
+  // ---- this wavefront's partials for prefix partition p: row ln of each tile
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     float l_row = l_part[r];
     l_row += exact_xor<16>(l_row);
     l_row += exact_xor<32>(l_row);
-    // output rows 4 lg + e of the tile: their statistics live in lanes 4 lg + e
+    if (b_row[r] < 0) continue;
+    const size_t row = ((size_t)b_row[r] * nq + qi) * a.Hq + h * G + rr % G;
+    const size_t pi = row * a.num_parts + p;
+    float *acc = a.part_acc + pi * D + 4 * lg;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rt = 4 * lg + e;  // tile row
-      const int r_mem = ms + (tile0 + wave * RT + r) * mpt + rt / s.rpm;
-      const int r_rr = rt % s.rpm, r_qi = r_rr / G;
-      const float mr = __shfl(m_row[r], rt, 64);
-      const float lr = __shfl(l_row, rt, 64);
-      if (r_mem >= me || r_qi >= nq) continue;
-      const int rb = load_const(s.members + r_mem);
-      if (rb < 0 || rb >= a.B) continue;
-      const size_t row = ((size_t)rb * nq + r_qi) * a.Hq + h * G + r_rr % G;
-      const size_t pi = row * a.num_parts + p;
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) a.part_acc[pi * D + cb * 16 + ln] = o[r][cb][e];
-      if (ln == 0) {
-        a.part_m[pi] = bad ? nan : mr;
-        a.part_l[pi] = lr;
-      }
+    for (int cb = 0; cb < NCB; ++cb)
+      *reinterpret_cast<float4 *>(acc + cb * 16) =
+          make_float4(o[r][cb][0], o[r][cb][1], o[r][cb][2], o[r][cb][3]);
+    if (lg == 0) {
+      a.part_m[pi] = bad ? nan : m_row[r];
+      a.part_l[pi] = l_row;
     }
   }
 }
