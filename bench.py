@@ -78,6 +78,10 @@ def algorithmic_bytes(B, nq, Hq, Hkv, D, es, lens, max_blocks, with_lse=False):
 def kernel_label(wk) -> str:
     """Which launches one attention call makes, as the library plans them."""
     mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16
+    if getattr(wk, "share", False) and wk.groups.n_groups:
+        return ("prefix_mfma_kernel + " + ("verify_mfma_kernel" if mfma else
+                                           "decode_partition_kernel") +
+                " + reduce_partitions_kernel")
     if wk.part == -1 and not mfma:
         return "decode_stream_kernel + reduce_stream_kernel"
     main = "verify_mfma_kernel" if mfma else "decode_partition_kernel"
@@ -195,7 +199,7 @@ class PrefixVerifyWorkload:
     call (query i of K sees the first L - K + i + 1 tokens).
     """
 
-    def __init__(self, name: str, device, prefix: int | None = None):
+    def __init__(self, name: str, device, prefix: int | None = None, share: bool = True):
         import torch
 
         import paged_kv_cache_202_amd as pkv
@@ -260,6 +264,17 @@ class PrefixVerifyWorkload:
         self.scale = 1.0 / math.sqrt(D)
         self.part = w.partition_tokens
         ws = pkv.paged_attention_workspace_size(B, K, Hq, Hkv, D, self.max_blocks, bs, self.part)
+        # shared prefixes: groups found once from the host tables (they change
+        # only on fork or free), each shared block then read once per KV head
+        self.share = share
+        self.groups_s = 0.0
+        if share:
+            t0 = time.perf_counter()
+            self.groups = pkv.paged_kv_prefix_groups(tables, self.lens, K, bs)
+            self.groups_s = time.perf_counter() - t0
+            self.d_groups = self.groups.to_device(dev)
+            ws = max(ws, pkv.paged_attention_shared_workspace_size(
+                B, K, Hq, Hkv, D, self.max_blocks, bs, self.groups, self.part))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
         self.rotate = 1
         torch.cuda.synchronize()
@@ -268,6 +283,13 @@ class PrefixVerifyWorkload:
         self.pkv.paged_cache_write(self.k_step, self.v_step, self.kc, self.vc, self.d_step_slots)
 
     def attend(self, i: int) -> None:
+        if self.share:
+            self.pkv.paged_attention_decode_shared(self.out, self.d_q, self.kc, self.vc,
+                                                   self.d_tables, self.d_lens, self.scale,
+                                                   self.groups, self.d_groups,
+                                                   partition_tokens=self.part,
+                                                   workspace=self.ws)
+            return
         self.pkv.paged_attention_decode(self.out, self.d_q, self.kc, self.vc, self.d_tables,
                                         self.d_lens, self.scale, partition_tokens=self.part,
                                         workspace=self.ws)
@@ -447,6 +469,9 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=2,
                     help="pool copies used in turn so repeats cannot hit the 256 MB cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-share", action="store_true",
+                    help="prefix-sharing workloads: attend with the plain kernels, reading "
+                         "every shared block once per sequence")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run paged_kv_copy_blocks over MIB MiB of K and of V (a plain "
                          "copy of known size, to calibrate HBM byte counters), then exit")
@@ -478,7 +503,7 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe, dev)
     if args.workload.startswith("prefix_share"):
-        wk = PrefixVerifyWorkload(args.workload, dev)
+        wk = PrefixVerifyWorkload(args.workload, dev, share=not args.no_share)
     else:
         wk = Workload(args.workload, args.rotate, dev)
     log(f"[bench] workload {args.workload} ready; max_blocks {wk.max_blocks}")
@@ -509,7 +534,10 @@ def main() -> int:
     torch.cuda.synchronize()
     attn_ms = statistics.mean(b.elapsed_time(c) for a, b, c in ev)
     write_ms = statistics.mean(a.elapsed_time(b) for a, b, c in ev)
-    attn_bytes = wk.attention_bytes()
+    # the shared-prefix path's minimum is every physical block once; the plain
+    # path's is every sequence's visible K/V
+    attn_bytes = wk.unique_attention_bytes() if getattr(wk, "share", False) else \
+        wk.attention_bytes()
     achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
     log(f"[bench] attention {attn_ms * 1e3:.1f} us -> {achieved:.0f} GB/s; cache write "
         f"{write_ms * 1e3:.1f} us")
@@ -540,10 +568,14 @@ def main() -> int:
         "step_breakdown_us": {"cache_write": write_ms * 1e3, "attention": attn_ms * 1e3},
         "host_alloc_us": {"step_alloc": wk.alloc_step_s * 1e6},
     }
+    if getattr(wk, "share", False):
+        result["host_alloc_us"]["prefix_groups"] = wk.groups_s * 1e6
     if hasattr(wk, "unique_attention_bytes"):
-        ub = wk.unique_attention_bytes()
+        ub, lb = wk.unique_attention_bytes(), wk.attention_bytes()
         result["roofline"]["unique_bytes"] = ub
         result["roofline"]["achieved_unique"] = ub / (attn_ms * 1e-3) / 1e9
+        result["roofline"]["logical_bytes"] = lb
+        result["roofline"]["achieved_logical"] = lb / (attn_ms * 1e-3) / 1e9
     if not args.no_cpu_baseline and not hasattr(wk, "unique_attention_bytes"):
         result["cpu_baseline"] = cpu_baseline(wk)
         log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")

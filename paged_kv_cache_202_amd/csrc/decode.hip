@@ -208,9 +208,10 @@ Plan plan_launch(int64_t B, int64_t Hkv, int64_t max_ctx, int32_t req, bool stre
 
 template <int D>
 void launch_reduce(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
-  // grid.x = query rows per sequence; few slots per row: one group per row
+  // grid.x = query rows per sequence; up to 16 slots per row: one group per
+  // row, looping over them
   constexpr int NG = kReduceThreads / (D / 4);
-  if (a.num_parts <= 8) {
+  if (a.num_parts <= 16) {
     grid.x = (grid.x + NG - 1) / NG;
     hipLaunchKernelGGL((reduce_partitions_kernel<D, 1>), grid, dim3(kReduceThreads), 0, s, a);
   } else {

@@ -171,11 +171,77 @@ __device__ __forceinline__ void read_kv<256>(u32x4_t (&k)[8], uint2 (&v)[16],
       : "memory");
 }
 
+// The same for the two adjacent slots of a trip of two tiles (the second
+// slot's operands at the same addresses plus one tile).
+template <int D>
+__device__ __forceinline__ void read_kv2(u32x4_t (&k)[2][D / 32], uint2 (&v)[2][D / 16],
+                                         const PKV_LDS char *kp,
+                                         const PKV_LDS char *const (&va)[D / 16]);
+
+template <>
+__device__ __forceinline__ void read_kv2<64>(u32x4_t (&k)[2][2], uint2 (&v)[2][4],
+                                            const PKV_LDS char *kp,
+                                            const PKV_LDS char *const (&va)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %12 offset:1024\n\t"
+      "ds_read_b128 %2, %12 offset:4096\n\t"
+      "ds_read_b128 %3, %12 offset:5120\n\t"
+      "ds_read_b64_tr_b16 %4, %13\n\t"
+      "ds_read_b64_tr_b16 %5, %14\n\t"
+      "ds_read_b64_tr_b16 %6, %15\n\t"
+      "ds_read_b64_tr_b16 %7, %16\n\t"
+      "ds_read_b64_tr_b16 %8, %13 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %9, %14 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %15 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %16 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+      : "v"(kp), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_kv2<128>(u32x4_t (&k)[2][4], uint2 (&v)[2][8],
+                                            const PKV_LDS char *kp,
+                                            const PKV_LDS char *const (&va)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %24\n\t"
+      "ds_read_b128 %1, %24 offset:1024\n\t"
+      "ds_read_b128 %2, %24 offset:2048\n\t"
+      "ds_read_b128 %3, %24 offset:3072\n\t"
+      "ds_read_b128 %4, %24 offset:8192\n\t"
+      "ds_read_b128 %5, %24 offset:9216\n\t"
+      "ds_read_b128 %6, %24 offset:10240\n\t"
+      "ds_read_b128 %7, %24 offset:11264\n\t"
+      "ds_read_b64_tr_b16 %8, %25\n\t"
+      "ds_read_b64_tr_b16 %9, %26\n\t"
+      "ds_read_b64_tr_b16 %10, %27\n\t"
+      "ds_read_b64_tr_b16 %11, %28\n\t"
+      "ds_read_b64_tr_b16 %12, %29\n\t"
+      "ds_read_b64_tr_b16 %13, %30\n\t"
+      "ds_read_b64_tr_b16 %14, %31\n\t"
+      "ds_read_b64_tr_b16 %15, %32\n\t"
+      "ds_read_b64_tr_b16 %16, %25 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %17, %26 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %18, %27 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %19, %28 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %20, %29 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %21, %30 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %22, %31 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %23, %32 offset:8192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[0][2]), "=&v"(k[0][3]), "=&v"(k[1][0]), "=&v"(k[1][1]), "=&v"(k[1][2]), "=&v"(k[1][3]), "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]), "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]), "=&v"(v[1][7])
+      : "v"(kp), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
+      : "memory");
+}
+
 template <int D, int W, int RT>
 __global__ void __launch_bounds__(W * 64)
 prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   using Gp = PrefixGeo<D>;
   constexpr int NC = Gp::NC, NCB = Gp::NCB, kSlots = Gp::kSlots;
+  constexpr int TT = D <= 128 ? 2 : 1;  // 16-token tiles per trip
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   __shared__ u32x4_t sm_ring[kSlots * Gp::kTileBytes / 16];
 
@@ -312,66 +378,94 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   float scale_log2 = a.scale_log2;  // waited for here, not inside the loop
   settle_s(scale_log2);
 
-  // prologue: tiles 0 .. kSlots - 2 in flight
+  // keys of this partition visible to row ln of tile r
+  int lim_p[RT];
 #pragma unroll
-  for (int k = 0; k < kSlots - 1; ++k)
-    if (k < n_tiles) stage(k, k, __builtin_amdgcn_readlane(tblv, k));
-  for (int k = 0; k < n_tiles; ++k) {
-    // this wavefront's gathers of tile k have landed (the later ones, up to
-    // kSlots - 2 tiles, may not)
-    const int ahead = min(n_tiles - 1 - k, kSlots - 2);
-    static_for<kSlots - 1>([&](auto ac) {
-      constexpr int A = decltype(ac)::value;
-      if (ahead == A) wait_vmcnt<A * kPerWave>();
-    });
-    // ... and so have everyone's; everyone is done reading tile k - 1, whose
-    // slot takes tile k + kSlots - 1
-    __builtin_amdgcn_s_barrier();
-    const int kn = k + kSlots - 1;
-    if (kn < n_tiles) {
-      if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
+  for (int r = 0; r < RT; ++r) lim_p[r] = min(lim_r[r], t_end);
+
+  // TT tiles per trip share one barrier, one LDS wait and one softmax step;
+  // every trip stages all TT tiles (past the end: the last tile again), so
+  // that each wavefront's count of gathers in flight stays exact
+  constexpr int kTrips = kSlots / TT;  // trips the ring holds
+  const int n_trips = (n_tiles + TT - 1) / TT;
+  auto stage_trip = [&](int j) {
+#pragma unroll
+    for (int u = 0; u < TT; ++u) {
+      const int kn = TT * j + u;
+      if ((kn & 63) == 0 && kn > 0) {  // next window of block ids (drains the ring once)
         tblv = table_window(kn >> 6);
         settle_v(tblv);
       }
-      stage(kn % kSlots, kn, __builtin_amdgcn_readlane(tblv, kn & 63));
+      stage(kn % kSlots, min(kn, n_tiles - 1), __builtin_amdgcn_readlane(tblv, kn & 63));
     }
-    const PKV_LDS char *kt = ring + (k % kSlots) * Gp::kTileBytes;
-    const int t0 = t_begin + k * kTile;
+  };
 
-    u32x4_t kr[NC];
-    uint2 vb[NCB];
+  // prologue: trips 0 .. kTrips - 2 in flight
+#pragma unroll
+  for (int j = 0; j < kTrips - 1; ++j)
+    if (j < n_trips) stage_trip(j);
+  for (int j = 0; j < n_trips; ++j) {
+    // this wavefront's gathers of trip j have landed (the later ones, up to
+    // kTrips - 2 trips, may not)
+    const int ahead = min(n_trips - 1 - j, kTrips - 2);
+    static_for<kTrips - 1>([&](auto ac) {
+      constexpr int A = decltype(ac)::value;
+      if (ahead == A) wait_vmcnt<A * TT * kPerWave>();
+    });
+    // ... and so have everyone's; everyone is done reading trip j - 1, whose
+    // slots take trip j + kTrips - 1
+    __builtin_amdgcn_s_barrier();
+    if (j + kTrips - 1 < n_trips) stage_trip(j + kTrips - 1);
+    const PKV_LDS char *kt = ring + ((TT * j) % kSlots) * Gp::kTileBytes;
+    const int t0 = t_begin + TT * j * kTile;
+
+    u32x4_t kr[TT][NC];
+    uint2 vb[TT][NCB];
     {
       const PKV_LDS char *va[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) va[cb] = kt + v_addr[cb];
-      read_kv<D>(kr, vb, kt + lane * 16, va);
+      if constexpr (TT == 2)
+        read_kv2<D>(kr, vb, kt + lane * 16, va);
+      else
+        read_kv<D>(kr[0], vb[0], kt + lane * 16, va);
     }
 
-    // S^T = K Q^T per row tile: sv[r][e] = score of row ln with token t0 + 4 lg + e
-    f32x4_t sv[RT];
+    // S^T = K Q^T per tile and row tile: sv[u][r][e] = score of row ln with
+    // token t0 + 16 u + 4 lg + e
+    f32x4_t sv[TT][RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) sv[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < TT; ++u)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sv[u][r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
-        sv[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
-                                                        __builtin_bit_cast(bf16x8_t, qb[r][c]),
-                                                        sv[r], 0, 0, 0);
-    uint2 pa[RT];
+      for (int u = 0; u < TT; ++u)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          sv[u][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, kr[u][c]), __builtin_bit_cast(bf16x8_t, qb[r][c]),
+              sv[u][r], 0, 0, 0);
+    uint2 pa[TT][RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      float sc[4];
+      float sc[TT][4];
       bool need = false;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool vis = t0 + 4 * lg + e < lim_r[r];
-        sc[e] = vis ? sv[r][e] * scale_log2 : kNegInf;
-        need |= sc[e] > m_row[r] + kLazyLog2;
-      }
+      for (int u = 0; u < TT; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = t0 + 16 * u + 4 * lg + e < lim_p[r];
+          sc[u][e] = vis ? sv[u][r][e] * scale_log2 : kNegInf;
+          need |= sc[u][e] > m_row[r] + kLazyLog2;
+        }
       if (__any(need)) {
         // row ln's scores are spread over the four lane groups
-        float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        float tmax = kNegInf;
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+          tmax = fmaxf(tmax, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
         tmax = fmaxf(tmax, exact_xor<16>(tmax));
         tmax = fmaxf(tmax, exact_xor<32>(tmax));
         const float mn = fmaxf(m_row[r], tmax);
@@ -381,24 +475,38 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) o[r][cb] *= alpha;
       }
-      float pw[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pw[e] = sc[e] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[e] - m_row[r]);
-        l_part[r] += pw[e];
+      for (int u = 0; u < TT; ++u) {
+        float pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pw[e] = sc[u][e] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[u][e] - m_row[r]);
+          l_part[r] += pw[e];
+        }
+        pa[u][r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
       }
-      pa[r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
     }
 
-    // O^T += V^T P^T: A operand V[token 4 lg + u][dim cb * 16 + ln], B operand
-    // P[row ln][token 4 lg + u], u = 0..3; the V read serves all row tiles
+    // O^T += V^T P^T: A operand V[token][dim cb * 16 + ln], B operand
+    // P[row ln][token]; lane group lg supplies tokens 4 lg .. 4 lg + 3 of each
+    // tile of the trip (the same token order on both sides), and the V read
+    // serves all row tiles
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int r = 0; r < RT; ++r)
-        o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            __builtin_bit_cast(i16x4_t, vb[cb]), __builtin_bit_cast(i16x4_t, pa[r]), o[r][cb],
-            0, 0, 0);
+      for (int r = 0; r < RT; ++r) {
+        if constexpr (TT == 2) {
+          const u32x4_t va2 = {vb[0][cb].x, vb[0][cb].y, vb[1][cb].x, vb[1][cb].y};
+          const u32x4_t pb2 = {pa[0][r].x, pa[0][r].y, pa[1][r].x, pa[1][r].y};
+          o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, va2), __builtin_bit_cast(bf16x8_t, pb2), o[r][cb], 0,
+              0, 0);
+        } else {
+          o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(i16x4_t, vb[0][cb]), __builtin_bit_cast(i16x4_t, pa[0][r]),
+              o[r][cb], 0, 0, 0);
+        }
+      }
   }
 
   // ---- this wavefront's partials for prefix partition p: row ln of each tile
