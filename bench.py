@@ -36,6 +36,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, decimal GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 KERNEL_SOURCES = ["paged_kv_cache_202_amd/csrc/decode_kernel.h",
                   "paged_kv_cache_202_amd/csrc/decode_inst_bf16_d128.hip",
                   "paged_kv_cache_202_amd/csrc/decode.hip"]
@@ -75,8 +76,24 @@ def algorithmic_bytes(B, nq, Hq, Hkv, D, es, lens, max_blocks, with_lse=False):
     return kv + q + out + tables + 4 * B
 
 
+def is_chunk(wk) -> bool:
+    """More than one 16-row tile of query rows per KV head: chunked prefill."""
+    return wk.w.dtype == "bf16" and wk.Hq // wk.Hkv * wk.nq > 16
+
+
+def chunk_flops(B, nq, Hq, D, lens) -> int:
+    """Multiply-adds of a causal chunk call, counted as 2 FLOPs each: every
+    row does q.k and p.v (2 D each) for each key it sees."""
+    seen = 0
+    for L in np.asarray(lens, dtype=np.int64):
+        seen += int(np.sum(L - nq + np.arange(nq) + 1))
+    return 4 * D * Hq * seen
+
+
 def kernel_label(wk) -> str:
     """Which launches one attention call makes, as the library plans them."""
+    if is_chunk(wk):
+        return "chunk_mfma_kernel + reduce_partitions_kernel"
     mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16
     if getattr(wk, "share", False) and wk.groups.n_groups:
         return ("prefix_mfma_kernel + " + ("verify_mfma_kernel" if mfma else
@@ -570,6 +587,17 @@ def main() -> int:
     }
     if getattr(wk, "share", False):
         result["host_alloc_us"]["prefix_groups"] = wk.groups_s * 1e6
+    if is_chunk(wk):
+        # a prefill chunk is a dense contraction: priced against bf16 MFMA
+        fl = chunk_flops(wk.B, wk.nq, wk.Hq, wk.D, wk.lens)
+        tf = fl / (attn_ms * 1e-3) / 1e12
+        result["value"] = wk.B * wk.nq / (ms_step * 1e-3)
+        result["roofline"].update({
+            "bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": tf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": fl,
+            "hbm_achieved_GBs": achieved})
+        result["roofline"].pop("algorithmic_bytes")
+        result["roofline"]["algorithmic_bytes_hbm"] = attn_bytes
     if hasattr(wk, "unique_attention_bytes"):
         ub, lb = wk.unique_attention_bytes(), wk.attention_bytes()
         result["roofline"]["unique_bytes"] = ub

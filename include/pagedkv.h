@@ -248,7 +248,13 @@ int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
  * (up to 16 rows per KV head: G * nq rounded up to a power of two, 8 per
  * wavefront); bf16 caches with nq > 1 run on an MFMA tile of 16 query rows
  * per KV head (G * nq <= 16), e.g. 4 query heads x 4 draft tokens for
- * verification.
+ * verification. With bf16 caches and G * nq > 16 the call is a chunked
+ * prefill (a chunk of nq prompt tokens over the cached prefix plus the chunk
+ * itself, whose K/V were written first; the chunk decomposition of
+ * [KVNB s7]): an MFMA kernel over 16-row tiles of the chunk's rows, the
+ * context cut into partitions (partition_tokens > 0 fixes their length; 0
+ * and -1 let the library choose), then the log-sum-exp reduce; a workspace
+ * is always needed. fp32 caches take at most 16 rows per KV head.
  * Host-checked: sizes, Hq % Hkv == 0, D and block_size supported, rows per
  * KV head within those limits, scale finite, workspace large enough ->
  * EINVAL. */

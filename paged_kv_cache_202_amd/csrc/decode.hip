@@ -55,12 +55,14 @@ reduce_partitions_kernel(const DecodeArgs a) {
     }
     return;
   }
-  // slots written for this row: partitions [0, ceil(L / P)); with a shared
-  // prefix, prefix pieces [0, ceil(start / PP)) and then the suffix's
-  // partitions from slot part_base on
+  // slots written for this row: partitions [0, ceil(lim / P)) for a row that
+  // sees lim keys (a partition past them may have been skipped altogether);
+  // with a shared prefix, prefix pieces [0, ceil(start / PP)) and then the
+  // suffix's partitions from slot part_base on
   const int start = a.starts ? min(max(load_const(a.starts + b), 0), L) : 0;
   const int np_pre = a.starts ? (start + a.prefix_part - 1) / a.prefix_part : 0;
-  const int np_suf = (L - start + a.part_tokens - 1) / a.part_tokens;
+  const int lim = L - a.nq + (row_ok ? rowq : 0) / a.Hq + 1;  // keys this row sees
+  const int np_suf = (max(lim - start, 0) + a.part_tokens - 1) / a.part_tokens;
   const int np = row_ok ? min(a.num_parts, a.part_base + np_suf) : 0;
   const float *pm = a.part_m + row * a.num_parts;
   const float *pl = a.part_l + row * a.num_parts;
@@ -284,10 +286,49 @@ static bool use_mfma(int dtype, int32_t nq, int32_t G) {
   return dtype == PKV_BF16 && nq > 1 && G * nq <= kVerifyRows;
 }
 
+// Chunked prefill: more than one 16-row tile of query rows per KV head, on
+// the MFMA row-tile kernel (bf16).
+static bool use_chunk(int dtype, int32_t nq, int32_t G) {
+  return dtype == PKV_BF16 && G * nq > kVerifyRows;
+}
+
 static int check_rows(int dtype, int32_t nq, int32_t G) {
-  if (use_mfma(dtype, nq, G)) return PKV_OK;
+  if (use_mfma(dtype, nq, G) || use_chunk(dtype, nq, G)) return PKV_OK;
   if (G * next_pow2(nq) > kMaxRows)
-    return fail(PKV_EINVAL, "G * nq = %d * %d exceeds the supported rows per KV head", G, nq);
+    return fail(PKV_EINVAL,
+                "G * nq = %d * %d rows per KV head: more than %d need bf16 caches", G, nq,
+                kMaxRows);
+  return PKV_OK;
+}
+
+// Launch shape of the chunk kernel: W wavefronts x RT row tiles per
+// workgroup, `chunks` workgroups per (sequence, KV head) along grid.z, and
+// the context cut into np partitions of pp tokens (all multiples of 16).
+struct ChunkPlan {
+  int32_t W, RT, chunks, np, pp;
+};
+
+static int chunk_plan(int32_t B, int32_t nq, int32_t G, int32_t Hkv, int32_t D, int64_t max_ctx,
+                      int32_t part, ChunkPlan *cp) {
+  const int32_t tiles = (G * nq + kVerifyRows - 1) / kVerifyRows;  // row tiles per KV head
+  cp->RT = tiles >= 16 && D <= 128 ? 2 : 1;
+  const int32_t per_wave = (tiles + cp->RT - 1) / cp->RT;
+  cp->W = per_wave >= 8 ? 8 : next_pow2(per_wave);
+  cp->chunks = (tiles + cp->W * cp->RT - 1) / (cp->W * cp->RT);
+  if ((int64_t)B * cp->chunks > 65535)
+    return fail(PKV_EINVAL, "B * row chunks = %d * %d exceed one launch", B, cp->chunks);
+  if (part > 0) {
+    cp->pp = part;
+  } else {
+    // enough partitions that the workgroups fill a round of wavefronts
+    const int64_t per_part = (int64_t)B * Hkv * cp->chunks * cp->W;
+    int64_t np = (kResidentWaves + per_part - 1) / per_part;
+    const int64_t most = (max_ctx + 2 * kTile - 1) / (2 * kTile);  // at least 32 tokens each
+    if (np > most) np = most;
+    if (np < 1) np = 1;
+    cp->pp = (int32_t)(((max_ctx + np - 1) / np + kTile - 1) / kTile * kTile);
+  }
+  cp->np = (int32_t)((max_ctx + cp->pp - 1) / cp->pp);
   return PKV_OK;
 }
 
@@ -305,6 +346,11 @@ static void row_split(int32_t G, int32_t nq, int32_t *RP, int32_t *S) {
 
 static size_t workspace_need(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t D,
                              int64_t max_ctx, int32_t part) {
+  if (use_chunk(PKV_BF16, nq, Hq / Hkv)) {
+    ChunkPlan cp;
+    if (chunk_plan(B, nq, Hq / Hkv, Hkv, D, max_ctx, part, &cp)) return 0;
+    return partial_bytes((int64_t)B * nq * Hq, cp.np, D);
+  }
   int32_t RP, S;
   row_split(Hq / Hkv, nq, &RP, &S);
   const int64_t units = (int64_t)B * Hkv * S;
@@ -327,7 +373,70 @@ extern "C" int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
                                               int32_t part, size_t *bytes) {
   if (!bytes) return fail(PKV_EINVAL, "bytes is NULL");
   if (int rc = check_sizes(B, nq, Hq, Hkv, D, max_blocks, bs, part)) return rc;
+  if (use_chunk(PKV_BF16, nq, Hq / Hkv)) {
+    ChunkPlan cp;
+    if (int rc = chunk_plan(B, nq, Hq / Hkv, Hkv, D, (int64_t)max_blocks * bs, part, &cp))
+      return rc;
+  }
   *bytes = workspace_need(B, nq, Hq, Hkv, D, (int64_t)max_blocks * bs, part);
+  return PKV_OK;
+}
+
+// Chunked prefill (bf16, more than 16 query rows per KV head): the chunk
+// kernel writes (m, l, acc) per row and context partition; the partition
+// reduce merges them (a single partition too: it also normalises).
+static int chunk_attention(float *out, const void *q, const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, int32_t max_blocks,
+                           const int32_t *context_lens, int32_t B, int32_t nq, int32_t Hq,
+                           int32_t Hkv, int32_t D, int32_t bs, int32_t num_blocks, float scale,
+                           int32_t part, void *workspace, size_t workspace_bytes, float *lse_out,
+                           hipStream_t s) {
+  const int32_t G = Hq / Hkv;
+  ChunkPlan cp;
+  if (int rc = chunk_plan(B, nq, G, Hkv, D, (int64_t)max_blocks * bs, part, &cp)) return rc;
+  PrefixLauncher chunk = pick_prefix(D, cp.W, cp.RT, true);
+  if (!chunk) return fail(PKV_EINVAL, "no chunk kernel for D=%d", D);
+  const int64_t rows = (int64_t)B * nq * Hq;
+  const size_t need = partial_bytes(rows, cp.np, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_EINVAL, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((uintptr_t)workspace % 256) return fail(PKV_EINVAL, "workspace must be 256-byte aligned");
+  DecodeArgs a{};
+  a.out = out;
+  a.lse = lse_out;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.B = B;
+  a.max_blocks = max_blocks;
+  a.nq = nq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.bs = bs;
+  a.num_blocks = num_blocks;
+  a.part_tokens = cp.pp;
+  a.num_parts = cp.np;
+  a.slices = 1;
+  a.scale_log2 = scale * kLog2e;
+  char *w = (char *)workspace;
+  a.part_acc = (float *)w;
+  w += align_up((size_t)rows * cp.np * D * 4, 256);
+  a.part_m = (float *)w;
+  w += align_up((size_t)rows * cp.np * 4, 256);
+  a.part_l = (float *)w;
+  ShareArgs sh{};
+  sh.chunks = cp.chunks;
+  sh.prefix_part = cp.pp;
+  chunk(a, sh, dim3(cp.np, Hkv, B * cp.chunks), s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "chunk launch: %s", hipGetErrorString(e));
+  StreamArgs sa{};
+  pick_reduce(D)(a, sa, dim3(nq * Hq, B), s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }
 
@@ -349,6 +458,10 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   if (!std::isfinite(scale)) return fail(PKV_EINVAL, "scale must be finite");
   const int G = Hq / Hkv;
   if (int rc = check_rows(dtype, nq, G)) return rc;
+  if (use_chunk(dtype, nq, G))
+    return chunk_attention(out, q, k_cache, v_cache, block_tables, max_blocks, context_lens, B,
+                           nq, Hq, Hkv, D, bs, num_blocks, scale, part, workspace,
+                           workspace_bytes, lse_out, (hipStream_t)stream);
   const bool mfma = use_mfma(dtype, nq, G);
   const Plan pl =
       plan_launch(B, Hkv, (int64_t)max_blocks * bs, part, !mfma && stream_fits(dtype, D, B));

@@ -1,34 +1,43 @@
-// Instantiations of the shared-prefix kernel (bf16 caches).
+// Instantiations of the MFMA row-tile kernels (bf16 caches): the shared-prefix
+// kernel and the chunked-prefill kernel.
 #include "shared_prefix.h"
 
 namespace pkv {
 namespace decode {
 
-template <int D, int W, int RT>
-void launch_prefix(const DecodeArgs &a, const ShareArgs &s, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefix_mfma_kernel<D, W, RT>), grid, dim3(W * 64), 0, st, a, s);
+template <int D, int W, int RT, bool CHUNK>
+void launch_rows(const DecodeArgs &a, const ShareArgs &s, dim3 grid, hipStream_t st) {
+  if constexpr (CHUNK)
+    hipLaunchKernelGGL((chunk_mfma_kernel<D, W, RT>), grid, dim3(W * 64), 0, st, a, s);
+  else
+    hipLaunchKernelGGL((prefix_mfma_kernel<D, W, RT>), grid, dim3(W * 64), 0, st, a, s);
 }
 
-template <int D>
+template <int D, bool CHUNK>
 PrefixLauncher pick_for_dim(int W, int RT) {
   if (RT == 2) {
     // two row tiles hold twice the accumulators: built where they fit in registers
-    if constexpr (D <= 128) return W == 8 ? &launch_prefix<D, 8, 2> : nullptr;
+    if constexpr (D <= 128) return W == 8 ? &launch_rows<D, 8, 2, CHUNK> : nullptr;
     return nullptr;
   }
   if (RT != 1) return nullptr;
-  return W == 8 ? &launch_prefix<D, 8, 1>
-       : W == 4 ? &launch_prefix<D, 4, 1>
-       : W == 2 ? &launch_prefix<D, 2, 1>
-       : W == 1 ? &launch_prefix<D, 1, 1>
+  return W == 8 ? &launch_rows<D, 8, 1, CHUNK>
+       : W == 4 ? &launch_rows<D, 4, 1, CHUNK>
+       : W == 2 ? &launch_rows<D, 2, 1, CHUNK>
+       : W == 1 ? &launch_rows<D, 1, 1, CHUNK>
                 : nullptr;
 }
 
-PrefixLauncher pick_prefix(int D, int W, int RT) {
-  return D == 64    ? pick_for_dim<64>(W, RT)
-         : D == 128 ? pick_for_dim<128>(W, RT)
-         : D == 256 ? pick_for_dim<256>(W, RT)
+template <bool CHUNK>
+PrefixLauncher pick_rows_kernel(int D, int W, int RT) {
+  return D == 64    ? pick_for_dim<64, CHUNK>(W, RT)
+         : D == 128 ? pick_for_dim<128, CHUNK>(W, RT)
+         : D == 256 ? pick_for_dim<256, CHUNK>(W, RT)
                     : nullptr;
+}
+
+PrefixLauncher pick_prefix(int D, int W, int RT, bool chunk) {
+  return chunk ? pick_rows_kernel<true>(D, W, RT) : pick_rows_kernel<false>(D, W, RT);
 }
 
 }  // namespace decode

@@ -236,9 +236,14 @@ __device__ __forceinline__ void read_kv2<128>(u32x4_t (&k)[2][4], uint2 (&v)[2][
       : "memory");
 }
 
-template <int D, int W, int RT>
-__global__ void __launch_bounds__(W * 64)
-prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
+// Where the query rows of a workgroup come from.
+enum class RowSource {
+  kSharedGroups,  // stacked rows of a sharing group's members over their common prefix
+  kChunk,         // one sequence's query chunk (G x nq rows) over its own context, causal
+};
+
+template <int D, int W, int RT, RowSource SRC>
+__device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareArgs &s) {
   using Gp = PrefixGeo<D>;
   constexpr int NC = Gp::NC, NCB = Gp::NCB, kSlots = Gp::kSlots;
   constexpr int TT = D <= 128 ? 2 : 1;  // 16-token tiles per trip
@@ -249,41 +254,84 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;
   const int p = blockIdx.x, h = blockIdx.y;
-  const int grp = blockIdx.z / s.chunks, chunk = blockIdx.z % s.chunks;
-  if (grp >= s.n_groups) return;
-  // group bounds are clamped to the members array, so that inconsistent
-  // arrays cannot send reads out of it
-  const int ms = max(0, min(s.n_members, load_const(s.group_start + grp)));
-  const int me = max(ms, min(s.n_members, load_const(s.group_start + grp + 1)));
-  const int prefix_req = load_const(s.group_tokens + grp);
-  const int max_ctx = a.max_blocks * a.bs;
-  // a prefix that is not whole tiles or runs past the table poisons the group
-  const int prefix = max(0, min(prefix_req, max_ctx)) & ~(kTile - 1);
-  const int t_begin = p * s.prefix_part;
-  const int mpt = kVerifyRows / s.rpm;  // members per row tile
-  const int tile0 = chunk * W * RT;     // first row tile of this workgroup
-  // workgroup-uniform exits: no tokens in this partition, no rows in this chunk
-  if (t_begin >= prefix || ms + tile0 * mpt >= me) return;
-  const int t_end = min(prefix, t_begin + s.prefix_part);
-  const int n_tiles = (t_end - t_begin) / kTile;  // prefix is a multiple of 16
   const int nq = a.nq, G = a.Hq / a.Hkv;
+  const int max_ctx = a.max_blocks * a.bs;
+  const int tile0 = (blockIdx.z % s.chunks) * W * RT;  // first row tile of this workgroup
   const float nan = __builtin_nanf("");
 
-  // ---- set-up: two short chains of dependent loads, issued side by side ----
-  // (1) the leader's table row, whose entries address the shared tiles;
-  // (2) this lane's query rows: row ln of each of the wavefront's RT tiles.
-  const int leader_raw = load_const(s.members + ms);
-  const int rr = ln % s.rpm;  // row within the member
-  const int qi = rr / G;
-  int b_row[RT];              // sequence of row ln of tile r (-1: none)
+  // Per workgroup: the partition's tokens [t_begin, t_end) and the table row
+  // that addresses them. Per lane and row tile r: the sequence of row ln
+  // (-1: none), its flat row index (b, query, head) and the keys it sees.
+  int t_begin, t_end, bad;
+  const int32_t *trow;
+  int b_row[RT], lim_r[RT];
+  size_t qrow[RT];
+  if constexpr (SRC == RowSource::kSharedGroups) {
+    const int grp = blockIdx.z / s.chunks;
+    if (grp >= s.n_groups) return;
+    // group bounds are clamped to the members array, so that inconsistent
+    // arrays cannot send reads out of it
+    const int ms = max(0, min(s.n_members, load_const(s.group_start + grp)));
+    const int me = max(ms, min(s.n_members, load_const(s.group_start + grp + 1)));
+    const int prefix_req = load_const(s.group_tokens + grp);
+    // a prefix that is not whole tiles or runs past the table poisons the group
+    const int prefix = max(0, min(prefix_req, max_ctx)) & ~(kTile - 1);
+    t_begin = p * s.prefix_part;
+    const int mpt = kVerifyRows / s.rpm;  // members per row tile
+    // workgroup-uniform exits: no tokens in this partition, no rows in this chunk
+    if (t_begin >= prefix || ms + tile0 * mpt >= me) return;
+    t_end = min(prefix, t_begin + s.prefix_part);
+    // the leader's table row holds the shared blocks
+    const int leader_raw = load_const(s.members + ms);
+    const int leader = leader_raw >= 0 && leader_raw < a.B ? leader_raw : 0;
+    trow = a.tables + (size_t)leader * a.max_blocks;
+    bad = leader != leader_raw || prefix != prefix_req;
+    const int rr = ln % s.rpm;  // row within the member
+    const int qi = rr / G;
 #pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int mem_idx = ms + (tile0 + wave * RT + r) * mpt + ln / s.rpm;
-    const int b_raw = mem_idx < me && qi < nq ? s.members[mem_idx] : -1;
-    b_row[r] = b_raw >= 0 && b_raw < a.B ? b_raw : -1;
+    for (int r = 0; r < RT; ++r) {
+      const int mem_idx = ms + (tile0 + wave * RT + r) * mpt + ln / s.rpm;
+      const int b_raw = mem_idx < me && qi < nq ? s.members[mem_idx] : -1;
+      b_row[r] = b_raw >= 0 && b_raw < a.B ? b_raw : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int b = max(b_row[r], 0);
+      const int L = a.lens[b];
+      // a member whose length is out of range is left to the merge kernel (NaN)
+      const bool live = b_row[r] >= 0 && L >= nq && L <= max_ctx;
+      lim_r[r] = live ? L - nq + qi + 1 : 0;
+      qrow[r] = ((size_t)b * nq + min(qi, nq - 1)) * a.Hq + h * G + rr % G;
+    }
+  } else {
+    // rows r = query * G + head of one sequence; query i sees the first
+    // L - nq + i + 1 keys
+    const int b = blockIdx.z / s.chunks;
+    if (b >= a.B) return;
+    const int L = load_const(a.lens + b);
+    // a length out of range is left to the merge kernel (NaN)
+    if (L < nq || L > max_ctx) return;
+    const int rows = G * nq;
+    if (tile0 * kVerifyRows >= rows) return;
+    const int r_last = min(rows, (tile0 + W * RT) * kVerifyRows) - 1;
+    const int lim_max = L - nq + r_last / G + 1;  // keys seen by the workgroup's last row
+    t_begin = p * s.prefix_part;
+    if (t_begin >= lim_max) return;  // causal: no row here sees this partition
+    t_end = min(lim_max, t_begin + s.prefix_part);
+    trow = a.tables + (size_t)b * a.max_blocks;
+    bad = 0;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const int R = (tile0 + wave * RT + r) * kVerifyRows + ln;
+      const int qi = min(R, rows - 1) / G, g = min(R, rows - 1) % G;
+      b_row[r] = R < rows ? b : -1;
+      lim_r[r] = R < rows ? L - nq + qi + 1 : 0;
+      qrow[r] = ((size_t)b * nq + qi) * a.Hq + h * G + g;
+    }
   }
-  const int leader = leader_raw >= 0 && leader_raw < a.B ? leader_raw : 0;
-  const int32_t *trow = a.tables + (size_t)leader * a.max_blocks;
+  const int n_tiles = (t_end - t_begin + kTile - 1) / kTile;
+
+  // ---- set-up loads, issued side by side: the table window, the query rows --
   // lane i holds the block id of tile 64 w + i of the current window w
   // (clamped to the partition's last tile)
   auto table_window = [&](int w) {
@@ -291,20 +339,13 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   };
   int tblv = table_window(0);
   uint4 qb[RT][NC];
-  int lim_r[RT];  // keys visible to row ln of tile r
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int b = max(b_row[r], 0);
-    const int L = a.lens[b];
-    // a member whose length is out of range is left to the merge kernel (NaN)
-    const bool live = b_row[r] >= 0 && L >= nq && L <= max_ctx;
-    lim_r[r] = live ? L - nq + qi + 1 : 0;
-    const size_t row = ((size_t)b * nq + min(qi, nq - 1)) * a.Hq + h * G + rr % G;
-    const uint16_t *qp = (const uint16_t *)a.q + row * D + lg * (D / 4);
+    const uint16_t *qp = (const uint16_t *)a.q + qrow[r] * D + lg * (D / 4);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const uint4 v = *reinterpret_cast<const uint4 *>(qp + c * 8);
-      qb[r][c] = live ? v : make_uint4(0, 0, 0, 0);
+      qb[r][c] = lim_r[r] > 0 ? v : make_uint4(0, 0, 0, 0);
     }
   }
   // all of it is waited for here, once, before the first gather
@@ -319,9 +360,8 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   const char *kbase = (const char *)a.kc;
   const char *vbase = (const char *)a.vc;
   PKV_LDS char *ring = (PKV_LDS char *)&sm_ring[0];
-  // a prefix tile came from a bad table entry, or the group's description
-  // was unusable (workgroup-uniform): the group's partials become NaN
-  int bad = leader != leader_raw || prefix != prefix_req;
+  // bad (workgroup-uniform): a tile came from a bad table entry, or the
+  // group's description was unusable; the rows' partials become NaN
   // global byte offsets, inside a tile, of the 16 bytes lane l moves in
   // gather j: K in A-operand read order, V in swizzled token rows
   const int k_src = ln * (D * 2) + lg * (D / 2);  // + 16 j
@@ -430,6 +470,22 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
       else
         read_kv<D>(kr[0], vb[0], kt + lane * 16, va);
     }
+    if (t0 + TT * kTile > t_end) {
+      // the last trip: V of tokens past the partition (stale slots past a
+      // context's end, or the repeated last tile) is zeroed, since a zero
+      // weight times a non-finite value would still poison the product
+#pragma unroll
+      for (int u = 0; u < TT; ++u) {
+        const int tk = t0 + u * kTile + 4 * lg;
+        const unsigned xm = (tk < t_end ? 0xffffu : 0u) | (tk + 1 < t_end ? 0xffff0000u : 0u);
+        const unsigned ym = (tk + 2 < t_end ? 0xffffu : 0u) | (tk + 3 < t_end ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          vb[u][cb].x &= xm;
+          vb[u][cb].y &= ym;
+        }
+      }
+    }
 
     // S^T = K Q^T per tile and row tile: sv[u][r][e] = score of row ln with
     // token t0 + 16 u + 4 lg + e
@@ -516,8 +572,7 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
     l_row += exact_xor<16>(l_row);
     l_row += exact_xor<32>(l_row);
     if (b_row[r] < 0) continue;
-    const size_t row = ((size_t)b_row[r] * nq + qi) * a.Hq + h * G + rr % G;
-    const size_t pi = row * a.num_parts + p;
+    const size_t pi = qrow[r] * a.num_parts + p;
     float *acc = a.part_acc + pi * D + 4 * lg;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -530,12 +585,26 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   }
 }
 
+template <int D, int W, int RT>
+__global__ void __launch_bounds__(W * 64)
+prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
+  mfma_rows_body<D, W, RT, RowSource::kSharedGroups>(a, s);
+}
+
+// Chunked prefill: grid (KV partitions, Hkv, B x chunks); s carries only
+// chunks and prefix_part (the partition length).
+template <int D, int W, int RT>
+__global__ void __launch_bounds__(W * 64)
+chunk_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
+  mfma_rows_body<D, W, RT, RowSource::kChunk>(a, s);
+}
+
 using PrefixLauncher = void (*)(const DecodeArgs &, const ShareArgs &, dim3, hipStream_t);
 
-// Launcher of the prefix kernel for a head dim, W wavefronts per workgroup
-// (1, 2, 4 or 8) and RT row tiles per wavefront (1 or 2); nullptr if none.
-// Defined in shared_inst.hip.
-PrefixLauncher pick_prefix(int D, int W, int RT);
+// Launcher of the prefix kernel (chunk = false) or the chunk kernel for a
+// head dim, W wavefronts per workgroup (1, 2, 4 or 8) and RT row tiles per
+// wavefront (1 or 2); nullptr if none. Defined in shared_inst.hip.
+PrefixLauncher pick_prefix(int D, int W, int RT, bool chunk = false);
 
 }  // namespace decode
 }  // namespace pkv

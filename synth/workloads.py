@@ -91,6 +91,12 @@ WORKLOADS = {
         index=5, name="prefix_share_verify_k4", dtype="bf16", q_heads=32,
         kv_heads=8, head_dim=128, block_size=16, batch=64, num_blocks=4096,
         queries_per_seq=4, shared_prefix=2048, unique_suffix=512),
+    # chunked prefill: each sequence's last 512-token prompt chunk over its
+    # 7680 cached tokens (the notebook's 16 chunks of 512 for an 8K prompt)
+    "llama3_8b_chunk512_b4_8k": Workload(
+        index=6, name="llama3_8b_chunk512_b4_8k", dtype="bf16", q_heads=32,
+        kv_heads=8, head_dim=128, block_size=16, batch=4, num_blocks=2560,
+        queries_per_seq=512, context=8192),
 }
 
 

@@ -12,7 +12,8 @@ The oracles are checked against things outside themselves:
   values; identical keys => mean of the values; the one-hot construction of
   the course notebook's Demo 2 stays finite and picks the right value;
 * split-K: partitions merged by log-sum-exp equal the unpartitioned result;
-* speculative verify: nq causal queries equal nq separate decodes.
+* speculative verify: nq causal queries equal nq separate decodes;
+* chunked prefill: the chunks' rows equal the one-shot prefill's rows.
 """
 
 import math
@@ -100,6 +101,8 @@ CASES = [
     ((1, 5, 16, 40), 8, 2, 32, 4, "bf16", 1),
     ((7, 12, 30), 4, 4, 16, 8, "f32", 3),
     ((20, 45), 8, 1, 16, 16, "bf16", 4),
+    # chunked prefill: a whole first chunk (L == nq) and a chunk over a prefix
+    ((40, 57), 4, 2, 16, 16, "bf16", 40),
 ]
 
 
@@ -225,6 +228,23 @@ def test_verify_equals_sequential_decodes(kind):
         single["lens"] = case["lens"] - (K - 1 - i)
         o1, l1 = run_oracle(kind, single, dtype, 0.25, bs)
         assert np.array_equal(out[:, i], o1[:, 0]) and np.array_equal(lse[:, i], l1[:, 0])
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_chunks_equal_one_shot_prefill(kind):
+    """Chunked prefill ([KVNB s7] chunk decomposition): the rows of chunk c,
+    attended with the context cut at the chunk's end, are the one-shot
+    prefill's rows c*C .. c*C + C - 1, bit for bit."""
+    lens, Hq, Hkv, D, bs, dtype, C = (48, 48), 4, 2, 16, 16, "bf16", 16
+    case = build_case(41, lens, Hq, Hkv, D, bs, dtype, nq=48)
+    out, lse = run_oracle(kind, case, dtype, 0.25, bs)
+    for c in range(3):
+        chunk = dict(case)
+        chunk["q"] = case["q"][:, c * C:(c + 1) * C].contiguous()
+        chunk["lens"] = np.full_like(case["lens"], (c + 1) * C)
+        oc, lc = run_oracle(kind, chunk, dtype, 0.25, bs)
+        assert np.array_equal(out[:, c * C:(c + 1) * C], oc)
+        assert np.array_equal(lse[:, c * C:(c + 1) * C], lc)
 
 
 def test_bf16_widening_matches_torch():
