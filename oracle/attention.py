@@ -50,6 +50,8 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         bits = np.asarray(x).view(np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)
+    if dtype == "f64":  # values already exact (e.g. a dequantized code pool)
+        return np.asarray(x, dtype=np.float64)
     raise ValueError(f"unsupported dtype {dtype!r}")
 
 

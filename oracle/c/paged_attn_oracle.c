@@ -22,6 +22,10 @@
  *
  * sigma is the float32 scale widened to double; every stored element is
  * widened exactly to double (bf16: the float32 with those upper 16 bits).
+ * A pool of per-row integer codes (the course page's teaching quantizer,
+ * project demo Demo 2: symmetric codes, one scale per row) holds int8 codes
+ * [num_blocks, Hkv, bs, D] and float32 scales [num_blocks, Hkv, bs]; its
+ * element is code * scale, in double (pkv_oracle_attention_q8).
  *
  * Return codes: 0 ok; 1 bad argument; 2 a visible token maps to a table
  * entry outside [0, num_blocks); 3 a row sees no key (n <= 0).
@@ -34,15 +38,27 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_Q8 = 2 };
 
-static double load_elem(const void *base, int dtype, size_t idx) {
+/* Element idx of a pool; `scales` (one per row of D elements) only for
+ * ORACLE_Q8. */
+static double load_elem(const void *base, int dtype, size_t idx, const float *scales,
+                        int D) {
   if (dtype == ORACLE_F32) return (double)((const float *)base)[idx];
+  if (dtype == ORACLE_Q8)
+    return (double)((const int8_t *)base)[idx] * (double)scales[idx / (size_t)D];
   uint32_t bits = (uint32_t)((const uint16_t *)base)[idx] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
   return (double)f;
 }
+
+static int attention_walk(const void *q, int q_dtype, const void *k_pool,
+                          const void *v_pool, int kv_dtype, const float *k_scales,
+                          const float *v_scales, const int32_t *tables, int max_blocks,
+                          const int32_t *lens, int B, int nq, int Hq, int Hkv, int D, int bs,
+                          int num_blocks, float scale, const int64_t *rows, int64_t n_rows,
+                          double *out, double *lse, int threads);
 
 int pkv_oracle_attention(const void *q, int q_dtype, const void *k_pool,
                          const void *v_pool, int kv_dtype,
@@ -51,13 +67,35 @@ int pkv_oracle_attention(const void *q, int q_dtype, const void *k_pool,
                          int D, int bs, int num_blocks, float scale,
                          const int64_t *rows, int64_t n_rows, double *out,
                          double *lse, int threads) {
+  if (kv_dtype != ORACLE_F32 && kv_dtype != ORACLE_BF16) return 1;
+  return attention_walk(q, q_dtype, k_pool, v_pool, kv_dtype, NULL, NULL, tables,
+                        max_blocks, lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, rows,
+                        n_rows, out, lse, threads);
+}
+
+int pkv_oracle_attention_q8(const void *q, int q_dtype, const int8_t *k_codes,
+                            const int8_t *v_codes, const float *k_scales,
+                            const float *v_scales, const int32_t *tables, int max_blocks,
+                            const int32_t *lens, int B, int nq, int Hq, int Hkv, int D,
+                            int bs, int num_blocks, float scale, const int64_t *rows,
+                            int64_t n_rows, double *out, double *lse, int threads) {
+  if (!k_scales || !v_scales) return 1;
+  return attention_walk(q, q_dtype, k_codes, v_codes, ORACLE_Q8, k_scales, v_scales, tables,
+                        max_blocks, lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, rows,
+                        n_rows, out, lse, threads);
+}
+
+static int attention_walk(const void *q, int q_dtype, const void *k_pool,
+                          const void *v_pool, int kv_dtype, const float *k_scales,
+                          const float *v_scales, const int32_t *tables, int max_blocks,
+                          const int32_t *lens, int B, int nq, int Hq, int Hkv, int D, int bs,
+                          int num_blocks, float scale, const int64_t *rows, int64_t n_rows,
+                          double *out, double *lse, int threads) {
   if (!q || !k_pool || !v_pool || !tables || !lens || !out) return 1;
   if (B <= 0 || nq <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 ||
       num_blocks <= 0 || max_blocks <= 0 || Hq % Hkv != 0)
     return 1;
-  if ((q_dtype != ORACLE_F32 && q_dtype != ORACLE_BF16) ||
-      (kv_dtype != ORACLE_F32 && kv_dtype != ORACLE_BF16))
-    return 1;
+  if (q_dtype != ORACLE_F32 && q_dtype != ORACLE_BF16) return 1;
   const int group = Hq / Hkv;
   const double sigma = (double)scale;
   const int64_t total_rows = (int64_t)B * nq * Hq;
@@ -111,8 +149,8 @@ int pkv_oracle_attention(const void *q, int q_dtype, const void *k_pool,
             (((size_t)blk * Hkv + g) * bs + (size_t)(t % bs)) * D;
         double dot = 0.0;
         for (int d = 0; d < D; ++d)
-          dot += load_elem(q, q_dtype, qbase + d) *
-                 load_elem(k_pool, kv_dtype, kbase + d);
+          dot += load_elem(q, q_dtype, qbase + d, NULL, D) *
+                 load_elem(k_pool, kv_dtype, kbase + d, k_scales, D);
         scores[t] = sigma * dot;
         if (scores[t] > m) m = scores[t];
       }
@@ -131,7 +169,7 @@ int pkv_oracle_attention(const void *q, int q_dtype, const void *k_pool,
         const double p = exp(scores[t] - m);
         l += p;
         for (int d = 0; d < D; ++d)
-          acc[d] += p * load_elem(v_pool, kv_dtype, vbase + d);
+          acc[d] += p * load_elem(v_pool, kv_dtype, vbase + d, v_scales, D);
       }
       for (int d = 0; d < D; ++d) out[(size_t)r * D + d] = acc[d] / l;
       if (lse) lse[r] = m + log(l);

@@ -44,6 +44,14 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int]
+        lib.pkv_oracle_attention_q8.restype = ctypes.c_int
+        lib.pkv_oracle_attention_q8.argtypes = [
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int]
         lib.pkv_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -90,6 +98,45 @@ def attention(q, q_dtype: str, k_pool, v_pool, kv_dtype: str, tables, lens,
     lse = np.empty(n, dtype=np.float64)
     rc = lib.pkv_oracle_attention(
         _ptr(qa), _DT[q_dtype], _ptr(ka), _ptr(va), _DT[kv_dtype], _ptr(tb),
+        tb.shape[1], _ptr(ln), B, nq, Hq, Hkv, D, bs, NB, float(scale),
+        None if rw is None else _ptr(rw), n, _ptr(out), _ptr(lse), int(threads))
+    if rc != 0:
+        raise ValueError(f"C oracle rejected its input (code {rc})")
+    if rows is None:
+        return out.reshape(B, nq, Hq, D), lse.reshape(B, nq, Hq)
+    return out, lse
+
+
+def attention_q8(q, q_dtype: str, k_codes, v_codes, k_scales, v_scales, tables, lens,
+                 scale: float, block_size: int, rows=None, threads: int = 0):
+    """The C walk over a pool of per-row int8 codes: element = code * scale.
+
+    k_codes, v_codes: int8 [NB, Hkv, bs, D]; k_scales, v_scales: float32
+    [NB, Hkv, bs]. Other arguments and the result as in ``attention``."""
+    lib = _load()
+    qa = (np.ascontiguousarray(q, dtype=np.float32) if q_dtype == "f32"
+          else np.ascontiguousarray(np.asarray(q).view(np.uint16)))
+    kc = np.ascontiguousarray(k_codes, dtype=np.int8)
+    vc = np.ascontiguousarray(v_codes, dtype=np.int8)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    B, nq, Hq, D = qa.shape
+    NB, Hkv, bs, Dk = kc.shape
+    if Dk != D or bs != block_size or ks.shape != (NB, Hkv, bs) or vs.shape != ks.shape \
+            or vc.shape != kc.shape:
+        raise ValueError("pool shape does not match")
+    tb = np.ascontiguousarray(tables, dtype=np.int32)
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    if rows is None:
+        n = B * nq * Hq
+        rw = None
+    else:
+        rw = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rw.shape[0]
+    out = np.empty((n, D), dtype=np.float64)
+    lse = np.empty(n, dtype=np.float64)
+    rc = lib.pkv_oracle_attention_q8(
+        _ptr(qa), _DT[q_dtype], _ptr(kc), _ptr(vc), _ptr(ks), _ptr(vs), _ptr(tb),
         tb.shape[1], _ptr(ln), B, nq, Hq, Hkv, D, bs, NB, float(scale),
         None if rw is None else _ptr(rw), n, _ptr(out), _ptr(lse), int(threads))
     if rc != 0:
