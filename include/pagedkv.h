@@ -62,7 +62,10 @@ enum {
 };
 
 /* ---- element types of caches and queries ------------------------------ */
-enum { PKV_F32 = 0, PKV_BF16 = 1 };
+/* PKV_I8: int8 codes of a cache holding per-row integer codes (see
+ * paged_cache_write_q8); accepted by paged_kv_copy_blocks (codes) and as the
+ * byte type of such caches, never as a query type. */
+enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_I8 = 2 };
 
 /* Thread-local text describing the last error of this thread's calls. */
 const char *paged_kv_last_error(void);
@@ -266,6 +269,45 @@ int paged_attention_decode(float *out, const void *q, const void *k_cache,
                            float scale, int dtype, int32_t partition_tokens,
                            void *workspace, size_t workspace_bytes,
                            float *lse_out, void *stream);
+
+/* ---- caches of 8-bit per-row codes --------------------------------------
+ * The teaching quantizer of [KVNB demo] Demo 2 (symmetric integer codes,
+ * one scale per row), 8 bits, applied to every (token, KV head) row of K
+ * and of V as it is written: scale = max |x| / 127 (1 for a row of zeros),
+ * code = clip(round-half-even(x / scale), -127, 127), computed in float64;
+ * the scale is stored as float32. Such a cache is four device arrays:
+ *   k_codes, v_codes:   int8    [num_blocks, Hkv, block_size, D]
+ *   k_scales, v_scales: float32 [num_blocks, Hkv, block_size]
+ * (D + 4 bytes per token and head instead of 2 D for bf16). */
+
+/* Quantize and scatter T new rows: k_new, v_new device `dtype` (f32 or
+ * bf16) [T, Hkv, D]; slot_mapping as in paged_cache_write (-1 or out of
+ * range: skipped). D in {64, 128, 256}. Asynchronous on `stream`.
+ * Copy-on-write for such a cache: paged_kv_copy_blocks on the codes
+ * (dtype PKV_I8) and on the scales (dtype PKV_F32, D = 1). */
+int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
+                         int8_t *v_codes, float *k_scales, float *v_scales,
+                         const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
+                         int32_t Hkv, int32_t D, int32_t block_size, int dtype,
+                         void *stream);
+
+/* paged_attention_decode over a cache of 8-bit codes: the same attention
+ * with each K and V element taken as code * its row's scale ([KVNB demo]
+ * Demo 2 reconstruction), dequantized inside the kernel. q is bf16
+ * [B, nq, Hq, D]; out, lse, tables, lengths, partition_tokens and workspace
+ * as there (paged_attention_workspace_size gives the size; -1 is taken as 0
+ * here). Rows per KV head: G * nq rounded up to a power of two <= 16 (VALU
+ * kernels, at most 4 rows per wavefront). Scale arrays 16-byte aligned.
+ * Host-checked as paged_attention_decode -> EINVAL. */
+int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
+                              const int8_t *v_codes, const float *k_scales,
+                              const float *v_scales, const int32_t *block_tables,
+                              int32_t max_blocks, const int32_t *context_lens,
+                              int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t block_size, int32_t num_blocks,
+                              float scale, int32_t partition_tokens,
+                              void *workspace, size_t workspace_bytes,
+                              float *lse_out, void *stream);
 
 /* ----------------------------------------------------------------------
  * Shared prefixes ([vLLM]: blocks shared within and across requests;

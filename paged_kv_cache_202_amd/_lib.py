@@ -11,7 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PKV_OK, PKV_EINVAL, PKV_ENOENT, PKV_EEXIST, PKV_ENOMEM, PKV_ECORRUPT, PKV_EHIP = range(7)
-PKV_F32, PKV_BF16 = 0, 1
+PKV_F32, PKV_BF16, PKV_I8 = 0, 1, 2
 
 c_i32, c_i64, c_int, c_void_p, c_size_t, c_float = (
     ctypes.c_int32, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
@@ -62,6 +62,13 @@ PROTOTYPES = {
                                        c_i32, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                        c_i32, c_i32, c_float, c_int, c_i32, c_void_p,
                                        c_size_t, c_void_p, c_void_p]),
+    "paged_cache_write_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                     c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                     c_int, c_void_p]),
+    "paged_attention_decode_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_i32, c_void_p, c_i32, c_i32,
+                                          c_i32, c_i32, c_i32, c_i32, c_i32, c_float, c_i32,
+                                          c_void_p, c_size_t, c_void_p, c_void_p]),
     "paged_kv_prefix_groups": (c_int, [P_i32, c_i32, P_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                        P_i32, P_i32, P_i32, P_i32, P_i32, P_i32, P_i32]),
     "paged_attention_shared_workspace_size": (c_int, [c_i32, c_i32, c_i32, c_i32, c_i32,

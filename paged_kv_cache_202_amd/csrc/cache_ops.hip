@@ -60,7 +60,60 @@ copy_blocks_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
   }
 }
 
-int elem_bytes(int dtype) { return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : 0; }
+// Per-row integer codes of the course page's teaching quantizer (project
+// demo, Demo 2: symmetric codes, one scale per row), 8 bits: for each new
+// (token, KV head) row x of D values, scale = max |x| / 127 (1 for a row of
+// zeros), code = clip(round-half-even(x / scale), -127, 127), in float64 as
+// the page computes; the scale is stored as float32. One wavefront per row:
+// each lane holds D / 64 consecutive elements.
+template <int D, typename T>
+__global__ void __launch_bounds__(256)
+cache_write_q8_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
+                      int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes,
+                      float *__restrict__ k_scales, float *__restrict__ v_scales,
+                      const int32_t *__restrict__ slots, int64_t rows, int32_t Hkv, int32_t bs,
+                      int64_t num_slots) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * Hkv + h
+  if (row >= rows) return;
+  const int64_t t = row / Hkv;
+  const int32_t h = (int32_t)(row - t * Hkv);
+  const int64_t s = slots[t];
+  if (s < 0 || s >= num_slots) return;
+  const int64_t blk = s / bs, off = s - blk * bs;
+  const int64_t dst = (blk * Hkv + h) * bs + off;  // row of the code and scale pools
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const T *src = (which ? v_new : k_new) + row * D + lane * EPL;
+    double x[EPL];
+    double mx = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      if constexpr (sizeof(T) == 2) {  // bf16 bits: the float32 with these upper bits
+        x[e] = (double)__uint_as_float((uint32_t)((const uint16_t *)src)[e] << 16);
+      } else {
+        x[e] = (double)src[e];
+      }
+      mx = fmax(mx, fabs(x[e]));
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
+    double scale = mx / 127.0;
+    if (scale == 0.0) scale = 1.0;
+    int8_t *codes = (which ? v_codes : k_codes) + dst * D + lane * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const double c = fmin(fmax(rint(x[e] / scale), -127.0), 127.0);
+      codes[e] = (int8_t)(int)c;
+    }
+    if (lane == 0) (which ? v_scales : k_scales)[dst] = (float)scale;
+  }
+}
+
+int elem_bytes(int dtype) {
+  return dtype == PKV_F32 ? 4 : dtype == PKV_BF16 ? 2 : dtype == PKV_I8 ? 1 : 0;
+}
 
 }  // namespace
 
@@ -115,5 +168,40 @@ extern "C" int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_
                      (uint4 *)k_cache, (uint4 *)v_cache, pairs, vpb, num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, "block copy launch: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+extern "C" int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
+                                    int8_t *v_codes, float *k_scales, float *v_scales,
+                                    const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
+                                    int32_t Hkv, int32_t D, int32_t block_size, int dtype,
+                                    void *stream) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "new rows must be f32 or bf16 (dtype %d)", dtype);
+  if (T < 0 || num_blocks <= 0 || Hkv <= 0 || block_size <= 0)
+    return fail(PKV_EINVAL, "sizes must be positive (T >= 0)");
+  if (D != 64 && D != 128 && D != 256) return fail(PKV_EINVAL, "head dim %d unsupported", D);
+  if (T == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_codes || !v_codes || !k_scales || !v_scales || !slot_mapping)
+    return fail(PKV_EINVAL, "NULL pointer");
+  const int64_t rows = (int64_t)T * Hkv;
+  const int64_t num_slots = (int64_t)num_blocks * block_size;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+#define PKV_Q8(d)                                                                          \
+  if (D == d) {                                                                            \
+    if (dtype == PKV_BF16)                                                                 \
+      hipLaunchKernelGGL((cache_write_q8_kernel<d, uint16_t>), grid, block, 0, s,           \
+                         (const uint16_t *)k_new, (const uint16_t *)v_new, k_codes, v_codes, \
+                         k_scales, v_scales, slot_mapping, rows, Hkv, block_size, num_slots); \
+    else                                                                                   \
+      hipLaunchKernelGGL((cache_write_q8_kernel<d, float>), grid, block, 0, s,              \
+                         (const float *)k_new, (const float *)v_new, k_codes, v_codes,      \
+                         k_scales, v_scales, slot_mapping, rows, Hkv, block_size, num_slots); \
+  }
+  PKV_Q8(64) PKV_Q8(128) PKV_Q8(256)
+#undef PKV_Q8
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PKV_EHIP, "cache write q8 launch: %s", hipGetErrorString(e));
   return PKV_OK;
 }

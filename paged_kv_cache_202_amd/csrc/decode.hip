@@ -255,6 +255,10 @@ Launcher pick_launcher(int dtype, int D, int G, int RP, int W) {
     if (D == 64) return pick_rows<PKV_BF16, 64>(G, RP, W);
     if (D == 128) return pick_rows<PKV_BF16, 128>(G, RP, W);
     if (D == 256) return pick_rows<PKV_BF16, 256>(G, RP, W);
+  } else if (dtype == PKV_I8) {
+    if (D == 64) return pick_rows<PKV_I8, 64>(G, RP, W);
+    if (D == 128) return pick_rows<PKV_I8, 128>(G, RP, W);
+    if (D == 256) return pick_rows<PKV_I8, 256>(G, RP, W);
   }
   return nullptr;
 }
@@ -440,15 +444,14 @@ static int chunk_attention(float *out, const void *q, const void *k_cache, const
   return PKV_OK;
 }
 
-extern "C" int paged_attention_decode(float *out, const void *q, const void *k_cache,
-                                      const void *v_cache, const int32_t *block_tables,
-                                      int32_t max_blocks, const int32_t *context_lens, int32_t B,
-                                      int32_t nq, int32_t Hq, int32_t Hkv, int32_t D,
-                                      int32_t bs, int32_t num_blocks, float scale, int dtype,
-                                      int32_t part, void *workspace, size_t workspace_bytes,
-                                      float *lse_out, void *stream) {
-  const int es = elem_bytes(dtype);
-  if (!es) return fail(PKV_EINVAL, "unsupported dtype %d", dtype);
+// The attention call for fp32 and bf16 caches (ks = vs = nullptr) and for
+// caches of int8 codes (dtype PKV_I8, bf16 queries, per-row scales ks, vs).
+static int decode_impl(float *out, const void *q, const void *k_cache, const void *v_cache,
+                       const float *ks, const float *vs, const int32_t *block_tables,
+                       int32_t max_blocks, const int32_t *context_lens, int32_t B, int32_t nq,
+                       int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t num_blocks,
+                       float scale, int dtype, int32_t part, void *workspace,
+                       size_t workspace_bytes, float *lse_out, void *stream) {
   if (int rc = check_sizes(B, nq, Hq, Hkv, D, max_blocks, bs, part)) return rc;
   if (num_blocks <= 0) return fail(PKV_EINVAL, "num_blocks must be positive");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -469,6 +472,10 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   int32_t RP, S;
   row_split(G, nq, &RP, &S);
   if (mfma) S = 1;
+  if (dtype == PKV_I8 && RP > 4) {  // int8 codes: at most 4 rows per wavefront
+    S *= RP / 4;
+    RP = 4;
+  }
   const int32_t RW = RP;
   Launcher launch = mfma ? pick_verify(D) : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
@@ -493,6 +500,8 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   a.num_parts = NP;
   a.slices = S;
   a.scale_log2 = scale * kLog2e;
+  a.ks = ks;
+  a.vs = vs;
   StreamArgs sa{};
   size_t need = 0;
   if (streamed)
@@ -534,6 +543,37 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
     if (e != hipSuccess) return fail(PKV_EHIP, "reduce launch: %s", hipGetErrorString(e));
   }
   return PKV_OK;
+}
+
+extern "C" int paged_attention_decode(float *out, const void *q, const void *k_cache,
+                                      const void *v_cache, const int32_t *block_tables,
+                                      int32_t max_blocks, const int32_t *context_lens, int32_t B,
+                                      int32_t nq, int32_t Hq, int32_t Hkv, int32_t D,
+                                      int32_t bs, int32_t num_blocks, float scale, int dtype,
+                                      int32_t part, void *workspace, size_t workspace_bytes,
+                                      float *lse_out, void *stream) {
+  if (!elem_bytes(dtype))
+    return fail(PKV_EINVAL, "unsupported dtype %d (int8 codes: paged_attention_decode_q8)",
+                dtype);
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks,
+                     context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype, part,
+                     workspace, workspace_bytes, lse_out, stream);
+}
+
+extern "C" int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
+                                         const int8_t *v_codes, const float *k_scales,
+                                         const float *v_scales, const int32_t *block_tables,
+                                         int32_t max_blocks, const int32_t *context_lens,
+                                         int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                                         int32_t D, int32_t bs, int32_t num_blocks, float scale,
+                                         int32_t part, void *workspace, size_t workspace_bytes,
+                                         float *lse_out, void *stream) {
+  if (!k_scales || !v_scales) return fail(PKV_EINVAL, "NULL pointer");
+  if ((uintptr_t)k_scales % 16 || (uintptr_t)v_scales % 16)
+    return fail(PKV_EINVAL, "scale arrays must be 16-byte aligned");
+  return decode_impl(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, max_blocks,
+                     context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, PKV_I8, part,
+                     workspace, workspace_bytes, lse_out, stream);
 }
 
 // ---------------------------------------------------------------------------

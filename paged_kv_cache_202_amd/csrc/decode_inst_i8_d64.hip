@@ -1,0 +1,27 @@
+// Partition-kernel instantiations for caches of int8 codes (per-row float32
+// scales) with head dim 64; bf16 queries. No stream kernel for this type.
+#include "decode_kernel.h"
+
+namespace pkv {
+namespace decode {
+
+template <>
+Launcher pick_rows<PKV_I8, 64>(int G, int RP, int W) {
+  constexpr int DT = PKV_I8, D = 64;
+#define PKV_CASE(g, rp)                                                  \
+  if (G == g && RP == rp)                                                \
+    return W == 8   ? &launch_decode<DT, D, g, rp, 8>                   \
+           : W == 4 ? &launch_decode<DT, D, g, rp, 4>                   \
+           : W == 1 ? &launch_decode<DT, D, g, rp, 1>                   \
+                    : nullptr;
+  // at most 4 rows per wavefront: 16 fp32 accumulators per row and lane
+  PKV_CASE(1, 1) PKV_CASE(1, 2) PKV_CASE(1, 4)
+  PKV_CASE(2, 2) PKV_CASE(2, 4)
+  PKV_CASE(4, 4)
+  PKV_CASE(8, 4)
+#undef PKV_CASE
+  return nullptr;
+}
+
+}  // namespace decode
+}  // namespace pkv

@@ -69,6 +69,31 @@ __device__ __forceinline__ float dot2_bf16_first(uint32_t a, uint32_t b) {
   asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// q.k of two fp16 pairs into an fp32 sum (v_dot2_f32_f16: exact products).
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                c, false);
+}
+
+// Two int8 codes (bytes 0 and 1, or 2 and 3, of w) as the fp16 pair
+// (1152 + c0, 1152 + c1): with u = c + 128 in 0..255, the fp16 whose bits
+// are 0x6400 | u is exactly 1024 + u, so the conversion is byte moves only.
+__device__ __forceinline__ uint32_t codes_f16_lo(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  return (u & 0xffu) | ((u & 0xff00u) << 8) | 0x64006400u;
+}
+__device__ __forceinline__ uint32_t codes_f16_hi(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  return ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u) | 0x64006400u;
+}
+// Code k (0..3) of w as a float: the signed byte, widened.
+template <int K>
+__device__ __forceinline__ float code_f32(uint32_t w) {
+  return (float)(int8_t)(uint8_t)(w >> (8 * K));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -119,14 +144,16 @@ __device__ __forceinline__ float xor_partner(float x) {
   }
 }
 
-// The lane exactly lane ^ M (M >= 8): unlike xor_partner, lower lane bits are
+// The lane exactly lane ^ M (M >= 4): unlike xor_partner, lower lane bits are
 // preserved, as needed when lanes below M hold different data.
 template <int M>
 __device__ __forceinline__ float exact_xor(float x) {
-  if constexpr (M == 8) {
+  if constexpr (M == 4) {  // (final sums only) a bit-mode swizzle: xor mask 4
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101f));
+  } else if constexpr (M == 8) {
     return dpp_mov<0x128>(x);  // row_ror:8 within a 16-lane row is lane ^ 8
   } else {
-    static_assert(M == 16 || M == 32, "exact_xor covers lane bits 3..5");
+    static_assert(M == 16 || M == 32, "exact_xor covers lane bits 2..5");
     return xor_partner<M>(x);  // the permlane swaps are exact
   }
 }
@@ -169,7 +196,8 @@ __device__ __forceinline__ float group_bcast(float x, int lane) {
 // Geometry of one (dtype, head dim) pair as seen by a wavefront.
 template <int DT, int D>
 struct Geo {
-  static constexpr int ES = DT == PKV_F32 ? 4 : 2;  // bytes per element
+  // bytes per element: fp32, bf16, or int8 codes
+  static constexpr int ES = DT == PKV_F32 ? 4 : DT == PKV_I8 ? 1 : 2;
   static constexpr int TB = D * ES;                  // bytes per token row
   static constexpr int LPT = TB / 16;                // lanes sharing one token
   static constexpr int TPL = 64 / LPT;               // tokens per 1 KiB load
@@ -203,6 +231,10 @@ struct DecodeArgs {
   const int32_t *starts;
   int32_t part_base;
   int32_t prefix_part;
+  // Caches of int8 codes only (else nullptr): the float32 scale of each
+  // (block, KV head, slot) row of K and of V, [num_blocks, Hkv, bs].
+  const float *ks;
+  const float *vs;
 };
 
 // One step of the reduce-scatter over lane bit M with `cnt` live values:
@@ -311,6 +343,11 @@ template <int AUX>
 __device__ __forceinline__ void gather_lds16(const char *src, PKV_LDS char *dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, AUX);
 }
+// The same with 4 bytes per lane (256 bytes).
+template <int AUX>
+__device__ __forceinline__ void gather_lds4(const char *src, PKV_LDS char *dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, AUX);
+}
 
 // A value a loop reads, waited for here and kept in a register from here
 // on: if its load were first used inside the loop, the compiler's wait for
@@ -341,14 +378,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 // barrier; the compiler cannot track which LDS bytes a pending DMA writes,
 // so the read-back and its waits are written out here.
 // ---------------------------------------------------------------------------
-template <int NL>
+template <int NL, bool SC = false>
 struct TileRing {
-  static constexpr int kTileBytes = 2 * NL * 1024;
-  // at least one tile, else as many as fit 16 KiB: two tiles of a
+  static constexpr int kCodeBytes = 2 * NL * 1024;
+  // with per-row scales (int8 codes), after the K and V rows: the tile's 16
+  // K scales, its 16 V scales, and 128 bytes the other lanes of their
+  // 4-byte gather fill with copies (every lane takes part: a gather under a
+  // lane mask could be split by the compiler into several instructions,
+  // which would break the counting of loads in flight)
+  static constexpr int kTileBytes = kCodeBytes + (SC ? 256 : 0);
+  // at least one tile, else as many as fit 16 KiB of rows: two tiles of a
   // D = 128 bf16 head, four of a D = 64 one
-  static constexpr int kSlots = kTileBytes >= 16384 ? 1 : 16384 / kTileBytes;
+  static constexpr int kSlots = kCodeBytes >= 16384 ? 1 : 16384 / kCodeBytes;
   static constexpr int kBytes = kSlots * kTileBytes;  // per wavefront
-  static constexpr int kLoads = 2 * NL;               // DMA instructions per tile
+  static constexpr int kLoads = 2 * NL + (SC ? 1 : 0);  // DMA instructions per tile
   static_assert((kSlots & (kSlots - 1)) == 0, "slot count must be a power of two");
 
   PKV_LDS char *base;  // this wavefront's ring (wavefront-uniform)
@@ -360,13 +403,44 @@ struct TileRing {
   }
 
   // Gather one tile into `slot`: kp / vp already include this lane's 16 B.
-  __device__ __forceinline__ void stage(int slot, const char *kp, const char *vp) {
+  // With scales, sp is this lane's 4 bytes of them: lane l takes K scale
+  // l % 16 (l % 32 < 16) or V scale l % 16 (otherwise); issued first, so
+  // that waiting for the K rows also covers both scales.
+  __device__ __forceinline__ void stage(int slot, const char *kp, const char *vp,
+                                        const char *sp = nullptr) {
     PKV_LDS char *dst = base + slot * kTileBytes;
+    if constexpr (SC) gather_lds4<kKvNonTemporal>(sp, dst + kCodeBytes);
 #pragma unroll
     for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(kp + i * 1024, dst + i * 1024);
 #pragma unroll
     for (int i = 0; i < NL; ++i)
       gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
+  }
+
+  // After fetch<HALF>: the scales of tokens tok[c] of the tile in `slot`
+  // (K scales for HALF = 0, V scales for HALF = 1).
+  template <int HALF, int C>
+  __device__ __forceinline__ void scales(int slot, const int (&tok)[C], float (&out)[C]) const {
+    const PKV_LDS char *p = base + slot * kTileBytes + kCodeBytes + HALF * 64;
+    if constexpr (C == 1) {
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                   : "=v"(out[0])
+                   : "v"(p + tok[0] * 4)
+                   : "memory");
+    } else if constexpr (C == 2) {
+      asm volatile(
+          "ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(out[0]), "=&v"(out[1])
+          : "v"(p + tok[0] * 4), "v"(p + tok[1] * 4)
+          : "memory");
+    } else {
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(out[c])
+                     : "v"(p + tok[c] * 4)
+                     : "memory");
+    }
   }
 
   // Read back the K half (HALF = 0) or the V half (HALF = 1) of the tile in
@@ -384,7 +458,9 @@ struct TileRing {
     });
     const PKV_LDS char *p = mine + slot * kTileBytes + HALF * NL * 1024;
     u32x4_t t[NL];
-    if constexpr (NL <= 8) {
+    if constexpr (NL == 1) {
+      asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(t[0]) : "v"(p) : "memory");
+    } else if constexpr (NL <= 8) {
       lds_rows<NL>(t, p);
     } else {
 #pragma unroll
@@ -411,6 +487,11 @@ struct DecodeWave {
   int lane, grp, jl, d0;
   uint32_t qw[RP][4];  // bf16 query slices, two per word
   float qf[RP][4];     // fp32 query slices
+  // int8 codes: the 16-dim query slice as fp16 pairs, scaled by 2^-e per
+  // row so that it fits fp16; 1152 times the slice's sum (the offset of the
+  // codes' fp16 form); 2^e
+  uint32_t qh[RP][8];
+  float qcorr[RP], qpow[RP];
   int own_row[C], own_tok[C], own_lim[C];
   float acc[RP][EPL];
   float m_run[RP];
@@ -448,6 +529,33 @@ struct DecodeWave {
         uint4 w = make_uint4(0, 0, 0, 0);
         if (qi < nq) w = *reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
         qw[r][0] = w.x; qw[r][1] = w.y; qw[r][2] = w.z; qw[r][3] = w.w;
+      } else if constexpr (DT == PKV_I8) {
+        // bf16 queries over int8 codes: 16 dims per lane
+        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
+        if (qi < nq) {
+          const uint4 *src = reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
+          w0 = src[0];
+          w1 = src[1];
+        }
+        const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float mx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(ww[j])), fabsf(bf16_hi(ww[j]))));
+#pragma unroll
+        for (int m = 1; m < LPT; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+        int ex = 0;
+        frexpf(mx, &ex);  // 2^(ex-1) <= mx < 2^ex
+        const int e = mx > 0.f ? ex - 8 : 0;  // the scaled row's largest entry in [2^7, 2^8)
+        float corr = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const _Float16 lo = (_Float16)ldexpf(bf16_lo(ww[j]), -e);
+          const _Float16 hi = (_Float16)ldexpf(bf16_hi(ww[j]), -e);
+          corr += (float)lo + (float)hi;
+          qh[r][j] = __builtin_bit_cast(uint32_t, f16x2_t{lo, hi});
+        }
+        qcorr[r] = 1152.f * corr;
+        qpow[r] = ldexpf(1.f, e);
       } else {
         float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
         if (qi < nq) w = *reinterpret_cast<const float4 *>((const float *)a.q + row * D + d0);
@@ -485,9 +593,28 @@ struct DecodeWave {
   // Consume one 16-token tile starting at logical token t0: its K rows are
   // in kr, and get_v(vr) supplies its V rows once the weights are known (so
   // the V half of a gather may still be landing during the q.k work).
-  template <class GetV>
+  // With int8 codes, get_ks / get_vs supply the K / V scales of this lane's
+  // owned tokens (after the K / V rows have been fetched).
+  struct NoScales {
+    __device__ void operator()(float (&)[C]) const {}
+  };
+  template <class GetV, class GetKS = NoScales, class GetVS = NoScales>
   __device__ __forceinline__ void process(const uint4 (&kr)[NL], GetV &&get_v, int t0,
-                                          float scale_log2) {
+                                          float scale_log2, GetKS get_ks = {},
+                                          GetVS get_vs = {}) {
+    // int8 codes as fp16 pairs (1152 + code), shared by all rows
+    uint32_t km[NL][8];
+    if constexpr (DT == PKV_I8) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          km[i][2 * j] = codes_f16_lo(kw[j]);
+          km[i][2 * j + 1] = codes_f16_hi(kw[j]);
+        }
+      }
+    }
     // partial q.k over this lane's EPL dims: x[r * NL + i]
     float x[V];
 #pragma unroll
@@ -495,7 +622,12 @@ struct DecodeWave {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         float s = 0.f;
-        if constexpr (DT == PKV_BF16) {
+        if constexpr (DT == PKV_I8) {
+          // sum_d q_d (1152 + c_d) - 1152 sum_d q_d = sum_d q_d c_d
+#pragma unroll
+          for (int j = 0; j < 8; ++j) s = dot2_f16(qh[r][j], km[i][j], s);
+          s -= qcorr[r];
+        } else if constexpr (DT == PKV_BF16) {
           s = dot2_bf16_first(qw[r][0], kr[i].x);
           s = dot2_bf16(qw[r][1], kr[i].y, s);
           s = dot2_bf16(qw[r][2], kr[i].z, s);
@@ -511,12 +643,27 @@ struct DecodeWave {
     }
     reduce_scatter<LPT, V>(x, jl);
 
+    float fac[C];  // per owned score: scale_log2, times the K scale and 2^e
+#pragma unroll
+    for (int c = 0; c < C; ++c) fac[c] = scale_log2;
+    if constexpr (DT == PKV_I8) {
+      float ksc[C];
+      get_ks(ksc);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        float qp = 1.f;
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+          if (own_row[c] == r) qp = qpow[r];
+        fac[c] = ksc[c] * qp * scale_log2;
+      }
+    }
     float sc[C];
     bool need = false;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool vis = t0 + own_tok[c] < own_lim[c];
-      sc[c] = vis ? x[c] * scale_log2 : kNegInf;
+      sc[c] = vis ? x[c] * fac[c] : kNegInf;
       need |= sc[c] > m_own[c] + kLazyLog2;
     }
     if (__any(need)) {
@@ -564,10 +711,30 @@ struct DecodeWave {
       for (int i = 0; i < NL; ++i)
         if (t0 + i * TPL + grp >= L) vr[i] = make_uint4(0u, 0u, 0u, 0u);
     }
+    // the weight each owner broadcasts: with int8 codes it carries the
+    // token's V scale (a masked token's stale scale is never multiplied)
+    float pwv[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) pwv[c] = pw[c];
+    if constexpr (DT == PKV_I8) {
+      float vsc[C];
+      get_vs(vsc);
+#pragma unroll
+      for (int c = 0; c < C; ++c) pwv[c] = sc[c] == kNegInf ? 0.f : pw[c] * vsc[c];
+    }
     static_for<NL>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       float vv[EPL];
-      if constexpr (DT == PKV_BF16) {
+      if constexpr (DT == PKV_I8) {
+        const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          vv[4 * j] = code_f32<0>(vw[j]);
+          vv[4 * j + 1] = code_f32<1>(vw[j]);
+          vv[4 * j + 2] = code_f32<2>(vw[j]);
+          vv[4 * j + 3] = code_f32<3>(vw[j]);
+        }
+      } else if constexpr (DT == PKV_BF16) {
         vv[0] = bf16_lo(vr[i].x); vv[1] = bf16_hi(vr[i].x);
         vv[2] = bf16_lo(vr[i].y); vv[3] = bf16_hi(vr[i].y);
         vv[4] = bf16_lo(vr[i].z); vv[5] = bf16_hi(vr[i].z);
@@ -580,7 +747,7 @@ struct DecodeWave {
         constexpr int r = decltype(rc)::value;
         constexpr int v = r * NL + i;
         constexpr int src = V >= LPT ? v / C : v * DUP;
-        const float w = group_bcast<LPT, src>(pw[v % C], lane);
+        const float w = group_bcast<LPT, src>(pwv[v % C], lane);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(w, vv[e], acc[r][e]);
       });
@@ -627,7 +794,7 @@ decode_partition_kernel(const DecodeArgs a) {
   constexpr int NL = Gm::NL, EPL = Gm::EPL;
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
-  using Ring = TileRing<NL>;
+  using Ring = TileRing<NL, DT == PKV_I8>;
   constexpr int kSlots = Ring::kSlots;
 
   // the tile rings while streaming; the wavefronts' partials once done
@@ -683,12 +850,22 @@ decode_partition_kernel(const DecodeArgs a) {
   const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
   const char *kbase = (const char *)a.kc;
   const char *vbase = (const char *)a.vc;
-  auto tile_offset = [&](int t0, int blk) -> size_t {
+  // gather the tile at logical token t0 (from block blk) into a ring slot
+  auto stage_tile = [&](auto &ring, int slot, int t0, int blk) {
     if (blk < 0 || blk >= a.num_blocks) {  // bad table entry: read block 0, poison later
       st.bad = 1;
       blk = 0;
     }
-    return tile_bytes_offset<Gm::TB>(a, g, t0, blk, lane);
+    const size_t off = tile_bytes_offset<Gm::TB>(a, g, t0, blk, lane);
+    if constexpr (DT == PKV_I8) {
+      // the tile's 16 K and 16 V scales, one per lane (lanes 32..63 repeat)
+      const size_t so = (((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs)) * 4 +
+                        (size_t)(lane & 15) * 4;
+      ring.stage(slot, kbase + off, vbase + off,
+                 (const char *)((lane & 16) ? a.vs : a.ks) + so);
+    } else {
+      ring.stage(slot, kbase + off, vbase + off);
+    }
   };
 
   // Pipeline: up to kSlots tiles are gathered into the wavefront's LDS ring
@@ -706,10 +883,7 @@ decode_partition_kernel(const DecodeArgs a) {
     ring.init((PKV_LDS char *)&sm.ring[0] + wave * Ring::kBytes, lane);
 #pragma unroll
     for (int k = 0; k < kSlots; ++k)
-      if (k < n_tiles) {
-        const size_t off = tile_offset(tile_t0(k), table_at(k));
-        ring.stage(k, kbase + off, vbase + off);
-      }
+      if (k < n_tiles) stage_tile(ring, k, tile_t0(k), table_at(k));
     int blk_next = table_at(kSlots);
     // the scale is waited for here, not at its first use inside the loop,
     // where the wait would also catch each step's block-id read
@@ -720,17 +894,24 @@ decode_partition_kernel(const DecodeArgs a) {
       const int ahead = min(n_tiles - 1 - k, kSlots - 1);
       uint4 kr[NL];
       ring.template fetch<0>(slot, ahead, kr);
+      // the V scales are read before the slot is refilled
+      float vsc[W::C];
       st.process(
           kr,
           [&](uint4 (&vr)[NL]) {
             ring.template fetch<1>(slot, ahead, vr);
+            if constexpr (DT == PKV_I8) ring.template scales<1>(slot, st.own_tok, vsc);
             if (k + kSlots < n_tiles) {  // the slot is free again: refill it
-              const size_t off = tile_offset(tile_t0(k + kSlots), blk_next);
-              ring.stage(slot, kbase + off, vbase + off);
+              stage_tile(ring, slot, tile_t0(k + kSlots), blk_next);
               blk_next = table_at(k + kSlots + 1);
             }
           },
-          tile_t0(k), scale_log2);
+          tile_t0(k), scale_log2,
+          [&](float (&ksc)[W::C]) { ring.template scales<0>(slot, st.own_tok, ksc); },
+          [&](float (&v)[W::C]) {
+#pragma unroll
+            for (int c = 0; c < W::C; ++c) v[c] = vsc[c];
+          });
     }
   }
 
@@ -1061,7 +1242,7 @@ constexpr int64_t stream_lds_bytes(int64_t B) {
 template <int DT, int D, int G, int RP, int W>
 void launch_decode(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
   // eight wavefronts' tile rings must fit the workgroup's LDS
-  constexpr int kRing = TileRing<Geo<DT, D>::NL>::kBytes;
+  constexpr int kRing = TileRing<Geo<DT, D>::NL, DT == PKV_I8>::kBytes;
   if constexpr (W == 8 && 8 * kRing > kLdsLimit) {
     launch_decode<DT, D, G, RP, 4>(a, sa, grid, s);
   } else if constexpr (W == 0) {  // stream kernel + its reduce; grid.x persistent workgroups
