@@ -65,11 +65,14 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(B, nq, Hq, Hkv, D, es, lens, max_blocks, with_lse=False):
+def algorithmic_bytes(B, nq, Hq, Hkv, D, es, lens, max_blocks, with_lse=False,
+                      kv_row_bytes=None):
     """Bytes the attention call must move at minimum: every visible K and V
     element once per KV head, q read, fp32 out written, block-table entries
-    and context lengths read."""
-    kv = 2 * Hkv * D * es * int(np.sum(lens))
+    and context lengths read. kv_row_bytes: bytes of one token's K (or V)
+    row of one KV head, when it is not D * es (8-bit codes: D + 4)."""
+    row = D * es if kv_row_bytes is None else kv_row_bytes
+    kv = 2 * Hkv * row * int(np.sum(lens))
     q = B * nq * Hq * D * es
     out = B * nq * Hq * D * 4 + (B * nq * Hq * 4 if with_lse else 0)
     tables = 4 * int(np.sum(-(-np.asarray(lens) // 16)))
@@ -92,6 +95,8 @@ def chunk_flops(B, nq, Hq, D, lens) -> int:
 
 def kernel_label(wk) -> str:
     """Which launches one attention call makes, as the library plans them."""
+    if getattr(wk, "q8", False):
+        return "decode_partition_kernel<int8 codes> (one launch per attention call)"
     if is_chunk(wk):
         return "chunk_mfma_kernel + reduce_partitions_kernel"
     mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16
@@ -158,13 +163,20 @@ class Workload:
         self.pre_slots, self.step_slots = pre_slots, step_slots
         dev = device
         shape = (w.num_blocks, Hkv, bs, D)
-        self.kc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
-        self.vc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
+        self.q8 = w.kv_codes == 8
+        if self.q8:
+            self.qc = [pkv.Q8Cache(w.num_blocks, Hkv, bs, D, dev) for _ in range(rotate)]
+        else:
+            self.kc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
+            self.vc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
         kpre = k_all[torch.from_numpy(pre_idx)].to(dev)
         vpre = v_all[torch.from_numpy(pre_idx)].to(dev)
         d_pre_slots = torch.from_numpy(pre_slots).to(dev)
         for i in range(rotate):
-            pkv.paged_cache_write(kpre, vpre, self.kc[i], self.vc[i], d_pre_slots)
+            if self.q8:
+                pkv.paged_cache_write_q8(kpre, vpre, self.qc[i], d_pre_slots)
+            else:
+                pkv.paged_cache_write(kpre, vpre, self.kc[i], self.vc[i], d_pre_slots)
         del kpre, vpre
         self.k_step = k_all[torch.from_numpy(new_idx)].to(dev)
         self.v_step = v_all[torch.from_numpy(new_idx)].to(dev)
@@ -184,11 +196,20 @@ class Workload:
 
     def cache_write(self, i: int) -> None:
         r = i % self.rotate
+        if self.q8:
+            self.pkv.paged_cache_write_q8(self.k_step, self.v_step, self.qc[r],
+                                          self.d_step_slots)
+            return
         self.pkv.paged_cache_write(self.k_step, self.v_step, self.kc[r], self.vc[r],
                                    self.d_step_slots)
 
     def attend(self, i: int) -> None:
         r = i % self.rotate
+        if self.q8:
+            self.pkv.paged_attention_decode_q8(self.out, self.d_q, self.qc[r], self.d_tables,
+                                               self.d_lens, self.scale,
+                                               partition_tokens=self.part, workspace=self.ws)
+            return
         self.pkv.paged_attention_decode(self.out, self.d_q, self.kc[r], self.vc[r],
                                         self.d_tables, self.d_lens, self.scale,
                                         partition_tokens=self.part, workspace=self.ws)
@@ -198,6 +219,9 @@ class Workload:
         self.attend(i)
 
     def attention_bytes(self) -> int:
+        if self.q8:  # a code byte per element and a 4-byte scale per row
+            return algorithmic_bytes(self.B, self.nq, self.Hq, self.Hkv, self.D, self.es,
+                                     self.lens, self.max_blocks, kv_row_bytes=self.D + 4)
         return algorithmic_bytes(self.B, self.nq, self.Hq, self.Hkv, self.D, self.es,
                                  self.lens, self.max_blocks)
 
@@ -468,7 +492,8 @@ def summarize_profile(args) -> int:
         "traffic_bytes_per_launch": fetch * 1024 * ffac + write * 1024 * wfac,
         "algorithmic_bytes_per_launch": algorithmic_bytes(
             w.batch, w.queries_per_seq, w.q_heads, w.kv_heads, w.head_dim, w.esize, lens,
-            -(-int(lens.max()) // w.block_size)),
+            -(-int(lens.max()) // w.block_size),
+            kv_row_bytes=w.head_dim + 4 if w.kv_codes == 8 else None),
     }
     path = os.path.join(ROOT, "profiles", f"decode_{args.workload}.json")
     with open(path, "w") as f:
@@ -575,7 +600,8 @@ def main() -> int:
         "config": {"workload": wk.w.name, "batch": wk.B, "context": int(wk.lens.max()),
                    "q_heads": wk.Hq, "kv_heads": wk.Hkv, "head_dim": wk.D,
                    "block_size": wk.bs, "queries_per_seq": wk.nq,
-                   "kv_dtype": wk.w.dtype, "pool_blocks": wk.w.num_blocks,
+                   "kv_dtype": "int8 codes + f32 row scales" if getattr(wk, "q8", False)
+                   else wk.w.dtype, "pool_blocks": wk.w.num_blocks,
                    "placement": "seeded permutation", "pool_rotation": args.rotate},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -604,7 +630,8 @@ def main() -> int:
         result["roofline"]["achieved_unique"] = ub / (attn_ms * 1e-3) / 1e9
         result["roofline"]["logical_bytes"] = lb
         result["roofline"]["achieved_logical"] = lb / (attn_ms * 1e-3) / 1e9
-    if not args.no_cpu_baseline and not hasattr(wk, "unique_attention_bytes"):
+    if (not args.no_cpu_baseline and not hasattr(wk, "unique_attention_bytes")
+            and not getattr(wk, "q8", False) and not is_chunk(wk)):
         result["cpu_baseline"] = cpu_baseline(wk)
         log(f"[bench] cpu baseline {result['cpu_baseline']['value']:.1f} tokens/s")
     print(json.dumps(result), flush=True)

@@ -190,3 +190,59 @@ def test_q8_bad_table_and_short_context_give_nan(device):
     rows = np.arange(0, 2 * 8, dtype=np.int64)  # sequence 0
     ref, _ = c.run_oracle(rows=rows)
     assert np.abs(out[0].reshape(-1, 128) - ref).max() <= 1e-2
+
+
+def test_q8_full_size_sampled(device):
+    """The 8K decode batch (32 sequences, Llama-3-8B layer geometry) over an
+    8-bit code cache, in the launch configuration bench.py times: slots and
+    tables bit for bit, the codes of four sequences bit for bit, and their
+    rows against the C oracle."""
+    import bench
+
+    name = "llama3_8b_b32_8k_q8"
+    print(f"q8 full size: {name}", flush=True)
+    wk = bench.Workload(name, 1, device)
+    opool = PagedPool(wk.w.num_blocks, wk.bs, wk.stack.tolist())
+    pre = (wk.lens - wk.nq).tolist()
+    pre_slots, step_slots = [], []
+    for b in range(wk.B):
+        opool.create(b)
+    for b in range(wk.B):
+        pre_slots += opool.append(b, pre[b])[0]
+    for b in range(wk.B):
+        step_slots += opool.append(b, wk.nq)[0]
+    assert np.array_equal(wk.pre_slots, pre_slots)
+    assert np.array_equal(wk.step_slots, step_slots)
+    tables, lens = opool.block_tables(range(wk.B), wk.max_blocks)
+    tables, lens = np.array(tables, np.int32), np.array(lens, np.int32)
+    assert np.array_equal(wk.tables_host, tables)
+    wk.step(0)
+    torch.cuda.synchronize()
+    out = wk.out.cpu().numpy()
+    # the oracle quantizes the rows of sequences 0, 9, 20 and 31 only
+    seqs = [0, 9, 20, 31]
+    starts = np.concatenate([[0], np.cumsum(wk.lens)[:-1]])
+    kbits, vbits = host_bits(wk.host_k), host_bits(wk.host_v)
+    shape = (wk.w.num_blocks, wk.Hkv, wk.bs, wk.D)
+    kc = np.zeros(shape, np.int8)
+    vc = np.zeros(shape, np.int8)
+    ks = np.ones(shape[:3], np.float32)
+    vs = np.ones(shape[:3], np.float32)
+    pre_off = np.concatenate([[0], np.cumsum(pre)])
+    for b in seqs:
+        tok = np.arange(starts[b], starts[b] + wk.lens[b])
+        sl = list(pre_slots[pre_off[b]:pre_off[b + 1]]) + [step_slots[b]]
+        quant.cache_write_q(kc, vc, ks, vs, widen(kbits[tok], "bf16"), widen(vbits[tok], "bf16"),
+                            sl, wk.bs)
+    g = wk.qc[0]
+    gk, gks = g.k_codes.cpu().numpy(), g.k_scales.cpu().numpy()
+    for b in seqs:
+        for blk in tables[b][:-(-int(lens[b]) // wk.bs)]:
+            assert np.array_equal(gk[blk], kc[blk]) and np.array_equal(gks[blk], ks[blk])
+    rows = np.concatenate([np.arange(b * wk.Hq, (b + 1) * wk.Hq) for b in seqs]).astype(np.int64)
+    ref, _ = native.attention_q8(host_bits(wk.host_q), "bf16", kc, vc, ks, vs, tables, lens,
+                                 wk.scale, wk.bs, rows=rows,
+                                 threads=min(16, len(os.sched_getaffinity(0))))
+    err = np.abs(out.reshape(-1, wk.D)[rows] - ref).max()
+    print(f"  max-abs error {err:.3e} over {len(rows)} rows", flush=True)
+    assert np.isfinite(out).all() and err <= 1e-2
