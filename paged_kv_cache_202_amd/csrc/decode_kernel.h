@@ -80,13 +80,13 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
 // Two int8 codes (bytes 0 and 1, or 2 and 3, of w) as the fp16 pair
 // (1152 + c0, 1152 + c1): with u = c + 128 in 0..255, the fp16 whose bits
 // are 0x6400 | u is exactly 1024 + u, so the conversion is byte moves only.
+// (v_perm_b32 picks each result byte from the 8 bytes {S0, S1}, S1 being
+// bytes 0..3: S0 = 0x64646464 supplies the high bytes.)
 __device__ __forceinline__ uint32_t codes_f16_lo(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
-  return (u & 0xffu) | ((u & 0xff00u) << 8) | 0x64006400u;
+  return __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, 0x04010400u);
 }
 __device__ __forceinline__ uint32_t codes_f16_hi(uint32_t w) {
-  const uint32_t u = w ^ 0x80808080u;
-  return ((u >> 16) & 0xffu) | ((u >> 8) & 0xff0000u) | 0x64006400u;
+  return __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, 0x04030402u);
 }
 // Code k (0..3) of w as a float: the signed byte, widened.
 template <int K>
@@ -417,30 +417,44 @@ struct TileRing {
       gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
   }
 
-  // After fetch<HALF>: the scales of tokens tok[c] of the tile in `slot`
-  // (K scales for HALF = 0, V scales for HALF = 1).
-  template <int HALF, int C>
-  __device__ __forceinline__ void scales(int slot, const int (&tok)[C], float (&out)[C]) const {
-    const PKV_LDS char *p = base + slot * kTileBytes + kCodeBytes + HALF * 64;
-    if constexpr (C == 1) {
-      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                   : "=v"(out[0])
-                   : "v"(p + tok[0] * 4)
-                   : "memory");
-    } else if constexpr (C == 2) {
+  // fetch<HALF> and, in the same wait, the scale of token tok of the tile
+  // (K scale for HALF = 0, V scale for HALF = 1): one LDS round trip.
+  template <int HALF>
+  __device__ __forceinline__ void fetch_sc(int slot, int ahead, uint4 (&r)[NL], int tok,
+                                           float &sc) const {
+    static_assert(SC, "tiles without scales");
+    static_for<kSlots>([&](auto ac) {
+      constexpr int A = decltype(ac)::value;
+      if (ahead == A) wait_vmcnt<A * kLoads + (HALF == 0 ? NL : 0)>();
+    });
+    const PKV_LDS char *p = mine + slot * kTileBytes + HALF * NL * 1024;
+    const PKV_LDS char *ps = base + slot * kTileBytes + kCodeBytes + HALF * 64 + tok * 4;
+    u32x4_t t[NL];
+    if constexpr (NL == 1) {
       asm volatile(
-          "ds_read_b32 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-          : "=&v"(out[0]), "=&v"(out[1])
-          : "v"(p + tok[0] * 4), "v"(p + tok[1] * 4)
+          "ds_read_b128 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(t[0]), "=&v"(sc)
+          : "v"(p), "v"(ps)
+          : "memory");
+    } else if constexpr (NL == 2) {
+      asm volatile(
+          "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:1024\n\t"
+          "ds_read_b32 %2, %4\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(sc)
+          : "v"(p), "v"(ps)
           : "memory");
     } else {
-#pragma unroll
-      for (int c = 0; c < C; ++c)
-        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
-                     : "=v"(out[c])
-                     : "v"(p + tok[c] * 4)
-                     : "memory");
+      static_assert(NL == 4, "1, 2 or 4 rows per lane");
+      asm volatile(
+          "ds_read_b128 %0, %5\n\tds_read_b128 %1, %5 offset:1024\n\t"
+          "ds_read_b128 %2, %5 offset:2048\n\tds_read_b128 %3, %5 offset:3072\n\t"
+          "ds_read_b32 %4, %6\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(sc)
+          : "v"(p), "v"(ps)
+          : "memory");
     }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) r[i] = make_uint4(t[i].x, t[i].y, t[i].z, t[i].w);
   }
 
   // Read back the K half (HALF = 0) or the V half (HALF = 1) of the tile in
@@ -893,25 +907,30 @@ decode_partition_kernel(const DecodeArgs a) {
       const int slot = k & (kSlots - 1);
       const int ahead = min(n_tiles - 1 - k, kSlots - 1);
       uint4 kr[NL];
-      ring.template fetch<0>(slot, ahead, kr);
-      // the V scales are read before the slot is refilled
-      float vsc[W::C];
+      // int8 codes: each lane's one owned token's K and V scales come with
+      // the rows (read before the slot is refilled)
+      float ksc = 0.f, vsc = 0.f;
+      if constexpr (DT == PKV_I8) {
+        static_assert(W::C == 1, "one owned score per lane with int8 codes");
+        ring.template fetch_sc<0>(slot, ahead, kr, st.own_tok[0], ksc);
+      } else {
+        ring.template fetch<0>(slot, ahead, kr);
+      }
       st.process(
           kr,
           [&](uint4 (&vr)[NL]) {
-            ring.template fetch<1>(slot, ahead, vr);
-            if constexpr (DT == PKV_I8) ring.template scales<1>(slot, st.own_tok, vsc);
+            if constexpr (DT == PKV_I8)
+              ring.template fetch_sc<1>(slot, ahead, vr, st.own_tok[0], vsc);
+            else
+              ring.template fetch<1>(slot, ahead, vr);
             if (k + kSlots < n_tiles) {  // the slot is free again: refill it
               stage_tile(ring, slot, tile_t0(k + kSlots), blk_next);
               blk_next = table_at(k + kSlots + 1);
             }
           },
           tile_t0(k), scale_log2,
-          [&](float (&ksc)[W::C]) { ring.template scales<0>(slot, st.own_tok, ksc); },
-          [&](float (&v)[W::C]) {
-#pragma unroll
-            for (int c = 0; c < W::C; ++c) v[c] = vsc[c];
-          });
+          [&](float (&ks)[W::C]) { ks[0] = ksc; },
+          [&](float (&vs)[W::C]) { vs[0] = vsc; });
     }
   }
 
