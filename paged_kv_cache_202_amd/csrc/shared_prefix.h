@@ -531,12 +531,15 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) o[r][cb] *= alpha;
       }
+      // a masked score (-inf) gives exp2(-inf) = 0; the maximum is floored so
+      // that a row with no visible key yet (maximum -inf) gives 0 too, not NaN
+      const float m_sub = fmaxf(m_row[r], -3.0e38f);
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         float pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pw[e] = sc[u][e] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[u][e] - m_row[r]);
+          pw[e] = __builtin_amdgcn_exp2f(sc[u][e] - m_sub);
           l_part[r] += pw[e];
         }
         pa[u][r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
