@@ -92,3 +92,46 @@ def test_every_kernel_launch_has_its_kernel():
     syms = subprocess.run([nm, "-D", lib], capture_output=True, text=True, check=True).stdout
     undefined = [l for l in syms.splitlines() if " U " in l and "__device_stub__" in l]
     assert not undefined, undefined
+
+
+def test_low_bit_and_chunk_host_checks_need_no_gpu():
+    """The 8-bit cache entry points and the chunked-prefill sizing check their
+    arguments on the host first (fake non-null pointers are never touched)."""
+    lib = pkv.load()
+    fake = ctypes.c_void_p(256)
+    # cache write of 8-bit codes
+    assert lib.paged_cache_write_q8(None, None, None, None, None, None, None, 0, 4, 8, 128, 16,
+                                    _lib.PKV_BF16, None) == _lib.PKV_OK  # nothing to write
+    assert lib.paged_cache_write_q8(fake, fake, fake, fake, fake, fake, fake, 3, 4, 8, 96, 16,
+                                    _lib.PKV_BF16, None) == _lib.PKV_EINVAL  # head dim
+    assert lib.paged_cache_write_q8(fake, fake, fake, fake, fake, fake, fake, 3, 4, 8, 128, 16,
+                                    _lib.PKV_I8, None) == _lib.PKV_EINVAL  # rows are f32/bf16
+    assert lib.paged_cache_write_q8(fake, fake, fake, fake, None, fake, fake, 3, 4, 8, 128, 16,
+                                    _lib.PKV_BF16, None) == _lib.PKV_EINVAL  # NULL scales
+    # decode over 8-bit codes
+
+    def q8(scales=fake, nq=1, Hq=32, part=0, D=128):
+        return lib.paged_attention_decode_q8(fake, fake, fake, fake, scales, scales, fake, 4,
+                                             fake, 2, nq, Hq, 8, D, 16, 8, 0.1, part, None, 0,
+                                             None, None)
+    assert q8(scales=None) == _lib.PKV_EINVAL
+    assert q8(scales=ctypes.c_void_p(260)) == _lib.PKV_EINVAL  # scales not 16-byte aligned
+    assert q8(D=96) == _lib.PKV_EINVAL
+    assert q8(nq=8) == _lib.PKV_EINVAL  # 4 heads x 8 queries: more than 16 rows per KV head
+    # the plain entry refuses int8 codes (they need their scales)
+    assert lib.paged_attention_decode(fake, fake, fake, fake, fake, 4, fake, 2, 1, 32, 8, 128,
+                                      16, 8, 0.1, _lib.PKV_I8, 0, None, 0, None, None) \
+        == _lib.PKV_EINVAL
+    # chunked prefill: more than 16 rows per KV head are sized as a chunk call
+    size = ctypes.c_size_t()
+    assert lib.paged_attention_workspace_size(2, 64, 32, 8, 128, 512, 16, 0,
+                                              ctypes.byref(size)) == _lib.PKV_OK
+    assert size.value >= 2 * 64 * 32 * (128 + 2) * 4  # at least one partial per row
+    # fp32 caches take at most 16 rows per KV head
+    assert lib.paged_attention_decode(fake, fake, fake, fake, fake, 4, fake, 2, 8, 32, 8, 128,
+                                      16, 8, 0.1, _lib.PKV_F32, 0, None, 0, None, None) \
+        == _lib.PKV_EINVAL
+    # a chunk call without its workspace is refused before any launch
+    assert lib.paged_attention_decode(fake, fake, fake, fake, fake, 4, fake, 2, 64, 32, 8, 128,
+                                      16, 8, 0.1, _lib.PKV_BF16, 0, None, 0, None, None) \
+        == _lib.PKV_EINVAL
