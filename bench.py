@@ -96,7 +96,8 @@ def chunk_flops(B, nq, Hq, D, lens) -> int:
 def kernel_label(wk) -> str:
     """Which launches one attention call makes, as the library plans them."""
     if getattr(wk, "q8", False):
-        return "decode_partition_kernel<int8 codes> (one launch per attention call)"
+        kind = "int8" if wk.w.kv_codes == 8 else "3-bit"
+        return f"decode_partition_kernel<{kind} codes> (one launch per attention call)"
     if is_chunk(wk):
         return "chunk_mfma_kernel + reduce_partitions_kernel"
     mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16
@@ -163,9 +164,14 @@ class Workload:
         self.pre_slots, self.step_slots = pre_slots, step_slots
         dev = device
         shape = (w.num_blocks, Hkv, bs, D)
-        self.q8 = w.kv_codes == 8
+        self.q8 = w.kv_codes in (8, 3)  # a cache of per-row codes
         if self.q8:
-            self.qc = [pkv.Q8Cache(w.num_blocks, Hkv, bs, D, dev) for _ in range(rotate)]
+            cls = pkv.Q8Cache if w.kv_codes == 8 else pkv.Q3Cache
+            self.qc = [cls(w.num_blocks, Hkv, bs, D, dev) for _ in range(rotate)]
+            self.write_q = (pkv.paged_cache_write_q8 if w.kv_codes == 8
+                            else pkv.paged_cache_write_q3)
+            self.decode_q = (pkv.paged_attention_decode_q8 if w.kv_codes == 8
+                             else pkv.paged_attention_decode_q3)
         else:
             self.kc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
             self.vc = [torch.empty(shape, dtype=tdt, device=dev) for _ in range(rotate)]
@@ -174,7 +180,7 @@ class Workload:
         d_pre_slots = torch.from_numpy(pre_slots).to(dev)
         for i in range(rotate):
             if self.q8:
-                pkv.paged_cache_write_q8(kpre, vpre, self.qc[i], d_pre_slots)
+                self.write_q(kpre, vpre, self.qc[i], d_pre_slots)
             else:
                 pkv.paged_cache_write(kpre, vpre, self.kc[i], self.vc[i], d_pre_slots)
         del kpre, vpre
@@ -197,8 +203,7 @@ class Workload:
     def cache_write(self, i: int) -> None:
         r = i % self.rotate
         if self.q8:
-            self.pkv.paged_cache_write_q8(self.k_step, self.v_step, self.qc[r],
-                                          self.d_step_slots)
+            self.write_q(self.k_step, self.v_step, self.qc[r], self.d_step_slots)
             return
         self.pkv.paged_cache_write(self.k_step, self.v_step, self.kc[r], self.vc[r],
                                    self.d_step_slots)
@@ -206,9 +211,8 @@ class Workload:
     def attend(self, i: int) -> None:
         r = i % self.rotate
         if self.q8:
-            self.pkv.paged_attention_decode_q8(self.out, self.d_q, self.qc[r], self.d_tables,
-                                               self.d_lens, self.scale,
-                                               partition_tokens=self.part, workspace=self.ws)
+            self.decode_q(self.out, self.d_q, self.qc[r], self.d_tables, self.d_lens,
+                          self.scale, partition_tokens=self.part, workspace=self.ws)
             return
         self.pkv.paged_attention_decode(self.out, self.d_q, self.kc[r], self.vc[r],
                                         self.d_tables, self.d_lens, self.scale,
@@ -219,9 +223,10 @@ class Workload:
         self.attend(i)
 
     def attention_bytes(self) -> int:
-        if self.q8:  # a code byte per element and a 4-byte scale per row
+        if self.q8:  # a code byte (or half a byte) per element and a 4-byte scale per row
+            row = self.D + 4 if self.w.kv_codes == 8 else self.D // 2 + 4
             return algorithmic_bytes(self.B, self.nq, self.Hq, self.Hkv, self.D, self.es,
-                                     self.lens, self.max_blocks, kv_row_bytes=self.D + 4)
+                                     self.lens, self.max_blocks, kv_row_bytes=row)
         return algorithmic_bytes(self.B, self.nq, self.Hq, self.Hkv, self.D, self.es,
                                  self.lens, self.max_blocks)
 
@@ -493,7 +498,7 @@ def summarize_profile(args) -> int:
         "algorithmic_bytes_per_launch": algorithmic_bytes(
             w.batch, w.queries_per_seq, w.q_heads, w.kv_heads, w.head_dim, w.esize, lens,
             -(-int(lens.max()) // w.block_size),
-            kv_row_bytes=w.head_dim + 4 if w.kv_codes == 8 else None),
+            kv_row_bytes={8: w.head_dim + 4, 3: w.head_dim // 2 + 4}.get(w.kv_codes)),
     }
     path = os.path.join(ROOT, "profiles", f"decode_{args.workload}.json")
     with open(path, "w") as f:
@@ -600,8 +605,9 @@ def main() -> int:
         "config": {"workload": wk.w.name, "batch": wk.B, "context": int(wk.lens.max()),
                    "q_heads": wk.Hq, "kv_heads": wk.Hkv, "head_dim": wk.D,
                    "block_size": wk.bs, "queries_per_seq": wk.nq,
-                   "kv_dtype": "int8 codes + f32 row scales" if getattr(wk, "q8", False)
-                   else wk.w.dtype, "pool_blocks": wk.w.num_blocks,
+                   "kv_dtype": (f"{wk.w.kv_codes}-bit codes + f32 row scales"
+                                if getattr(wk, "q8", False) else wk.w.dtype),
+                   "pool_blocks": wk.w.num_blocks,
                    "placement": "seeded permutation", "pool_rotation": args.rotate},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,

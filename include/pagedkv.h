@@ -309,6 +309,32 @@ int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
                               void *workspace, size_t workspace_bytes,
                               float *lse_out, void *stream);
 
+/* ---- caches of 3-bit per-row codes --------------------------------------
+ * The same quantizer with 3 bits ([KVNB demo] Demo 2; the 3-bit storage
+ * scenario of [KVNB s8]): limit 3, scale = max |x| / 3, code in [-3, 3].
+ * Codes are stored two per byte as code + 8 (dim 2 i in the low nibble of
+ * byte i): half a byte per element, byte-aligned for the decode kernels
+ * (the pages' 3 bits per element would not give whole bytes per lane):
+ *   k_codes, v_codes:   uint8   [num_blocks, Hkv, block_size, D / 2]
+ *   k_scales, v_scales: float32 [num_blocks, Hkv, block_size]
+ * D in {128, 256}. paged_cache_write_q3 / paged_attention_decode_q3 are the
+ * 8-bit calls' counterparts (same arguments, errors and copy-on-write: codes
+ * as PKV_I8 with D / 2 bytes per row). */
+int paged_cache_write_q3(const void *k_new, const void *v_new, uint8_t *k_codes,
+                         uint8_t *v_codes, float *k_scales, float *v_scales,
+                         const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
+                         int32_t Hkv, int32_t D, int32_t block_size, int dtype,
+                         void *stream);
+int paged_attention_decode_q3(float *out, const void *q, const uint8_t *k_codes,
+                              const uint8_t *v_codes, const float *k_scales,
+                              const float *v_scales, const int32_t *block_tables,
+                              int32_t max_blocks, const int32_t *context_lens,
+                              int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t block_size, int32_t num_blocks,
+                              float scale, int32_t partition_tokens,
+                              void *workspace, size_t workspace_bytes,
+                              float *lse_out, void *stream);
+
 /* ----------------------------------------------------------------------
  * Shared prefixes ([vLLM]: blocks shared within and across requests;
  * [KVNB s5] share_prefix forks a parent's leading blocks).

@@ -23,7 +23,7 @@ __all__ = [
     "paged_attention_workspace_size", "paged_attention_decode", "dtype_code",
     "PrefixGroups", "paged_kv_prefix_groups", "paged_attention_shared_workspace_size",
     "paged_attention_decode_shared", "Q8Cache", "paged_cache_write_q8",
-    "paged_attention_decode_q8",
+    "paged_attention_decode_q8", "Q3Cache", "paged_cache_write_q3", "paged_attention_decode_q3",
 ]
 
 
@@ -247,6 +247,69 @@ def paged_attention_decode_q8(out, q, cache: "Q8Cache", block_tables, context_le
         raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode_q8: shape mismatch")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode_q8(
+        _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.k_scales),
+        _dev(cache.v_scales), _dev(block_tables), max_blocks, _dev(context_lens), B, nq, Hq,
+        Hkv, D, bs, NB, float(scale), int(partition_tokens), _dev(workspace), ws_bytes,
+        _dev(lse), _stream(stream)))
+
+
+class Q3Cache:
+    """A paged cache of 3-bit per-row codes, two per byte (code + 8, even dim
+    in the low nibble): codes uint8 [NB, Hkv, bs, D / 2] and float32 scales
+    [NB, Hkv, bs], for K and for V (device tensors)."""
+
+    def __init__(self, num_blocks, Hkv, block_size, D, device):
+        import torch
+
+        shape = (num_blocks, Hkv, block_size, D // 2)
+        self.D = D
+        self.k_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
+        self.k_scales = torch.ones(shape[:3], dtype=torch.float32, device=device)
+        self.v_scales = torch.ones(shape[:3], dtype=torch.float32, device=device)
+
+    @property
+    def shape(self):
+        """(num_blocks, Hkv, block_size, D): the logical shape."""
+        return tuple(self.k_codes.shape[:3]) + (self.D,)
+
+    def copy_blocks(self, pairs, stream=None) -> None:
+        NB, Hkv, bs, D = self.shape
+        n = pairs.shape[0]
+        check(load().paged_kv_copy_blocks(_dev(self.k_codes), _dev(self.v_codes), _dev(pairs), n,
+                                          NB, Hkv, D // 2, bs, _lib.PKV_I8, _stream(stream)))
+        check(load().paged_kv_copy_blocks(_dev(self.k_scales), _dev(self.v_scales), _dev(pairs),
+                                          n, NB, Hkv, 1, bs, PKV_F32, _stream(stream)))
+
+
+def paged_cache_write_q3(k_new, v_new, cache: "Q3Cache", slot_mapping, stream=None) -> None:
+    """Quantize k_new, v_new [T, Hkv, D] (f32 or bf16) to 3-bit codes with one
+    scale per row and scatter them to their slots."""
+    NB, Hkv, bs, D = cache.shape
+    T = k_new.shape[0]
+    if (tuple(k_new.shape) != (T, Hkv, D) or v_new.shape != k_new.shape
+            or tuple(slot_mapping.shape) != (T,) or v_new.dtype != k_new.dtype):
+        raise InvalidArgument(_lib.PKV_EINVAL, "paged_cache_write_q3: shape or dtype mismatch")
+    check(load().paged_cache_write_q3(
+        _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes),
+        _dev(cache.k_scales), _dev(cache.v_scales), _dev(slot_mapping), T, NB, Hkv, D, bs,
+        dtype_code(k_new), _stream(stream)))
+
+
+def paged_attention_decode_q3(out, q, cache: "Q3Cache", block_tables, context_lens, scale,
+                              partition_tokens=0, workspace=None, lse=None,
+                              stream=None) -> None:
+    """paged_attention_decode over a cache of 3-bit codes; q bf16 [B, nq, Hq, D]."""
+    import torch
+
+    B, nq, Hq, D = q.shape
+    NB, Hkv, bs, Dk = cache.shape
+    max_blocks = block_tables.shape[1]
+    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
+            or tuple(context_lens.shape) != (B,) or q.dtype != torch.bfloat16):
+        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode_q3: shape mismatch")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(load().paged_attention_decode_q3(
         _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.k_scales),
         _dev(cache.v_scales), _dev(block_tables), max_blocks, _dev(context_lens), B, nq, Hq,
         Hkv, D, bs, NB, float(scale), int(partition_tokens), _dev(workspace), ws_bytes,

@@ -61,19 +61,23 @@ copy_blocks_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
 }
 
 // Per-row integer codes of the course page's teaching quantizer (project
-// demo, Demo 2: symmetric codes, one scale per row), 8 bits: for each new
-// (token, KV head) row x of D values, scale = max |x| / 127 (1 for a row of
-// zeros), code = clip(round-half-even(x / scale), -127, 127), in float64 as
-// the page computes; the scale is stored as float32. One wavefront per row:
-// each lane holds D / 64 consecutive elements.
-template <int D, typename T>
+// demo, Demo 2: symmetric codes, one scale per row), BITS = 8 or 3: for each
+// new (token, KV head) row x of D values, limit = 2^(BITS-1) - 1, scale =
+// max |x| / limit (1 for a row of zeros), code = clip(round-half-even(x /
+// scale), -limit, limit), in float64 as the page computes; the scale is
+// stored as float32. 8-bit codes are stored as int8; 3-bit codes two per
+// byte, code + 8, even dim in the low nibble. One wavefront per row: each
+// lane holds D / 64 consecutive elements.
+template <int D, int BITS, typename T>
 __global__ void __launch_bounds__(256)
-cache_write_q8_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
-                      int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes,
-                      float *__restrict__ k_scales, float *__restrict__ v_scales,
-                      const int32_t *__restrict__ slots, int64_t rows, int32_t Hkv, int32_t bs,
-                      int64_t num_slots) {
+cache_write_q_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
+                     int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes,
+                     float *__restrict__ k_scales, float *__restrict__ v_scales,
+                     const int32_t *__restrict__ slots, int64_t rows, int32_t Hkv, int32_t bs,
+                     int64_t num_slots) {
   constexpr int EPL = D / 64;
+  constexpr double kLimit = (1 << (BITS - 1)) - 1;
+  static_assert(BITS == 8 || (BITS == 3 && EPL % 2 == 0), "8-bit, or 3-bit with whole bytes");
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // t * Hkv + h
   if (row >= rows) return;
@@ -99,13 +103,20 @@ cache_write_q8_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) mx = fmax(mx, __shfl_xor(mx, m, 64));
-    double scale = mx / 127.0;
+    double scale = mx / kLimit;
     if (scale == 0.0) scale = 1.0;
-    int8_t *codes = (which ? v_codes : k_codes) + dst * D + lane * EPL;
+    int c[EPL];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const double c = fmin(fmax(rint(x[e] / scale), -127.0), 127.0);
-      codes[e] = (int8_t)(int)c;
+    for (int e = 0; e < EPL; ++e) c[e] = (int)fmin(fmax(rint(x[e] / scale), -kLimit), kLimit);
+    if constexpr (BITS == 8) {
+      int8_t *codes = (which ? v_codes : k_codes) + dst * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) codes[e] = (int8_t)c[e];
+    } else {
+      uint8_t *codes = (uint8_t *)(which ? v_codes : k_codes) + dst * (D / 2) + lane * (EPL / 2);
+#pragma unroll
+      for (int e = 0; e < EPL; e += 2)
+        codes[e / 2] = (uint8_t)((c[e] + 8) | ((c[e + 1] + 8) << 4));
     }
     if (lane == 0) (which ? v_scales : k_scales)[dst] = (float)scale;
   }
@@ -171,16 +182,17 @@ extern "C" int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_
   return PKV_OK;
 }
 
-extern "C" int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
-                                    int8_t *v_codes, float *k_scales, float *v_scales,
-                                    const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
-                                    int32_t Hkv, int32_t D, int32_t block_size, int dtype,
-                                    void *stream) {
+template <int BITS>
+static int cache_write_q(const void *k_new, const void *v_new, int8_t *k_codes, int8_t *v_codes,
+                         float *k_scales, float *v_scales, const int32_t *slot_mapping, int32_t T,
+                         int32_t num_blocks, int32_t Hkv, int32_t D, int32_t block_size,
+                         int dtype, void *stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16)
     return fail(PKV_EINVAL, "new rows must be f32 or bf16 (dtype %d)", dtype);
   if (T < 0 || num_blocks <= 0 || Hkv <= 0 || block_size <= 0)
     return fail(PKV_EINVAL, "sizes must be positive (T >= 0)");
-  if (D != 64 && D != 128 && D != 256) return fail(PKV_EINVAL, "head dim %d unsupported", D);
+  if (D != 128 && D != 256 && (BITS == 3 || D != 64))
+    return fail(PKV_EINVAL, "head dim %d unsupported for %d-bit codes", D, BITS);
   if (T == 0) return PKV_OK;
   if (!k_new || !v_new || !k_codes || !v_codes || !k_scales || !v_scales || !slot_mapping)
     return fail(PKV_EINVAL, "NULL pointer");
@@ -188,20 +200,43 @@ extern "C" int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t
   const int64_t num_slots = (int64_t)num_blocks * block_size;
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
-#define PKV_Q8(d)                                                                          \
-  if (D == d) {                                                                            \
-    if (dtype == PKV_BF16)                                                                 \
-      hipLaunchKernelGGL((cache_write_q8_kernel<d, uint16_t>), grid, block, 0, s,           \
-                         (const uint16_t *)k_new, (const uint16_t *)v_new, k_codes, v_codes, \
-                         k_scales, v_scales, slot_mapping, rows, Hkv, block_size, num_slots); \
-    else                                                                                   \
-      hipLaunchKernelGGL((cache_write_q8_kernel<d, float>), grid, block, 0, s,              \
-                         (const float *)k_new, (const float *)v_new, k_codes, v_codes,      \
-                         k_scales, v_scales, slot_mapping, rows, Hkv, block_size, num_slots); \
+#define PKV_Q(d)                                                                            \
+  if (D == d) {                                                                             \
+    if constexpr (BITS == 8 || d >= 128) {                                                  \
+      if (dtype == PKV_BF16)                                                                \
+        hipLaunchKernelGGL((cache_write_q_kernel<d, BITS, uint16_t>), grid, block, 0, s,     \
+                           (const uint16_t *)k_new, (const uint16_t *)v_new, k_codes,        \
+                           v_codes, k_scales, v_scales, slot_mapping, rows, Hkv, block_size, \
+                           num_slots);                                                      \
+      else                                                                                  \
+        hipLaunchKernelGGL((cache_write_q_kernel<d, BITS, float>), grid, block, 0, s,        \
+                           (const float *)k_new, (const float *)v_new, k_codes, v_codes,     \
+                           k_scales, v_scales, slot_mapping, rows, Hkv, block_size,          \
+                           num_slots);                                                      \
+    }                                                                                       \
   }
-  PKV_Q8(64) PKV_Q8(128) PKV_Q8(256)
-#undef PKV_Q8
+  PKV_Q(64) PKV_Q(128) PKV_Q(256)
+#undef PKV_Q
   const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PKV_EHIP, "cache write q8 launch: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(PKV_EHIP, "cache write launch: %s", hipGetErrorString(e));
   return PKV_OK;
+}
+
+extern "C" int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
+                                    int8_t *v_codes, float *k_scales, float *v_scales,
+                                    const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
+                                    int32_t Hkv, int32_t D, int32_t block_size, int dtype,
+                                    void *stream) {
+  return cache_write_q<8>(k_new, v_new, k_codes, v_codes, k_scales, v_scales, slot_mapping, T,
+                          num_blocks, Hkv, D, block_size, dtype, stream);
+}
+
+extern "C" int paged_cache_write_q3(const void *k_new, const void *v_new, uint8_t *k_codes,
+                                    uint8_t *v_codes, float *k_scales, float *v_scales,
+                                    const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
+                                    int32_t Hkv, int32_t D, int32_t block_size, int dtype,
+                                    void *stream) {
+  return cache_write_q<3>(k_new, v_new, (int8_t *)k_codes, (int8_t *)v_codes, k_scales,
+                          v_scales, slot_mapping, T, num_blocks, Hkv, D, block_size, dtype,
+                          stream);
 }

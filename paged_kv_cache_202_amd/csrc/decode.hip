@@ -259,6 +259,9 @@ Launcher pick_launcher(int dtype, int D, int G, int RP, int W) {
     if (D == 64) return pick_rows<PKV_I8, 64>(G, RP, W);
     if (D == 128) return pick_rows<PKV_I8, 128>(G, RP, W);
     if (D == 256) return pick_rows<PKV_I8, 256>(G, RP, W);
+  } else if (dtype == kCodes3) {
+    if (D == 128) return pick_rows<kCodes3, 128>(G, RP, W);
+    if (D == 256) return pick_rows<kCodes3, 256>(G, RP, W);
   }
   return nullptr;
 }
@@ -472,7 +475,7 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   int32_t RP, S;
   row_split(G, nq, &RP, &S);
   if (mfma) S = 1;
-  if (dtype == PKV_I8 && RP > 4) {  // int8 codes: at most 4 rows per wavefront
+  if ((dtype == PKV_I8 || dtype == kCodes3) && RP > 4) {  // codes: at most 4 rows per wavefront
     S *= RP / 4;
     RP = 4;
   }
@@ -557,6 +560,23 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
                 dtype);
   return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks,
                      context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype, part,
+                     workspace, workspace_bytes, lse_out, stream);
+}
+
+extern "C" int paged_attention_decode_q3(float *out, const void *q, const uint8_t *k_codes,
+                                         const uint8_t *v_codes, const float *k_scales,
+                                         const float *v_scales, const int32_t *block_tables,
+                                         int32_t max_blocks, const int32_t *context_lens,
+                                         int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                                         int32_t D, int32_t bs, int32_t num_blocks, float scale,
+                                         int32_t part, void *workspace, size_t workspace_bytes,
+                                         float *lse_out, void *stream) {
+  if (!k_scales || !v_scales) return fail(PKV_EINVAL, "NULL pointer");
+  if ((uintptr_t)k_scales % 16 || (uintptr_t)v_scales % 16)
+    return fail(PKV_EINVAL, "scale arrays must be 16-byte aligned");
+  if (D != 128 && D != 256) return fail(PKV_EINVAL, "head dim %d unsupported for 3-bit codes", D);
+  return decode_impl(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, max_blocks,
+                     context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, kCodes3, part,
                      workspace, workspace_bytes, lse_out, stream);
 }
 

@@ -55,8 +55,9 @@ class Workload:
     shared_prefix: int = 0  # prefix-sharing workload: tokens shared by all
     unique_suffix: int = 0  # prefix-sharing workload: private tokens per seq
     cache_write_in_step: bool = True
-    # 8: the cache holds 8-bit per-row codes (int8 + a float32 scale per row)
-    # written from `dtype` rows; 0: the cache holds `dtype` itself
+    # 8 or 3: the cache holds 8-bit (int8) or 3-bit (two per byte) per-row
+    # codes with a float32 scale per row, written from `dtype` rows; 0: the
+    # cache holds `dtype` itself
     kv_codes: int = 0
 
     @property
@@ -99,6 +100,11 @@ WORKLOADS = {
         index=7, name="llama3_8b_b32_8k_q8", dtype="bf16", q_heads=32,
         kv_heads=8, head_dim=128, block_size=16, batch=32, num_blocks=16384,
         context=8192, kv_codes=8),
+    # ... and over 3-bit codes (the notebook's 16 -> 3 bit storage scenario)
+    "llama3_8b_b32_8k_q3": Workload(
+        index=8, name="llama3_8b_b32_8k_q3", dtype="bf16", q_heads=32,
+        kv_heads=8, head_dim=128, block_size=16, batch=32, num_blocks=16384,
+        context=8192, kv_codes=3),
     # chunked prefill: each sequence's last 512-token prompt chunk over its
     # 7680 cached tokens (the notebook's 16 chunks of 512 for an 8K prompt)
     "llama3_8b_chunk512_b4_8k": Workload(

@@ -1,7 +1,8 @@
-"""GPU parity for caches of 8-bit per-row codes.
+"""GPU parity for caches of 8-bit and 3-bit per-row codes.
 
 The library quantizes each new (token, KV head) row as it writes it
-(paged_cache_write_q8) and attends over the codes (paged_attention_decode_q8).
+(paged_cache_write_q8 / _q3) and attends over the codes
+(paged_attention_decode_q8 / _q3).
 The oracle quantizes the same rows with oracle/quant.py (the course page's
 teaching quantizer, float64) into its own host pool built by its own
 allocator, and walks the tables in float64 over code * scale. Codes and
@@ -34,8 +35,17 @@ def host_bits(t):
     return t.numpy()
 
 
+def unpack3(codes):
+    """int8 codes of a 3-bit cache's bytes (code + 8, even dim low nibble)."""
+    lo = (codes & 0xF).astype(np.int16) - 8
+    hi = (codes >> 4).astype(np.int16) - 8
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (-1,)).astype(np.int8)
+
+
 class Q8Case:
-    def __init__(self, lens, Hq, Hkv, D, nq=1, bs=16, seed=0, in_dtype="bf16", device="cuda:0"):
+    def __init__(self, lens, Hq, Hkv, D, nq=1, bs=16, seed=0, in_dtype="bf16", device="cuda:0",
+                 bits=8):
+        self.bits = bits
         self.lens = [int(n) for n in lens]
         self.B, self.Hq, self.Hkv, self.D, self.nq, self.bs = len(lens), Hq, Hkv, D, nq, bs
         self.device = device
@@ -67,7 +77,7 @@ class Q8Case:
         self.o_vs = np.full(shape[:3], np.nan, np.float32)
         quant.cache_write_q(self.o_kc, self.o_vc, self.o_ks, self.o_vs,
                             widen(host_bits(self.k_new), in_dtype),
-                            widen(host_bits(self.v_new), in_dtype), slots, bs)
+                            widen(host_bits(self.v_new), in_dtype), slots, bs, bits=bits)
         t, l = opool.block_tables(range(self.B), self.max_blocks)
         self.o_tables, self.o_lens = np.array(t, np.int32), np.array(l, np.int32)
         self.o_slots = np.array(slots, np.int32)
@@ -79,13 +89,16 @@ class Q8Case:
         assert np.array_equal(lslots, self.o_slots)
         tt, ll = pool.block_tables(list(range(self.B)), self.max_blocks)
         assert np.array_equal(tt, self.o_tables)
-        self.cache = pkv.Q8Cache(self.num_blocks, Hkv, bs, D, device)
+        self.cache = (pkv.Q8Cache if bits == 8 else pkv.Q3Cache)(self.num_blocks, Hkv, bs, D,
+                                                                 device)
         self.cache.k_scales.fill_(float("nan"))
         self.cache.v_scales.fill_(float("nan"))
-        self.cache.k_codes.fill_(-128)  # a code the quantizer never writes
-        self.cache.v_codes.fill_(-128)
-        pkv.paged_cache_write_q8(self.k_new.to(device), self.v_new.to(device), self.cache,
-                                 torch.from_numpy(lslots).to(device))
+        # codes the quantizer never writes: -128, or nibbles 0 (code -8)
+        self.cache.k_codes.fill_(-128 if bits == 8 else 0)
+        self.cache.v_codes.fill_(-128 if bits == 8 else 0)
+        write = pkv.paged_cache_write_q8 if bits == 8 else pkv.paged_cache_write_q3
+        write(self.k_new.to(device), self.v_new.to(device), self.cache,
+              torch.from_numpy(lslots).to(device))
         self.d_tables = torch.from_numpy(tt).to(device)
         self.d_lens = torch.from_numpy(ll).to(device)
         self.d_q = self.q.to(device)
@@ -102,10 +115,18 @@ class Q8Case:
         n = pkv.paged_attention_workspace_size(self.B, self.nq, self.Hq, self.Hkv, self.D,
                                                self.max_blocks, self.bs, part)
         ws = torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
-        pkv.paged_attention_decode_q8(out, self.d_q, self.cache, self.d_tables, self.d_lens,
-                                      self.scale, partition_tokens=part, workspace=ws, lse=lse)
+        decode = pkv.paged_attention_decode_q8 if self.bits == 8 else pkv.paged_attention_decode_q3
+        decode(out, self.d_q, self.cache, self.d_tables, self.d_lens, self.scale,
+               partition_tokens=part, workspace=ws, lse=lse)
         torch.cuda.synchronize()
         return out.cpu().numpy(), lse.cpu().numpy()
+
+    def codes(self):
+        """The library's codes as int8 arrays (3-bit ones unpacked)."""
+        kc, vc = self.cache.k_codes.cpu().numpy(), self.cache.v_codes.cpu().numpy()
+        if self.bits == 3:
+            return unpack3(kc), unpack3(vc)
+        return kc, vc
 
     def run_oracle(self, rows=None):
         return native.attention_q8(host_bits(self.q), "bf16", self.o_kc, self.o_vc, self.o_ks,
@@ -114,13 +135,12 @@ class Q8Case:
 
 
 @pytest.mark.parametrize("in_dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_cache_write_codes_bit_exact(in_dtype, D, device):
-    print(f"q8 cache write: {in_dtype} D {D}", flush=True)
-    c = Q8Case((1, 17, 40, 77), 8, 2, D, seed=D, in_dtype=in_dtype, device=device)
+@pytest.mark.parametrize("D,bits", [(64, 8), (128, 8), (256, 8), (128, 3), (256, 3)])
+def test_cache_write_codes_bit_exact(in_dtype, D, bits, device):
+    print(f"code cache write: {bits} bits, {in_dtype} D {D}", flush=True)
+    c = Q8Case((1, 17, 40, 77), 8, 2, D, seed=D, in_dtype=in_dtype, device=device, bits=bits)
     live = c.live_mask()
-    kc = c.cache.k_codes.cpu().numpy()
-    vc = c.cache.v_codes.cpu().numpy()
+    kc, vc = c.codes()
     ks = c.cache.k_scales.cpu().numpy()
     vs = c.cache.v_scales.cpu().numpy()
     for got, want in ((kc, c.o_kc), (vc, c.o_vc)):
@@ -130,7 +150,7 @@ def test_cache_write_codes_bit_exact(in_dtype, D, device):
         w = want.transpose(0, 2, 1)[live].view(np.uint32)
         assert np.array_equal(g, w)
     # slots nobody wrote keep their fill
-    assert (kc.transpose(0, 2, 1, 3)[~live] == -128).all()
+    assert (kc.transpose(0, 2, 1, 3)[~live] == (-128 if bits == 8 else -8)).all()
     assert np.isnan(ks.transpose(0, 2, 1)[~live]).all()
 
 
@@ -162,12 +182,15 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("bits", [8, 3])
 @pytest.mark.parametrize("ci", range(len(CASES)))
-def test_q8_attention_matches_oracle(ci, device):
+def test_q8_attention_matches_oracle(ci, bits, device):
     lens, Hq, Hkv, D, nq, part = CASES[ci]
-    print(f"q8 attention case {ci}: lens {lens} Hq {Hq} Hkv {Hkv} D {D} nq {nq} part {part}",
-          flush=True)
-    c = Q8Case(lens, Hq, Hkv, D, nq=nq, seed=100 + ci, device=device)
+    if bits == 3 and D == 64:
+        pytest.skip("3-bit codes are built for D 128 and 256")
+    print(f"{bits}-bit attention case {ci}: lens {lens} Hq {Hq} Hkv {Hkv} D {D} nq {nq} "
+          f"part {part}", flush=True)
+    c = Q8Case(lens, Hq, Hkv, D, nq=nq, seed=100 + ci, device=device, bits=bits)
     out, lse = c.run_gpu(part)
     ref, ref_lse = c.run_oracle()
     err = np.abs(out - ref).max()
@@ -192,14 +215,14 @@ def test_q8_bad_table_and_short_context_give_nan(device):
     assert np.abs(out[0].reshape(-1, 128) - ref).max() <= 1e-2
 
 
-def test_q8_full_size_sampled(device):
+@pytest.mark.parametrize("name,bits", [("llama3_8b_b32_8k_q8", 8), ("llama3_8b_b32_8k_q3", 3)])
+def test_q8_full_size_sampled(name, bits, device):
     """The 8K decode batch (32 sequences, Llama-3-8B layer geometry) over an
-    8-bit code cache, in the launch configuration bench.py times: slots and
-    tables bit for bit, the codes of four sequences bit for bit, and their
-    rows against the C oracle."""
+    8-bit (3-bit) code cache, in the launch configuration bench.py times:
+    slots and tables bit for bit, the codes of four sequences bit for bit,
+    and their rows against the C oracle."""
     import bench
 
-    name = "llama3_8b_b32_8k_q8"
     print(f"q8 full size: {name}", flush=True)
     wk = bench.Workload(name, 1, device)
     opool = PagedPool(wk.w.num_blocks, wk.bs, wk.stack.tolist())
@@ -233,9 +256,11 @@ def test_q8_full_size_sampled(device):
         tok = np.arange(starts[b], starts[b] + wk.lens[b])
         sl = list(pre_slots[pre_off[b]:pre_off[b + 1]]) + [step_slots[b]]
         quant.cache_write_q(kc, vc, ks, vs, widen(kbits[tok], "bf16"), widen(vbits[tok], "bf16"),
-                            sl, wk.bs)
+                            sl, wk.bs, bits=bits)
     g = wk.qc[0]
     gk, gks = g.k_codes.cpu().numpy(), g.k_scales.cpu().numpy()
+    if bits == 3:
+        gk = unpack3(gk)
     for b in seqs:
         for blk in tables[b][:-(-int(lens[b]) // wk.bs)]:
             assert np.array_equal(gk[blk], kc[blk]) and np.array_equal(gks[blk], ks[blk])
