@@ -1019,21 +1019,26 @@ decode_partition_kernel(const DecodeArgs a) {
 
   // Pipeline: up to kSlots tiles are gathered into the wavefront's LDS ring
   // ahead of the one being consumed; a slot is refilled as soon as its tile
-  // has been read back. Block ids are read one tile before their gather.
+  // has been read back.
   const int n_tiles = t_begin + wave * kTile < t_end
                           ? (t_end - (t_begin + wave * kTile) + kStride - 1) / kStride
                           : 0;
   auto tile_t0 = [&](int k) { return t_begin + wave * kTile + k * kStride; };
-  auto table_at = [&](int k) {
-    return load_const(trow + tile_t0(k < n_tiles ? k : n_tiles - 1) / a.bs);
+  // Block ids: lane i holds that of this wavefront's tile 64 w + i of the
+  // current window w (one vector load per 64 tiles, read out with
+  // v_readlane; no scalar load inside the loop).
+  auto table_window = [&](int w) {
+    return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
   };
   if (n_tiles > 0) {
+    int tblv = table_window(0);
+    settle_v(tblv);
+    auto table_at = [&](int k) { return __builtin_amdgcn_readlane(tblv, k & 63); };
     Ring ring;
     ring.init((PKV_LDS char *)&sm.ring[0] + wave * Ring::kBytes, lane);
 #pragma unroll
     for (int k = 0; k < kSlots; ++k)
       if (k < n_tiles) stage_tile(ring, k, tile_t0(k), table_at(k));
-    int blk_next = table_at(kSlots);
     // the scale is waited for here, not at its first use inside the loop,
     // where the wait would also catch each step's block-id read
     float scale_log2 = a.scale_log2;
@@ -1059,8 +1064,12 @@ decode_partition_kernel(const DecodeArgs a) {
             else
               ring.template fetch<1>(slot, ahead, vr);
             if (k + kSlots < n_tiles) {  // the slot is free again: refill it
-              stage_tile(ring, slot, tile_t0(k + kSlots), blk_next);
-              blk_next = table_at(k + kSlots + 1);
+              const int kn = k + kSlots;
+              if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
+                tblv = table_window(kn >> 6);
+                settle_v(tblv);
+              }
+              stage_tile(ring, slot, tile_t0(kn), table_at(kn));
             }
           },
           tile_t0(k), scale_log2,
