@@ -1,0 +1,73 @@
+"""The decode step under HIP graph capture.
+
+Every entry point allocates nothing and clears nothing (no memset nodes), so
+a step -- the slot-mapped cache write and a split-K attention call, or the
+same over a cache of 8-bit codes -- can be captured once and replayed. Each
+replay, with eager work and synchronisation between replays, must equal the
+eager result bit for bit (same kernels, same order of arithmetic).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_202_amd as pkv
+from scenario import Case
+
+pytestmark = pytest.mark.gpu
+
+
+def replay_matches(step, out, device, replays=3):
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    out.fill_(float("nan"))
+    stream = torch.cuda.Stream(device=device)  # default priority
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    for i in range(replays):
+        out.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i} differs from the eager step"
+
+
+def test_decode_step_replays(device):
+    print("graph: cache write + split-K decode", flush=True)
+    case = Case((300, 1000, 77), 32, 8, 128, 16, "bf16", seed=11, stack_seed=11, device=device)
+    out = torch.empty((case.B, 1, case.Hq, case.D), dtype=torch.float32, device=device)
+    n = pkv.paged_attention_workspace_size(case.B, 1, case.Hq, case.Hkv, case.D,
+                                           case.max_blocks, case.bs, 128)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    k_new, v_new = case.k_new.to(device), case.v_new.to(device)
+
+    def step():
+        pkv.paged_cache_write(k_new, v_new, case.k_cache, case.v_cache, case.d_slots)
+        pkv.paged_attention_decode(out, case.d_q, case.k_cache, case.v_cache, case.d_tables,
+                                   case.d_lens, case.scale, partition_tokens=128,
+                                   workspace=ws)
+
+    replay_matches(step, out, device)
+    ref, _ = case.run_oracle()
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-2
+
+
+def test_code_cache_decode_replays(device):
+    print("graph: 8-bit code cache write + decode", flush=True)
+    case = Case((300, 1000, 77), 32, 8, 128, 16, "bf16", seed=12, stack_seed=12, device=device)
+    cache = pkv.Q8Cache(case.num_blocks, case.Hkv, case.bs, case.D, device)
+    out = torch.empty((case.B, 1, case.Hq, case.D), dtype=torch.float32, device=device)
+    k_new, v_new = case.k_new.to(device), case.v_new.to(device)
+
+    def step():
+        pkv.paged_cache_write_q8(k_new, v_new, cache, case.d_slots)
+        pkv.paged_attention_decode_q8(out, case.d_q, cache, case.d_tables, case.d_lens,
+                                      case.scale)
+
+    replay_matches(step, out, device)
