@@ -536,7 +536,7 @@ def main() -> int:
     if args.summarize_profile:
         return summarize_profile(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each GPU would run its own pool and sequences with no exchange).",
               file=sys.stderr)
         return 2

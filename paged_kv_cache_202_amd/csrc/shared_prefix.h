@@ -10,7 +10,7 @@
 // rest of every context is handled by the ordinary kernels from the
 // group's prefix length on, and a log-sum-exp merge joins the two.
 //
-// Design (this build's, for CDNA4):
+// Design (for CDNA4):
 //   * the query rows of all members of a group are stacked: a 16-row MFMA
 //     tile holds 16 / RPM members' rows (RPM = G x query tokens, padded to a
 //     power of two). One workgroup = W wavefronts = W row tiles of the same

@@ -8,7 +8,7 @@
 // online; "NeuralOps v1.3.4", Speculative Decoding Pipeline, names the
 // single-pass parallel verification this serves.
 //
-// Design (this build's, for CDNA4):
+// Design (for CDNA4):
 //   * one workgroup of kWaves wavefronts per (partition, KV head, sequence);
 //     wavefronts take interleaved 16-token tiles, merged in LDS at the end;
 //   * per tile, S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (D/32 of them):

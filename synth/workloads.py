@@ -28,7 +28,7 @@ import numpy as np
 
 SEED = 20260801
 
-# Bytes per element for the cache dtypes this build supports.
+# Bytes per element of the floating-point cache dtypes.
 DTYPE_BYTES = {"f32": 4, "bf16": 2}
 
 
