@@ -97,7 +97,7 @@ def kernel_label(wk) -> str:
     """Which launches one attention call makes, as the library plans them."""
     if getattr(wk, "q8", False):
         kind = "int8" if wk.w.kv_codes == 8 else "3-bit"
-        return f"decode_partition_kernel<{kind} codes> (one launch per attention call)"
+        return f"codes_mfma_kernel<{kind} codes> (one launch per attention call)"
     if is_chunk(wk):
         return "chunk_mfma_kernel + reduce_partitions_kernel"
     mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16

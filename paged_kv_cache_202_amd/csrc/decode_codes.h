@@ -1,0 +1,543 @@
+#pragma once
+// Paged attention decode over caches of 8-bit or 3-bit per-row codes, on
+// the matrix cores (gfx950). Same contract and partials as the partition
+// kernel of decode_kernel.h, instantiated in decode_inst_codes_d<D>.hip.
+//
+// What it computes: attention of each sequence's query rows over its paged
+// K/V (vLLM abstract on the papers page "external vector cache"; causal
+// visibility of several query tokens: course page "Module 10. KV Caches and
+// Efficient Inference", notebook section 2), with every K and V element
+// taken as code * its row's scale -- the reconstruction of that page's
+// project demo (Demo 2) quantizer.
+//
+// Design (for CDNA4; the pages give no kernel): per 16-token tile the VALU
+// form spends about 340 vector instructions per wavefront (code widening,
+// 64 dot2, reduce-scatter, broadcast weights, 128 FMAs), and at 16 lanes
+// per SIMD that costs as long as the tile's HBM traffic. Here both products
+// run on MFMA and the VALU only widens codes and runs the softmax:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = a token's codes
+//     widened to fp16 (lane l: token l % 16, a quarter of its row), B = the
+//     query rows as fp16 (row l % 16, the same quarter). The output leaves
+//     lane l the scores of row l % 16 for tokens 4 (l / 16) .. + 3.
+//   * those four weights, times their tokens' V scales, are the B operand
+//     of O^T += V^T P^T (v_mfma_f32_16x16x16_f16) as they stand. The A
+//     operand (4 tokens x 1 dim per lane) comes from the gfx950 transposing
+//     LDS read ds_read_b64_tr_b8: in each 16-lane group, lane i receives
+//     byte i % 8 of the 8 bytes named by lanes i / 8 + 2 u, u = 0..7, so
+//     one read gives a lane 4 tokens of two 16-dim column blocks.
+//   * codes widen exactly: (code ^ 0x80) in the low byte of fp16 0x64xx is
+//     1152 + code (8 bits); the offsets are removed once per score
+//     (1152 x sum q) and once per output (1152 x the sum of the fp16
+//     weights used). A stored nibble (code + 8) there is 1032 + code, and
+//     one packed fp16 add takes it to the code itself: next to codes of at
+//     most 3 an offset of 1032 would cancel too many bits of the fp32 sums.
+//   * 3-bit codes, two per byte (dim 2 i in the low nibble of byte i): the
+//     same tile scheme on rows of D / 2 bytes. A K word (8 dims) widens
+//     low nibbles then high nibbles, so the query's dims are taken in that
+//     order too; a transposed V byte gives two dims (2 c, 2 c + 1), so one
+//     read feeds four output column blocks whose rows interleave.
+//   * up to 16 query rows (G x query tokens) per wavefront at no extra MFMA
+//     work; the staging, ring, lazy softmax and partials are the partition
+//     kernel's. K rows are stored in the LDS ring with their 16-byte chunks
+//     permuted per token (chunk c of token t at c ^ (t mod 16-chunk count))
+//     so the per-token reads of the A operand spread over the LDS banks.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "decode_kernel.h"
+
+namespace pkv {
+namespace decode {
+
+typedef _Float16 h16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8_t __attribute__((ext_vector_type(8)));
+typedef float c32x4_t __attribute__((ext_vector_type(4)));
+
+// Byte geometry of a tile whose token rows are RB bytes (D for 8-bit codes,
+// D / 2 for 3-bit ones).
+template <int RB>
+struct CodeGeo {
+  static constexpr int CPT = RB / 16;   // 16-byte chunks per token row
+  static constexpr int TPL = 64 / CPT;  // tokens per 1 KiB load row
+  static constexpr int NL = kTile / TPL;  // load rows per half tile
+  static constexpr int KCH = CPT / 4;   // K chunks a lane reads (a quarter row)
+  static constexpr int NV = RB / 32;    // transposing V reads per tile
+  static_assert(CPT >= 4 && CPT <= 16 && NL >= 1, "rows of 64, 128 or 256 bytes");
+};
+
+// This lane's byte offset inside a tile's K rows for the gathers: lane i
+// of a load row fetches chunk (i % CPT) ^ s of token i / CPT of that row,
+// s = (i / CPT) % CPT, so that LDS position p of token t holds chunk
+// p ^ s(t) (the permutation depends only on the token's place in its row).
+template <int RB>
+__device__ __forceinline__ int code_k_lane_offset(int lane) {
+  using Gc = CodeGeo<RB>;
+  const int tl = lane / Gc::CPT, p = lane % Gc::CPT;
+  return tl * RB + 16 * (p ^ (tl % Gc::CPT));
+}
+
+// One tile's operands from an LDS slot, with one wait for all of them.
+// K: this lane's KCH chunks (token l % 16, chunks KCH (l / 16) .. + KCH - 1,
+// at LDS offsets ka[c]); V: NV transposing reads at va + 32 j; scales: the
+// K and V scales of tokens 4 (l / 16) .. + 3. RB: bytes per token row.
+template <int RB>
+__device__ __forceinline__ void read_codes(u32x4_t (&k)[CodeGeo<RB>::KCH],
+                                           uint2 (&v)[CodeGeo<RB>::NV], float4 &ks,
+                                           float4 &vs, const PKV_LDS char *const (&ka)[CodeGeo<RB>::KCH],
+                                           const PKV_LDS char *va, const PKV_LDS char *sa);
+
+template <>
+__device__ __forceinline__ void read_codes<64>(u32x4_t (&k)[1], uint2 (&v)[2], float4 &ks,
+                                               float4 &vs, const PKV_LDS char *const (&ka)[1],
+                                               const PKV_LDS char *va, const PKV_LDS char *sa) {
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b64_tr_b8 %1, %6\n\t"
+      "ds_read_b64_tr_b8 %2, %6 offset:32\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "ds_read_b128 %4, %7 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(ks), "=&v"(vs)
+      : "v"(ka[0]), "v"(va), "v"(sa)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_codes<128>(u32x4_t (&k)[2], uint2 (&v)[4], float4 &ks,
+                                                float4 &vs, const PKV_LDS char *const (&ka)[2],
+                                                const PKV_LDS char *va, const PKV_LDS char *sa) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b64_tr_b8 %2, %10\n\t"
+      "ds_read_b64_tr_b8 %3, %10 offset:32\n\t"
+      "ds_read_b64_tr_b8 %4, %10 offset:64\n\t"
+      "ds_read_b64_tr_b8 %5, %10 offset:96\n\t"
+      "ds_read_b128 %6, %11\n\t"
+      "ds_read_b128 %7, %11 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+        "=&v"(ks), "=&v"(vs)
+      : "v"(ka[0]), "v"(ka[1]), "v"(va), "v"(sa)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_codes<256>(u32x4_t (&k)[4], uint2 (&v)[8], float4 &ks,
+                                                float4 &vs, const PKV_LDS char *const (&ka)[4],
+                                                const PKV_LDS char *va, const PKV_LDS char *sa) {
+  asm volatile(
+      "ds_read_b128 %0, %14\n\t"
+      "ds_read_b128 %1, %15\n\t"
+      "ds_read_b128 %2, %16\n\t"
+      "ds_read_b128 %3, %17\n\t"
+      "ds_read_b64_tr_b8 %4, %18\n\t"
+      "ds_read_b64_tr_b8 %5, %18 offset:32\n\t"
+      "ds_read_b64_tr_b8 %6, %18 offset:64\n\t"
+      "ds_read_b64_tr_b8 %7, %18 offset:96\n\t"
+      "ds_read_b64_tr_b8 %8, %18 offset:128\n\t"
+      "ds_read_b64_tr_b8 %9, %18 offset:160\n\t"
+      "ds_read_b64_tr_b8 %10, %18 offset:192\n\t"
+      "ds_read_b64_tr_b8 %11, %18 offset:224\n\t"
+      "ds_read_b128 %12, %19\n\t"
+      "ds_read_b128 %13, %19 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
+        "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(ks), "=&v"(vs)
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va), "v"(sa)
+      : "memory");
+}
+
+// Four int8 codes (one word) as four fp16 values 1152 + code.
+__device__ __forceinline__ uint2 codes_f16x4(uint32_t w) {
+  return make_uint2(codes_f16_lo(w), codes_f16_hi(w));
+}
+// Four nibble codes u (the low or high nibbles of a word, masked into byte
+// positions) as four fp16 values 1024 + u.
+__device__ __forceinline__ uint2 nibbles_f16x4(uint32_t n) {
+  return make_uint2(__builtin_amdgcn_perm(0x64646464u, n, 0x04010400u),
+                    __builtin_amdgcn_perm(0x64646464u, n, 0x04030402u));
+}
+// The same as the codes themselves (stored nibble - 8), exactly: with
+// offsets as large as 1032 next to codes of at most 3 the fp32 sums would
+// cancel away too many bits.
+__device__ __forceinline__ uint2 nibble_codes_f16x4(uint32_t n) {
+  const uint2 u = nibbles_f16x4(n);
+  const f16x2_t off = {(_Float16)-1032.f, (_Float16)-1032.f};
+  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u.x) + off),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u.y) + off));
+}
+__device__ __forceinline__ uint32_t low_nibbles(uint32_t w) { return w & 0x0f0f0f0fu; }
+__device__ __forceinline__ uint32_t high_nibbles(uint32_t w) { return (w >> 4) & 0x0f0f0f0fu; }
+
+template <int DT, int D, int RW, int kWaves>
+__global__ void __launch_bounds__(kWaves * 64)
+codes_mfma_kernel(const DecodeArgs a) {
+  constexpr bool kNib = DT == kCodes3;
+  constexpr int RB = kNib ? D / 2 : D;  // bytes per token row
+  using Gc = CodeGeo<RB>;
+  constexpr int NL = Gc::NL, KCH = Gc::KCH, NV = Gc::NV;
+  constexpr int NC = D / 32;   // q.k MFMAs per tile (32 dims each)
+  constexpr int NCB = D / 16;  // 16-dim output column blocks
+  constexpr float kOffset = kNib ? 0.f : 1152.f;  // fp16 form = offset + code
+  constexpr float kNegInf = -std::numeric_limits<float>::infinity();
+  constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
+  using Ring = TileRing<NL, true>;
+  constexpr int kSlots = Ring::kSlots;
+  static_assert(DT == PKV_I8 || DT == kCodes3, "8-bit or 3-bit codes");
+  static_assert(RW == 4 || RW == 8 || RW == 16, "rows per wavefront");
+
+  struct Merge {
+    float acc[kWaves][RW][D];
+    float m[kWaves][RW];
+    float l[kWaves][RW];
+    int bad[kWaves];
+  };
+  __shared__ union {
+    u32x4_t ring[kWaves * Ring::kBytes / 16];
+    Merge mg;
+  } sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15, lg = lane >> 4;  // MFMA column (query row) and lane group
+  const int p = blockIdx.x, b = blockIdx.z;
+  const int g = blockIdx.y % a.Hkv, row0 = (blockIdx.y / a.Hkv) * RW;
+  const int nq = a.nq, G = a.Hq / a.Hkv;
+  const int L = load_const(a.lens + b);
+  const int max_ctx = a.max_blocks * a.bs;
+
+  if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
+    if (a.num_parts == 1 && p == 0) {
+      const float nan = __builtin_nanf("");
+      for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+        const int r = row0 + idx / D, d = idx % D, qi = r / G;
+        if (qi >= nq) continue;
+        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
+        a.out[row * D + d] = nan;
+        if (d == 0 && a.lse) a.lse[row] = nan;
+      }
+    }
+    return;  // with partitions, the reduce kernel writes the NaN rows
+  }
+  const int t_begin = p * a.part_tokens;
+  if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
+  const int t_end = min(L, t_begin + a.part_tokens);
+
+  // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
+  //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA in the order
+  //      the K codes widen, scaled by 2^-e so that the row's largest entry is
+  //      in [2^7, 2^8) (fp16 keeps 11 bits) ---------------------------------
+  const int rr = row0 + ln, qi = rr / G;
+  const bool row_live = ln < RW && qi < nq;
+  uint32_t qb[NC][4];
+  float qcorr, qfac;
+  int lim;  // keys visible to row ln
+  {
+    uint32_t w[D / 8];  // bf16 pairs: dims 2 j, 2 j + 1 of the quarter
+    if (row_live) {
+      const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
+      const uint4 *src =
+          reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + lg * (D / 4));
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j) {
+        const uint4 t = src[j];
+        w[4 * j] = t.x; w[4 * j + 1] = t.y; w[4 * j + 2] = t.z; w[4 * j + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j) w[j] = 0u;
+    }
+    auto qdim = [&](int d) { return d % 2 ? bf16_hi(w[d / 2]) : bf16_lo(w[d / 2]); };
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+    mx = fmaxf(mx, exact_xor<16>(mx));
+    mx = fmaxf(mx, exact_xor<32>(mx));
+    int ex = 0;
+    frexpf(mx, &ex);
+    const int e = mx > 0.f ? ex - 8 : 0;
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1) for 8-bit
+        // codes; low nibbles (dims 0, 2, 4, 6) then high ones for 3-bit
+        const int d0 = kNib ? 8 * c + (j < 2 ? 4 * j : 4 * (j - 2) + 1) : 8 * c + 2 * j;
+        const int d1 = kNib ? d0 + 2 : d0 + 1;
+        const _Float16 lo = (_Float16)ldexpf(qdim(d0), -e);
+        const _Float16 hi = (_Float16)ldexpf(qdim(d1), -e);
+        sum += (float)lo + (float)hi;
+        qb[c][j] = __builtin_bit_cast(uint32_t, f16x2_t{lo, hi});
+      }
+    sum += exact_xor<16>(sum);
+    sum += exact_xor<32>(sum);
+    qcorr = kOffset * sum;
+    qfac = ldexpf(1.f, e) * a.scale_log2;
+    lim = row_live ? L - nq + qi + 1 : 0;
+  }
+
+  const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
+  const char *kbase = (const char *)a.kc;
+  const char *vbase = (const char *)a.vc;
+  const int koff = code_k_lane_offset<RB>(lane);
+  int bad = 0;
+  // gather the tile at logical token t0 (from block blk) into a ring slot
+  auto stage_tile = [&](Ring &ring, int slot, int t0, int blk) {
+    if (blk < 0 || blk >= a.num_blocks) {  // bad table entry: read block 0, poison later
+      bad = 1;
+      blk = 0;
+    }
+    const size_t rowi = ((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs);
+    const size_t so = rowi * 4 + (size_t)(lane & 15) * 4;
+    ring.stage(slot, kbase + rowi * RB + koff, vbase + rowi * RB + lane * 16,
+               (const char *)((lane & 16) ? a.vs : a.ks) + so);
+  };
+
+  const int n_tiles = t_begin + wave * kTile < t_end
+                          ? (t_end - (t_begin + wave * kTile) + kStride - 1) / kStride
+                          : 0;
+  auto tile_t0 = [&](int k) { return t_begin + wave * kTile + k * kStride; };
+  auto table_window = [&](int w) {
+    return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
+  };
+
+  // O^T accumulators, offsets included: o[cb][e] = O^T[m = 4 lg + e][row ln]
+  // of column block cb (8-bit: dim 16 cb + m; 3-bit: see the merge below)
+  c32x4_t o[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) o[cb] = c32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_row = kNegInf, l_part = 0.f, w_part = 0.f;
+
+  if (n_tiles > 0) {
+    int tblv = table_window(0);
+    settle_v(tblv);
+    auto table_at = [&](int k) { return __builtin_amdgcn_readlane(tblv, k & 63); };
+    Ring ring;
+    PKV_LDS char *ring_base = (PKV_LDS char *)&sm.ring[0] + wave * Ring::kBytes;
+    ring.init(ring_base, lane);
+    // read-back addresses inside slot 0 (a slot adds slot * kTileBytes)
+    const PKV_LDS char *ka[KCH];
+    {
+      const int t = ln, tl = t % Gc::TPL;
+      const PKV_LDS char *row = ring_base + (t / Gc::TPL) * 1024 + tl * RB;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) ka[c] = row + 16 * ((KCH * lg + c) ^ (tl % Gc::CPT));
+    }
+    // V: lane s of group lg names token 4 lg + (s / 2) % 4, bytes
+    // 16 ((s / 2) / 4) + 8 (s % 2) .. + 7 of each 32-byte column pair
+    const PKV_LDS char *va;
+    {
+      const int u = ln >> 1, t = 4 * lg + (u & 3);
+      va = ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB + 16 * (u >> 2) +
+           8 * (ln & 1);
+    }
+    const PKV_LDS char *sa = ring_base + Ring::kCodeBytes + 16 * lg;
+#pragma unroll
+    for (int k = 0; k < kSlots; ++k)
+      if (k < n_tiles) stage_tile(ring, k, tile_t0(k), table_at(k));
+    const uint32_t ones = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)1.f, (_Float16)1.f});
+
+    for (int k = 0; k < n_tiles; ++k) {
+      const int slot = k & (kSlots - 1);
+      const int ahead = min(n_tiles - 1 - k, kSlots - 1);
+      static_for<kSlots>([&](auto ac) {
+        constexpr int A = decltype(ac)::value;
+        if (ahead == A) wait_vmcnt<A * Ring::kLoads>();
+      });
+      u32x4_t kr[KCH];
+      uint2 vt[NV];
+      float4 ksc, vsc;
+      {
+        const int so = slot * Ring::kTileBytes;
+        const PKV_LDS char *kas[KCH];
+#pragma unroll
+        for (int c = 0; c < KCH; ++c) kas[c] = ka[c] + so;
+        read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
+      }
+      if (k + kSlots < n_tiles) {  // the slot is free again: refill it
+        const int kn = k + kSlots;
+        if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
+          tblv = table_window(kn >> 6);
+          settle_v(tblv);
+        }
+        stage_tile(ring, slot, tile_t0(kn), table_at(kn));
+      }
+
+      // S^T = K Q^T: s[e] = row ln . token 4 lg + e (codes with offsets)
+      c32x4_t s = c32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        u32x4_t av;
+        if constexpr (kNib) {  // one word: 8 dims, low nibbles first
+          const u32x4_t kw = kr[c / 4];
+          const uint32_t wd = kw[c % 4];
+          const uint2 lo = nibble_codes_f16x4(low_nibbles(wd));
+          const uint2 hi = nibble_codes_f16x4(high_nibbles(wd));
+          av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        } else {  // two words: 8 dims in order
+          const u32x4_t kw = kr[c / 2];
+          const uint2 lo = codes_f16x4(kw[2 * (c % 2)]), hi = codes_f16x4(kw[2 * (c % 2) + 1]);
+          av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+        const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8_t, av),
+                                                   __builtin_bit_cast(h16x8_t, bv), s, 0, 0, 0);
+      }
+      const int t0 = tile_t0(k);
+      const float kss[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
+      const float vss[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
+      float sc[4];
+      bool need = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool vis = t0 + 4 * lg + e < lim;
+        sc[e] = vis ? (s[e] - qcorr) * (kss[e] * qfac) : kNegInf;
+        need |= sc[e] > m_row + kLazyLog2;
+      }
+      if (__any(need)) {  // raise the running maximum of row ln
+        float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        tmax = fmaxf(tmax, exact_xor<16>(tmax));
+        tmax = fmaxf(tmax, exact_xor<32>(tmax));
+        const float mn = fmaxf(m_row, tmax);
+        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row - mn);
+        m_row = mn;
+        l_part *= alpha;
+        w_part *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+      }
+      // exp2(-inf) = 0 for masked scores; the maximum is floored so that a
+      // row with no visible key yet gives 0, not NaN
+      const float m_sub = fmaxf(m_row, -3.0e38f);
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);
+        l_part += pw;
+        // the V scale of a masked token may be stale: never multiplied
+        pv[e] = sc[e] == kNegInf ? 0.f : pw * vss[e];
+      }
+      const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
+      const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
+      // the fp16 weights' sum: what the V offsets add, removed at the end
+      if constexpr (!kNib) w_part = dot2_f16(p01, ones, dot2_f16(p23, ones, w_part));
+      const h16x4_t pb = __builtin_bit_cast(h16x4_t, make_uint2(p01, p23));
+
+      // O^T += V^T P^T: A = V[tokens 4 lg .. + 3][one dim per lane]
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        if constexpr (kNib) {  // bytes 32 j + ln and 32 j + 16 + ln: four dims
+          const uint32_t x = vt[j].x, y = vt[j].y;
+          o[4 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(low_nibbles(x))), pb, o[4 * j], 0, 0, 0);
+          o[4 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(high_nibbles(x))), pb, o[4 * j + 1], 0,
+              0, 0);
+          o[4 * j + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(low_nibbles(y))), pb, o[4 * j + 2], 0,
+              0, 0);
+          o[4 * j + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(high_nibbles(y))), pb, o[4 * j + 3], 0,
+              0, 0);
+        } else {  // dims 32 j + ln and 32 j + 16 + ln
+          o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].x)), pb, o[2 * j], 0, 0, 0);
+          o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].y)), pb, o[2 * j + 1], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- wavefront totals: row ln's weight sums over the four lane groups,
+  //      the V offsets removed, then the merge of the wavefronts in LDS -----
+  l_part += exact_xor<16>(l_part);
+  l_part += exact_xor<32>(l_part);
+  w_part += exact_xor<16>(w_part);
+  w_part += exact_xor<32>(w_part);
+  const float off = -kOffset * w_part;
+  __syncthreads();  // the partials overwrite the other wavefronts' rings
+  if (ln < RW) {
+    float *dst = sm.mg.acc[wave][ln];
+    if constexpr (kNib) {
+      // block 4 j + 2 h + n holds dim 64 j + 32 h + 2 m + n (m = 4 lg + e):
+      // the two nibble blocks interleave into 8 consecutive dims
+#pragma unroll
+      for (int jh = 0; jh < NCB / 2; ++jh) {
+        const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
+        float *q8 = dst + 32 * jh + 8 * lg;
+        *reinterpret_cast<float4 *>(q8) =
+            make_float4(lo[0] + off, hi[0] + off, lo[1] + off, hi[1] + off);
+        *reinterpret_cast<float4 *>(q8 + 4) =
+            make_float4(lo[2] + off, hi[2] + off, lo[3] + off, hi[3] + off);
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
+            make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
+    }
+    if (lg == 0) {
+      sm.mg.m[wave][ln] = m_row;
+      sm.mg.l[wave][ln] = l_part;
+    }
+  }
+  bad = __builtin_amdgcn_readfirstlane(bad);
+  if (lane == 0) sm.mg.bad[wave] = bad;
+  __syncthreads();
+
+  int any_bad = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) any_bad |= sm.mg.bad[w];
+  const float nan = __builtin_nanf("");
+  for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+    const int r = idx / D, d = idx % D, rrow = row0 + r, qr = rrow / G;
+    if (qr >= nq) continue;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][r]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm.mg.m[w][r];
+      const float f = mw == kNegInf ? 0.f : exp2f(mw - M);
+      num = fmaf(f, sm.mg.acc[w][r][d], num);
+      den = fmaf(f, sm.mg.l[w][r], den);
+    }
+    const size_t row = ((size_t)b * nq + qr) * a.Hq + g * G + (rrow % G);
+    if (a.num_parts == 1) {
+      a.out[row * D + d] = any_bad || den == 0.f ? nan : num / den;
+      if (d == 0 && a.lse) a.lse[row] = any_bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
+    } else {
+      const size_t pi = row * a.num_parts + a.part_base + p;
+      a.part_acc[pi * D + d] = num;
+      if (d == 0) {
+        a.part_m[pi] = any_bad ? nan : M;
+        a.part_l[pi] = den;
+      }
+    }
+  }
+}
+
+template <int DT, int D, int RW, int W>
+void launch_codes(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
+  constexpr int RB = DT == kCodes3 ? D / 2 : D;
+  static_assert(W * TileRing<CodeGeo<RB>::NL, true>::kBytes <= 163840, "LDS of the rings");
+  hipLaunchKernelGGL((codes_mfma_kernel<DT, D, RW, W>), grid, dim3(W * 64), 0, s, a);
+}
+
+// Launcher of the MFMA kernel over codes (DT = PKV_I8 or kCodes3) for head
+// dim D, RW query rows per wavefront (4, 8 or 16) and W wavefronts per
+// workgroup (1, 4 or 8); nullptr if none. Defined in
+// decode_inst_codes_d<D>.hip.
+template <int D>
+Launcher pick_codes(int DT, int RW, int W);
+
+}  // namespace decode
+}  // namespace pkv
