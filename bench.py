@@ -37,26 +37,37 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, decimal GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
-KERNEL_SOURCES = ["paged_kv_cache_202_amd/csrc/decode_kernel.h",
-                  "paged_kv_cache_202_amd/csrc/decode_inst_bf16_d128.hip",
-                  "paged_kv_cache_202_amd/csrc/decode.hip"]
+def kernel_sources(workload: str) -> list:
+    """The sources whose code a workload's dominant kernel is built from: the
+    bf16/fp32 partition kernel, or the matrix-core kernel over code caches."""
+    from synth.workloads import WORKLOADS
+
+    csrc = "paged_kv_cache_202_amd/csrc/"
+    if WORKLOADS[workload].kv_codes:
+        return [csrc + "decode_kernel.h", csrc + "decode_codes.h",
+                csrc + "decode_inst_codes_d128.hip", csrc + "decode.hip"]
+    return [csrc + "decode_kernel.h", csrc + "decode_inst_bf16_d128.hip", csrc + "decode.hip"]
+
+
+def sources_sha256(workload: str) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for src in kernel_sources(workload):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def profiled_traffic(workload: str):
     """HBM bytes per attention call from the committed rocprofv3 counter summary,
     or None when there is none or the kernel sources changed since it was taken."""
-    import hashlib
-
     path = os.path.join(ROOT, "profiles", f"decode_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         prof = json.load(f)
-    h = hashlib.sha256()
-    for src in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
-    if h.hexdigest() != prof.get("kernel_sources_sha256"):
+    if sources_sha256(workload) != prof.get("kernel_sources_sha256"):
         return None
     return prof["traffic_bytes_per_launch"]
 
@@ -456,8 +467,6 @@ def summarize_profile(args) -> int:
     dispatch (--pmc FETCH_SIZE, WRITE_SIZE) scaled by what the same counters
     read for a plain copy of known size (--copy-probe), and a hash of the
     kernel sources they were taken on."""
-    import hashlib
-
     kre = args.kernel_regex
     stats = [r for r in _csv_rows(args.trace_dir, "kernel_stats.csv") if re.search(kre, r["Name"])]
     if len(stats) != 1:
@@ -469,10 +478,6 @@ def summarize_profile(args) -> int:
     cwrite, _ = _counter_per_dispatch(args.copy_write_dir, "WRITE_SIZE", "copy_blocks")
     moved = 2 * args.copy_mib * 2**20  # K and V, read once and written once
     ffac, wfac = moved / (cfetch * 1024), moved / (cwrite * 1024)
-    h = hashlib.sha256()
-    for src in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, src), "rb") as f:
-            h.update(f.read())
     from synth.workloads import WORKLOADS
 
     w = WORKLOADS[args.workload]
@@ -482,7 +487,7 @@ def summarize_profile(args) -> int:
     out = {
         "kernel": st["Name"],
         "workload": args.workload,
-        "kernel_sources_sha256": h.hexdigest(),
+        "kernel_sources_sha256": sources_sha256(args.workload),
         "trace": {"calls": int(st["Calls"]), "avg_ns": float(st["AverageNs"]),
                   "min_ns": float(st["MinNs"]), "max_ns": float(st["MaxNs"])},
         "pmc": {"FETCH_SIZE_kib_per_dispatch": fetch, "WRITE_SIZE_kib_per_dispatch": write,

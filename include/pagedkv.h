@@ -296,8 +296,8 @@ int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
  * Demo 2 reconstruction), dequantized inside the kernel. q is bf16
  * [B, nq, Hq, D]; out, lse, tables, lengths, partition_tokens and workspace
  * as there (paged_attention_workspace_size gives the size; -1 is taken as 0
- * here). Rows per KV head: G * nq rounded up to a power of two <= 16 (VALU
- * kernels, at most 4 rows per wavefront). Scale arrays 16-byte aligned.
+ * here). Rows per KV head: G * nq rounded up to a power of two <= 16 (one
+ * matrix-core wavefront holds them all). Scale arrays 16-byte aligned.
  * Host-checked as paged_attention_decode -> EINVAL. */
 int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
                               const int8_t *v_codes, const float *k_scales,

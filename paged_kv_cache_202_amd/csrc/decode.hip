@@ -263,13 +263,6 @@ Launcher pick_launcher(int dtype, int D, int G, int RP, int W) {
     if (D == 64) return pick_rows<PKV_BF16, 64>(G, RP, W);
     if (D == 128) return pick_rows<PKV_BF16, 128>(G, RP, W);
     if (D == 256) return pick_rows<PKV_BF16, 256>(G, RP, W);
-  } else if (dtype == PKV_I8) {
-    if (D == 64) return pick_rows<PKV_I8, 64>(G, RP, W);
-    if (D == 128) return pick_rows<PKV_I8, 128>(G, RP, W);
-    if (D == 256) return pick_rows<PKV_I8, 256>(G, RP, W);
-  } else if (dtype == kCodes3) {
-    if (D == 128) return pick_rows<kCodes3, 128>(G, RP, W);
-    if (D == 256) return pick_rows<kCodes3, 256>(G, RP, W);
   }
   return nullptr;
 }

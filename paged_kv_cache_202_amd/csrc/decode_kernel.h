@@ -88,17 +88,6 @@ __device__ __forceinline__ uint32_t codes_f16_lo(uint32_t w) {
 __device__ __forceinline__ uint32_t codes_f16_hi(uint32_t w) {
   return __builtin_amdgcn_perm(0x64646464u, w ^ 0x80808080u, 0x04030402u);
 }
-// Byte k (0..3) of w as a float (unsigned).
-template <int K>
-__device__ __forceinline__ float code_u8(uint32_t w) {
-  return (float)((w >> (8 * K)) & 0xffu);
-}
-// Code k (0..3) of w as a float: the signed byte, widened.
-template <int K>
-__device__ __forceinline__ float code_f32(uint32_t w) {
-  return (float)(int8_t)(uint8_t)(w >> (8 * K));
-}
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
@@ -205,14 +194,13 @@ constexpr int kCodes3 = 3;
 // Geometry of one (dtype, head dim) pair as seen by a wavefront.
 template <int DT, int D>
 struct Geo {
-  // bytes per element: fp32, bf16, or int8 codes (3-bit codes: half a byte)
-  static constexpr int ES = DT == PKV_F32 ? 4 : DT == PKV_I8 || DT == kCodes3 ? 1 : 2;
-  static constexpr int TB = DT == kCodes3 ? D / 2 : D * ES;  // bytes per token row
-  static constexpr int LB = DT == kCodes3 ? 8 : 16;  // bytes of a row a lane holds
+  static constexpr int ES = DT == PKV_F32 ? 4 : 2;  // bytes per element (fp32, bf16)
+  static constexpr int TB = D * ES;                   // bytes per token row
+  static constexpr int LB = 16;                       // bytes of a row a lane holds
   static constexpr int LPT = TB / LB;                // lanes sharing one token
   static constexpr int TPL = 64 / LPT;               // tokens per load row
   static constexpr int NL = kTile / TPL;             // loads per lane per tile
-  static constexpr int EPL = DT == kCodes3 ? 16 : 16 / ES;  // elements per lane per load
+  static constexpr int EPL = 16 / ES;  // elements per lane per load
   static_assert(LPT >= 1 && LPT <= 64 && 64 % LPT == 0, "unsupported head size");
   static_assert(NL >= 1, "a tile must cover whole loads");
 };
@@ -241,8 +229,9 @@ struct DecodeArgs {
   const int32_t *starts;
   int32_t part_base;
   int32_t prefix_part;
-  // Caches of int8 codes only (else nullptr): the float32 scale of each
-  // (block, KV head, slot) row of K and of V, [num_blocks, Hkv, bs].
+  // Caches of codes only (the matrix-core code kernel; else nullptr): the
+  // float32 scale of each (block, KV head, slot) row of K and of V,
+  // [num_blocks, Hkv, bs].
   const float *ks;
   const float *vs;
 };
@@ -391,7 +380,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int NL, bool SC = false>
 struct TileRing {
   static constexpr int kCodeBytes = 2 * NL * 1024;
-  // with per-row scales (int8 codes), after the K and V rows: the tile's 16
+  // with per-row scales (code caches), after the K and V rows: the tile's 16
   // K scales, its 16 V scales, and 128 bytes the other lanes of their
   // 4-byte gather fill with copies (every lane takes part: a gather under a
   // lane mask could be split by the compiler into several instructions,
@@ -427,46 +416,6 @@ struct TileRing {
       gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
   }
 
-  // fetch<HALF> and, in the same wait, the scale of token tok of the tile
-  // (K scale for HALF = 0, V scale for HALF = 1): one LDS round trip.
-  template <int HALF>
-  __device__ __forceinline__ void fetch_sc(int slot, int ahead, uint4 (&r)[NL], int tok,
-                                           float &sc) const {
-    static_assert(SC, "tiles without scales");
-    static_for<kSlots>([&](auto ac) {
-      constexpr int A = decltype(ac)::value;
-      if (ahead == A) wait_vmcnt<A * kLoads + (HALF == 0 ? NL : 0)>();
-    });
-    const PKV_LDS char *p = mine + slot * kTileBytes + HALF * NL * 1024;
-    const PKV_LDS char *ps = base + slot * kTileBytes + kCodeBytes + HALF * 64 + tok * 4;
-    u32x4_t t[NL];
-    if constexpr (NL == 1) {
-      asm volatile(
-          "ds_read_b128 %0, %2\n\tds_read_b32 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-          : "=&v"(t[0]), "=&v"(sc)
-          : "v"(p), "v"(ps)
-          : "memory");
-    } else if constexpr (NL == 2) {
-      asm volatile(
-          "ds_read_b128 %0, %3\n\tds_read_b128 %1, %3 offset:1024\n\t"
-          "ds_read_b32 %2, %4\n\ts_waitcnt lgkmcnt(0)"
-          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(sc)
-          : "v"(p), "v"(ps)
-          : "memory");
-    } else {
-      static_assert(NL == 4, "1, 2 or 4 rows per lane");
-      asm volatile(
-          "ds_read_b128 %0, %5\n\tds_read_b128 %1, %5 offset:1024\n\t"
-          "ds_read_b128 %2, %5 offset:2048\n\tds_read_b128 %3, %5 offset:3072\n\t"
-          "ds_read_b32 %4, %6\n\ts_waitcnt lgkmcnt(0)"
-          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(sc)
-          : "v"(p), "v"(ps)
-          : "memory");
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) r[i] = make_uint4(t[i].x, t[i].y, t[i].z, t[i].w);
-  }
-
   // Read back the K half (HALF = 0) or the V half (HALF = 1) of the tile in
   // `slot` once its gathers have landed. `ahead` (wavefront-uniform, below
   // kSlots) whole tiles were staged after it and stay in flight:
@@ -495,77 +444,6 @@ struct TileRing {
   }
 };
 
-// Ring of tiles of 3-bit codes (two per byte) with their scales: the same
-// scheme as TileRing with scales, but each lane reads back 8 bytes (16
-// codes) of a token row per load: the tile's K rows (NL loads of 512 bytes)
-// arrive by 16-byte gathers, NL / 2 per half, in the order they are stored.
-template <int NL>
-struct NibbleRing {
-  static constexpr int kHalfBytes = NL * 512;
-  static constexpr int kGathers = kHalfBytes / 1024;  // per half
-  static constexpr int kCodeBytes = 2 * kHalfBytes;
-  static constexpr int kTileBytes = kCodeBytes + 256;  // + scales, as in TileRing
-  static constexpr int kSlots = kCodeBytes >= 16384 ? 1 : 16384 / kCodeBytes;
-  static constexpr int kBytes = kSlots * kTileBytes;
-  static constexpr int kLoads = 2 * kGathers + 1;
-  static_assert(kHalfBytes % 1024 == 0, "a half must be whole gathers");
-  static_assert((kSlots & (kSlots - 1)) == 0, "slot count must be a power of two");
-
-  PKV_LDS char *base;
-  const PKV_LDS char *mine;  // base + 8 * lane
-
-  __device__ __forceinline__ void init(PKV_LDS char *ring, int lane) {
-    base = ring;
-    mine = ring + lane * 8;
-  }
-
-  // kp / vp: the tile's K / V rows plus 16 * lane; sp as in TileRing.
-  __device__ __forceinline__ void stage(int slot, const char *kp, const char *vp,
-                                        const char *sp) {
-    PKV_LDS char *dst = base + slot * kTileBytes;
-    gather_lds4<kKvNonTemporal>(sp, dst + kCodeBytes);
-#pragma unroll
-    for (int g = 0; g < kGathers; ++g)
-      gather_lds16<kKvNonTemporal>(kp + g * 1024, dst + g * 1024);
-#pragma unroll
-    for (int g = 0; g < kGathers; ++g)
-      gather_lds16<kKvNonTemporal>(vp + g * 1024, dst + kHalfBytes + g * 1024);
-  }
-
-  // The K (HALF = 0) or V (HALF = 1) row pieces of the tile and the scale of
-  // token tok, in one LDS round trip.
-  template <int HALF>
-  __device__ __forceinline__ void fetch_sc(int slot, int ahead, uint2 (&r)[NL], int tok,
-                                           float &sc) const {
-    static_for<kSlots>([&](auto ac) {
-      constexpr int A = decltype(ac)::value;
-      if (ahead == A) wait_vmcnt<A * kLoads + (HALF == 0 ? kGathers : 0)>();
-    });
-    const PKV_LDS char *p = mine + slot * kTileBytes + HALF * kHalfBytes;
-    const PKV_LDS char *ps = base + slot * kTileBytes + kCodeBytes + HALF * 64 + tok * 4;
-    unsigned long long t[NL];
-    if constexpr (NL == 2) {
-      asm volatile(
-          "ds_read_b64 %0, %3\n\tds_read_b64 %1, %3 offset:512\n\t"
-          "ds_read_b32 %2, %4\n\ts_waitcnt lgkmcnt(0)"
-          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(sc)
-          : "v"(p), "v"(ps)
-          : "memory");
-    } else {
-      static_assert(NL == 4, "2 or 4 rows per lane");
-      asm volatile(
-          "ds_read_b64 %0, %5\n\tds_read_b64 %1, %5 offset:512\n\t"
-          "ds_read_b64 %2, %5 offset:1024\n\tds_read_b64 %3, %5 offset:1536\n\t"
-          "ds_read_b32 %4, %6\n\ts_waitcnt lgkmcnt(0)"
-          : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(sc)
-          : "v"(p), "v"(ps)
-          : "memory");
-    }
-#pragma unroll
-    for (int i = 0; i < NL; ++i) r[i] = make_uint2((uint32_t)t[i], (uint32_t)(t[i] >> 32));
-  }
-};
-
 // ---------------------------------------------------------------------------
 // One wavefront's attention state for RP query rows of one KV head:
 // queries, running max / sum and fp32 accumulators, and the per-tile math.
@@ -578,19 +456,11 @@ struct DecodeWave {
   static constexpr int C = V >= LPT ? V / LPT : 1;    // whole scores per lane
   static constexpr int DUP = V >= LPT ? 1 : LPT / V;  // lanes holding the same score
   static constexpr float kNegInf = -std::numeric_limits<float>::infinity();
-  // what one load gives a lane: 16 bytes, or 8 bytes of 3-bit codes
-  using Row = std::conditional_t<DT == kCodes3, uint2, uint4>;
+  using Row = uint4;  // what one load gives a lane: 16 bytes
 
   int lane, grp, jl, d0;
   uint32_t qw[RP][4];  // bf16 query slices, two per word
   float qf[RP][4];     // fp32 query slices
-  // int8 codes: the 16-dim query slice as fp16 pairs, scaled by 2^-e per
-  // row so that it fits fp16; 1152 times the slice's sum (the offset of the
-  // codes' fp16 form); 2^e
-  uint32_t qh[RP][8];
-  float qcorr[RP], qpow[RP];
-  // 3-bit codes: V is accumulated as code + 8; the weights' sum removes the 8
-  float wsum[RP];
   int own_row[C], own_tok[C], own_lim[C];
   float acc[RP][EPL];
   float m_run[RP];
@@ -628,35 +498,6 @@ struct DecodeWave {
         uint4 w = make_uint4(0, 0, 0, 0);
         if (qi < nq) w = *reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
         qw[r][0] = w.x; qw[r][1] = w.y; qw[r][2] = w.z; qw[r][3] = w.w;
-      } else if constexpr (DT == PKV_I8 || DT == kCodes3) {
-        // bf16 queries over int8 (or 3-bit) codes: 16 dims per lane
-        uint4 w0 = make_uint4(0, 0, 0, 0), w1 = w0;
-        if (qi < nq) {
-          const uint4 *src = reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + d0);
-          w0 = src[0];
-          w1 = src[1];
-        }
-        const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        float mx = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(ww[j])), fabsf(bf16_hi(ww[j]))));
-#pragma unroll
-        for (int m = 1; m < LPT; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-        int ex = 0;
-        frexpf(mx, &ex);  // 2^(ex-1) <= mx < 2^ex
-        const int e = mx > 0.f ? ex - 8 : 0;  // the scaled row's largest entry in [2^7, 2^8)
-        float corr = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const _Float16 lo = (_Float16)ldexpf(bf16_lo(ww[j]), -e);
-          const _Float16 hi = (_Float16)ldexpf(bf16_hi(ww[j]), -e);
-          corr += (float)lo + (float)hi;
-          qh[r][j] = __builtin_bit_cast(uint32_t, f16x2_t{lo, hi});
-        }
-        // the codes' fp16 form: 1152 + code (int8), 1032 + code (3-bit)
-        qcorr[r] = (DT == PKV_I8 ? 1152.f : 1032.f) * corr;
-        qpow[r] = ldexpf(1.f, e);
-        wsum[r] = 0.f;
       } else {
         float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
         if (qi < nq) w = *reinterpret_cast<const float4 *>((const float *)a.q + row * D + d0);
@@ -681,7 +522,6 @@ struct DecodeWave {
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
       m_run[r] = kNegInf;
-      wsum[r] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[r][e] = 0.f;
     }
@@ -695,44 +535,9 @@ struct DecodeWave {
   // Consume one 16-token tile starting at logical token t0: its K rows are
   // in kr, and get_v(vr) supplies its V rows once the weights are known (so
   // the V half of a gather may still be landing during the q.k work).
-  // With int8 codes, get_ks / get_vs supply the K / V scales of this lane's
-  // owned tokens (after the K / V rows have been fetched).
-  struct NoScales {
-    __device__ void operator()(float (&)[C]) const {}
-  };
-  template <class GetV, class GetKS = NoScales, class GetVS = NoScales>
+  template <class GetV>
   __device__ __forceinline__ void process(const Row (&kr)[NL], GetV &&get_v, int t0,
-                                          float scale_log2, GetKS get_ks = {},
-                                          GetVS get_vs = {}) {
-    // int8 codes as fp16 pairs (1152 + code), 3-bit codes as (1032 + code),
-    // shared by all rows
-    uint32_t km[NL][8];
-    if constexpr (DT == kCodes3) {
-      // byte b of word j holds dims 8 j + 2 b (low nibble) and 8 j + 2 b + 1
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const uint32_t kw[2] = {kr[i].x, kr[i].y};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t lo = kw[j] & 0x0f0f0f0fu, hi = (kw[j] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            km[i][4 * j + b] =
-                __builtin_amdgcn_perm(hi, lo, 0x0c000c00u | ((4u + b) << 16) | b) | 0x64006400u;
-        }
-      }
-    }
-    if constexpr (DT == PKV_I8) {
-#pragma unroll
-      for (int i = 0; i < NL; ++i) {
-        const uint32_t kw[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          km[i][2 * j] = codes_f16_lo(kw[j]);
-          km[i][2 * j + 1] = codes_f16_hi(kw[j]);
-        }
-      }
-    }
+                                          float scale_log2) {
     // partial q.k over this lane's EPL dims: x[r * NL + i]
     float x[V];
 #pragma unroll
@@ -740,12 +545,7 @@ struct DecodeWave {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         float s = 0.f;
-        if constexpr (DT == PKV_I8 || DT == kCodes3) {
-          // sum_d q_d (1152 + c_d) - 1152 sum_d q_d = sum_d q_d c_d (1032 for 3 bits)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) s = dot2_f16(qh[r][j], km[i][j], s);
-          s -= qcorr[r];
-        } else if constexpr (DT == PKV_BF16) {
+        if constexpr (DT == PKV_BF16) {
           s = dot2_bf16_first(qw[r][0], kr[i].x);
           s = dot2_bf16(qw[r][1], kr[i].y, s);
           s = dot2_bf16(qw[r][2], kr[i].z, s);
@@ -761,27 +561,12 @@ struct DecodeWave {
     }
     reduce_scatter<LPT, V>(x, jl);
 
-    float fac[C];  // per owned score: scale_log2, times the K scale and 2^e
-#pragma unroll
-    for (int c = 0; c < C; ++c) fac[c] = scale_log2;
-    if constexpr (DT == PKV_I8 || DT == kCodes3) {
-      float ksc[C];
-      get_ks(ksc);
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        float qp = 1.f;
-#pragma unroll
-        for (int r = 0; r < RP; ++r)
-          if (own_row[c] == r) qp = qpow[r];
-        fac[c] = ksc[c] * qp * scale_log2;
-      }
-    }
     float sc[C];
     bool need = false;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const bool vis = t0 + own_tok[c] < own_lim[c];
-      sc[c] = vis ? x[c] * fac[c] : kNegInf;
+      sc[c] = vis ? x[c] * scale_log2 : kNegInf;
       need |= sc[c] > m_own[c] + kLazyLog2;
     }
     if (__any(need)) {
@@ -811,10 +596,6 @@ struct DecodeWave {
         m_own[c] = mo;
         l_own[c] *= al;
       }
-      if constexpr (DT == kCodes3) {
-#pragma unroll
-        for (int r = 0; r < RP; ++r) wsum[r] *= alpha[r];
-      }
     }
     float pw[C];
 #pragma unroll
@@ -828,51 +609,15 @@ struct DecodeWave {
     // their V is zeroed (before widening) so that 0 * NaN cannot reach acc
     Row vr[NL];
     get_v(vr);
-    if constexpr (DT == PKV_F32 || DT == PKV_BF16) {  // codes are never NaN
-      if (t0 + kTile > min_lim) {  // wavefront-uniform: only a context's last tile
+    if (t0 + kTile > min_lim) {  // wavefront-uniform: only a context's last tile
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-          if (t0 + i * TPL + grp >= L) vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-    // the weight each owner broadcasts: with int8 codes it carries the
-    // token's V scale (a masked token's stale scale is never multiplied)
-    float pwv[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) pwv[c] = pw[c];
-    if constexpr (DT == PKV_I8 || DT == kCodes3) {
-      float vsc[C];
-      get_vs(vsc);
-#pragma unroll
-      for (int c = 0; c < C; ++c) pwv[c] = sc[c] == kNegInf ? 0.f : pw[c] * vsc[c];
+      for (int i = 0; i < NL; ++i)
+        if (t0 + i * TPL + grp >= L) vr[i] = make_uint4(0u, 0u, 0u, 0u);
     }
     static_for<NL>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       float vv[EPL];
-      if constexpr (DT == kCodes3) {  // code + 8, as stored
-        const uint32_t vw[2] = {vr[i].x, vr[i].y};
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint32_t lo = vw[j] & 0x0f0f0f0fu, hi = (vw[j] >> 4) & 0x0f0f0f0fu;
-          vv[8 * j + 0] = code_u8<0>(lo);
-          vv[8 * j + 1] = code_u8<0>(hi);
-          vv[8 * j + 2] = code_u8<1>(lo);
-          vv[8 * j + 3] = code_u8<1>(hi);
-          vv[8 * j + 4] = code_u8<2>(lo);
-          vv[8 * j + 5] = code_u8<2>(hi);
-          vv[8 * j + 6] = code_u8<3>(lo);
-          vv[8 * j + 7] = code_u8<3>(hi);
-        }
-      } else if constexpr (DT == PKV_I8) {
-        const uint32_t vw[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          vv[4 * j] = code_f32<0>(vw[j]);
-          vv[4 * j + 1] = code_f32<1>(vw[j]);
-          vv[4 * j + 2] = code_f32<2>(vw[j]);
-          vv[4 * j + 3] = code_f32<3>(vw[j]);
-        }
-      } else if constexpr (DT == PKV_BF16) {
+      if constexpr (DT == PKV_BF16) {
         vv[0] = bf16_lo(vr[i].x); vv[1] = bf16_hi(vr[i].x);
         vv[2] = bf16_lo(vr[i].y); vv[3] = bf16_hi(vr[i].y);
         vv[4] = bf16_lo(vr[i].z); vv[5] = bf16_hi(vr[i].z);
@@ -885,10 +630,9 @@ struct DecodeWave {
         constexpr int r = decltype(rc)::value;
         constexpr int v = r * NL + i;
         constexpr int src = V >= LPT ? v / C : v * DUP;
-        const float w = group_bcast<LPT, src>(pwv[v % C], lane);
+        const float w = group_bcast<LPT, src>(pw[v % C], lane);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(w, vv[e], acc[r][e]);
-        if constexpr (DT == kCodes3) wsum[r] += w;
       });
     });
   }
@@ -897,16 +641,6 @@ struct DecodeWave {
   // dims) and return each row's sum of weights.
   __device__ __forceinline__ void totals(float (&l_row)[RP]) {
     sum_over_groups<LPT, LPT, RP, EPL>(acc);
-    if constexpr (DT == kCodes3) {  // remove the stored offset: acc -= 8 sum(w)
-      float ws[RP][1];
-#pragma unroll
-      for (int r = 0; r < RP; ++r) ws[r][0] = wsum[r];
-      sum_over_groups<LPT, LPT, RP, 1>(ws);
-#pragma unroll
-      for (int r = 0; r < RP; ++r)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[r][e] = fmaf(-8.f, ws[r][0], acc[r][e]);
-    }
     const bool counted = (jl % DUP) == 0;
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
@@ -943,7 +677,7 @@ decode_partition_kernel(const DecodeArgs a) {
   constexpr int NL = Gm::NL, EPL = Gm::EPL;
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
-  using Ring = std::conditional_t<DT == kCodes3, NibbleRing<NL>, TileRing<NL, DT == PKV_I8>>;
+  using Ring = TileRing<NL>;
   constexpr int kSlots = Ring::kSlots;
 
   // the tile rings while streaming; the wavefronts' partials once done
@@ -1006,15 +740,7 @@ decode_partition_kernel(const DecodeArgs a) {
       blk = 0;
     }
     const size_t off = tile_bytes_offset<Gm::TB>(a, g, t0, blk, lane);
-    if constexpr (DT == PKV_I8 || DT == kCodes3) {
-      // the tile's 16 K and 16 V scales, one per lane (lanes 32..63 repeat)
-      const size_t so = (((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs)) * 4 +
-                        (size_t)(lane & 15) * 4;
-      ring.stage(slot, kbase + off, vbase + off,
-                 (const char *)((lane & 16) ? a.vs : a.ks) + so);
-    } else {
-      ring.stage(slot, kbase + off, vbase + off);
-    }
+    ring.stage(slot, kbase + off, vbase + off);
   };
 
   // Pipeline: up to kSlots tiles are gathered into the wavefront's LDS ring
@@ -1047,22 +773,11 @@ decode_partition_kernel(const DecodeArgs a) {
       const int slot = k & (kSlots - 1);
       const int ahead = min(n_tiles - 1 - k, kSlots - 1);
       typename W::Row kr[NL];
-      // codes: each lane's one owned token's K and V scales come with the
-      // rows (read before the slot is refilled)
-      float ksc = 0.f, vsc = 0.f;
-      if constexpr (DT == PKV_I8 || DT == kCodes3) {
-        static_assert(W::C == 1, "one owned score per lane with codes");
-        ring.template fetch_sc<0>(slot, ahead, kr, st.own_tok[0], ksc);
-      } else {
-        ring.template fetch<0>(slot, ahead, kr);
-      }
+      ring.template fetch<0>(slot, ahead, kr);
       st.process(
           kr,
           [&](typename W::Row (&vr)[NL]) {
-            if constexpr (DT == PKV_I8 || DT == kCodes3)
-              ring.template fetch_sc<1>(slot, ahead, vr, st.own_tok[0], vsc);
-            else
-              ring.template fetch<1>(slot, ahead, vr);
+            ring.template fetch<1>(slot, ahead, vr);
             if (k + kSlots < n_tiles) {  // the slot is free again: refill it
               const int kn = k + kSlots;
               if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
@@ -1072,9 +787,7 @@ decode_partition_kernel(const DecodeArgs a) {
               stage_tile(ring, slot, tile_t0(kn), table_at(kn));
             }
           },
-          tile_t0(k), scale_log2,
-          [&](float (&ks)[W::C]) { ks[0] = ksc; },
-          [&](float (&vs)[W::C]) { vs[0] = vsc; });
+          tile_t0(k), scale_log2);
     }
   }
 
@@ -1405,9 +1118,7 @@ constexpr int64_t stream_lds_bytes(int64_t B) {
 template <int DT, int D, int G, int RP, int W>
 void launch_decode(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
   // eight wavefronts' tile rings must fit the workgroup's LDS
-  using RingT = std::conditional_t<DT == kCodes3, NibbleRing<Geo<DT, D>::NL>,
-                                   TileRing<Geo<DT, D>::NL, DT == PKV_I8>>;
-  constexpr int kRing = RingT::kBytes;
+  constexpr int kRing = TileRing<Geo<DT, D>::NL>::kBytes;
   if constexpr (W == 8 && 8 * kRing > kLdsLimit) {
     launch_decode<DT, D, G, RP, 4>(a, sa, grid, s);
   } else if constexpr (W == 0) {  // stream kernel + its reduce; grid.x persistent workgroups

@@ -176,8 +176,8 @@ CASES = [
     ((1, 17, 250, 1000), 32, 8, 128, 1, 0),
     ((33, 700), 8, 8, 64, 1, 64),
     ((129, 300), 16, 2, 256, 1, 0),
-    ((515, 47, 2000), 64, 8, 128, 1, -1),   # G = 8: two slices of 4 rows
-    ((90, 600), 32, 8, 128, 4, 0),          # 4 drafts x 4 heads: four slices
+    ((515, 47, 2000), 64, 8, 128, 1, -1),   # G = 8: 8 rows per wavefront
+    ((90, 600), 32, 8, 128, 4, 0),          # 4 drafts x 4 heads: 16 rows per wavefront
     ((400,), 8, 4, 64, 2, 128),
 ]
 
