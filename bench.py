@@ -43,10 +43,17 @@ def kernel_sources(workload: str) -> list:
     from synth.workloads import WORKLOADS
 
     csrc = "paged_kv_cache_202_amd/csrc/"
-    if WORKLOADS[workload].kv_codes:
-        return [csrc + "decode_kernel.h", csrc + "decode_codes.h",
-                csrc + "decode_inst_codes_d128.hip", csrc + "decode.hip"]
+    w = WORKLOADS[workload]
+    if w.kv_codes or mfma_decode(w.dtype, w.queries_per_seq, w.head_dim, w.partition_tokens):
+        return [csrc + "decode_kernel.h", csrc + "verify_mfma.h", csrc + "decode_mfma.h",
+                csrc + "decode_inst_mfma_d128.hip", csrc + "decode.hip"]
     return [csrc + "decode_kernel.h", csrc + "decode_inst_bf16_d128.hip", csrc + "decode.hip"]
+
+
+def mfma_decode(dtype: str, nq: int, D: int, part: int) -> bool:
+    """Whether the library plans a bf16 attention call on the MFMA decode
+    kernel: one query token, head dim up to 128, not the stream plan."""
+    return dtype == "bf16" and nq == 1 and D <= 128 and part != -1
 
 
 def sources_sha256(workload: str) -> str:
@@ -106,9 +113,10 @@ def chunk_flops(B, nq, Hq, D, lens) -> int:
 
 def kernel_label(wk) -> str:
     """Which launches one attention call makes, as the library plans them."""
+    tail = " + reduce_partitions_kernel" if wk.ws is not None else " (one launch per attention call)"
     if getattr(wk, "q8", False):
         kind = "int8" if wk.w.kv_codes == 8 else "3-bit"
-        return f"codes_mfma_kernel<{kind} codes> (one launch per attention call)"
+        return f"decode_mfma_kernel<{kind} codes>" + tail
     if is_chunk(wk):
         return "chunk_mfma_kernel + reduce_partitions_kernel"
     mfma = wk.w.dtype == "bf16" and wk.nq > 1 and wk.Hq // wk.Hkv * wk.nq <= 16
@@ -118,9 +126,10 @@ def kernel_label(wk) -> str:
                 " + reduce_partitions_kernel")
     if wk.part == -1 and not mfma:
         return "decode_stream_kernel + reduce_stream_kernel"
+    if mfma_decode(wk.w.dtype, wk.nq, wk.D, wk.part):
+        return "decode_mfma_kernel<bf16>" + tail
     main = "verify_mfma_kernel" if mfma else "decode_partition_kernel"
-    return main + (" + reduce_partitions_kernel" if wk.ws is not None else
-                   " (one launch per attention call)")
+    return main + tail
 
 
 class Workload:
@@ -530,7 +539,7 @@ def main() -> int:
     ap.add_argument("--summarize-profile", action="store_true",
                     help="no GPU work: condense rocprofv3 output (the --*-dir options) into "
                          "profiles/decode_<workload>.json")
-    ap.add_argument("--kernel-regex", default="decode_partition_kernel")
+    ap.add_argument("--kernel-regex", default="decode_(partition|mfma)_kernel")
     ap.add_argument("--trace-dir")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")

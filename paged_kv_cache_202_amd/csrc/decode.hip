@@ -12,7 +12,7 @@
 #include "decode_kernel.h"
 #include "verify_mfma.h"
 #include "shared_prefix.h"
-#include "decode_codes.h"
+#include "decode_mfma.h"
 #include "pagedkv.h"
 #include "status.h"
 
@@ -247,10 +247,10 @@ size_t stream_bytes(int64_t B, int64_t units, int32_t RP, int32_t D) {
          2 * align_up(S * RP * 4, 256);
 }
 
-Launcher pick_codes_kernel(int dtype, int D, int RW, int W) {
-  if (D == 64) return pick_codes<64>(dtype, RW, W);
-  if (D == 128) return pick_codes<128>(dtype, RW, W);
-  if (D == 256) return pick_codes<256>(dtype, RW, W);
+Launcher pick_mfma_decode(int dtype, int D, int RW, int W) {
+  if (D == 64) return pick_mfma<64>(dtype, RW, W);
+  if (D == 128) return pick_mfma<128>(dtype, RW, W);
+  if (D == 256) return pick_mfma<256>(dtype, RW, W);
   return nullptr;
 }
 
@@ -476,15 +476,18 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   int32_t RP, S;
   row_split(G, nq, &RP, &S);
   if (mfma) S = 1;
-  const bool codes = dtype == PKV_I8 || dtype == kCodes3;
-  if (codes) {  // matrix-core kernel: every row of a KV head in one wavefront
+  // matrix-core kernel: every row of a KV head in one wavefront (code caches;
+  // bf16 decode with one query token and D <= 128, outside the stream plan)
+  const bool codes = dtype == PKV_I8 || dtype == kCodes3 ||
+                     (dtype == PKV_BF16 && nq == 1 && D <= 128 && pl.waves != 0 && !mfma);
+  if (codes) {
     const int32_t rows = G * nq;
     RP = rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
     S = 1;
   }
   const int32_t RW = RP;
   Launcher launch = mfma    ? pick_verify(D)
-                    : codes ? pick_codes_kernel(dtype, D, RP, pl.waves)
+                    : codes ? pick_mfma_decode(dtype, D, RP, pl.waves)
                             : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
   const bool streamed = pl.waves == 0 && !mfma;

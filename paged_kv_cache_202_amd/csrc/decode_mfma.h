@@ -1,30 +1,40 @@
 #pragma once
-// Paged attention decode over caches of 8-bit or 3-bit per-row codes, on
-// the matrix cores (gfx950). Same contract and partials as the partition
-// kernel of decode_kernel.h, instantiated in decode_inst_codes_d<D>.hip.
+// Paged attention decode on the matrix cores (gfx950), over bf16 caches and
+// over caches of 8-bit or 3-bit per-row codes. Same contract and partials as
+// the partition kernel of decode_kernel.h, instantiated in
+// decode_inst_mfma_d<D>.hip.
 //
 // What it computes: attention of each sequence's query rows over its paged
 // K/V (vLLM abstract on the papers page "external vector cache"; causal
 // visibility of several query tokens: course page "Module 10. KV Caches and
-// Efficient Inference", notebook section 2), with every K and V element
-// taken as code * its row's scale -- the reconstruction of that page's
+// Efficient Inference", notebook section 2); for code caches every K and V
+// element is code * its row's scale -- the reconstruction of that page's
 // project demo (Demo 2) quantizer.
 //
 // Design (for CDNA4; the pages give no kernel): per 16-token tile the VALU
-// form spends about 340 vector instructions per wavefront (code widening,
-// 64 dot2, reduce-scatter, broadcast weights, 128 FMAs), and at 16 lanes
-// per SIMD that costs as long as the tile's HBM traffic. Here both products
-// run on MFMA and the VALU only widens codes and runs the softmax:
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_f16: A = a token's codes
-//     widened to fp16 (lane l: token l % 16, a quarter of its row), B = the
-//     query rows as fp16 (row l % 16, the same quarter). The output leaves
-//     lane l the scores of row l % 16 for tokens 4 (l / 16) .. + 3.
-//   * those four weights, times their tokens' V scales, are the B operand
-//     of O^T += V^T P^T (v_mfma_f32_16x16x16_f16) as they stand. The A
-//     operand (4 tokens x 1 dim per lane) comes from the gfx950 transposing
-//     LDS read ds_read_b64_tr_b8: in each 16-lane group, lane i receives
-//     byte i % 8 of the 8 bytes named by lanes i / 8 + 2 u, u = 0..7, so
-//     one read gives a lane 4 tokens of two 16-dim column blocks.
+// form spends about 310 (bf16) to 400 (3-bit codes) vector instructions per
+// wavefront (widening, dot products, a reduce-scatter, weight broadcasts,
+// 128 FMAs), and at 16 lanes per SIMD that costs about as long as the
+// tile's HBM traffic. Here both products run on MFMA and the VALU only
+// widens codes and runs the softmax:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32 (bf16, or f16 for codes): A = a
+//     token's row (lane l: token l % 16, a quarter of the row; codes widened
+//     to fp16 in registers), B = the query rows (row l % 16, the same
+//     quarter). The output leaves lane l the scores of row l % 16 for
+//     tokens 4 (l / 16) .. + 3.
+//   * those four weights (times their tokens' V scales for codes) are the
+//     B operand of O^T += V^T P^T as they stand. Its A operand (4 tokens x
+//     1 dim per lane) comes from the gfx950 transposing LDS reads: for
+//     bf16, ds_read_b64_tr_b16 (in each 16-lane group lane i receives
+//     element i % 4 of the 4 named by lanes i / 4 + 4 u, u = 0..3); for
+//     codes, ds_read_b64_tr_b8 (lane i receives byte i % 8 of the 8 named
+//     by lanes i / 8 + 2 u, u = 0..7), so one read gives a lane 4 tokens of
+//     two 16-dim column blocks.
+//   * bf16 weights are split into bf16 pairs hi + lo and contracted in one
+//     16x16x32 product whose k runs over (tokens, hi) then (tokens, lo) with
+//     V repeated: 16 significant bits per weight, so results move by no
+//     more than fp32 rounding across partitionings. In a context's last
+//     tile, V slots past its end (stale bits, maybe NaN) are zeroed.
 //   * codes widen exactly: (code ^ 0x80) in the low byte of fp16 0x64xx is
 //     1152 + code (8 bits); the offsets are removed once per score
 //     (1152 x sum q) and once per output (1152 x the sum of the fp16
@@ -39,7 +49,7 @@
 //   * up to 16 query rows (G x query tokens) per wavefront at no extra MFMA
 //     work; the staging, ring, lazy softmax and partials are the partition
 //     kernel's. K rows are stored in the LDS ring with their 16-byte chunks
-//     permuted per token (chunk c of token t at c ^ (t mod 16-chunk count))
+//     permuted per token (chunk c of token t at c ^ (t mod chunks per row))
 //     so the per-token reads of the A operand spread over the LDS banks.
 #include <hip/hip_runtime.h>
 
@@ -48,6 +58,7 @@
 #include <limits>
 
 #include "decode_kernel.h"
+#include "verify_mfma.h"
 
 namespace pkv {
 namespace decode {
@@ -68,15 +79,14 @@ struct CodeGeo {
   static_assert(CPT >= 4 && CPT <= 16 && NL >= 1, "rows of 64, 128 or 256 bytes");
 };
 
-// This lane's byte offset inside a tile's K rows for the gathers: lane i
-// of a load row fetches chunk (i % CPT) ^ s of token i / CPT of that row,
-// s = (i / CPT) % CPT, so that LDS position p of token t holds chunk
-// p ^ s(t) (the permutation depends only on the token's place in its row).
+// This lane's byte offset inside a tile's K rows for the gather of load
+// row i: lane l fetches chunk (l % CPT) ^ (t % CPT) of token t = i * TPL +
+// l / CPT, so that LDS position p of token t holds chunk p ^ (t % CPT).
 template <int RB>
-__device__ __forceinline__ int code_k_lane_offset(int lane) {
+__device__ __forceinline__ int code_k_lane_offset(int lane, int i) {
   using Gc = CodeGeo<RB>;
-  const int tl = lane / Gc::CPT, p = lane % Gc::CPT;
-  return tl * RB + 16 * (p ^ (tl % Gc::CPT));
+  const int tl = lane / Gc::CPT, t = i * Gc::TPL + tl;
+  return i * 1024 + tl * RB + 16 * ((lane % Gc::CPT) ^ (t % Gc::CPT));
 }
 
 // One tile's operands from an LDS slot, with one wait for all of them.
@@ -152,6 +162,56 @@ __device__ __forceinline__ void read_codes<256>(u32x4_t (&k)[4], uint2 (&v)[8], 
       : "memory");
 }
 
+// bf16 tiles: KCH K chunks (as for codes) and D / 16 transposing 16-bit V
+// reads at va + 32 cb (ds_read_b64_tr_b16: in each 16-lane group lane i
+// receives element i % 4 of the 4 named by lanes i / 4 + 4 u, u = 0..3).
+template <int RB>
+__device__ __forceinline__ void read_bf16(u32x4_t (&k)[CodeGeo<RB>::KCH],
+                                          uint2 (&v)[RB / 32],
+                                          const PKV_LDS char *const (&ka)[CodeGeo<RB>::KCH],
+                                          const PKV_LDS char *va);
+
+template <>
+__device__ __forceinline__ void read_bf16<128>(u32x4_t (&k)[2], uint2 (&v)[4],
+                                               const PKV_LDS char *const (&ka)[2],
+                                               const PKV_LDS char *va) {
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b64_tr_b16 %2, %8\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ka[0]), "v"(ka[1]), "v"(va)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_bf16<256>(u32x4_t (&k)[4], uint2 (&v)[8],
+                                               const PKV_LDS char *const (&ka)[4],
+                                               const PKV_LDS char *va) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b64_tr_b16 %4, %16\n\t"
+      "ds_read_b64_tr_b16 %5, %16 offset:32\n\t"
+      "ds_read_b64_tr_b16 %6, %16 offset:64\n\t"
+      "ds_read_b64_tr_b16 %7, %16 offset:96\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+      "ds_read_b64_tr_b16 %9, %16 offset:160\n\t"
+      "ds_read_b64_tr_b16 %10, %16 offset:192\n\t"
+      "ds_read_b64_tr_b16 %11, %16 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
+        "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va)
+      : "memory");
+}
+
 // Four int8 codes (one word) as four fp16 values 1152 + code.
 __device__ __forceinline__ uint2 codes_f16x4(uint32_t w) {
   return make_uint2(codes_f16_lo(w), codes_f16_hi(w));
@@ -176,19 +236,21 @@ __device__ __forceinline__ uint32_t high_nibbles(uint32_t w) { return (w >> 4) &
 
 template <int DT, int D, int RW, int kWaves>
 __global__ void __launch_bounds__(kWaves * 64)
-codes_mfma_kernel(const DecodeArgs a) {
+decode_mfma_kernel(const DecodeArgs a) {
   constexpr bool kNib = DT == kCodes3;
-  constexpr int RB = kNib ? D / 2 : D;  // bytes per token row
+  constexpr bool kBf = DT == PKV_BF16;  // bf16 K/V: no codes, no scales
+  constexpr int RB = kBf ? 2 * D : kNib ? D / 2 : D;  // bytes per token row
   using Gc = CodeGeo<RB>;
   constexpr int NL = Gc::NL, KCH = Gc::KCH, NV = Gc::NV;
   constexpr int NC = D / 32;   // q.k MFMAs per tile (32 dims each)
   constexpr int NCB = D / 16;  // 16-dim output column blocks
-  constexpr float kOffset = kNib ? 0.f : 1152.f;  // fp16 form = offset + code
+  constexpr float kOffset = DT == PKV_I8 ? 1152.f : 0.f;  // fp16 form = offset + code
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
-  using Ring = TileRing<NL, true>;
+  using Ring = TileRing<NL, !kBf>;
   constexpr int kSlots = Ring::kSlots;
-  static_assert(DT == PKV_I8 || DT == kCodes3, "8-bit or 3-bit codes");
+  static_assert(DT == PKV_BF16 || DT == PKV_I8 || DT == kCodes3, "bf16, 8-bit or 3-bit codes");
+  static_assert(!kBf || NV == NCB, "one transposing read per bf16 column block");
   static_assert(RW == 4 || RW == 8 || RW == 16, "rows per wavefront");
 
   struct Merge {
@@ -229,9 +291,10 @@ codes_mfma_kernel(const DecodeArgs a) {
   const int t_end = min(L, t_begin + a.part_tokens);
 
   // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
-  //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA in the order
-  //      the K codes widen, scaled by 2^-e so that the row's largest entry is
-  //      in [2^7, 2^8) (fp16 keeps 11 bits) ---------------------------------
+  //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA; bf16 as is
+  //      for bf16 K, else fp16 in the order the K codes widen, scaled by 2^-e
+  //      so that the row's largest entry is in [2^7, 2^8) (fp16 keeps 11
+  //      bits) ---------------------------------------------------------------
   const int rr = row0 + ln, qi = rr / G;
   const bool row_live = ln < RW && qi < nq;
   uint32_t qb[NC][4];
@@ -253,6 +316,12 @@ codes_mfma_kernel(const DecodeArgs a) {
       for (int j = 0; j < D / 8; ++j) w[j] = 0u;
     }
     auto qdim = [&](int d) { return d % 2 ? bf16_hi(w[d / 2]) : bf16_lo(w[d / 2]); };
+    if constexpr (kBf) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qb[c][j] = w[4 * c + j];
+    }
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < D / 8; ++j) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
@@ -260,10 +329,10 @@ codes_mfma_kernel(const DecodeArgs a) {
     mx = fmaxf(mx, exact_xor<32>(mx));
     int ex = 0;
     frexpf(mx, &ex);
-    const int e = mx > 0.f ? ex - 8 : 0;
+    const int e = kBf || mx == 0.f ? 0 : ex - 8;
     float sum = 0.f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC && !kBf; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1) for 8-bit
@@ -285,18 +354,31 @@ codes_mfma_kernel(const DecodeArgs a) {
   const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
   const char *kbase = (const char *)a.kc;
   const char *vbase = (const char *)a.vc;
-  const int koff = code_k_lane_offset<RB>(lane);
+  int koff[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) koff[i] = code_k_lane_offset<RB>(lane, i);
   int bad = 0;
-  // gather the tile at logical token t0 (from block blk) into a ring slot
+  // gather the tile at logical token t0 (from block blk) into a ring slot,
+  // in TileRing::stage's order: the scales (codes), the K rows (chunks
+  // permuted per token), the V rows
   auto stage_tile = [&](Ring &ring, int slot, int t0, int blk) {
     if (blk < 0 || blk >= a.num_blocks) {  // bad table entry: read block 0, poison later
       bad = 1;
       blk = 0;
     }
     const size_t rowi = ((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs);
-    const size_t so = rowi * 4 + (size_t)(lane & 15) * 4;
-    ring.stage(slot, kbase + rowi * RB + koff, vbase + rowi * RB + lane * 16,
-               (const char *)((lane & 16) ? a.vs : a.ks) + so);
+    PKV_LDS char *dst = ring.base + slot * Ring::kTileBytes;
+    if constexpr (!kBf) {
+      const size_t so = rowi * 4 + (size_t)(lane & 15) * 4;
+      gather_lds4<kKvNonTemporal>((const char *)((lane & 16) ? a.vs : a.ks) + so,
+                                  dst + Ring::kCodeBytes);
+    }
+    const char *kp = kbase + rowi * RB, *vp = vbase + rowi * RB + lane * 16;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(kp + koff[i], dst + i * 1024);
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
   };
 
   const int n_tiles = t_begin + wave * kTile < t_end
@@ -327,15 +409,16 @@ codes_mfma_kernel(const DecodeArgs a) {
       const int t = ln, tl = t % Gc::TPL;
       const PKV_LDS char *row = ring_base + (t / Gc::TPL) * 1024 + tl * RB;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) ka[c] = row + 16 * ((KCH * lg + c) ^ (tl % Gc::CPT));
+      for (int c = 0; c < KCH; ++c) ka[c] = row + 16 * ((KCH * lg + c) ^ (t % Gc::CPT));
     }
-    // V: lane s of group lg names token 4 lg + (s / 2) % 4, bytes
-    // 16 ((s / 2) / 4) + 8 (s % 2) .. + 7 of each 32-byte column pair
+    // V, codes: lane s of group lg names token 4 lg + (s / 2) % 4, bytes
+    // 16 ((s / 2) / 4) + 8 (s % 2) .. + 7 of each 32-byte column pair; bf16:
+    // token 4 lg + s / 4, dims 4 (s % 4) .. + 3 of each 16-dim column block
     const PKV_LDS char *va;
     {
-      const int u = ln >> 1, t = 4 * lg + (u & 3);
-      va = ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB + 16 * (u >> 2) +
-           8 * (ln & 1);
+      const int u = kBf ? ln >> 2 : ln >> 1, t = 4 * lg + (u & 3);
+      const int col = kBf ? 8 * (ln & 3) : 16 * (u >> 2) + 8 * (ln & 1);
+      va = ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB + col;
     }
     const PKV_LDS char *sa = ring_base + Ring::kCodeBytes + 16 * lg;
 #pragma unroll
@@ -352,13 +435,16 @@ codes_mfma_kernel(const DecodeArgs a) {
       });
       u32x4_t kr[KCH];
       uint2 vt[NV];
-      float4 ksc, vsc;
+      float4 ksc = make_float4(1.f, 1.f, 1.f, 1.f), vsc = ksc;
       {
         const int so = slot * Ring::kTileBytes;
         const PKV_LDS char *kas[KCH];
 #pragma unroll
         for (int c = 0; c < KCH; ++c) kas[c] = ka[c] + so;
-        read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
+        if constexpr (kBf)
+          read_bf16<RB>(kr, vt, kas, va + so);
+        else
+          read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
       }
       if (k + kSlots < n_tiles) {  // the slot is free again: refill it
         const int kn = k + kSlots;
@@ -373,6 +459,13 @@ codes_mfma_kernel(const DecodeArgs a) {
       c32x4_t s = c32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
+        if constexpr (kBf) {
+          const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
+          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
+                                                      __builtin_bit_cast(bf16x8_t, bv), s, 0, 0,
+                                                      0);
+          continue;
+        }
         u32x4_t av;
         if constexpr (kNib) {  // one word: 8 dims, low nibbles first
           const u32x4_t kw = kr[c / 4];
@@ -397,7 +490,7 @@ codes_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const bool vis = t0 + 4 * lg + e < lim;
-        sc[e] = vis ? (s[e] - qcorr) * (kss[e] * qfac) : kNegInf;
+        sc[e] = vis ? (kBf ? s[e] * qfac : (s[e] - qcorr) * (kss[e] * qfac)) : kNegInf;
         need |= sc[e] > m_row + kLazyLog2;
       }
       if (__any(need)) {  // raise the running maximum of row ln
@@ -421,12 +514,43 @@ codes_mfma_kernel(const DecodeArgs a) {
         const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);
         l_part += pw;
         // the V scale of a masked token may be stale: never multiplied
-        pv[e] = sc[e] == kNegInf ? 0.f : pw * vss[e];
+        pv[e] = sc[e] == kNegInf ? 0.f : kBf ? pw : pw * vss[e];
+      }
+      if constexpr (kBf) {
+        // O^T += V^T P^T with bf16 weights; in a context's last tile the
+        // slots past it may hold stale bits (even NaN), zeroed so that a
+        // zero weight times NaN cannot reach the accumulators
+        if (t0 + kTile > L) {  // wavefront-uniform
+          const int tv = t0 + 4 * lg;
+          const uint32_t m01 = (tv < L ? 0xffffu : 0u) | (tv + 1 < L ? 0xffff0000u : 0u);
+          const uint32_t m23 = (tv + 2 < L ? 0xffffu : 0u) | (tv + 3 < L ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int j = 0; j < NV; ++j) {
+            vt[j].x &= m01;
+            vt[j].y &= m23;
+          }
+        }
+        // each weight as a bf16 pair hi + lo (16 significant bits): one
+        // 16x16x32 product over k = (tokens, hi) then (tokens, lo), V
+        // repeated along k, so the weights lose no more than fp32 rounding
+        // would across partitionings
+        const uint32_t h01 = pack_bf16(pv[0], pv[1]), h23 = pack_bf16(pv[2], pv[3]);
+        const uint32_t l01 = pack_bf16(pv[0] - bf16_lo(h01), pv[1] - bf16_hi(h01));
+        const uint32_t l23 = pack_bf16(pv[2] - bf16_lo(h23), pv[3] - bf16_hi(h23));
+        const u32x4_t pb2 = {h01, h23, l01, l23};
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const u32x4_t va2 = {vt[cb].x, vt[cb].y, vt[cb].x, vt[cb].y};
+          o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va2),
+                                                          __builtin_bit_cast(bf16x8_t, pb2),
+                                                          o[cb], 0, 0, 0);
+        }
+        continue;
       }
       const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
       const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
       // the fp16 weights' sum: what the V offsets add, removed at the end
-      if constexpr (!kNib) w_part = dot2_f16(p01, ones, dot2_f16(p23, ones, w_part));
+      if constexpr (DT == PKV_I8) w_part = dot2_f16(p01, ones, dot2_f16(p23, ones, w_part));
       const h16x4_t pb = __builtin_bit_cast(h16x4_t, make_uint2(p01, p23));
 
       // O^T += V^T P^T: A = V[tokens 4 lg .. + 3][one dim per lane]
@@ -526,18 +650,19 @@ codes_mfma_kernel(const DecodeArgs a) {
 }
 
 template <int DT, int D, int RW, int W>
-void launch_codes(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
-  constexpr int RB = DT == kCodes3 ? D / 2 : D;
-  static_assert(W * TileRing<CodeGeo<RB>::NL, true>::kBytes <= 163840, "LDS of the rings");
-  hipLaunchKernelGGL((codes_mfma_kernel<DT, D, RW, W>), grid, dim3(W * 64), 0, s, a);
+void launch_mfma(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
+  constexpr int RB = DT == PKV_BF16 ? 2 * D : DT == kCodes3 ? D / 2 : D;
+  static_assert(W * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16>::kBytes <= 163840,
+                "LDS of the rings");
+  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, RW, W>), grid, dim3(W * 64), 0, s, a);
 }
 
-// Launcher of the MFMA kernel over codes (DT = PKV_I8 or kCodes3) for head
-// dim D, RW query rows per wavefront (4, 8 or 16) and W wavefronts per
-// workgroup (1, 4 or 8); nullptr if none. Defined in
-// decode_inst_codes_d<D>.hip.
+// Launcher of the MFMA decode kernel for DT = PKV_BF16 (D 64 or 128),
+// PKV_I8 or kCodes3, head dim D, RW query rows per wavefront (4, 8 or 16)
+// and W wavefronts per workgroup (1, 4 or 8); nullptr if none. Defined in
+// decode_inst_mfma_d<D>.hip.
 template <int D>
-Launcher pick_codes(int DT, int RW, int W);
+Launcher pick_mfma(int DT, int RW, int W);
 
 }  // namespace decode
 }  // namespace pkv
