@@ -5,6 +5,7 @@
 // decode_kernel.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -71,14 +72,17 @@ reduce_partitions_kernel(const DecodeArgs a) {
   float M = kNegInf, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   bool bad = false;
+  // the MFMA kernel's independent wavefronts leave one partial per run of
+  // parts_per_wg partitions, in the run's first slot
+  const int run = a.parts_per_wg > 1 ? a.parts_per_wg : 1;
 #pragma unroll 4
-  for (int p = sub; p < np; p += GPR) {
+  for (int p = sub * run; p < np; p += GPR * run) {
     if (p >= np_pre && p < a.part_base) continue;  // prefix pieces past this row's prefix
     const float m = pm[p];
+    bad |= m != m;
+    if (m == kNegInf) continue;  // no visible key in the partition (or an empty slot)
     const float l = pl[p];
     const float4 v = pacc[(size_t)p * TPG + t];
-    bad |= m != m;
-    if (m == kNegInf) continue;  // no visible key in the partition
     if (m > M) {
       const float c = exp2f(M - m);  // 0 while M is still -inf
       num.x *= c; num.y *= c; num.z *= c; num.w *= c;
@@ -486,12 +490,24 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
     S = 1;
   }
   const int32_t RW = RP;
+  const bool streamed = pl.waves == 0 && !mfma;
+  // Short partitions on the MFMA kernel: rather than a one-wavefront
+  // workgroup per partition, workgroups of 8 independent wavefronts, each
+  // streaming ppw consecutive partitions (as many as leave about one round
+  // of wavefronts) and writing their partials.
+  int32_t ppw = 0, W = pl.waves;
+  dim3 grid = streamed ? dim3(pl.grid_x) : dim3(NP, Hkv * S, B);
+  if (codes && pl.waves == 1 && NP > 1) {
+    ppw = (int32_t)std::min<int64_t>(
+        NP, std::max<int64_t>(1, (int64_t)B * Hkv * NP / kResidentWaves));
+    const int32_t runs = (NP + ppw - 1) / ppw;
+    W = 8;
+    grid.x = (runs + W - 1) / W;
+  }
   Launcher launch = mfma    ? pick_verify(D)
-                    : codes ? pick_mfma_decode(dtype, D, RP, pl.waves)
+                    : codes ? pick_mfma_decode(dtype, D, RP, W)
                             : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
-  const bool streamed = pl.waves == 0 && !mfma;
-  const dim3 grid = streamed ? dim3(pl.grid_x) : dim3(NP, Hkv * S, B);
   DecodeArgs a{};
   a.out = out;
   a.lse = lse_out;
@@ -513,6 +529,7 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   a.scale_log2 = scale * kLog2e;
   a.ks = ks;
   a.vs = vs;
+  a.parts_per_wg = ppw;
   StreamArgs sa{};
   size_t need = 0;
   if (streamed)

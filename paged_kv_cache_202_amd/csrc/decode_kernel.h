@@ -234,6 +234,12 @@ struct DecodeArgs {
   // [num_blocks, Hkv, bs].
   const float *ks;
   const float *vs;
+  // MFMA decode kernel only: > 0 makes its wavefronts independent, each
+  // streaming a run of this many consecutive partitions through its ring and
+  // writing the run's partials into its first partition's slot (the reduce
+  // reads those slots only); 0: the wavefronts of a workgroup share one
+  // partition and merge in LDS.
+  int32_t parts_per_wg;
 };
 
 // One step of the reduce-scatter over lane bit M with `cnt` live values:

@@ -267,7 +267,18 @@ decode_mfma_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, lg = lane >> 4;  // MFMA column (query row) and lane group
-  const int p = blockIdx.x, b = blockIdx.z;
+  // Independent wavefronts (parts_per_wg > 0): wavefront w of workgroup x
+  // streams the run of parts_per_wg consecutive partitions from
+  // p = (x W + w) ppw on as one softmax state and writes it itself as the
+  // partial of partition p; the reduce reads only the runs' first slots. No
+  // store is issued while tiles are in flight (stores count in vmcnt too,
+  // and would make the ring's counted waits drain it). Else the
+  // workgroup's wavefronts interleave the tiles of partition p = x and
+  // merge in LDS.
+  const bool indep = a.parts_per_wg > 0;
+  const int ppw = indep ? a.parts_per_wg : 1;
+  const int p = indep ? ((int)blockIdx.x * kWaves + wave) * ppw : (int)blockIdx.x;
+  const int b = blockIdx.z;
   const int g = blockIdx.y % a.Hkv, row0 = (blockIdx.y / a.Hkv) * RW;
   const int nq = a.nq, G = a.Hq / a.Hkv;
   const int L = load_const(a.lens + b);
@@ -288,7 +299,7 @@ decode_mfma_kernel(const DecodeArgs a) {
   }
   const int t_begin = p * a.part_tokens;
   if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
-  const int t_end = min(L, t_begin + a.part_tokens);
+  const int t_end = min(L, t_begin + ppw * a.part_tokens);
 
   // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
   //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA; bf16 as is
@@ -381,10 +392,10 @@ decode_mfma_kernel(const DecodeArgs a) {
       gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
   };
 
-  const int n_tiles = t_begin + wave * kTile < t_end
-                          ? (t_end - (t_begin + wave * kTile) + kStride - 1) / kStride
-                          : 0;
-  auto tile_t0 = [&](int k) { return t_begin + wave * kTile + k * kStride; };
+  const int wstart = indep ? t_begin : t_begin + wave * kTile;  // this wavefront's first tile
+  const int wstride = indep ? kTile : kStride;                   // and the step between its tiles
+  const int n_tiles = wstart < t_end ? (t_end - wstart + wstride - 1) / wstride : 0;
+  auto tile_t0 = [&](int k) { return wstart + k * wstride; };
   auto table_window = [&](int w) {
     return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
   };
@@ -395,6 +406,42 @@ decode_mfma_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) o[cb] = c32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_row = kNegInf, l_part = 0.f, w_part = 0.f;
+
+  // The partial of partition pp straight from the registers (independent
+  // wavefronts).
+  auto flush = [&](int pp) {
+    float lt = l_part, wt = w_part;
+    lt += exact_xor<16>(lt);
+    lt += exact_xor<32>(lt);
+    wt += exact_xor<16>(wt);
+    wt += exact_xor<32>(wt);
+    const float off = -kOffset * wt;
+    if (row_live) {
+      const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
+      const size_t pi = row * a.num_parts + a.part_base + pp;
+      float *dst = a.part_acc + pi * D;
+      if constexpr (kNib) {
+#pragma unroll
+        for (int jh = 0; jh < NCB / 2; ++jh) {
+          const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
+          float *q8 = dst + 32 * jh + 8 * lg;
+          *reinterpret_cast<float4 *>(q8) =
+              make_float4(lo[0] + off, hi[0] + off, lo[1] + off, hi[1] + off);
+          *reinterpret_cast<float4 *>(q8 + 4) =
+              make_float4(lo[2] + off, hi[2] + off, lo[3] + off, hi[3] + off);
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
+              make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
+      }
+      if (lg == 0) {
+        a.part_m[pi] = bad ? __builtin_nanf("") : m_row;
+        a.part_l[pi] = lt;
+      }
+    }
+  };
 
   if (n_tiles > 0) {
     int tblv = table_window(0);
@@ -577,6 +624,11 @@ decode_mfma_kernel(const DecodeArgs a) {
         }
       }
     }
+  }
+
+  if (indep) {
+    flush(p);
+    return;
   }
 
   // ---- wavefront totals: row ln's weight sums over the four lane groups,

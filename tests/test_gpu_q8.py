@@ -199,6 +199,20 @@ def test_q8_attention_matches_oracle(ci, bits, device):
     assert np.abs(lse - ref_lse).max() <= 1e-2
 
 
+@pytest.mark.parametrize("bits", [8, 3])
+def test_q8_many_partitions_per_workgroup(bits, device):
+    """2 sequences x 8 KV heads x 256 partitions of 16 tokens: one wavefront
+    streams a run of two consecutive partitions as one partial."""
+    c = Q8Case((4096, 2700), 32, 8, 128, nq=1, seed=31, device=device, bits=bits)
+    ref, ref_lse = c.run_oracle()
+    for part in (16, 0):
+        out, lse = c.run_gpu(part)
+        err = np.abs(out - ref).max()
+        print(f"{bits}-bit, partition {part}: max-abs error {err:.3e}", flush=True)
+        assert np.isfinite(out).all() and err <= 1e-2
+        assert np.abs(lse - ref_lse).max() <= 1e-2
+
+
 def test_q8_bad_table_and_short_context_give_nan(device):
     c = Q8Case((50, 60, 70), 8, 2, 128, nq=2, seed=9, device=device)
     tables = c.d_tables.clone()
