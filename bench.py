@@ -52,8 +52,9 @@ def kernel_sources(workload: str) -> list:
 
 def mfma_decode(dtype: str, nq: int, D: int, part: int) -> bool:
     """Whether the library plans a bf16 attention call on the MFMA decode
-    kernel: one query token, head dim up to 128, not the stream plan."""
-    return dtype == "bf16" and nq == 1 and D <= 128 and part != -1
+    kernel: one query token, head dim up to 128 (the stream plan,
+    partition_tokens = -1, runs it in stream mode)."""
+    return dtype == "bf16" and nq == 1 and D <= 128
 
 
 def sources_sha256(workload: str) -> str:
@@ -124,6 +125,8 @@ def kernel_label(wk) -> str:
         return ("prefix_mfma_kernel + " + ("verify_mfma_kernel" if mfma else
                                            "decode_partition_kernel") +
                 " + reduce_partitions_kernel")
+    if wk.part == -1 and mfma_decode(wk.w.dtype, wk.nq, wk.D, wk.part):
+        return "decode_mfma_kernel<bf16> stream mode + reduce_stream_kernel"
     if wk.part == -1 and not mfma:
         return "decode_stream_kernel + reduce_stream_kernel"
     if mfma_decode(wk.w.dtype, wk.nq, wk.D, wk.part):
@@ -489,10 +492,15 @@ def summarize_profile(args) -> int:
     ffac, wfac = moved / (cfetch * 1024), moved / (cwrite * 1024)
     from synth.workloads import WORKLOADS
 
+    from synth import workloads as wl
+
     w = WORKLOADS[args.workload]
-    if w.context is None:
-        raise SystemExit("profile summaries cover equal-length workloads")
-    lens = np.full(w.batch, w.context, dtype=np.int64)
+    if w.context is None:  # the seeded lengths, drawn as the workload draws them
+        rng = np.random.default_rng(w.rng_seed)
+        wl.free_stack_permutation(rng, w.num_blocks)
+        lens = wl.draw_lengths(rng, w).astype(np.int64)
+    else:
+        lens = np.full(w.batch, w.context, dtype=np.int64)
     out = {
         "kernel": st["Name"],
         "workload": args.workload,

@@ -251,6 +251,16 @@ size_t stream_bytes(int64_t B, int64_t units, int32_t RP, int32_t D) {
          2 * align_up(S * RP * 4, 256);
 }
 
+Launcher pick_mfma_stream_decode(int D, int RW) {
+  if (D == 64) return pick_mfma_stream<64>(RW);
+  if (D == 128) return pick_mfma_stream<128>(RW);
+  return nullptr;
+}
+
+// Rows per wavefront of the matrix-core kernels for `rows` query rows of a
+// KV head.
+int32_t mfma_rows(int32_t rows) { return rows <= 4 ? 4 : rows <= 8 ? 8 : 16; }
+
 Launcher pick_mfma_decode(int dtype, int D, int RW, int W) {
   if (D == 64) return pick_mfma<64>(dtype, RW, W);
   if (D == 128) return pick_mfma<128>(dtype, RW, W);
@@ -371,9 +381,11 @@ static size_t workspace_need(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int
   for (bool stream_ok : {true, false}) {
     const Plan pl = plan_launch(B, Hkv, max_ctx, part, stream_ok);
     size_t n = 0;
-    if (pl.waves == 0)
+    if (pl.waves == 0) {
       n = stream_bytes(B, units, RW, D);
-    else if (pl.num_parts > 1)
+      if (nq == 1 && D <= 128)  // the matrix-core kernel's stream mode (bf16)
+        n = std::max(n, stream_bytes(B, (int64_t)B * Hkv, mfma_rows(Hq / Hkv), D));
+    } else if (pl.num_parts > 1)
       n = partial_bytes((int64_t)B * nq * Hq, pl.num_parts, D);
     if (n > need) need = n;
   }
@@ -480,13 +492,16 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   int32_t RP, S;
   row_split(G, nq, &RP, &S);
   if (mfma) S = 1;
+  // bf16 decode with one query token and D <= 128 under the stream plan:
+  // the matrix-core kernel's stream mode
+  const bool mstream = pl.waves == 0 && !mfma && dtype == PKV_BF16 && nq == 1 && D <= 128 &&
+                       B <= kMfmaStreamSeqs;
   // matrix-core kernel: every row of a KV head in one wavefront (code caches;
-  // bf16 decode with one query token and D <= 128, outside the stream plan)
-  const bool codes = dtype == PKV_I8 || dtype == kCodes3 ||
+  // bf16 decode with one query token and D <= 128)
+  const bool codes = dtype == PKV_I8 || dtype == kCodes3 || mstream ||
                      (dtype == PKV_BF16 && nq == 1 && D <= 128 && pl.waves != 0 && !mfma);
   if (codes) {
-    const int32_t rows = G * nq;
-    RP = rows <= 4 ? 4 : rows <= 8 ? 8 : 16;
+    RP = mfma_rows(G * nq);
     S = 1;
   }
   const int32_t RW = RP;
@@ -497,15 +512,19 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   // of wavefronts) and writing their partials.
   int32_t ppw = 0, W = pl.waves;
   dim3 grid = streamed ? dim3(pl.grid_x) : dim3(NP, Hkv * S, B);
-  if (codes && pl.waves == 1 && NP > 1) {
+  if (mstream) {
+    W = 8;
+    grid = dim3((uint32_t)(kResidentWaves / 8));
+  } else if (codes && pl.waves == 1 && NP > 1) {
     ppw = (int32_t)std::min<int64_t>(
         NP, std::max<int64_t>(1, (int64_t)B * Hkv * NP / kResidentWaves));
     const int32_t runs = (NP + ppw - 1) / ppw;
     W = 8;
     grid.x = (runs + W - 1) / W;
   }
-  Launcher launch = mfma    ? pick_verify(D)
-                    : codes ? pick_mfma_decode(dtype, D, RP, W)
+  Launcher launch = mfma      ? pick_verify(D)
+                    : mstream ? pick_mfma_stream_decode(D, RP)
+                    : codes   ? pick_mfma_decode(dtype, D, RP, W)
                             : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);
   DecodeArgs a{};
@@ -546,7 +565,7 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
       const size_t nseg = stream_segments((int64_t)B * Hkv * S);
       sa.tile_pre = (int32_t *)w;
       w += align_up((size_t)(B + 1) * 4, 256);
-      sa.n_waves = (int32_t)(pl.grid_x * kStreamWaves);
+      sa.n_waves = mstream ? (int32_t)(grid.x * 8) : (int32_t)(pl.grid_x * kStreamWaves);
       a.part_acc = (float *)w;
       w += align_up(nseg * RW * D * 4, 256);
       a.part_m = (float *)w;

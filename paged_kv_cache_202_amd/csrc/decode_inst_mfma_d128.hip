@@ -21,5 +21,13 @@ Launcher pick_mfma<128>(int DT, int RW, int W) {
   return nullptr;
 }
 
+template <>
+Launcher pick_mfma_stream<128>(int RW) {
+  return RW == 4    ? &launch_mfma_stream<128, 4>
+         : RW == 8  ? &launch_mfma_stream<128, 8>
+         : RW == 16 ? &launch_mfma_stream<128, 16>
+                    : nullptr;
+}
+
 }  // namespace decode
 }  // namespace pkv

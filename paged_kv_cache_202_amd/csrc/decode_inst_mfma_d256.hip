@@ -20,5 +20,10 @@ Launcher pick_mfma<256>(int DT, int RW, int W) {
   return nullptr;
 }
 
+template <>
+Launcher pick_mfma_stream<256>(int) {
+  return nullptr;  // bf16 stream mode covers head dims up to 128
+}
+
 }  // namespace decode
 }  // namespace pkv

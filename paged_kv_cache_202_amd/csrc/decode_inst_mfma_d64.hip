@@ -20,5 +20,13 @@ Launcher pick_mfma<64>(int DT, int RW, int W) {
   return nullptr;
 }
 
+template <>
+Launcher pick_mfma_stream<64>(int RW) {
+  return RW == 4    ? &launch_mfma_stream<64, 4>
+         : RW == 8  ? &launch_mfma_stream<64, 8>
+         : RW == 16 ? &launch_mfma_stream<64, 16>
+                    : nullptr;
+}
+
 }  // namespace decode
 }  // namespace pkv

@@ -1056,56 +1056,74 @@ decode_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
   }
 }
 
-// Merge of the stream kernel's segments: one workgroup per (query row,
-// sequence), thread d owns output element d; one pass with a running
-// maximum over the unit's segments w + u, w = w0 .. w1.
-template <int D, int RW, int G>
-__global__ void __launch_bounds__(D)
+// Merge of the stream kernels' segments (this file's VALU kernel and the
+// matrix-core kernel's stream mode): one workgroup per (unit, sequence) --
+// grid (Hkv * slices, B) -- holding the unit's RW rows, D / 4 threads per
+// row and four output elements per thread; two passes over the unit's
+// segments w + u, w = w0 .. w1 (their maximum, then the weighted sums), so
+// that the loads of each pass are independent.
+template <int D, int RW>
+__global__ void __launch_bounds__(RW * D / 4)
 reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
-  const int rowq = blockIdx.x;  // qi * Hq + h
-  const int b = blockIdx.y;
-  const int d = threadIdx.x;
-  const int nq = a.nq, HU = a.Hkv * a.slices;
-  const int qi = rowq / a.Hq, h = rowq % a.Hq;
-  const int rr = qi * G + (h % G);             // row within the KV head
-  const int vg = (h / G) * a.slices + rr / RW;  // its unit within the sequence
-  const int r = rr % RW;                        // its row within the unit
-  const size_t row = (size_t)b * nq * a.Hq + rowq;
+  constexpr int TPR = D / 4;  // threads per row
+  const int vg = blockIdx.x, b = blockIdx.y;  // unit within the sequence, sequence
+  const int r = threadIdx.x / TPR, d4 = (threadIdx.x % TPR) * 4;
+  const int nq = a.nq, S = a.slices, HU = a.Hkv * S, G = a.Hq / a.Hkv;
+  const int g = vg / S, rr = (vg % S) * RW + r;  // KV head, row within it
+  if (rr >= G * nq) return;                      // a padding row of the unit
+  const int qi = rr / G;
+  const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + rr % G;
   const float nan = __builtin_nanf("");
+  float4 *dst = reinterpret_cast<float4 *>(a.out + row * D + d4);
+  // the sequence's metadata in one round of independent loads
   const int L = load_const(a.lens + b);
+  const int pre_b = load_const(sa.tile_pre + b), pre_b1 = load_const(sa.tile_pre + b + 1);
+  const int pre_all = load_const(sa.tile_pre + a.B);
   if (L < nq || L > a.max_blocks * a.bs) {
-    a.out[row * D + d] = nan;
-    if (d == 0 && a.lse) a.lse[row] = nan;
+    *dst = make_float4(nan, nan, nan, nan);
+    if (d4 == 0 && a.lse) a.lse[row] = nan;
     return;
   }
-  const int64_t T = (int64_t)load_const(sa.tile_pre + a.B) * HU;
+  const int64_t T = (int64_t)pre_all * HU;
   const int64_t N = sa.n_waves;
-  const int nt = load_const(sa.tile_pre + b + 1) - load_const(sa.tile_pre + b);
-  const int64_t first = (int64_t)load_const(sa.tile_pre + b) * HU + (int64_t)vg * nt;
+  const int nt = pre_b1 - pre_b;
+  const int64_t first = (int64_t)pre_b * HU + (int64_t)vg * nt;
   const int64_t w0 = stream_wave(first, T, N), w1 = stream_wave(first + nt - 1, T, N);
   const int64_t u = (int64_t)b * HU + vg;
-  float M = kNegInf, num = 0.f, den = 0.f;
+  // with fewer tiles than wavefronts, some wavefronts hold none (and wrote
+  // nothing under their id)
+  auto held = [&](int64_t w) { return T >= N || w * T / N != (w + 1) * T / N; };
+  float M = kNegInf;
   bool bad = false;
+#pragma unroll 4
   for (int64_t w = w0; w <= w1; ++w) {
-    // with fewer tiles than wavefronts, some wavefronts hold none
-    if (T < N && w * T / N == (w + 1) * T / N) continue;
-    const size_t sid = (size_t)(w + u);
-    const float m = a.part_m[sid * RW + r];
+    const float m = held(w) ? a.part_m[(size_t)(w + u) * RW + r] : kNegInf;
     bad |= m != m;
-    if (m == kNegInf) continue;  // no visible key in the segment
-    if (m > M) {
-      const float c = exp2f(M - m);  // 0 while M is still -inf
-      num *= c;
-      den *= c;
-      M = m;
-    }
-    const float f = exp2f(m - M);
-    num = fmaf(f, a.part_acc[(sid * RW + r) * D + d], num);
-    den = fmaf(f, a.part_l[sid * RW + r], den);
+    M = fmaxf(M, m);
   }
-  a.out[row * D + d] = bad || den == 0.f ? nan : num / den;
-  if (d == 0 && a.lse) a.lse[row] = bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  if (M != kNegInf) {
+#pragma unroll 4
+    for (int64_t w = w0; w <= w1; ++w) {
+      if (!held(w)) continue;
+      const size_t si = (size_t)(w + u) * RW + r;
+      const float m = a.part_m[si];
+      // no visible key in the segment: weight 0 (m = -inf)
+      const float f = m == kNegInf ? 0.f : exp2f(m - M);
+      const float4 v = *reinterpret_cast<const float4 *>(a.part_acc + si * D + d4);
+      num.x = fmaf(f, v.x, num.x);
+      num.y = fmaf(f, v.y, num.y);
+      num.z = fmaf(f, v.z, num.z);
+      num.w = fmaf(f, v.w, num.w);
+      den = fmaf(f, a.part_l[si], den);
+    }
+  }
+  const bool dead = bad || den == 0.f;
+  *dst = dead ? make_float4(nan, nan, nan, nan)
+              : make_float4(num.x / den, num.y / den, num.z / den, num.w / den);
+  if (d4 == 0 && a.lse) a.lse[row] = dead ? nan : (M + log2f(den)) * kLn2;
 }
 
 using Launcher = void (*)(const DecodeArgs &, const StreamArgs &, dim3, hipStream_t);
@@ -1130,8 +1148,8 @@ void launch_decode(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStre
   } else if constexpr (W == 0) {  // stream kernel + its reduce; grid.x persistent workgroups
     hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, RP>), grid, dim3(kStreamWaves * 64),
                        (a.B + 1) * sizeof(int), s, a, sa);
-    hipLaunchKernelGGL((reduce_stream_kernel<D, RP, G>), dim3(a.nq * a.Hq, a.B), dim3(D),
-                       0, s, a, sa);
+    hipLaunchKernelGGL((reduce_stream_kernel<D, RP>), dim3(a.Hkv * a.slices, a.B),
+                       dim3(RP * D / 4), 0, s, a, sa);
   } else {
     hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, RP, W>), grid, dim3(W * 64), 0, s,
                        a);

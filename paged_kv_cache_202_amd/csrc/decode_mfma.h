@@ -234,9 +234,9 @@ __device__ __forceinline__ uint2 nibble_codes_f16x4(uint32_t n) {
 __device__ __forceinline__ uint32_t low_nibbles(uint32_t w) { return w & 0x0f0f0f0fu; }
 __device__ __forceinline__ uint32_t high_nibbles(uint32_t w) { return (w >> 4) & 0x0f0f0f0fu; }
 
-template <int DT, int D, int RW, int kWaves>
+template <int DT, int D, int RW, int kWaves, bool kStream>
 __global__ void __launch_bounds__(kWaves * 64)
-decode_mfma_kernel(const DecodeArgs a) {
+decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
   constexpr bool kNib = DT == kCodes3;
   constexpr bool kBf = DT == PKV_BF16;  // bf16 K/V: no codes, no scales
   constexpr int RB = kBf ? 2 * D : kNib ? D / 2 : D;  // bytes per token row
@@ -252,6 +252,7 @@ decode_mfma_kernel(const DecodeArgs a) {
   static_assert(DT == PKV_BF16 || DT == PKV_I8 || DT == kCodes3, "bf16, 8-bit or 3-bit codes");
   static_assert(!kBf || NV == NCB, "one transposing read per bf16 column block");
   static_assert(RW == 4 || RW == 8 || RW == 16, "rows per wavefront");
+  static_assert(!kStream || kWaves == 8, "stream mode: eight wavefronts per workgroup");
 
   struct Merge {
     float acc[kWaves][RW][D];
@@ -275,31 +276,114 @@ decode_mfma_kernel(const DecodeArgs a) {
   // and would make the ring's counted waits drain it). Else the
   // workgroup's wavefronts interleave the tiles of partition p = x and
   // merge in LDS.
-  const bool indep = a.parts_per_wg > 0;
-  const int ppw = indep ? a.parts_per_wg : 1;
-  const int p = indep ? ((int)blockIdx.x * kWaves + wave) * ppw : (int)blockIdx.x;
-  const int b = blockIdx.z;
-  const int g = blockIdx.y % a.Hkv, row0 = (blockIdx.y / a.Hkv) * RW;
+  //
+  // Stream mode (kStream): the stream decomposition of the VALU stream
+  // kernel on the matrix cores. The (sequence, KV head) units are laid end
+  // to end as one stream of 16-token tiles (unit u = b Hkv + g holds
+  // ceil(L_b / 16) tiles) and wavefront w of the N = sa.n_waves takes tiles
+  // [w T / N, (w + 1) T / N): equal shares whatever the lengths. Its range
+  // is cut into segments at unit boundaries; each segment runs as an
+  // independent run (q set-up, ring, softmax state) and leaves its
+  // unnormalised partials under id w + u, RW rows each, for
+  // reduce_stream_kernel. A segment's partial is stored only once its last
+  // tile has been consumed, so no store overlaps gathers in flight.
+  const bool indep = kStream || a.parts_per_wg > 0;
   const int nq = a.nq, G = a.Hq / a.Hkv;
-  const int L = load_const(a.lens + b);
   const int max_ctx = a.max_blocks * a.bs;
 
-  if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
-    if (a.num_parts == 1 && p == 0) {
-      const float nan = __builtin_nanf("");
-      for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
-        const int r = row0 + idx / D, d = idx % D, qi = r / G;
-        if (qi >= nq) continue;
-        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
-        a.out[row * D + d] = nan;
-        if (d == 0 && a.lse) a.lse[row] = nan;
-      }
+  int64_t spos = 0, send = 0;               // stream: this wavefront's tile range
+  int cur_b = 0, cur_g = 0, cur_k = 0, cur_nt = 0, cur_L = 0;  // and the tile to take next
+  int64_t stream_w = 0;
+  if constexpr (kStream) {
+    // tiles per sequence, prefix over sequences, in LDS (the ring's space,
+    // before any tile is staged); workgroup 0 also leaves it for the reduce
+    int *tp = reinterpret_cast<int *>(&sm.ring[0]);  // [B + 1]
+    int *scan = tp + a.B + 1;                        // [kWaves * 64]
+    constexpr int kThreads = kWaves * 64;
+    const int B = a.B, tid = threadIdx.x;
+    const int per = (B + kThreads - 1) / kThreads;
+    const int lo = min(B, tid * per), hi = min(B, lo + per);
+    int own = 0;
+    for (int bb = lo; bb < hi; ++bb) own += seq_tiles(load_const(a.lens + bb), nq, max_ctx);
+    scan[tid] = own;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
+      const int v = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
     }
-    return;  // with partitions, the reduce kernel writes the NaN rows
+    int run_tot = scan[tid] - own;
+    for (int bb = lo; bb < hi; ++bb) {
+      tp[bb] = run_tot;
+      run_tot += seq_tiles(load_const(a.lens + bb), nq, max_ctx);
+    }
+    if (tid == kThreads - 1) tp[B] = scan[kThreads - 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int i = tid; i <= B; i += kThreads) sa.tile_pre[i] = tp[i];
+    const int HU = a.Hkv;
+    const int64_t T = (int64_t)__builtin_amdgcn_readfirstlane(tp[B]) * HU;
+    const int64_t N = sa.n_waves;
+    stream_w = (int64_t)blockIdx.x * kWaves + wave;
+    spos = stream_w * T / N;
+    send = (stream_w + 1) * T / N;
+    if (spos < send) {  // the unit holding tile spos: HU tp[lo] <= spos < HU tp[lo + 1]
+      int l0 = 0, h0 = B;
+      while (h0 - l0 > 1) {
+        const int mid = (l0 + h0) >> 1;
+        if ((int64_t)__builtin_amdgcn_readfirstlane(tp[mid]) * HU <= spos) l0 = mid; else h0 = mid;
+      }
+      const int pre = __builtin_amdgcn_readfirstlane(tp[l0]);
+      cur_b = l0;
+      cur_nt = __builtin_amdgcn_readfirstlane(tp[l0 + 1]) - pre;
+      const int local = (int)(spos - (int64_t)pre * HU);
+      cur_g = local / cur_nt;
+      cur_k = local - cur_g * cur_nt;
+      cur_L = load_const(a.lens + l0);
+    }
+    __syncthreads();  // the prefix is read: the ring's space is free again
   }
-  const int t_begin = p * a.part_tokens;
-  if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
-  const int t_end = min(L, t_begin + ppw * a.part_tokens);
+
+  for (;;) {  // one pass, or one pass per segment in stream mode
+  int seg_tiles = 0;  // stream: tiles of this segment
+  int ppw, p, b, g, row0, L, t_begin, t_end;
+  if constexpr (kStream) {
+    if (spos >= send) return;
+    seg_tiles = (int)min<int64_t>(cur_nt - cur_k, send - spos);
+    ppw = 1;
+    p = 0;
+    b = cur_b;
+    g = cur_g;
+    row0 = 0;
+    L = cur_L;
+    t_begin = cur_k * kTile;
+    t_end = min(L, (cur_k + seg_tiles) * kTile);
+  } else {
+    ppw = indep ? a.parts_per_wg : 1;
+    p = indep ? ((int)blockIdx.x * kWaves + wave) * ppw : (int)blockIdx.x;
+    b = blockIdx.z;
+    g = blockIdx.y % a.Hkv;
+    row0 = (blockIdx.y / a.Hkv) * RW;
+    L = load_const(a.lens + b);
+
+    if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
+      if (a.num_parts == 1 && p == 0) {
+        const float nan = __builtin_nanf("");
+        for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+          const int r = row0 + idx / D, d = idx % D, qi = r / G;
+          if (qi >= nq) continue;
+          const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
+          a.out[row * D + d] = nan;
+          if (d == 0 && a.lse) a.lse[row] = nan;
+        }
+      }
+      return;  // with partitions, the reduce kernel writes the NaN rows
+    }
+    t_begin = p * a.part_tokens;
+    if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
+    t_end = min(L, t_begin + ppw * a.part_tokens);
+  }
 
   // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
   //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA; bf16 as is
@@ -407,9 +491,9 @@ decode_mfma_kernel(const DecodeArgs a) {
   for (int cb = 0; cb < NCB; ++cb) o[cb] = c32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_row = kNegInf, l_part = 0.f, w_part = 0.f;
 
-  // The partial of partition pp straight from the registers (independent
-  // wavefronts).
-  auto flush = [&](int pp) {
+  // The partial of partition pp, or in stream mode of segment id pp,
+  // straight from the registers (independent wavefronts).
+  auto flush = [&](int64_t pp) {
     float lt = l_part, wt = w_part;
     lt += exact_xor<16>(lt);
     lt += exact_xor<32>(lt);
@@ -418,7 +502,7 @@ decode_mfma_kernel(const DecodeArgs a) {
     const float off = -kOffset * wt;
     if (row_live) {
       const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
-      const size_t pi = row * a.num_parts + a.part_base + pp;
+      const size_t pi = kStream ? (size_t)pp * RW + ln : row * a.num_parts + a.part_base + pp;
       float *dst = a.part_acc + pi * D;
       if constexpr (kNib) {
 #pragma unroll
@@ -626,6 +710,22 @@ decode_mfma_kernel(const DecodeArgs a) {
     }
   }
 
+  if constexpr (kStream) {
+    flush(stream_w + (int64_t)b * a.Hkv + g);
+    spos += seg_tiles;
+    if (spos >= send) return;
+    // the segment ended at its unit's end: the next unit with tiles
+    cur_k = 0;
+    if (++cur_g == a.Hkv) {
+      cur_g = 0;
+      do {
+        ++cur_b;
+        cur_L = cur_b < a.B ? load_const(a.lens + cur_b) : 0;
+        cur_nt = cur_b < a.B ? seq_tiles(cur_L, nq, max_ctx) : 1;
+      } while (cur_nt == 0);
+    }
+    continue;
+  }
   if (indep) {
     flush(p);
     return;
@@ -699,14 +799,34 @@ decode_mfma_kernel(const DecodeArgs a) {
       }
     }
   }
+  return;
+  }  // the pass
 }
 
 template <int DT, int D, int RW, int W>
-void launch_mfma(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t s) {
+void launch_mfma(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
   constexpr int RB = DT == PKV_BF16 ? 2 * D : DT == kCodes3 ? D / 2 : D;
   static_assert(W * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16>::kBytes <= 163840,
                 "LDS of the rings");
-  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, RW, W>), grid, dim3(W * 64), 0, s, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, RW, W, false>), grid, dim3(W * 64), 0, s, a,
+                     sa);
+}
+
+// Most sequences of a stream-mode launch: its tile prefix [B + 1] and the
+// scan's 512 entries live in the ring's LDS before the first tile.
+constexpr int kMfmaStreamSeqs = 4096;
+
+// Stream mode over bf16 caches (eight independent wavefronts per
+// workgroup, grid.x = sa.n_waves / 8), then the merge of its segments.
+template <int D, int RW>
+void launch_mfma_stream(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
+  constexpr int RB = 2 * D;
+  static_assert(8 * TileRing<CodeGeo<RB>::NL, false>::kBytes >= (kMfmaStreamSeqs + 1 + 512) * 4,
+                "the tile prefix fits the rings' LDS");
+  hipLaunchKernelGGL((decode_mfma_kernel<PKV_BF16, D, RW, 8, true>), grid, dim3(8 * 64), 0, s,
+                     a, sa);
+  hipLaunchKernelGGL((reduce_stream_kernel<D, RW>), dim3(a.Hkv, a.B), dim3(RW * D / 4), 0, s,
+                     a, sa);
 }
 
 // Launcher of the MFMA decode kernel for DT = PKV_BF16 (D 64 or 128),
@@ -715,6 +835,12 @@ void launch_mfma(const DecodeArgs &a, const StreamArgs &, dim3 grid, hipStream_t
 // decode_inst_mfma_d<D>.hip.
 template <int D>
 Launcher pick_mfma(int DT, int RW, int W);
+
+// Launcher of the stream mode over bf16 caches (head dim D 64 or 128, RW
+// query rows per wavefront: 4, 8 or 16), which also launches the merge;
+// nullptr if none. Defined in decode_inst_mfma_d<D>.hip.
+template <int D>
+Launcher pick_mfma_stream(int RW);
 
 }  // namespace decode
 }  // namespace pkv

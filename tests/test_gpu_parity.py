@@ -88,6 +88,12 @@ CASES = [
     ((30, 100, 517), 16, 4, 64, "f32", 4, 0),
     ((30, 100, 517), 16, 4, 64, "f32", 4, -1),
     ((30, 100, 517), 16, 4, 128, "f32", 3, 64),
+    # the matrix-core kernel's stream mode (bf16, one query token): many
+    # short sequences, so that one wavefront's range spans many units;
+    # G = 1 and 2 (rows padded to 4 per wavefront), 16; head dim 64
+    (tuple(range(1, 400, 7)), 8, 8, 128, "bf16", 1, -1),
+    ((5, 64, 129, 700, 1025, 3), 16, 8, 64, "bf16", 1, -1),
+    ((33, 1000, 17, 2500), 16, 1, 128, "bf16", 1, -1),
 ]
 
 
@@ -154,7 +160,7 @@ def test_invalid_rows_are_nan_not_faults(device):
     lens[2] = case.max_blocks * 16 + 1
     case.d_lens = torch.from_numpy(lens).to(device)
     case.d_tables = torch.from_numpy(tables).to(device)
-    for part in (0, 16):
+    for part in (0, 16, -1):
         out, lse = case.run_gpu(part)
         for b in (0, 1, 2):
             assert np.isnan(out[b]).all() and np.isnan(lse[b]).all()
