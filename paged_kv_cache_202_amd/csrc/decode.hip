@@ -566,6 +566,7 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
       sa.tile_pre = (int32_t *)w;
       w += align_up((size_t)(B + 1) * 4, 256);
       sa.n_waves = mstream ? (int32_t)(grid.x * 8) : (int32_t)(pl.grid_x * kStreamWaves);
+      sa.seg_cost = mstream ? kMfmaStreamSegCost : 0;
       a.part_acc = (float *)w;
       w += align_up(nseg * RW * D * 4, 256);
       a.part_m = (float *)w;

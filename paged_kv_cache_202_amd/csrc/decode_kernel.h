@@ -867,8 +867,12 @@ constexpr int kStreamWaves = 4;  // wavefronts per workgroup (independent)
 
 // Stream geometry shared by the stream kernel and its reduce kernel.
 struct StreamArgs {
-  int32_t *tile_pre;  // [B + 1] tiles per unit, prefix over sequences
+  int32_t *tile_pre;  // [B + 1] slots per unit, prefix over sequences
   int32_t n_waves;    // N
+  // slots without work at the head of each unit with tiles (0 here: a
+  // unit's slots are its tiles; the matrix-core stream mode charges each
+  // unit the cost of starting a segment)
+  int32_t seg_cost;
 };
 
 __device__ __forceinline__ int seq_tiles(int L, int nq, int max_ctx) {
@@ -1087,8 +1091,8 @@ reduce_stream_kernel(const DecodeArgs a, const StreamArgs sa) {
   }
   const int64_t T = (int64_t)pre_all * HU;
   const int64_t N = sa.n_waves;
-  const int nt = pre_b1 - pre_b;
-  const int64_t first = (int64_t)pre_b * HU + (int64_t)vg * nt;
+  const int span = pre_b1 - pre_b, nt = span - sa.seg_cost;  // slots, tiles per unit
+  const int64_t first = (int64_t)pre_b * HU + (int64_t)vg * span + sa.seg_cost;  // first tile
   const int64_t w0 = stream_wave(first, T, N), w1 = stream_wave(first + nt - 1, T, N);
   const int64_t u = (int64_t)b * HU + vg;
   // with fewer tiles than wavefronts, some wavefronts hold none (and wrote

@@ -279,24 +279,36 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
   //
   // Stream mode (kStream): the stream decomposition of the VALU stream
   // kernel on the matrix cores. The (sequence, KV head) units are laid end
-  // to end as one stream of 16-token tiles (unit u = b Hkv + g holds
-  // ceil(L_b / 16) tiles) and wavefront w of the N = sa.n_waves takes tiles
-  // [w T / N, (w + 1) T / N): equal shares whatever the lengths. Its range
-  // is cut into segments at unit boundaries; each segment runs as an
-  // independent run (q set-up, ring, softmax state) and leaves its
-  // unnormalised partials under id w + u, RW rows each, for
-  // reduce_stream_kernel. A segment's partial is stored only once its last
-  // tile has been consumed, so no store overlaps gathers in flight.
+  // to end as one stream of slots: unit u = b Hkv + g holds c = sa.seg_cost
+  // slots without work (what starting a segment costs, in tile times)
+  // followed by its ceil(L_b / 16) tiles; wavefront w of the N =
+  // sa.n_waves takes slots [w T / N, (w + 1) T / N): equal costs whatever
+  // the lengths (with c = 0 a wavefront over many short units would start
+  // many segments and finish last). Its range is cut into segments at unit
+  // boundaries; each segment runs as an independent run (q set-up, ring,
+  // softmax state) and leaves its unnormalised partials under id w + u, RW
+  // rows each, for reduce_stream_kernel. A segment's partial is stored only
+  // once its last tile has been consumed, so no store overlaps gathers in
+  // flight.
   const bool indep = kStream || a.parts_per_wg > 0;
   const int nq = a.nq, G = a.Hq / a.Hkv;
   const int max_ctx = a.max_blocks * a.bs;
 
-  int64_t spos = 0, send = 0;               // stream: this wavefront's tile range
-  int cur_b = 0, cur_g = 0, cur_k = 0, cur_nt = 0, cur_L = 0;  // and the tile to take next
+  int64_t spos = 0, send = 0;  // stream: this wavefront's slot range
+  // the unit at hand: sequence, KV head, slots per unit of the sequence
+  // (c + its tiles), the sequence's length, the unit's first slot
+  int cur_b = 0, cur_g = 0, cur_span = 0, cur_L = 0;
+  int64_t cur_us = 0;
   int64_t stream_w = 0;
+  const int seg_cost = kStream ? sa.seg_cost : 0;
+  auto unit_span = [&](int len) {
+    const int nt = seq_tiles(len, nq, max_ctx);
+    return nt > 0 ? nt + seg_cost : 0;
+  };
   if constexpr (kStream) {
-    // tiles per sequence, prefix over sequences, in LDS (the ring's space,
-    // before any tile is staged); workgroup 0 also leaves it for the reduce
+    // slots per unit of each sequence, prefix over sequences, in LDS (the
+    // ring's space, before any tile is staged); workgroup 0 also leaves it
+    // for the reduce
     int *tp = reinterpret_cast<int *>(&sm.ring[0]);  // [B + 1]
     int *scan = tp + a.B + 1;                        // [kWaves * 64]
     constexpr int kThreads = kWaves * 64;
@@ -304,7 +316,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     const int per = (B + kThreads - 1) / kThreads;
     const int lo = min(B, tid * per), hi = min(B, lo + per);
     int own = 0;
-    for (int bb = lo; bb < hi; ++bb) own += seq_tiles(load_const(a.lens + bb), nq, max_ctx);
+    for (int bb = lo; bb < hi; ++bb) own += unit_span(load_const(a.lens + bb));
     scan[tid] = own;
     __syncthreads();
     for (int off = 1; off < kThreads; off <<= 1) {  // inclusive scan
@@ -316,7 +328,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     int run_tot = scan[tid] - own;
     for (int bb = lo; bb < hi; ++bb) {
       tp[bb] = run_tot;
-      run_tot += seq_tiles(load_const(a.lens + bb), nq, max_ctx);
+      run_tot += unit_span(load_const(a.lens + bb));
     }
     if (tid == kThreads - 1) tp[B] = scan[kThreads - 1];
     __syncthreads();
@@ -328,7 +340,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     stream_w = (int64_t)blockIdx.x * kWaves + wave;
     spos = stream_w * T / N;
     send = (stream_w + 1) * T / N;
-    if (spos < send) {  // the unit holding tile spos: HU tp[lo] <= spos < HU tp[lo + 1]
+    if (spos < send) {  // the unit holding slot spos: HU tp[lo] <= spos < HU tp[lo + 1]
       int l0 = 0, h0 = B;
       while (h0 - l0 > 1) {
         const int mid = (l0 + h0) >> 1;
@@ -336,29 +348,53 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       }
       const int pre = __builtin_amdgcn_readfirstlane(tp[l0]);
       cur_b = l0;
-      cur_nt = __builtin_amdgcn_readfirstlane(tp[l0 + 1]) - pre;
+      cur_span = __builtin_amdgcn_readfirstlane(tp[l0 + 1]) - pre;
       const int local = (int)(spos - (int64_t)pre * HU);
-      cur_g = local / cur_nt;
-      cur_k = local - cur_g * cur_nt;
+      cur_g = local / cur_span;
+      cur_us = (int64_t)pre * HU + (int64_t)cur_g * cur_span;
       cur_L = load_const(a.lens + l0);
     }
     __syncthreads();  // the prefix is read: the ring's space is free again
   }
 
+  // stream mode: the next unit of the stream (past this sequence's units,
+  // the next sequence with tiles); false past the last one
+  auto next_unit = [&]() {
+    cur_us += cur_span;
+    if (++cur_g < a.Hkv) return true;
+    cur_g = 0;
+    do {
+      if (++cur_b >= a.B) return false;
+      cur_L = load_const(a.lens + cur_b);
+      cur_span = unit_span(cur_L);
+    } while (cur_span == 0);
+    return true;
+  };
+
   for (;;) {  // one pass, or one pass per segment in stream mode
   int seg_tiles = 0;  // stream: tiles of this segment
   int ppw, p, b, g, row0, L, t_begin, t_end;
   if constexpr (kStream) {
-    if (spos >= send) return;
-    seg_tiles = (int)min<int64_t>(cur_nt - cur_k, send - spos);
+    // this range's part of the unit's tiles (none if it holds only the
+    // unit's cost slots)
+    int64_t lo_s, hi_s;
+    for (;;) {
+      if (spos >= send || cur_us >= send) return;
+      lo_s = max(spos, cur_us + seg_cost);
+      hi_s = min(send, cur_us + cur_span);
+      if (hi_s > lo_s) break;
+      if (cur_us + cur_span >= send || !next_unit()) return;
+    }
+    seg_tiles = (int)(hi_s - lo_s);
+    const int k0 = (int)(lo_s - cur_us - seg_cost);
     ppw = 1;
     p = 0;
     b = cur_b;
     g = cur_g;
     row0 = 0;
     L = cur_L;
-    t_begin = cur_k * kTile;
-    t_end = min(L, (cur_k + seg_tiles) * kTile);
+    t_begin = k0 * kTile;
+    t_end = min(L, (k0 + seg_tiles) * kTile);
   } else {
     ppw = indep ? a.parts_per_wg : 1;
     p = indep ? ((int)blockIdx.x * kWaves + wave) * ppw : (int)blockIdx.x;
@@ -712,18 +748,8 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 
   if constexpr (kStream) {
     flush(stream_w + (int64_t)b * a.Hkv + g);
-    spos += seg_tiles;
-    if (spos >= send) return;
-    // the segment ended at its unit's end: the next unit with tiles
-    cur_k = 0;
-    if (++cur_g == a.Hkv) {
-      cur_g = 0;
-      do {
-        ++cur_b;
-        cur_L = cur_b < a.B ? load_const(a.lens + cur_b) : 0;
-        cur_nt = cur_b < a.B ? seq_tiles(cur_L, nq, max_ctx) : 1;
-      } while (cur_nt == 0);
-    }
+    // the range ends in this unit, or goes on with the next one
+    if (cur_us + cur_span >= send || !next_unit()) return;
     continue;
   }
   if (indep) {
@@ -812,9 +838,14 @@ void launch_mfma(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream
                      sa);
 }
 
-// Most sequences of a stream-mode launch: its tile prefix [B + 1] and the
+// Most sequences of a stream-mode launch: its slot prefix [B + 1] and the
 // scan's 512 entries live in the ring's LDS before the first tile.
 constexpr int kMfmaStreamSeqs = 4096;
+// Slots without work at the head of each unit in stream mode: what a
+// segment's start costs (query load, block-id window, ring fill: a few
+// dependent memory latencies) in the time of one 16-token tile of a
+// wavefront (about 2.6 us on the 8K decode batch).
+constexpr int kMfmaStreamSegCost = 2;
 
 // Stream mode over bf16 caches (eight independent wavefronts per
 // workgroup, grid.x = sa.n_waves / 8), then the merge of its segments.
@@ -822,7 +853,7 @@ template <int D, int RW>
 void launch_mfma_stream(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
   constexpr int RB = 2 * D;
   static_assert(8 * TileRing<CodeGeo<RB>::NL, false>::kBytes >= (kMfmaStreamSeqs + 1 + 512) * 4,
-                "the tile prefix fits the rings' LDS");
+                "the slot prefix fits the rings' LDS");
   hipLaunchKernelGGL((decode_mfma_kernel<PKV_BF16, D, RW, 8, true>), grid, dim3(8 * 64), 0, s,
                      a, sa);
   hipLaunchKernelGGL((reduce_stream_kernel<D, RW>), dim3(a.Hkv, a.B), dim3(RW * D / 4), 0, s,
