@@ -131,6 +131,29 @@ def test_many_partitions_per_workgroup(device):
         assert np.abs(o - whole).max() <= 1e-5  # fp32 rounding order only
 
 
+@pytest.mark.parametrize("B", [4096, 4097])
+def test_stream_plan_at_the_sequence_limit(device, B):
+    """The balanced plan (partition_tokens = -1) runs on the matrix-core
+    kernel's stream mode for up to 4096 sequences (its slot prefix lives in
+    the ring's LDS) and on the VALU stream kernel past that; short random
+    lengths, so that one wavefront's share spans many units."""
+    lens = np.random.default_rng(B).integers(1, 40, B)
+    case = Case(lens, 8, 2, 64, 16, "bf16", seed=B, stack_seed=B)
+    check_case(case, -1)
+
+
+def test_stream_plan_placement_invariance_is_bitwise(device):
+    """The stream mode's arithmetic follows logical token order: another
+    physical placement of the same contents gives the same bits."""
+    lens = (700, 33, 1500, 5, 260, 16, 17)
+    a = Case(lens, 32, 8, 128, 16, "bf16", seed=19, stack_seed=1, num_blocks=300)
+    b = Case(lens, 32, 8, 128, 16, "bf16", seed=19, stack_seed=2, num_blocks=300)
+    assert not np.array_equal(a.tables_host, b.tables_host)
+    oa, la = a.run_gpu(-1)
+    ob, lb = b.run_gpu(-1)
+    assert np.array_equal(oa, ob) and np.array_equal(la, lb)
+
+
 def test_placement_invariance_is_bitwise(device):
     a = Case((700, 33, 1500), 32, 8, 128, 16, "bf16", seed=9, stack_seed=1, num_blocks=300)
     b = Case((700, 33, 1500), 32, 8, 128, 16, "bf16", seed=9, stack_seed=2, num_blocks=300)
