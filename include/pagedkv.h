@@ -247,9 +247,12 @@ int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
  * sequence with context_lens[b] > max_blocks * block_size, and rows whose
  * visible tokens meet a table entry outside [0, num_blocks) produce NaN in
  * out and lse instead of reading out of bounds.
- * Kernels: single query rows (nq = 1) and fp32 caches run on VALU kernels
- * (up to 16 rows per KV head: G * nq rounded up to a power of two, 8 per
- * wavefront); bf16 caches with nq > 1 run on an MFMA tile of 16 query rows
+ * Kernels: bf16 caches with one query token and D <= 128 run on a matrix-
+ * core decode kernel (all G rows of a KV head in one wavefront; with
+ * partition_tokens = -1 and B <= 4096 in its stream mode); fp32 caches and
+ * the other single-token cases run on VALU kernels (up to 16 rows per KV
+ * head: G * nq rounded up to a power of two, 8 per wavefront); bf16 caches
+ * with nq > 1 run on an MFMA tile of 16 query rows
  * per KV head (G * nq <= 16), e.g. 4 query heads x 4 draft tokens for
  * verification. With bf16 caches and G * nq > 16 the call is a chunked
  * prefill (a chunk of nq prompt tokens over the cached prefix plus the chunk
