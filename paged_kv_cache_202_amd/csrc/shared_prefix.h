@@ -508,14 +508,25 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
     for (int r = 0; r < RT; ++r) {
       float sc[TT][4];
       bool need = false;
+      if (__all(t0 + TT * kTile <= lim_p[r])) {
+        // every row of the tile sees all of the trip's tokens: no masks
 #pragma unroll
-      for (int u = 0; u < TT; ++u)
+        for (int u = 0; u < TT; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool vis = t0 + 16 * u + 4 * lg + e < lim_p[r];
-          sc[u][e] = vis ? sv[u][r][e] * scale_log2 : kNegInf;
-          need |= sc[u][e] > m_row[r] + kLazyLog2;
-        }
+          for (int e = 0; e < 4; ++e) {
+            sc[u][e] = sv[u][r][e] * scale_log2;
+            need |= sc[u][e] > m_row[r] + kLazyLog2;
+          }
+      } else {
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool vis = t0 + 16 * u + 4 * lg + e < lim_p[r];
+            sc[u][e] = vis ? sv[u][r][e] * scale_log2 : kNegInf;
+            need |= sc[u][e] > m_row[r] + kLazyLog2;
+          }
+      }
       if (__any(need)) {
         // row ln's scores are spread over the four lane groups
         float tmax = kNegInf;
