@@ -71,3 +71,27 @@ def test_code_cache_decode_replays(device):
                                       case.scale)
 
     replay_matches(step, out, device)
+
+
+def test_stream_plan_decode_replays(device):
+    """The balanced plan (partition_tokens = -1) on the matrix-core stream
+    mode: its slot prefix and segment partials live in the workspace, which
+    every call rewrites before reading."""
+    print("graph: cache write + stream-mode decode", flush=True)
+    case = Case((300, 1000, 77, 5, 2049), 32, 8, 128, 16, "bf16", seed=13, stack_seed=13,
+                device=device)
+    out = torch.empty((case.B, 1, case.Hq, case.D), dtype=torch.float32, device=device)
+    n = pkv.paged_attention_workspace_size(case.B, 1, case.Hq, case.Hkv, case.D,
+                                           case.max_blocks, case.bs, -1)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    k_new, v_new = case.k_new.to(device), case.v_new.to(device)
+
+    def step():
+        pkv.paged_cache_write(k_new, v_new, case.k_cache, case.v_cache, case.d_slots)
+        pkv.paged_attention_decode(out, case.d_q, case.k_cache, case.v_cache, case.d_tables,
+                                   case.d_lens, case.scale, partition_tokens=-1,
+                                   workspace=ws)
+
+    replay_matches(step, out, device)
+    ref, _ = case.run_oracle()
+    assert np.abs(out.cpu().numpy() - ref).max() <= 1e-2
