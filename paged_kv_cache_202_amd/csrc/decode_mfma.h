@@ -372,175 +372,401 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
   };
 
   for (;;) {  // one pass, or one pass per segment in stream mode
-  int seg_tiles = 0;  // stream: tiles of this segment
-  int ppw, p, b, g, row0, L, t_begin, t_end;
-  if constexpr (kStream) {
-    // this range's part of the unit's tiles (none if it holds only the
-    // unit's cost slots)
-    int64_t lo_s, hi_s;
-    for (;;) {
-      if (spos >= send || cur_us >= send) return;
-      lo_s = max(spos, cur_us + seg_cost);
-      hi_s = min(send, cur_us + cur_span);
-      if (hi_s > lo_s) break;
-      if (cur_us + cur_span >= send || !next_unit()) return;
-    }
-    seg_tiles = (int)(hi_s - lo_s);
-    const int k0 = (int)(lo_s - cur_us - seg_cost);
-    ppw = 1;
-    p = 0;
-    b = cur_b;
-    g = cur_g;
-    row0 = 0;
-    L = cur_L;
-    t_begin = k0 * kTile;
-    t_end = min(L, (k0 + seg_tiles) * kTile);
-  } else {
-    ppw = indep ? a.parts_per_wg : 1;
-    p = indep ? ((int)blockIdx.x * kWaves + wave) * ppw : (int)blockIdx.x;
-    b = blockIdx.z;
-    g = blockIdx.y % a.Hkv;
-    row0 = (blockIdx.y / a.Hkv) * RW;
-    L = load_const(a.lens + b);
+    int seg_tiles = 0;  // stream: tiles of this segment
+    int ppw, p, b, g, row0, L, t_begin, t_end;
+    if constexpr (kStream) {
+      // this range's part of the unit's tiles (none if it holds only the
+      // unit's cost slots)
+      int64_t lo_s, hi_s;
+      for (;;) {
+        if (spos >= send || cur_us >= send) return;
+        lo_s = max(spos, cur_us + seg_cost);
+        hi_s = min(send, cur_us + cur_span);
+        if (hi_s > lo_s) break;
+        if (cur_us + cur_span >= send || !next_unit()) return;
+      }
+      seg_tiles = (int)(hi_s - lo_s);
+      const int k0 = (int)(lo_s - cur_us - seg_cost);
+      ppw = 1;
+      p = 0;
+      b = cur_b;
+      g = cur_g;
+      row0 = 0;
+      L = cur_L;
+      t_begin = k0 * kTile;
+      t_end = min(L, (k0 + seg_tiles) * kTile);
+    } else {
+      ppw = indep ? a.parts_per_wg : 1;
+      p = indep ? ((int)blockIdx.x * kWaves + wave) * ppw : (int)blockIdx.x;
+      b = blockIdx.z;
+      g = blockIdx.y % a.Hkv;
+      row0 = (blockIdx.y / a.Hkv) * RW;
+      L = load_const(a.lens + b);
 
-    if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
-      if (a.num_parts == 1 && p == 0) {
-        const float nan = __builtin_nanf("");
-        for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
-          const int r = row0 + idx / D, d = idx % D, qi = r / G;
-          if (qi >= nq) continue;
-          const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
-          a.out[row * D + d] = nan;
-          if (d == 0 && a.lse) a.lse[row] = nan;
+      if (L < nq || L > max_ctx) {  // a row would see no key, or the table is too short
+        if (a.num_parts == 1 && p == 0) {
+          const float nan = __builtin_nanf("");
+          for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+            const int r = row0 + idx / D, d = idx % D, qi = r / G;
+            if (qi >= nq) continue;
+            const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (r % G);
+            a.out[row * D + d] = nan;
+            if (d == 0 && a.lse) a.lse[row] = nan;
+          }
+        }
+        return;  // with partitions, the reduce kernel writes the NaN rows
+      }
+      t_begin = p * a.part_tokens;
+      if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
+      t_end = min(L, t_begin + ppw * a.part_tokens);
+    }
+
+    // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
+    //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA; bf16 as is
+    //      for bf16 K, else fp16 in the order the K codes widen, scaled by 2^-e
+    //      so that the row's largest entry is in [2^7, 2^8) (fp16 keeps 11
+    //      bits) ---------------------------------------------------------------
+    const int rr = row0 + ln, qi = rr / G;
+    const bool row_live = ln < RW && qi < nq;
+    uint32_t qb[NC][4];
+    float qcorr, qfac;
+    int lim;  // keys visible to row ln
+    {
+      uint32_t w[D / 8];  // bf16 pairs: dims 2 j, 2 j + 1 of the quarter
+      if (row_live) {
+        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
+        const uint4 *src =
+            reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + lg * (D / 4));
+#pragma unroll
+        for (int j = 0; j < D / 32; ++j) {
+          const uint4 t = src[j];
+          w[4 * j] = t.x; w[4 * j + 1] = t.y; w[4 * j + 2] = t.z; w[4 * j + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) w[j] = 0u;
+      }
+      auto qdim = [&](int d) { return d % 2 ? bf16_hi(w[d / 2]) : bf16_lo(w[d / 2]); };
+      if constexpr (kBf) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) qb[c][j] = w[4 * c + j];
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 8; ++j)
+        mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+      mx = fmaxf(mx, exact_xor<16>(mx));
+      mx = fmaxf(mx, exact_xor<32>(mx));
+      int ex = 0;
+      frexpf(mx, &ex);
+      const int e = kBf || mx == 0.f ? 0 : ex - 8;
+      float sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC && !kBf; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1) for 8-bit
+          // codes; low nibbles (dims 0, 2, 4, 6) then high ones for 3-bit
+          const int d0 = kNib ? 8 * c + (j < 2 ? 4 * j : 4 * (j - 2) + 1) : 8 * c + 2 * j;
+          const int d1 = kNib ? d0 + 2 : d0 + 1;
+          const _Float16 lo = (_Float16)ldexpf(qdim(d0), -e);
+          const _Float16 hi = (_Float16)ldexpf(qdim(d1), -e);
+          sum += (float)lo + (float)hi;
+          qb[c][j] = __builtin_bit_cast(uint32_t, f16x2_t{lo, hi});
+        }
+      sum += exact_xor<16>(sum);
+      sum += exact_xor<32>(sum);
+      qcorr = kOffset * sum;
+      qfac = ldexpf(1.f, e) * a.scale_log2;
+      lim = row_live ? L - nq + qi + 1 : 0;
+    }
+
+    const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
+    const char *kbase = (const char *)a.kc;
+    const char *vbase = (const char *)a.vc;
+    int koff[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) koff[i] = code_k_lane_offset<RB>(lane, i);
+    int bad = 0;
+    // gather the tile at logical token t0 (from block blk) into a ring slot,
+    // in TileRing::stage's order: the scales (codes), the K rows (chunks
+    // permuted per token), the V rows
+    auto stage_tile = [&](Ring &ring, int slot, int t0, int blk) {
+      if (blk < 0 || blk >= a.num_blocks) {  // bad table entry: read block 0, poison later
+        bad = 1;
+        blk = 0;
+      }
+      const size_t rowi = ((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs);
+      PKV_LDS char *dst = ring.base + slot * Ring::kTileBytes;
+      if constexpr (!kBf) {
+        const size_t so = rowi * 4 + (size_t)(lane & 15) * 4;
+        gather_lds4<kKvNonTemporal>((const char *)((lane & 16) ? a.vs : a.ks) + so,
+                                    dst + Ring::kCodeBytes);
+      }
+      const char *kp = kbase + rowi * RB, *vp = vbase + rowi * RB + lane * 16;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(kp + koff[i], dst + i * 1024);
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+        gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
+    };
+
+    const int wstart = indep ? t_begin : t_begin + wave * kTile;  // this wavefront's first tile
+    const int wstride = indep ? kTile : kStride;                   // and the step between its tiles
+    const int n_tiles = wstart < t_end ? (t_end - wstart + wstride - 1) / wstride : 0;
+    auto tile_t0 = [&](int k) { return wstart + k * wstride; };
+    auto table_window = [&](int w) {
+      return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
+    };
+
+    // O^T accumulators, offsets included: o[cb][e] = O^T[m = 4 lg + e][row ln]
+    // of column block cb (8-bit: dim 16 cb + m; 3-bit: see the merge below)
+    c32x4_t o[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) o[cb] = c32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_row = kNegInf, l_part = 0.f, w_part = 0.f;
+
+    // The partial of partition pp, or in stream mode of segment id pp,
+    // straight from the registers (independent wavefronts).
+    auto flush = [&](int64_t pp) {
+      float lt = l_part, wt = w_part;
+      lt += exact_xor<16>(lt);
+      lt += exact_xor<32>(lt);
+      wt += exact_xor<16>(wt);
+      wt += exact_xor<32>(wt);
+      const float off = -kOffset * wt;
+      if (row_live) {
+        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
+        const size_t pi = kStream ? (size_t)pp * RW + ln : row * a.num_parts + a.part_base + pp;
+        float *dst = a.part_acc + pi * D;
+        if constexpr (kNib) {
+#pragma unroll
+          for (int jh = 0; jh < NCB / 2; ++jh) {
+            const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
+            float *q8 = dst + 32 * jh + 8 * lg;
+            *reinterpret_cast<float4 *>(q8) =
+                make_float4(lo[0] + off, hi[0] + off, lo[1] + off, hi[1] + off);
+            *reinterpret_cast<float4 *>(q8 + 4) =
+                make_float4(lo[2] + off, hi[2] + off, lo[3] + off, hi[3] + off);
+          }
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+            *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
+                make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
+        }
+        if (lg == 0) {
+          a.part_m[pi] = bad ? __builtin_nanf("") : m_row;
+          a.part_l[pi] = lt;
         }
       }
-      return;  // with partitions, the reduce kernel writes the NaN rows
-    }
-    t_begin = p * a.part_tokens;
-    if (t_begin >= L) return;  // past this sequence's end: the reduce reads nothing here
-    t_end = min(L, t_begin + ppw * a.part_tokens);
-  }
+    };
 
-  // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
-  //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA; bf16 as is
-  //      for bf16 K, else fp16 in the order the K codes widen, scaled by 2^-e
-  //      so that the row's largest entry is in [2^7, 2^8) (fp16 keeps 11
-  //      bits) ---------------------------------------------------------------
-  const int rr = row0 + ln, qi = rr / G;
-  const bool row_live = ln < RW && qi < nq;
-  uint32_t qb[NC][4];
-  float qcorr, qfac;
-  int lim;  // keys visible to row ln
-  {
-    uint32_t w[D / 8];  // bf16 pairs: dims 2 j, 2 j + 1 of the quarter
-    if (row_live) {
-      const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
-      const uint4 *src =
-          reinterpret_cast<const uint4 *>((const uint16_t *)a.q + row * D + lg * (D / 4));
+    if (n_tiles > 0) {
+      int tblv = table_window(0);
+      settle_v(tblv);
+      auto table_at = [&](int k) { return __builtin_amdgcn_readlane(tblv, k & 63); };
+      Ring ring;
+      PKV_LDS char *ring_base = (PKV_LDS char *)&sm.ring[0] + wave * Ring::kBytes;
+      ring.init(ring_base, lane);
+      // read-back addresses inside slot 0 (a slot adds slot * kTileBytes)
+      const PKV_LDS char *ka[KCH];
+      {
+        const int t = ln, tl = t % Gc::TPL;
+        const PKV_LDS char *row = ring_base + (t / Gc::TPL) * 1024 + tl * RB;
 #pragma unroll
-      for (int j = 0; j < D / 32; ++j) {
-        const uint4 t = src[j];
-        w[4 * j] = t.x; w[4 * j + 1] = t.y; w[4 * j + 2] = t.z; w[4 * j + 3] = t.w;
+        for (int c = 0; c < KCH; ++c) ka[c] = row + 16 * ((KCH * lg + c) ^ (t % Gc::CPT));
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 8; ++j) w[j] = 0u;
-    }
-    auto qdim = [&](int d) { return d % 2 ? bf16_hi(w[d / 2]) : bf16_lo(w[d / 2]); };
-    if constexpr (kBf) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) qb[c][j] = w[4 * c + j];
-    }
-    float mx = 0.f;
-#pragma unroll
-    for (int j = 0; j < D / 8; ++j) mx = fmaxf(mx, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
-    mx = fmaxf(mx, exact_xor<16>(mx));
-    mx = fmaxf(mx, exact_xor<32>(mx));
-    int ex = 0;
-    frexpf(mx, &ex);
-    const int e = kBf || mx == 0.f ? 0 : ex - 8;
-    float sum = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC && !kBf; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1) for 8-bit
-        // codes; low nibbles (dims 0, 2, 4, 6) then high ones for 3-bit
-        const int d0 = kNib ? 8 * c + (j < 2 ? 4 * j : 4 * (j - 2) + 1) : 8 * c + 2 * j;
-        const int d1 = kNib ? d0 + 2 : d0 + 1;
-        const _Float16 lo = (_Float16)ldexpf(qdim(d0), -e);
-        const _Float16 hi = (_Float16)ldexpf(qdim(d1), -e);
-        sum += (float)lo + (float)hi;
-        qb[c][j] = __builtin_bit_cast(uint32_t, f16x2_t{lo, hi});
+      // V, codes: lane s of group lg names token 4 lg + (s / 2) % 4, bytes
+      // 16 ((s / 2) / 4) + 8 (s % 2) .. + 7 of each 32-byte column pair; bf16:
+      // token 4 lg + s / 4, dims 4 (s % 4) .. + 3 of each 16-dim column block
+      const PKV_LDS char *va;
+      {
+        const int u = kBf ? ln >> 2 : ln >> 1, t = 4 * lg + (u & 3);
+        const int col = kBf ? 8 * (ln & 3) : 16 * (u >> 2) + 8 * (ln & 1);
+        va = ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB + col;
       }
-    sum += exact_xor<16>(sum);
-    sum += exact_xor<32>(sum);
-    qcorr = kOffset * sum;
-    qfac = ldexpf(1.f, e) * a.scale_log2;
-    lim = row_live ? L - nq + qi + 1 : 0;
-  }
-
-  const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
-  const char *kbase = (const char *)a.kc;
-  const char *vbase = (const char *)a.vc;
-  int koff[NL];
+      const PKV_LDS char *sa = ring_base + Ring::kCodeBytes + 16 * lg;
 #pragma unroll
-  for (int i = 0; i < NL; ++i) koff[i] = code_k_lane_offset<RB>(lane, i);
-  int bad = 0;
-  // gather the tile at logical token t0 (from block blk) into a ring slot,
-  // in TileRing::stage's order: the scales (codes), the K rows (chunks
-  // permuted per token), the V rows
-  auto stage_tile = [&](Ring &ring, int slot, int t0, int blk) {
-    if (blk < 0 || blk >= a.num_blocks) {  // bad table entry: read block 0, poison later
-      bad = 1;
-      blk = 0;
+      for (int k = 0; k < kSlots; ++k)
+        if (k < n_tiles) stage_tile(ring, k, tile_t0(k), table_at(k));
+      const uint32_t ones = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)1.f, (_Float16)1.f});
+
+      for (int k = 0; k < n_tiles; ++k) {
+        const int slot = k & (kSlots - 1);
+        const int ahead = min(n_tiles - 1 - k, kSlots - 1);
+        static_for<kSlots>([&](auto ac) {
+          constexpr int A = decltype(ac)::value;
+          if (ahead == A) wait_vmcnt<A * Ring::kLoads>();
+        });
+        u32x4_t kr[KCH];
+        uint2 vt[NV];
+        float4 ksc = make_float4(1.f, 1.f, 1.f, 1.f), vsc = ksc;
+        {
+          const int so = slot * Ring::kTileBytes;
+          const PKV_LDS char *kas[KCH];
+#pragma unroll
+          for (int c = 0; c < KCH; ++c) kas[c] = ka[c] + so;
+          if constexpr (kBf)
+            read_bf16<RB>(kr, vt, kas, va + so);
+          else
+            read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
+        }
+        if (k + kSlots < n_tiles) {  // the slot is free again: refill it
+          const int kn = k + kSlots;
+          if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
+            tblv = table_window(kn >> 6);
+            settle_v(tblv);
+          }
+          stage_tile(ring, slot, tile_t0(kn), table_at(kn));
+        }
+
+        // S^T = K Q^T: s[e] = row ln . token 4 lg + e (codes with offsets)
+        c32x4_t s = c32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if constexpr (kBf) {
+            const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
+                                                        __builtin_bit_cast(bf16x8_t, bv), s, 0, 0,
+                                                        0);
+            continue;
+          }
+          u32x4_t av;
+          if constexpr (kNib) {  // one word: 8 dims, low nibbles first
+            const u32x4_t kw = kr[c / 4];
+            const uint32_t wd = kw[c % 4];
+            const uint2 lo = nibble_codes_f16x4(low_nibbles(wd));
+            const uint2 hi = nibble_codes_f16x4(high_nibbles(wd));
+            av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+          } else {  // two words: 8 dims in order
+            const u32x4_t kw = kr[c / 2];
+            const uint2 lo = codes_f16x4(kw[2 * (c % 2)]), hi = codes_f16x4(kw[2 * (c % 2) + 1]);
+            av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+          }
+          const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
+          s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8_t, av),
+                                                     __builtin_bit_cast(h16x8_t, bv), s, 0, 0, 0);
+        }
+        const int t0 = tile_t0(k);
+        const float kss[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
+        const float vss[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
+        float sc[4];
+        bool need = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool vis = t0 + 4 * lg + e < lim;
+          sc[e] = vis ? (kBf ? s[e] * qfac : (s[e] - qcorr) * (kss[e] * qfac)) : kNegInf;
+          need |= sc[e] > m_row + kLazyLog2;
+        }
+        if (__any(need)) {  // raise the running maximum of row ln
+          float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+          tmax = fmaxf(tmax, exact_xor<16>(tmax));
+          tmax = fmaxf(tmax, exact_xor<32>(tmax));
+          const float mn = fmaxf(m_row, tmax);
+          const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row - mn);
+          m_row = mn;
+          l_part *= alpha;
+          w_part *= alpha;
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
+        }
+        // exp2(-inf) = 0 for masked scores; the maximum is floored so that a
+        // row with no visible key yet gives 0, not NaN
+        const float m_sub = fmaxf(m_row, -3.0e38f);
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);
+          l_part += pw;
+          // the V scale of a masked token may be stale: never multiplied
+          pv[e] = sc[e] == kNegInf ? 0.f : kBf ? pw : pw * vss[e];
+        }
+        if constexpr (kBf) {
+          // O^T += V^T P^T with bf16 weights; in a context's last tile the
+          // slots past it may hold stale bits (even NaN), zeroed so that a
+          // zero weight times NaN cannot reach the accumulators
+          if (t0 + kTile > L) {  // wavefront-uniform
+            const int tv = t0 + 4 * lg;
+            const uint32_t m01 = (tv < L ? 0xffffu : 0u) | (tv + 1 < L ? 0xffff0000u : 0u);
+            const uint32_t m23 = (tv + 2 < L ? 0xffffu : 0u) | (tv + 3 < L ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+              vt[j].x &= m01;
+              vt[j].y &= m23;
+            }
+          }
+          // each weight as a bf16 pair hi + lo (16 significant bits): one
+          // 16x16x32 product over k = (tokens, hi) then (tokens, lo), V
+          // repeated along k, so the weights lose no more than fp32 rounding
+          // would across partitionings
+          const uint32_t h01 = pack_bf16(pv[0], pv[1]), h23 = pack_bf16(pv[2], pv[3]);
+          const uint32_t l01 = pack_bf16(pv[0] - bf16_lo(h01), pv[1] - bf16_hi(h01));
+          const uint32_t l23 = pack_bf16(pv[2] - bf16_lo(h23), pv[3] - bf16_hi(h23));
+          const u32x4_t pb2 = {h01, h23, l01, l23};
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) {
+            const u32x4_t va2 = {vt[cb].x, vt[cb].y, vt[cb].x, vt[cb].y};
+            o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va2),
+                                                            __builtin_bit_cast(bf16x8_t, pb2),
+                                                            o[cb], 0, 0, 0);
+          }
+          continue;
+        }
+        const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
+        const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
+        // the fp16 weights' sum: what the V offsets add, removed at the end
+        if constexpr (DT == PKV_I8) w_part = dot2_f16(p01, ones, dot2_f16(p23, ones, w_part));
+        const h16x4_t pb = __builtin_bit_cast(h16x4_t, make_uint2(p01, p23));
+
+        // O^T += V^T P^T: A = V[tokens 4 lg .. + 3][one dim per lane]
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          if constexpr (kNib) {  // bytes 32 j + ln and 32 j + 16 + ln: four dims
+            const uint32_t x = vt[j].x, y = vt[j].y;
+            const uint32_t nib[4] = {low_nibbles(x), high_nibbles(x), low_nibbles(y),
+                                     high_nibbles(y)};
+#pragma unroll
+            for (int n = 0; n < 4; ++n)
+              o[4 * j + n] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                  __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(nib[n])), pb, o[4 * j + n],
+                  0, 0, 0);
+          } else {  // dims 32 j + ln and 32 j + 16 + ln
+            o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].x)), pb, o[2 * j], 0, 0, 0);
+            o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].y)), pb, o[2 * j + 1], 0, 0, 0);
+          }
+        }
+      }
     }
-    const size_t rowi = ((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs);
-    PKV_LDS char *dst = ring.base + slot * Ring::kTileBytes;
-    if constexpr (!kBf) {
-      const size_t so = rowi * 4 + (size_t)(lane & 15) * 4;
-      gather_lds4<kKvNonTemporal>((const char *)((lane & 16) ? a.vs : a.ks) + so,
-                                  dst + Ring::kCodeBytes);
+
+    if constexpr (kStream) {
+      flush(stream_w + (int64_t)b * a.Hkv + g);
+      // the range ends in this unit, or goes on with the next one
+      if (cur_us + cur_span >= send || !next_unit()) return;
+      continue;
     }
-    const char *kp = kbase + rowi * RB, *vp = vbase + rowi * RB + lane * 16;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(kp + koff[i], dst + i * 1024);
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-      gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
-  };
+    if (indep) {
+      flush(p);
+      return;
+    }
 
-  const int wstart = indep ? t_begin : t_begin + wave * kTile;  // this wavefront's first tile
-  const int wstride = indep ? kTile : kStride;                   // and the step between its tiles
-  const int n_tiles = wstart < t_end ? (t_end - wstart + wstride - 1) / wstride : 0;
-  auto tile_t0 = [&](int k) { return wstart + k * wstride; };
-  auto table_window = [&](int w) {
-    return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
-  };
-
-  // O^T accumulators, offsets included: o[cb][e] = O^T[m = 4 lg + e][row ln]
-  // of column block cb (8-bit: dim 16 cb + m; 3-bit: see the merge below)
-  c32x4_t o[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) o[cb] = c32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_row = kNegInf, l_part = 0.f, w_part = 0.f;
-
-  // The partial of partition pp, or in stream mode of segment id pp,
-  // straight from the registers (independent wavefronts).
-  auto flush = [&](int64_t pp) {
-    float lt = l_part, wt = w_part;
-    lt += exact_xor<16>(lt);
-    lt += exact_xor<32>(lt);
-    wt += exact_xor<16>(wt);
-    wt += exact_xor<32>(wt);
-    const float off = -kOffset * wt;
-    if (row_live) {
-      const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
-      const size_t pi = kStream ? (size_t)pp * RW + ln : row * a.num_parts + a.part_base + pp;
-      float *dst = a.part_acc + pi * D;
+    // ---- wavefront totals: row ln's weight sums over the four lane groups,
+    //      the V offsets removed, then the merge of the wavefronts in LDS -----
+    l_part += exact_xor<16>(l_part);
+    l_part += exact_xor<32>(l_part);
+    w_part += exact_xor<16>(w_part);
+    w_part += exact_xor<32>(w_part);
+    const float off = -kOffset * w_part;
+    __syncthreads();  // the partials overwrite the other wavefronts' rings
+    if (ln < RW) {
+      float *dst = sm.mg.acc[wave][ln];
       if constexpr (kNib) {
+        // block 4 j + 2 h + n holds dim 64 j + 32 h + 2 m + n (m = 4 lg + e):
+        // the two nibble blocks interleave into 8 consecutive dims
 #pragma unroll
         for (int jh = 0; jh < NCB / 2; ++jh) {
           const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
@@ -557,275 +783,46 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
               make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
       }
       if (lg == 0) {
-        a.part_m[pi] = bad ? __builtin_nanf("") : m_row;
-        a.part_l[pi] = lt;
+        sm.mg.m[wave][ln] = m_row;
+        sm.mg.l[wave][ln] = l_part;
       }
     }
-  };
+    bad = __builtin_amdgcn_readfirstlane(bad);
+    if (lane == 0) sm.mg.bad[wave] = bad;
+    __syncthreads();
 
-  if (n_tiles > 0) {
-    int tblv = table_window(0);
-    settle_v(tblv);
-    auto table_at = [&](int k) { return __builtin_amdgcn_readlane(tblv, k & 63); };
-    Ring ring;
-    PKV_LDS char *ring_base = (PKV_LDS char *)&sm.ring[0] + wave * Ring::kBytes;
-    ring.init(ring_base, lane);
-    // read-back addresses inside slot 0 (a slot adds slot * kTileBytes)
-    const PKV_LDS char *ka[KCH];
-    {
-      const int t = ln, tl = t % Gc::TPL;
-      const PKV_LDS char *row = ring_base + (t / Gc::TPL) * 1024 + tl * RB;
+    int any_bad = 0;
 #pragma unroll
-      for (int c = 0; c < KCH; ++c) ka[c] = row + 16 * ((KCH * lg + c) ^ (t % Gc::CPT));
-    }
-    // V, codes: lane s of group lg names token 4 lg + (s / 2) % 4, bytes
-    // 16 ((s / 2) / 4) + 8 (s % 2) .. + 7 of each 32-byte column pair; bf16:
-    // token 4 lg + s / 4, dims 4 (s % 4) .. + 3 of each 16-dim column block
-    const PKV_LDS char *va;
-    {
-      const int u = kBf ? ln >> 2 : ln >> 1, t = 4 * lg + (u & 3);
-      const int col = kBf ? 8 * (ln & 3) : 16 * (u >> 2) + 8 * (ln & 1);
-      va = ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB + col;
-    }
-    const PKV_LDS char *sa = ring_base + Ring::kCodeBytes + 16 * lg;
+    for (int w = 0; w < kWaves; ++w) any_bad |= sm.mg.bad[w];
+    const float nan = __builtin_nanf("");
+    for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
+      const int r = idx / D, d = idx % D, rrow = row0 + r, qr = rrow / G;
+      if (qr >= nq) continue;
+      float M = kNegInf;
 #pragma unroll
-    for (int k = 0; k < kSlots; ++k)
-      if (k < n_tiles) stage_tile(ring, k, tile_t0(k), table_at(k));
-    const uint32_t ones = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)1.f, (_Float16)1.f});
-
-    for (int k = 0; k < n_tiles; ++k) {
-      const int slot = k & (kSlots - 1);
-      const int ahead = min(n_tiles - 1 - k, kSlots - 1);
-      static_for<kSlots>([&](auto ac) {
-        constexpr int A = decltype(ac)::value;
-        if (ahead == A) wait_vmcnt<A * Ring::kLoads>();
-      });
-      u32x4_t kr[KCH];
-      uint2 vt[NV];
-      float4 ksc = make_float4(1.f, 1.f, 1.f, 1.f), vsc = ksc;
-      {
-        const int so = slot * Ring::kTileBytes;
-        const PKV_LDS char *kas[KCH];
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][r]);
+      float num = 0.f, den = 0.f;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) kas[c] = ka[c] + so;
-        if constexpr (kBf)
-          read_bf16<RB>(kr, vt, kas, va + so);
-        else
-          read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.mg.m[w][r];
+        const float f = mw == kNegInf ? 0.f : exp2f(mw - M);
+        num = fmaf(f, sm.mg.acc[w][r][d], num);
+        den = fmaf(f, sm.mg.l[w][r], den);
       }
-      if (k + kSlots < n_tiles) {  // the slot is free again: refill it
-        const int kn = k + kSlots;
-        if ((kn & 63) == 0) {  // next window of block ids (drains the ring once)
-          tblv = table_window(kn >> 6);
-          settle_v(tblv);
-        }
-        stage_tile(ring, slot, tile_t0(kn), table_at(kn));
-      }
-
-      // S^T = K Q^T: s[e] = row ln . token 4 lg + e (codes with offsets)
-      c32x4_t s = c32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if constexpr (kBf) {
-          const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
-          s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
-                                                      __builtin_bit_cast(bf16x8_t, bv), s, 0, 0,
-                                                      0);
-          continue;
-        }
-        u32x4_t av;
-        if constexpr (kNib) {  // one word: 8 dims, low nibbles first
-          const u32x4_t kw = kr[c / 4];
-          const uint32_t wd = kw[c % 4];
-          const uint2 lo = nibble_codes_f16x4(low_nibbles(wd));
-          const uint2 hi = nibble_codes_f16x4(high_nibbles(wd));
-          av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        } else {  // two words: 8 dims in order
-          const u32x4_t kw = kr[c / 2];
-          const uint2 lo = codes_f16x4(kw[2 * (c % 2)]), hi = codes_f16x4(kw[2 * (c % 2) + 1]);
-          av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-        }
-        const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8_t, av),
-                                                   __builtin_bit_cast(h16x8_t, bv), s, 0, 0, 0);
-      }
-      const int t0 = tile_t0(k);
-      const float kss[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
-      const float vss[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
-      float sc[4];
-      bool need = false;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool vis = t0 + 4 * lg + e < lim;
-        sc[e] = vis ? (kBf ? s[e] * qfac : (s[e] - qcorr) * (kss[e] * qfac)) : kNegInf;
-        need |= sc[e] > m_row + kLazyLog2;
-      }
-      if (__any(need)) {  // raise the running maximum of row ln
-        float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        tmax = fmaxf(tmax, exact_xor<16>(tmax));
-        tmax = fmaxf(tmax, exact_xor<32>(tmax));
-        const float mn = fmaxf(m_row, tmax);
-        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row - mn);
-        m_row = mn;
-        l_part *= alpha;
-        w_part *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) o[cb] *= alpha;
-      }
-      // exp2(-inf) = 0 for masked scores; the maximum is floored so that a
-      // row with no visible key yet gives 0, not NaN
-      const float m_sub = fmaxf(m_row, -3.0e38f);
-      float pv[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);
-        l_part += pw;
-        // the V scale of a masked token may be stale: never multiplied
-        pv[e] = sc[e] == kNegInf ? 0.f : kBf ? pw : pw * vss[e];
-      }
-      if constexpr (kBf) {
-        // O^T += V^T P^T with bf16 weights; in a context's last tile the
-        // slots past it may hold stale bits (even NaN), zeroed so that a
-        // zero weight times NaN cannot reach the accumulators
-        if (t0 + kTile > L) {  // wavefront-uniform
-          const int tv = t0 + 4 * lg;
-          const uint32_t m01 = (tv < L ? 0xffffu : 0u) | (tv + 1 < L ? 0xffff0000u : 0u);
-          const uint32_t m23 = (tv + 2 < L ? 0xffffu : 0u) | (tv + 3 < L ? 0xffff0000u : 0u);
-#pragma unroll
-          for (int j = 0; j < NV; ++j) {
-            vt[j].x &= m01;
-            vt[j].y &= m23;
-          }
-        }
-        // each weight as a bf16 pair hi + lo (16 significant bits): one
-        // 16x16x32 product over k = (tokens, hi) then (tokens, lo), V
-        // repeated along k, so the weights lose no more than fp32 rounding
-        // would across partitionings
-        const uint32_t h01 = pack_bf16(pv[0], pv[1]), h23 = pack_bf16(pv[2], pv[3]);
-        const uint32_t l01 = pack_bf16(pv[0] - bf16_lo(h01), pv[1] - bf16_hi(h01));
-        const uint32_t l23 = pack_bf16(pv[2] - bf16_lo(h23), pv[3] - bf16_hi(h23));
-        const u32x4_t pb2 = {h01, h23, l01, l23};
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const u32x4_t va2 = {vt[cb].x, vt[cb].y, vt[cb].x, vt[cb].y};
-          o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va2),
-                                                          __builtin_bit_cast(bf16x8_t, pb2),
-                                                          o[cb], 0, 0, 0);
-        }
-        continue;
-      }
-      const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
-      const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
-      // the fp16 weights' sum: what the V offsets add, removed at the end
-      if constexpr (DT == PKV_I8) w_part = dot2_f16(p01, ones, dot2_f16(p23, ones, w_part));
-      const h16x4_t pb = __builtin_bit_cast(h16x4_t, make_uint2(p01, p23));
-
-      // O^T += V^T P^T: A = V[tokens 4 lg .. + 3][one dim per lane]
-#pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        if constexpr (kNib) {  // bytes 32 j + ln and 32 j + 16 + ln: four dims
-          const uint32_t x = vt[j].x, y = vt[j].y;
-          o[4 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(low_nibbles(x))), pb, o[4 * j], 0, 0, 0);
-          o[4 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(high_nibbles(x))), pb, o[4 * j + 1], 0,
-              0, 0);
-          o[4 * j + 2] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(low_nibbles(y))), pb, o[4 * j + 2], 0,
-              0, 0);
-          o[4 * j + 3] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(high_nibbles(y))), pb, o[4 * j + 3], 0,
-              0, 0);
-        } else {  // dims 32 j + ln and 32 j + 16 + ln
-          o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].x)), pb, o[2 * j], 0, 0, 0);
-          o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].y)), pb, o[2 * j + 1], 0, 0, 0);
+      const size_t row = ((size_t)b * nq + qr) * a.Hq + g * G + (rrow % G);
+      if (a.num_parts == 1) {
+        a.out[row * D + d] = any_bad || den == 0.f ? nan : num / den;
+        if (d == 0 && a.lse) a.lse[row] = any_bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
+      } else {
+        const size_t pi = row * a.num_parts + a.part_base + p;
+        a.part_acc[pi * D + d] = num;
+        if (d == 0) {
+          a.part_m[pi] = any_bad ? nan : M;
+          a.part_l[pi] = den;
         }
       }
     }
-  }
-
-  if constexpr (kStream) {
-    flush(stream_w + (int64_t)b * a.Hkv + g);
-    // the range ends in this unit, or goes on with the next one
-    if (cur_us + cur_span >= send || !next_unit()) return;
-    continue;
-  }
-  if (indep) {
-    flush(p);
     return;
-  }
-
-  // ---- wavefront totals: row ln's weight sums over the four lane groups,
-  //      the V offsets removed, then the merge of the wavefronts in LDS -----
-  l_part += exact_xor<16>(l_part);
-  l_part += exact_xor<32>(l_part);
-  w_part += exact_xor<16>(w_part);
-  w_part += exact_xor<32>(w_part);
-  const float off = -kOffset * w_part;
-  __syncthreads();  // the partials overwrite the other wavefronts' rings
-  if (ln < RW) {
-    float *dst = sm.mg.acc[wave][ln];
-    if constexpr (kNib) {
-      // block 4 j + 2 h + n holds dim 64 j + 32 h + 2 m + n (m = 4 lg + e):
-      // the two nibble blocks interleave into 8 consecutive dims
-#pragma unroll
-      for (int jh = 0; jh < NCB / 2; ++jh) {
-        const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
-        float *q8 = dst + 32 * jh + 8 * lg;
-        *reinterpret_cast<float4 *>(q8) =
-            make_float4(lo[0] + off, hi[0] + off, lo[1] + off, hi[1] + off);
-        *reinterpret_cast<float4 *>(q8 + 4) =
-            make_float4(lo[2] + off, hi[2] + off, lo[3] + off, hi[3] + off);
-      }
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
-            make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
-    }
-    if (lg == 0) {
-      sm.mg.m[wave][ln] = m_row;
-      sm.mg.l[wave][ln] = l_part;
-    }
-  }
-  bad = __builtin_amdgcn_readfirstlane(bad);
-  if (lane == 0) sm.mg.bad[wave] = bad;
-  __syncthreads();
-
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) any_bad |= sm.mg.bad[w];
-  const float nan = __builtin_nanf("");
-  for (int idx = threadIdx.x; idx < RW * D; idx += kWaves * 64) {
-    const int r = idx / D, d = idx % D, rrow = row0 + r, qr = rrow / G;
-    if (qr >= nq) continue;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.mg.m[w][r]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.mg.m[w][r];
-      const float f = mw == kNegInf ? 0.f : exp2f(mw - M);
-      num = fmaf(f, sm.mg.acc[w][r][d], num);
-      den = fmaf(f, sm.mg.l[w][r], den);
-    }
-    const size_t row = ((size_t)b * nq + qr) * a.Hq + g * G + (rrow % G);
-    if (a.num_parts == 1) {
-      a.out[row * D + d] = any_bad || den == 0.f ? nan : num / den;
-      if (d == 0 && a.lse) a.lse[row] = any_bad || den == 0.f ? nan : (M + log2f(den)) * kLn2;
-    } else {
-      const size_t pi = row * a.num_parts + a.part_base + p;
-      a.part_acc[pi * D + d] = num;
-      if (d == 0) {
-        a.part_m[pi] = any_bad ? nan : M;
-        a.part_l[pi] = den;
-      }
-    }
-  }
-  return;
   }  // the pass
 }
 
