@@ -181,10 +181,16 @@ struct Plan {
   int32_t grid_x;
 };
 
+// Whether the stream kernels' per-sequence prefix of slots (32-bit) holds
+// B sequences of up to max_ctx tokens, each charged `cost` extra slots.
+bool stream_prefix_fits(int64_t B, int64_t max_ctx, int64_t cost) {
+  return B * ((max_ctx + kTile - 1) / kTile + cost) <= INT32_MAX;
+}
+
 Plan plan_launch(int64_t B, int64_t Hkv, int64_t max_ctx, int32_t req, bool stream_ok) {
   Plan pl{};
   const int64_t units = B * Hkv;
-  if (req == -1 && stream_ok) {
+  if (req == -1 && stream_ok && stream_prefix_fits(B, max_ctx, 0)) {
     pl.waves = 0;
     pl.part_tokens = 0;
     pl.num_parts = 1;
@@ -495,7 +501,8 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   // bf16 decode with one query token and D <= 128 under the stream plan:
   // the matrix-core kernel's stream mode
   const bool mstream = pl.waves == 0 && !mfma && dtype == PKV_BF16 && nq == 1 && D <= 128 &&
-                       B <= kMfmaStreamSeqs;
+                       B <= kMfmaStreamSeqs &&
+                       stream_prefix_fits(B, (int64_t)max_blocks * bs, kMfmaStreamSegCost);
   // matrix-core kernel: every row of a KV head in one wavefront (code caches;
   // bf16 decode with one query token and D <= 128)
   const bool codes = dtype == PKV_I8 || dtype == kCodes3 || mstream ||

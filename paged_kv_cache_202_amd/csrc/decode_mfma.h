@@ -349,8 +349,8 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       const int pre = __builtin_amdgcn_readfirstlane(tp[l0]);
       cur_b = l0;
       cur_span = __builtin_amdgcn_readfirstlane(tp[l0 + 1]) - pre;
-      const int local = (int)(spos - (int64_t)pre * HU);
-      cur_g = local / cur_span;
+      const int64_t local = spos - (int64_t)pre * HU;
+      cur_g = (int)(local / cur_span);
       cur_us = (int64_t)pre * HU + (int64_t)cur_g * cur_span;
       cur_L = load_const(a.lens + l0);
     }

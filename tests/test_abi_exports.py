@@ -82,6 +82,15 @@ def test_workspace_grows_with_partitions():
         pkv.paged_attention_workspace_size(64, 1, 32, 8, 128, 512, 16, -2)
 
 
+def test_stream_plan_needs_its_prefix_to_fit_32_bits():
+    # 4096 sequences x 2^20 tiles of table each: the stream kernels' slot
+    # prefix would overflow, so the balanced plan falls back to one partition
+    # per (sequence, KV head), which needs no workspace
+    assert pkv.paged_attention_workspace_size(4096, 1, 32, 8, 128, 1 << 20, 16, -1) == 0
+    # the same batch with short tables streams
+    assert pkv.paged_attention_workspace_size(4096, 1, 32, 8, 128, 64, 16, -1) > 0
+
+
 def test_every_kernel_launch_has_its_kernel():
     """A kernel template whose host-side check fails is dropped without an
     error, leaving its launch stub undefined; the library must have none."""
