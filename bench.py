@@ -117,6 +117,8 @@ def kernel_label(wk) -> str:
     tail = " + reduce_partitions_kernel" if wk.ws is not None else " (one launch per attention call)"
     if getattr(wk, "q8", False):
         kind = "int8" if wk.w.kv_codes == 8 else "3-bit"
+        if wk.part == -1:
+            return f"decode_mfma_kernel<{kind} codes> stream mode + reduce_stream_kernel"
         return f"decode_mfma_kernel<{kind} codes>" + tail
     if is_chunk(wk):
         return "chunk_mfma_kernel + reduce_partitions_kernel"

@@ -249,7 +249,8 @@ int paged_attention_workspace_size(int32_t B, int32_t nq, int32_t Hq,
  * out and lse instead of reading out of bounds.
  * Kernels: bf16 caches with one query token and D <= 128 run on a matrix-
  * core decode kernel (all G rows of a KV head in one wavefront; with
- * partition_tokens = -1 and B <= 4096 in its stream mode); fp32 caches and
+ * partition_tokens = -1 and B <= 4096 in its stream mode, as do the code
+ * caches below); fp32 caches and
  * the other single-token cases run on VALU kernels (up to 16 rows per KV
  * head: G * nq rounded up to a power of two, 8 per wavefront); bf16 caches
  * with nq > 1 run on an MFMA tile of 16 query rows

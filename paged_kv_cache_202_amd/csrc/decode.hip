@@ -257,9 +257,9 @@ size_t stream_bytes(int64_t B, int64_t units, int32_t RP, int32_t D) {
          2 * align_up(S * RP * 4, 256);
 }
 
-Launcher pick_mfma_stream_decode(int D, int RW) {
-  if (D == 64) return pick_mfma_stream<64>(RW);
-  if (D == 128) return pick_mfma_stream<128>(RW);
+Launcher pick_mfma_stream_decode(int dtype, int D, int RW) {
+  if (D == 64) return pick_mfma_stream<64>(dtype, RW);
+  if (D == 128) return pick_mfma_stream<128>(dtype, RW);
   return nullptr;
 }
 
@@ -492,17 +492,22 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
                            nq, Hq, Hkv, D, bs, num_blocks, scale, part, workspace,
                            workspace_bytes, lse_out, (hipStream_t)stream);
   const bool mfma = use_mfma(dtype, nq, G);
-  const Plan pl =
-      plan_launch(B, Hkv, (int64_t)max_blocks * bs, part, !mfma && stream_fits(dtype, D, B));
+  // the matrix-core kernel's stream mode: one query token, D <= 128, bf16
+  // caches or caches of codes, batches whose slot prefix fits its LDS and
+  // 32 bits
+  const bool mstream_ok =
+      !mfma && nq == 1 && D <= 128 &&
+      (dtype == PKV_BF16 || dtype == PKV_I8 || dtype == kCodes3) && B <= kMfmaStreamSeqs &&
+      stream_prefix_fits(B, (int64_t)max_blocks * bs, kMfmaStreamSegCost);
+  const Plan pl = plan_launch(B, Hkv, (int64_t)max_blocks * bs, part,
+                              !mfma && (mstream_ok || stream_fits(dtype, D, B)));
   const int32_t P = pl.part_tokens, NP = pl.num_parts;
   int32_t RP, S;
   row_split(G, nq, &RP, &S);
   if (mfma) S = 1;
-  // bf16 decode with one query token and D <= 128 under the stream plan:
-  // the matrix-core kernel's stream mode
-  const bool mstream = pl.waves == 0 && !mfma && dtype == PKV_BF16 && nq == 1 && D <= 128 &&
-                       B <= kMfmaStreamSeqs &&
-                       stream_prefix_fits(B, (int64_t)max_blocks * bs, kMfmaStreamSegCost);
+  // the balanced plan on the stream mode where it serves the call (else on
+  // the VALU stream kernel: fp32, D = 256, more sequences)
+  const bool mstream = pl.waves == 0 && mstream_ok;
   // matrix-core kernel: every row of a KV head in one wavefront (code caches;
   // bf16 decode with one query token and D <= 128)
   const bool codes = dtype == PKV_I8 || dtype == kCodes3 || mstream ||
@@ -530,7 +535,7 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
     grid.x = (runs + W - 1) / W;
   }
   Launcher launch = mfma      ? pick_verify(D)
-                    : mstream ? pick_mfma_stream_decode(D, RP)
+                    : mstream ? pick_mfma_stream_decode(dtype, D, RP)
                     : codes   ? pick_mfma_decode(dtype, D, RP, W)
                             : pick_launcher(dtype, D, G, RP, pl.waves);
   if (!launch) return fail(PKV_EINVAL, "no kernel for G=%d, nq=%d", G, nq);

@@ -22,11 +22,23 @@ Launcher pick_mfma<128>(int DT, int RW, int W) {
 }
 
 template <>
-Launcher pick_mfma_stream<128>(int RW) {
-  return RW == 4    ? &launch_mfma_stream<128, 4>
-         : RW == 8  ? &launch_mfma_stream<128, 8>
-         : RW == 16 ? &launch_mfma_stream<128, 16>
-                    : nullptr;
+Launcher pick_mfma_stream<128>(int DT, int RW) {
+  if (DT == PKV_BF16)
+    return RW == 4    ? &launch_mfma_stream<PKV_BF16, 128, 4>
+           : RW == 8  ? &launch_mfma_stream<PKV_BF16, 128, 8>
+           : RW == 16 ? &launch_mfma_stream<PKV_BF16, 128, 16>
+                      : nullptr;
+  if (DT == PKV_I8)
+    return RW == 4    ? &launch_mfma_stream<PKV_I8, 128, 4>
+           : RW == 8  ? &launch_mfma_stream<PKV_I8, 128, 8>
+           : RW == 16 ? &launch_mfma_stream<PKV_I8, 128, 16>
+                      : nullptr;
+  if (DT == kCodes3)
+    return RW == 4    ? &launch_mfma_stream<kCodes3, 128, 4>
+           : RW == 8  ? &launch_mfma_stream<kCodes3, 128, 8>
+           : RW == 16 ? &launch_mfma_stream<kCodes3, 128, 16>
+                      : nullptr;
+  return nullptr;
 }
 
 }  // namespace decode

@@ -21,8 +21,8 @@ Launcher pick_mfma<256>(int DT, int RW, int W) {
 }
 
 template <>
-Launcher pick_mfma_stream<256>(int) {
-  return nullptr;  // bf16 stream mode covers head dims up to 128
+Launcher pick_mfma_stream<256>(int, int) {
+  return nullptr;  // the stream mode covers head dims up to 128
 }
 
 }  // namespace decode

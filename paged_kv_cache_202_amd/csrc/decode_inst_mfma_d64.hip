@@ -21,11 +21,18 @@ Launcher pick_mfma<64>(int DT, int RW, int W) {
 }
 
 template <>
-Launcher pick_mfma_stream<64>(int RW) {
-  return RW == 4    ? &launch_mfma_stream<64, 4>
-         : RW == 8  ? &launch_mfma_stream<64, 8>
-         : RW == 16 ? &launch_mfma_stream<64, 16>
-                    : nullptr;
+Launcher pick_mfma_stream<64>(int DT, int RW) {
+  if (DT == PKV_BF16)
+    return RW == 4    ? &launch_mfma_stream<PKV_BF16, 64, 4>
+           : RW == 8  ? &launch_mfma_stream<PKV_BF16, 64, 8>
+           : RW == 16 ? &launch_mfma_stream<PKV_BF16, 64, 16>
+                      : nullptr;
+  if (DT == PKV_I8)
+    return RW == 4    ? &launch_mfma_stream<PKV_I8, 64, 4>
+           : RW == 8  ? &launch_mfma_stream<PKV_I8, 64, 8>
+           : RW == 16 ? &launch_mfma_stream<PKV_I8, 64, 16>
+                      : nullptr;
+  return nullptr;
 }
 
 }  // namespace decode

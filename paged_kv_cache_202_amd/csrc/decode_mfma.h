@@ -844,15 +844,17 @@ constexpr int kMfmaStreamSeqs = 4096;
 // wavefront (about 2.6 us on the 8K decode batch).
 constexpr int kMfmaStreamSegCost = 2;
 
-// Stream mode over bf16 caches (eight independent wavefronts per
-// workgroup, grid.x = sa.n_waves / 8), then the merge of its segments.
-template <int D, int RW>
+// Stream mode over bf16 caches or caches of codes (eight independent
+// wavefronts per workgroup, grid.x = sa.n_waves / 8), then the merge of its
+// segments.
+template <int DT, int D, int RW>
 void launch_mfma_stream(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
-  constexpr int RB = 2 * D;
-  static_assert(8 * TileRing<CodeGeo<RB>::NL, false>::kBytes >= (kMfmaStreamSeqs + 1 + 512) * 4,
+  constexpr int RB = DT == PKV_BF16 ? 2 * D : DT == kCodes3 ? D / 2 : D;
+  static_assert(8 * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16>::kBytes >=
+                    (kMfmaStreamSeqs + 1 + 512) * 4,
                 "the slot prefix fits the rings' LDS");
-  hipLaunchKernelGGL((decode_mfma_kernel<PKV_BF16, D, RW, 8, true>), grid, dim3(8 * 64), 0, s,
-                     a, sa);
+  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, RW, 8, true>), grid, dim3(8 * 64), 0, s, a,
+                     sa);
   hipLaunchKernelGGL((reduce_stream_kernel<D, RW>), dim3(a.Hkv, a.B), dim3(RW * D / 4), 0, s,
                      a, sa);
 }
@@ -864,11 +866,12 @@ void launch_mfma_stream(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hi
 template <int D>
 Launcher pick_mfma(int DT, int RW, int W);
 
-// Launcher of the stream mode over bf16 caches (head dim D 64 or 128, RW
-// query rows per wavefront: 4, 8 or 16), which also launches the merge;
-// nullptr if none. Defined in decode_inst_mfma_d<D>.hip.
+// Launcher of the stream mode over DT = PKV_BF16 or PKV_I8 (head dim D 64
+// or 128) or kCodes3 (D 128), RW query rows per wavefront (4, 8 or 16),
+// which also launches the merge; nullptr if none. Defined in
+// decode_inst_mfma_d<D>.hip.
 template <int D>
-Launcher pick_mfma_stream(int RW);
+Launcher pick_mfma_stream(int DT, int RW);
 
 }  // namespace decode
 }  // namespace pkv

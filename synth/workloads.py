@@ -105,6 +105,13 @@ WORKLOADS = {
         index=8, name="llama3_8b_b32_8k_q3", dtype="bf16", q_heads=32,
         kv_heads=8, head_dim=128, block_size=16, batch=32, num_blocks=16384,
         context=8192, kv_codes=3),
+    # the variable-length batch over 8-bit codes (same seed, so the same
+    # lengths and placement as the bf16 batch)
+    "llama3_8b_varlen_b256_q8": Workload(
+        index=3, name="llama3_8b_varlen_b256_q8", dtype="bf16", q_heads=32,
+        kv_heads=8, head_dim=128, block_size=16, batch=256, num_blocks=32768,
+        lognormal_median=1024.0, lognormal_sigma=1.0, length_clip=(16, 8192),
+        partition_tokens=-1, kv_codes=8),
     # chunked prefill: each sequence's last 512-token prompt chunk over its
     # 7680 cached tokens (the notebook's 16 chunks of 512 for an 8K prompt)
     "llama3_8b_chunk512_b4_8k": Workload(

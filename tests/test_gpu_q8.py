@@ -179,6 +179,10 @@ CASES = [
     ((515, 47, 2000), 64, 8, 128, 1, -1),   # G = 8: 8 rows per wavefront
     ((90, 600), 32, 8, 128, 4, 0),          # 4 drafts x 4 heads: 16 rows per wavefront
     ((400,), 8, 4, 64, 2, 128),
+    # the balanced plan on the stream mode: mixed lengths, G = 4 and 2
+    ((1, 15, 16, 17, 100, 333, 2049, 700), 32, 8, 128, 1, -1),
+    ((5, 64, 129, 700, 1025, 3), 16, 8, 64, 1, -1),
+    (tuple(range(1, 300, 11)), 8, 2, 128, 1, -1),
 ]
 
 
