@@ -233,11 +233,13 @@ def test_q8_bad_table_and_short_context_give_nan(device):
     assert np.abs(out[0].reshape(-1, 128) - ref).max() <= 1e-2
 
 
-@pytest.mark.parametrize("name,bits", [("llama3_8b_b32_8k_q8", 8), ("llama3_8b_b32_8k_q3", 3)])
+@pytest.mark.parametrize("name,bits", [("llama3_8b_b32_8k_q8", 8), ("llama3_8b_b32_8k_q3", 3),
+                                       ("llama3_8b_varlen_b256_q8", 8)])
 def test_q8_full_size_sampled(name, bits, device):
     """The 8K decode batch (32 sequences, Llama-3-8B layer geometry) over an
-    8-bit (3-bit) code cache, in the launch configuration bench.py times:
-    slots and tables bit for bit, the codes of four sequences bit for bit,
+    8-bit (3-bit) code cache, and the variable-length batch of 256 over 8-bit
+    codes (the stream mode), in the launch configuration bench.py times:
+    slots and tables bit for bit, the codes of a few sequences bit for bit,
     and their rows against the C oracle."""
     import bench
 
@@ -260,8 +262,10 @@ def test_q8_full_size_sampled(name, bits, device):
     wk.step(0)
     torch.cuda.synchronize()
     out = wk.out.cpu().numpy()
-    # the oracle quantizes the rows of sequences 0, 9, 20 and 31 only
-    seqs = [0, 9, 20, 31]
+    # the oracle quantizes the rows of a few sequences only (for the
+    # variable-length batch also the longest and the last one)
+    seqs = [0, 9, 20, 31] if wk.B == 32 else sorted({0, 9, 100, int(np.argmax(wk.lens)),
+                                                      wk.B - 1})
     starts = np.concatenate([[0], np.cumsum(wk.lens)[:-1]])
     kbits, vbits = host_bits(wk.host_k), host_bits(wk.host_v)
     shape = (wk.w.num_blocks, wk.Hkv, wk.bs, wk.D)
