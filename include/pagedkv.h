@@ -121,12 +121,16 @@ int paged_kv_alloc(pkv_pool *pool, int64_t seq_id, int32_t n_tokens,
                    int32_t *slot_mapping_out, pkv_cow_t *cow_out,
                    int32_t *n_cow_out);
 
-/* paged_kv_alloc for n_seqs sequences in order, as separate calls would.
- * Slots are written back to back into slot_mapping_out (sum of n_tokens
- * entries); copy pairs back to back into cow_out (capacity n_seqs);
- * *n_cow_out gets their count and *n_done the number of sequences handled.
- * Stops at the first failing sequence (earlier ones stay applied) and
- * returns its code. */
+/* paged_kv_alloc for n_seqs sequences in order, with the results separate
+ * calls would give (an id may repeat; a copy made for one member counts when
+ * a later member writes into the same shared block). All or nothing
+ * ([KVNB s5]: allocation is preflighted so a failure changes nothing): the
+ * whole batch is checked first -- unknown ids (ENOENT), negative counts or a
+ * length past INT32_MAX (EINVAL), and the free blocks all members take
+ * together (ENOMEM) -- and on any error the pool is unchanged and *n_done
+ * is 0. On success slots are written back to back into slot_mapping_out
+ * (sum of n_tokens entries), copy pairs back to back into cow_out (capacity
+ * n_seqs), *n_cow_out gets their count and *n_done = n_seqs. */
 int paged_kv_alloc_batch(pkv_pool *pool, const int64_t *seq_ids,
                          const int32_t *n_tokens, int32_t n_seqs,
                          int32_t *slot_mapping_out, pkv_cow_t *cow_out,

@@ -75,7 +75,8 @@ class PagedKVPool:
         return slots[:n_tokens], [(cow[i].src, cow[i].dst) for i in range(n_cow.value)]
 
     def alloc_batch(self, seq_ids, n_tokens):
-        """Returns (slots, copy pairs [n, 2] int32, n_done); raises on failure."""
+        """Returns (slots, copy pairs [n, 2] int32). All or nothing: on any error the
+        pool is unchanged and the error is raised."""
         ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
         ns = np.ascontiguousarray(n_tokens, dtype=np.int32)
         slots = np.empty(max(int(ns.sum()), 1), dtype=np.int32)

@@ -18,6 +18,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
@@ -46,14 +47,16 @@ using pkv::fail;
 
 struct SeqState {
   int32_t length = 0;
-  std::vector<int32_t> blocks;
+  std::vector<int32_t> blocks;  // exactly ceil(length / bs) ids
 };
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct pkv_pool {
   int32_t total = 0;
   int32_t bs = 0;
   std::vector<int32_t> free_stack;  // back() is handed out next
-  std::vector<int32_t> refs;
+  std::vector<int32_t> refs;        // table entries naming each block
   std::map<int64_t, SeqState> seqs;
 
   int32_t take() {
@@ -62,20 +65,19 @@ struct pkv_pool {
     refs[b] = 1;
     return b;
   }
-  void drop(int32_t b) {
-    if (--refs[b] == 0) free_stack.push_back(b);
+  // One reference less for each id, in order; blocks nobody names any more
+  // go on top of the free stack in that order.
+  void unref(const int32_t *b, size_t n) {
+    for (size_t i = 0; i < n; ++i) refs[b[i]] -= 1;
+    for (size_t i = 0; i < n; ++i)
+      if (refs[b[i]] == 0) free_stack.push_back(b[i]);
   }
-  // Blocks an append of n tokens needs, counting a private copy of a shared
-  // partial last block.
-  int64_t blocks_needed(const SeqState &s, int64_t n) const {
-    if (n == 0) return 0;
-    int64_t used = s.length % bs, room = 0, extra = 0;
-    if (!s.blocks.empty() && used) {
-      room = bs - used;
-      if (refs[s.blocks.back()] > 1) extra = 1;
-    }
-    int64_t rest = std::max<int64_t>(0, n - room);
-    return extra + (rest + bs - 1) / bs;
+  // Table entries a sequence of `len` tokens gains by growing by n.
+  int64_t grow(int64_t len, int64_t n) const { return ceil_div(len + n, bs) - ceil_div(len, bs); }
+  // A write of n > 0 tokens into a partial last block that `tail_refs`
+  // tables name must first move the sequence to a private copy.
+  bool copy_first(int64_t len, int64_t n, int32_t tail_refs) const {
+    return n > 0 && len % bs != 0 && tail_refs > 1;
   }
   std::vector<int32_t> fills() const {
     std::vector<int32_t> f(total, 0);
@@ -94,45 +96,112 @@ static int check_pool(const pkv_pool *p) {
   return p ? PKV_OK : fail(PKV_EINVAL, "pool handle is NULL");
 }
 
-// Append without argument checks (callers check); returns status.
-static int do_alloc(pkv_pool *p, int64_t id, int32_t n, int32_t *slots,
-                    pkv_cow_t *cow, int32_t *n_cow) {
-  auto it = p->seqs.find(id);
-  if (it == p->seqs.end()) return fail(PKV_ENOENT, "unknown sequence %lld", (long long)id);
-  SeqState &s = it->second;
-  if ((int64_t)s.length + n > INT32_MAX)
-    return fail(PKV_EINVAL, "sequence %lld would exceed INT32_MAX tokens", (long long)id);
-  int64_t need = p->blocks_needed(s, n);
-  if (need > (int64_t)p->free_stack.size())
-    return fail(PKV_ENOMEM, "need %lld free blocks, %zu remain", (long long)need,
-                p->free_stack.size());
+// Grow a sequence by n tokens; the caller has checked that the free stack
+// holds what this takes. The private copy (if any) is taken first, then the
+// new table entries in order; each new token's slot follows from the table.
+static void apply_alloc(pkv_pool *p, SeqState &s, int32_t n, int32_t *slots, pkv_cow_t *cow,
+                        int32_t *n_cow) {
   *n_cow = 0;
-  if (n == 0) return PKV_OK;
+  if (!s.blocks.empty() && p->copy_first(s.length, n, p->refs[s.blocks.back()])) {
+    const int32_t shared = s.blocks.back();
+    p->refs[shared] -= 1;  // another table still names it
+    s.blocks.back() = p->take();
+    cow[0].src = shared;
+    cow[0].dst = s.blocks.back();
+    *n_cow = 1;
+  }
+  for (int64_t g = p->grow(s.length, n); g > 0; --g) s.blocks.push_back(p->take());
   const int32_t bs = p->bs;
-  int32_t used = s.length % bs;
-  int32_t k = 0;
-  if (!s.blocks.empty() && used) {
-    int32_t last = s.blocks.back();
-    if (p->refs[last] > 1) {
-      p->refs[last] -= 1;
-      int32_t fresh = p->take();
-      s.blocks.back() = fresh;
-      cow[0].src = last;
-      cow[0].dst = fresh;
-      *n_cow = 1;
+  for (int32_t k = 0; k < n; ++k) {
+    const int32_t t = s.length + k;
+    slots[k] = s.blocks[t / bs] * bs + t % bs;
+  }
+  s.length += n;
+}
+
+// Preflight of appends of ns[i] tokens to ids[i], i < n, in order, as
+// separate appends would see the pool: unknown ids, the int32 length limit
+// and the free blocks all of them take together (new entries, plus a copy
+// when a member writes into a partial last block still named by another
+// table; a copy made earlier in the batch lowers that block's count, and a
+// sequence whose append went through owns its last block). Changes nothing.
+static int preflight(const pkv_pool *p, const int64_t *ids, const int32_t *ns, int32_t n,
+                     std::vector<SeqState *> *rows) {
+  std::unordered_map<int64_t, int64_t> len;      // lengths as the batch leaves them
+  std::unordered_map<int64_t, char> owns_tail;   // a nonzero append happened
+  std::unordered_map<int32_t, int32_t> copied;   // copies made off each shared block
+  int64_t need = 0;
+  rows->assign(n, nullptr);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = p->seqs.find(ids[i]);
+    if (it == p->seqs.end()) return fail(PKV_ENOENT, "no sequence with id %lld", (long long)ids[i]);
+    SeqState *s = const_cast<SeqState *>(&it->second);
+    (*rows)[i] = s;
+    auto lit = len.find(ids[i]);
+    const int64_t L = lit == len.end() ? s->length : lit->second;
+    if (L + ns[i] > INT32_MAX)
+      return fail(PKV_EINVAL, "sequence %lld would pass INT32_MAX tokens", (long long)ids[i]);
+    need += p->grow(L, ns[i]);
+    if (!owns_tail[ids[i]] && !s->blocks.empty()) {
+      const int32_t tail = s->blocks.back();
+      if (p->copy_first(L, ns[i], p->refs[tail] - copied[tail])) {
+        need += 1;
+        copied[tail] += 1;
+      }
     }
-    int32_t take = std::min(n, bs - used);
-    const int32_t base = s.blocks.back() * bs + used;
-    for (int32_t j = 0; j < take; ++j) slots[k++] = base + j;
-    s.length += take;
+    if (ns[i] > 0) owns_tail[ids[i]] = 1;
+    len[ids[i]] = L + ns[i];
   }
-  while (k < n) {
-    int32_t take = std::min(n - k, bs);
-    int32_t b = p->take();
-    s.blocks.push_back(b);
-    for (int32_t j = 0; j < take; ++j) slots[k++] = b * bs + j;
-    s.length += take;
+  if (need > (int64_t)p->free_stack.size())
+    return fail(PKV_ENOMEM, "append wants %lld blocks; the pool has %zu", (long long)need,
+                p->free_stack.size());
+  return PKV_OK;
+}
+
+// The invariants of the page pool's validate. Fills are derived from the
+// tables once those are known to name only ids inside the pool; `fill_in`
+// (when not NULL) stands in for them, so a checker can hand in fills that
+// disagree with the tables.
+static int check_invariants(const pkv_pool *p, const std::vector<int32_t> *fill_in) {
+  const int32_t n = p->total;
+  std::vector<char> on_stack(n, 0);
+  for (int32_t b : p->free_stack) {
+    if (b < 0 || b >= n) return fail(PKV_ECORRUPT, "free stack names id %d outside the pool", b);
+    if (on_stack[b]) return fail(PKV_ECORRUPT, "free stack names block %d twice", b);
+    on_stack[b] = 1;
   }
+  std::vector<int64_t> named(n, 0);
+  int64_t logical = 0;
+  for (const auto &kv : p->seqs) {
+    const SeqState &s = kv.second;
+    const long long id = (long long)kv.first;
+    if (s.length < 0) return fail(PKV_ECORRUPT, "sequence %lld has a negative length", id);
+    if ((int64_t)s.blocks.size() != ceil_div(s.length, p->bs))
+      return fail(PKV_ECORRUPT, "sequence %lld: table size disagrees with its length", id);
+    std::vector<int32_t> sorted(s.blocks);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
+      return fail(PKV_ECORRUPT, "sequence %lld names one block twice", id);
+    for (int32_t b : s.blocks) {
+      if (b < 0 || b >= n) return fail(PKV_ECORRUPT, "sequence %lld names id %d outside the pool", id, b);
+      named[b] += 1;
+    }
+    logical += s.length;
+  }
+  const std::vector<int32_t> fill = fill_in ? *fill_in : p->fills();
+  int64_t payload = 0;
+  for (int32_t b = 0; b < n; ++b) {
+    if (p->refs[b] != named[b])
+      return fail(PKV_ECORRUPT, "block %d: count %d but %lld names", b, p->refs[b],
+                  (long long)named[b]);
+    if (named[b] && on_stack[b]) return fail(PKV_ECORRUPT, "block %d is named and also free", b);
+    if (!named[b] && !on_stack[b]) return fail(PKV_ECORRUPT, "block %d is neither named nor free", b);
+    if (named[b]) {
+      if (fill[b] < 1 || fill[b] > p->bs) return fail(PKV_ECORRUPT, "block %d holds %d tokens", b, fill[b]);
+      payload += fill[b];
+    }
+  }
+  if (payload > logical) return fail(PKV_ECORRUPT, "more tokens stored than the sequences hold");
   return PKV_OK;
 }
 
@@ -173,7 +242,7 @@ void paged_kv_pool_destroy(pkv_pool *pool) { delete pool; }
 
 int paged_kv_seq_create(pkv_pool *p, int64_t id) {
   if (int rc = check_pool(p)) return rc;
-  if (p->seqs.count(id)) return fail(PKV_EEXIST, "sequence %lld already exists", (long long)id);
+  if (p->seqs.count(id)) return fail(PKV_EEXIST, "id %lld is taken", (long long)id);
   p->seqs.emplace(id, SeqState{});
   return PKV_OK;
 }
@@ -181,10 +250,13 @@ int paged_kv_seq_create(pkv_pool *p, int64_t id) {
 int paged_kv_alloc(pkv_pool *p, int64_t id, int32_t n, int32_t *slots,
                    pkv_cow_t *cow, int32_t *n_cow) {
   if (int rc = check_pool(p)) return rc;
-  if (n < 0) return fail(PKV_EINVAL, "n_tokens must be >= 0");
+  if (n < 0) return fail(PKV_EINVAL, "an append needs n_tokens >= 0");
   if ((n > 0 && !slots) || !cow || !n_cow)
     return fail(PKV_EINVAL, "slot_mapping_out, cow_out and n_cow_out are required");
-  return do_alloc(p, id, n, slots, cow, n_cow);
+  std::vector<SeqState *> row;
+  if (int rc = preflight(p, &id, &n, 1, &row)) return rc;
+  apply_alloc(p, *row[0], n, slots, cow, n_cow);
+  return PKV_OK;
 }
 
 int paged_kv_alloc_batch(pkv_pool *p, const int64_t *ids, const int32_t *ns,
@@ -194,36 +266,37 @@ int paged_kv_alloc_batch(pkv_pool *p, const int64_t *ids, const int32_t *ns,
   if (n_seqs < 0) return fail(PKV_EINVAL, "n_seqs must be >= 0");
   if (!n_cow || !n_done || (n_seqs > 0 && (!ids || !ns || !cow)))
     return fail(PKV_EINVAL, "NULL argument");
+  *n_cow = 0;
+  *n_done = 0;
   int64_t total = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     if (ns[i] < 0) return fail(PKV_EINVAL, "n_tokens[%d] < 0", i);
     total += ns[i];
   }
   if (total > 0 && !slots) return fail(PKV_EINVAL, "slot_mapping_out is NULL");
-  *n_cow = 0;
-  *n_done = 0;
+  std::vector<SeqState *> rows;
+  if (int rc = preflight(p, ids, ns, n_seqs, &rows)) return rc;
   int64_t off = 0;
   for (int32_t i = 0; i < n_seqs; ++i) {
     int32_t c = 0;
-    int rc = do_alloc(p, ids[i], ns[i], slots + off, cow + *n_cow, &c);
-    if (rc) return rc;
+    apply_alloc(p, *rows[i], ns[i], slots + off, cow + *n_cow, &c);
     off += ns[i];
     *n_cow += c;
-    *n_done = i + 1;
   }
+  *n_done = n_seqs;
   return PKV_OK;
 }
 
 int paged_kv_fork(pkv_pool *p, int64_t parent, int64_t child, int32_t prefix) {
   if (int rc = check_pool(p)) return rc;
   auto it = p->seqs.find(parent);
-  if (it == p->seqs.end()) return fail(PKV_ENOENT, "unknown sequence %lld", (long long)parent);
+  if (it == p->seqs.end()) return fail(PKV_ENOENT, "no sequence with id %lld", (long long)parent);
   if (prefix < 0) return fail(PKV_EINVAL, "prefix_tokens must be >= 0");
   if (prefix > it->second.length)
-    return fail(PKV_EINVAL, "prefix_tokens %d exceeds parent length %d", prefix,
+    return fail(PKV_EINVAL, "prefix of %d tokens is longer than the parent (%d)", prefix,
                 it->second.length);
   if (p->seqs.count(child))
-    return fail(PKV_EEXIST, "target sequence %lld already exists", (long long)child);
+    return fail(PKV_EEXIST, "fork target %lld is taken", (long long)child);
   SeqState s;
   s.length = prefix;
   int32_t count = (prefix + p->bs - 1) / p->bs;
@@ -236,8 +309,8 @@ int paged_kv_fork(pkv_pool *p, int64_t parent, int64_t child, int32_t prefix) {
 int paged_kv_free(pkv_pool *p, int64_t id) {
   if (int rc = check_pool(p)) return rc;
   auto it = p->seqs.find(id);
-  if (it == p->seqs.end()) return fail(PKV_ENOENT, "unknown sequence %lld", (long long)id);
-  for (int32_t b : it->second.blocks) p->drop(b);
+  if (it == p->seqs.end()) return fail(PKV_ENOENT, "no sequence with id %lld", (long long)id);
+  p->unref(it->second.blocks.data(), it->second.blocks.size());
   p->seqs.erase(it);
   return PKV_OK;
 }
@@ -245,13 +318,14 @@ int paged_kv_free(pkv_pool *p, int64_t id) {
 int paged_kv_truncate(pkv_pool *p, int64_t id, int32_t new_length) {
   if (int rc = check_pool(p)) return rc;
   auto it = p->seqs.find(id);
-  if (it == p->seqs.end()) return fail(PKV_ENOENT, "unknown sequence %lld", (long long)id);
+  if (it == p->seqs.end()) return fail(PKV_ENOENT, "no sequence with id %lld", (long long)id);
   SeqState &s = it->second;
   if (new_length < 0 || new_length > s.length)
-    return fail(PKV_EINVAL, "new_length %d outside [0, %d]", new_length, s.length);
-  size_t keep = (size_t)((new_length + p->bs - 1) / p->bs);
-  for (size_t j = keep; j < s.blocks.size(); ++j) p->drop(s.blocks[j]);
+    return fail(PKV_EINVAL, "a new length must lie in [0, %d], not %d", s.length, new_length);
+  const size_t keep = (size_t)ceil_div(new_length, p->bs);
+  std::vector<int32_t> dropped(s.blocks.begin() + keep, s.blocks.end());
   s.blocks.resize(keep);
+  p->unref(dropped.data(), dropped.size());
   s.length = new_length;
   return PKV_OK;
 }
@@ -260,7 +334,7 @@ int paged_kv_seq_length(const pkv_pool *p, int64_t id, int32_t *len) {
   if (int rc = check_pool(p)) return rc;
   if (!len) return fail(PKV_EINVAL, "len is NULL");
   auto it = p->seqs.find(id);
-  if (it == p->seqs.end()) return fail(PKV_ENOENT, "unknown sequence %lld", (long long)id);
+  if (it == p->seqs.end()) return fail(PKV_ENOENT, "no sequence with id %lld", (long long)id);
   *len = it->second.length;
   return PKV_OK;
 }
@@ -281,7 +355,7 @@ int paged_kv_page_table(const pkv_pool *p, int64_t id, int32_t *out, int32_t cap
   if (int rc = check_pool(p)) return rc;
   if (!n_out) return fail(PKV_EINVAL, "n_out is NULL");
   auto it = p->seqs.find(id);
-  if (it == p->seqs.end()) return fail(PKV_ENOENT, "unknown sequence %lld", (long long)id);
+  if (it == p->seqs.end()) return fail(PKV_ENOENT, "no sequence with id %lld", (long long)id);
   const auto &bl = it->second.blocks;
   *n_out = (int32_t)bl.size();
   if ((size_t)cap < bl.size() || (cap > 0 && !out))
@@ -310,7 +384,7 @@ int paged_kv_block_tables(const pkv_pool *p, const int64_t *ids, int32_t n,
   for (int32_t i = 0; i < n; ++i) {
     auto it = p->seqs.find(ids[i]);
     if (it == p->seqs.end())
-      return fail(PKV_ENOENT, "unknown sequence %lld", (long long)ids[i]);
+      return fail(PKV_ENOENT, "no sequence with id %lld", (long long)ids[i]);
     if ((int64_t)it->second.blocks.size() > max_blocks)
       return fail(PKV_EINVAL, "sequence %lld has %zu blocks > max_blocks %d",
                   (long long)ids[i], it->second.blocks.size(), max_blocks);
@@ -346,48 +420,7 @@ int paged_kv_stats(const pkv_pool *p, pkv_stats_t *st) {
 
 int paged_kv_validate(const pkv_pool *p) {
   if (int rc = check_pool(p)) return rc;
-  const int32_t n = p->total;
-  std::vector<char> on_free(n, 0);
-  for (int32_t b : p->free_stack) {
-    if (b < 0 || b >= n) return fail(PKV_ECORRUPT, "free stack holds invalid id %d", b);
-    if (on_free[b]) return fail(PKV_ECORRUPT, "free stack holds %d twice", b);
-    on_free[b] = 1;
-  }
-  std::vector<int64_t> expect(n, 0);
-  int64_t logical = 0;
-  for (const auto &kv : p->seqs) {
-    const SeqState &s = kv.second;
-    if (s.length < 0) return fail(PKV_ECORRUPT, "negative length");
-    if ((int64_t)s.blocks.size() != ((int64_t)s.length + p->bs - 1) / p->bs)
-      return fail(PKV_ECORRUPT, "table length does not match length of %lld",
-                  (long long)kv.first);
-    std::vector<int32_t> sorted(s.blocks);
-    std::sort(sorted.begin(), sorted.end());
-    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end())
-      return fail(PKV_ECORRUPT, "sequence %lld names a block twice", (long long)kv.first);
-    for (int32_t b : s.blocks) {
-      if (b < 0 || b >= n) return fail(PKV_ECORRUPT, "table holds invalid id %d", b);
-      expect[b] += 1;
-    }
-    logical += s.length;
-  }
-  std::vector<int32_t> f = p->fills();
-  int64_t payload = 0;
-  for (int32_t b = 0; b < n; ++b) {
-    if (p->refs[b] != expect[b])
-      return fail(PKV_ECORRUPT, "block %d: ref %d but %lld table entries", b, p->refs[b],
-                  (long long)expect[b]);
-    if (p->refs[b] == 0) {
-      if (!on_free[b] || f[b] != 0)
-        return fail(PKV_ECORRUPT, "unreferenced block %d is not clean and free", b);
-    } else {
-      if (on_free[b]) return fail(PKV_ECORRUPT, "referenced block %d is free", b);
-      if (f[b] < 1 || f[b] > p->bs) return fail(PKV_ECORRUPT, "block %d fill %d", b, f[b]);
-      payload += f[b];
-    }
-  }
-  if (logical < payload) return fail(PKV_ECORRUPT, "payload exceeds logical tokens");
-  return PKV_OK;
+  return check_invariants(p, nullptr);
 }
 
 }  // extern "C"

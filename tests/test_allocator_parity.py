@@ -98,7 +98,7 @@ def test_block_tables_pad_and_reject():
         pool.block_tables([1], 2)
 
 
-def test_batch_alloc_matches_sequential_and_stops_on_failure():
+def test_batch_alloc_matches_sequential_appends():
     stack = np.random.default_rng(9).permutation(12)
     a = pkv.PagedKVPool(12, 4, initial_free_stack=stack)
     o = PagedPool(12, 4, initial_free_stack=stack.tolist())
@@ -112,11 +112,90 @@ def test_batch_alloc_matches_sequential_and_stops_on_failure():
     for s, n in zip([0, 1, 2, 3], [3, 5, 0, 2]):
         expect += o.append(s, n)[0]
     assert slots.tolist() == expect and pairs.shape == (0, 2)
-    with pytest.raises(MemoryError):
-        a.alloc_batch([1, 2], [3, 40])
-    assert a.last_batch_done == 1
-    o.append(1, 3)
-    assert a.free_stack() == o.free
+    assert a.last_batch_done == 4
+
+
+def test_failing_batch_changes_nothing():
+    """[KVNB §5] preflight: a batch that runs out of blocks at its k-th member
+    leaves every table, count and the free stack as they were (the members
+    before it are not applied either)."""
+    stack = np.random.default_rng(9).permutation(12)
+    a = pkv.PagedKVPool(12, 4, initial_free_stack=stack)
+    for s in range(3):
+        a.seq_create(s)
+    a.alloc(0, 6)          # blocks for 6 tokens: the last one partial
+    a.fork(0, 3, 6)        # ... and shared
+    before = (snapshot(a), a.free_stack())
+    # 10 free blocks. First batch: sequence 1 takes 3, sequence 3 a copy of
+    # the shared tail + 1, sequence 2 six (11). Last: sequence 3 copies, so
+    # sequence 0's tail is no longer shared and needs no copy; then sequence
+    # 3 grows by 10 blocks (11).
+    for ids, ns in (([1, 3, 2], [12, 6, 21]), ([1, 2], [3, 40]), ([3, 0, 3], [2, 2, 40])):
+        with pytest.raises(MemoryError):
+            a.alloc_batch(ids, ns)
+        assert a.last_batch_done == 0
+        assert (snapshot(a), a.free_stack()) == before
+        a.validate()
+    with pytest.raises(KeyError):  # an unknown id late in the batch
+        a.alloc_batch([1, 2, 99], [1, 1, 1])
+    assert (snapshot(a), a.free_stack()) == before
+    with pytest.raises(pkv.InvalidArgument):
+        a.alloc_batch([1, 2], [1, -1])
+    assert (snapshot(a), a.free_stack()) == before
+    # the same batch fits once it asks for exactly the free blocks
+    a.alloc_batch([1, 3, 2], [12, 6, 20])
+    assert a.stats()["free_blocks"] == 0
+    a.validate()
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_batches_all_or_nothing(seed):
+    """Random batches over shared partial tails (copies whose counts change
+    within the batch) and repeated ids: a batch succeeds exactly when the
+    same appends one by one would all succeed, with the same slots, pairs
+    and free stack; otherwise nothing changes."""
+    import copy
+
+    rnd = random.Random(7000 + seed)
+    bs = rnd.choice([2, 4, 16])
+    nblocks = rnd.randint(6, 40)
+    stack = np.random.default_rng(seed).permutation(nblocks).tolist()
+    lib = pkv.PagedKVPool(nblocks, bs, initial_free_stack=stack)
+    ora = PagedPool(nblocks, bs, initial_free_stack=stack)
+    lib.seq_create(0)
+    ora.create(0)
+    n0 = rnd.randint(1, 3 * bs)
+    lib.alloc(0, n0)
+    ora.append(0, n0)
+    live = [0]
+    for c in range(1, rnd.randint(2, 6)):
+        p = rnd.randint(0, ora.sequence_length(0))
+        lib.fork(0, c, p)
+        ora.share_prefix(0, c, p)
+        live.append(c)
+    for _ in range(12):
+        ids = [rnd.choice(live) for _ in range(rnd.randint(1, 6))]
+        ns = [rnd.randint(0, 2 * bs) for _ in ids]
+        trial = copy.deepcopy(ora)
+        try:
+            expect_slots, expect_pairs = [], []
+            for s, n in zip(ids, ns):
+                sl, cw = trial.append(s, n)
+                expect_slots += sl
+                expect_pairs += cw
+        except MemoryError:
+            before = (snapshot(lib), lib.free_stack())
+            with pytest.raises(MemoryError):
+                lib.alloc_batch(ids, ns)
+            assert (snapshot(lib), lib.free_stack()) == before
+        else:
+            slots, pairs = lib.alloc_batch(ids, ns)
+            assert slots.tolist() == expect_slots
+            assert [tuple(x) for x in pairs.tolist()] == expect_pairs
+            ora = trial
+        lib.validate()
+        assert lib.free_stack() == ora.free
+        assert snapshot(lib) == ora.snapshot()
 
 
 @pytest.mark.parametrize("seed", range(40))
