@@ -200,11 +200,24 @@ int paged_kv_validate(const pkv_pool *pool);
  *   k_cache[s / bs, h, s % bs, :] = k_new[t, h, :]   (and V), all h < Hkv.
  * Bit-exact copy. Slots < 0 or >= num_blocks * block_size are skipped.
  * k_new, v_new: device [T, Hkv, D]; slot_mapping: device int32 [T].
- * Two tokens must not name the same slot (the allocator never does). */
+ * Two tokens must not name the same slot (the allocator never does; see
+ * paged_kv_check_slots). */
 int paged_cache_write(const void *k_new, const void *v_new, void *k_cache,
                       void *v_cache, const int32_t *slot_mapping, int32_t T,
                       int32_t num_blocks, int32_t Hkv, int32_t D,
                       int32_t block_size, int dtype, void *stream);
+
+/* Check a slot mapping in HOST memory before a cache write: PKV_EINVAL if
+ * two of its T tokens name the same slot in [0, num_slots) -- the write's
+ * result would then depend on which token lands last -- with the later
+ * token's index in *first_dup (NULL allowed; -1 when there is none); PKV_OK
+ * otherwise. Slots < 0 or >= num_slots are ignored, as the write skips
+ * them. The allocator never emits a repeated slot; this is a debugging aid.
+ * A build with PKV_DEBUG_SLOTS defined runs it inside paged_cache_write and
+ * its 8-bit and 3-bit variants (copying the mapping to the host and waiting
+ * for the stream first) and returns its error instead of launching. */
+int paged_kv_check_slots(const int32_t *slots, int32_t T, int64_t num_slots,
+                         int32_t *first_dup);
 
 /* Copy-on-write device copy: for each of the n pairs (device array), copy
  * block src -> dst in both pools (all Hkv * block_size * D elements). Pairs

@@ -24,6 +24,7 @@ __all__ = [
     "PrefixGroups", "paged_kv_prefix_groups", "paged_attention_shared_workspace_size",
     "paged_attention_decode_shared", "Q8Cache", "paged_cache_write_q8",
     "paged_attention_decode_q8", "Q3Cache", "paged_cache_write_q3", "paged_attention_decode_q3",
+    "paged_kv_check_slots",
 ]
 
 
@@ -144,6 +145,14 @@ class PagedKVPool:
         check(self._lib.paged_kv_validate(self._h))
 
 
+def paged_kv_check_slots(slots, num_slots: int) -> None:
+    """Raise InvalidArgument if a host slot mapping names one slot in
+    [0, num_slots) twice (paged_kv_check_slots)."""
+    a = np.ascontiguousarray(slots, dtype=np.int32)
+    dup = ctypes.c_int32()
+    check(load().paged_kv_check_slots(_i32p(a), len(a), int(num_slots), ctypes.byref(dup)))
+
+
 # ---------------------------------------------------------------- device ops
 
 def dtype_code(t) -> int:
@@ -172,14 +181,68 @@ def _dev(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _fail(msg: str):
+    raise InvalidArgument(_lib.PKV_EINVAL, msg)
+
+
+def _expect(t, name: str, dtypes, shape=None) -> None:
+    """t has one of `dtypes` (a torch dtype or a tuple of them) and, when
+    given, exactly `shape`. The kernels read raw memory, so a wrong element
+    type or a short array would be read or written past its end."""
+    if t is None:
+        _fail(f"{name} is required")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        _fail(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        _fail(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+
+
+def _one_gpu(call: str, *tensors) -> None:
+    """Every tensor given is contiguous and on the same GPU."""
+    ts = [t for t in tensors if t is not None]
+    for t in ts:
+        if not t.is_cuda:
+            _fail(f"{call}: tensors must be on the GPU, one is on {t.device}")
+        if t.device != ts[0].device:
+            _fail(f"{call}: tensors on {ts[0].device} and {t.device}")
+        if not t.is_contiguous():
+            _fail(f"{call}: tensors must be contiguous")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _check_attention_io(call, out, lse, block_tables, context_lens, B, nq, Hq, D) -> int:
+    """Output, lse and index arrays of an attention call; returns max_blocks."""
+    torch = _torch()
+    _expect(out, "out", torch.float32, (B, nq, Hq, D))
+    if lse is not None:
+        _expect(lse, "lse", torch.float32, (B, nq, Hq))
+    _expect(block_tables, "block_tables", torch.int32)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        _fail(f"{call}: block_tables must be [B, max_blocks] with B = {B}")
+    _expect(context_lens, "context_lens", torch.int32, (B,))
+    return int(block_tables.shape[1])
+
+
 def paged_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """k_new, v_new [T, Hkv, D]; caches [NB, Hkv, bs, D]; slot_mapping int32 [T]."""
+    torch = _torch()
+    dt = (torch.float32, torch.bfloat16)
+    _expect(k_cache, "k_cache", dt)
+    if k_cache.dim() != 4:
+        _fail("paged_cache_write: caches must be [num_blocks, Hkv, block_size, D]")
     NB, Hkv, bs, D = k_cache.shape
     T = k_new.shape[0]
-    if (tuple(k_new.shape) != (T, Hkv, D) or v_new.shape != k_new.shape
-            or v_cache.shape != k_cache.shape or tuple(slot_mapping.shape) != (T,)
-            or k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_cache_write: shape or dtype mismatch")
+    _expect(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    _expect(k_new, "k_new", k_cache.dtype, (T, Hkv, D))
+    _expect(v_new, "v_new", k_cache.dtype, (T, Hkv, D))
+    _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
+    _one_gpu("paged_cache_write", k_new, v_new, k_cache, v_cache, slot_mapping)
     check(load().paged_cache_write(_dev(k_new), _dev(v_new), _dev(k_cache), _dev(v_cache),
                                    _dev(slot_mapping), T, NB, Hkv, D, bs,
                                    dtype_code(k_cache), _stream(stream)))
@@ -187,8 +250,15 @@ def paged_cache_write(k_new, v_new, k_cache, v_cache, slot_mapping, stream=None)
 
 def paged_kv_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     """pairs: device int32 [n, 2] of (src, dst)."""
+    torch = _torch()
+    _expect(k_cache, "k_cache", (torch.float32, torch.bfloat16))
+    if k_cache.dim() != 4:
+        _fail("paged_kv_copy_blocks: caches must be [num_blocks, Hkv, block_size, D]")
+    _expect(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
     NB, Hkv, bs, D = k_cache.shape
     n = pairs.shape[0]
+    _expect(pairs, "pairs", torch.int32, (n, 2))
+    _one_gpu("paged_kv_copy_blocks", k_cache, v_cache, pairs)
     check(load().paged_kv_copy_blocks(_dev(k_cache), _dev(v_cache), _dev(pairs), n, NB, Hkv,
                                       D, bs, dtype_code(k_cache), _stream(stream)))
 
@@ -214,6 +284,8 @@ class Q8Cache:
         """Copy-on-write of whole blocks: codes and scales."""
         NB, Hkv, bs, D = self.shape
         n = pairs.shape[0]
+        _expect(pairs, "pairs", _torch().int32, (n, 2))
+        _one_gpu("Q8Cache.copy_blocks", self.k_codes, pairs)
         check(load().paged_kv_copy_blocks(_dev(self.k_codes), _dev(self.v_codes), _dev(pairs), n,
                                           NB, Hkv, D, bs, _lib.PKV_I8, _stream(stream)))
         check(load().paged_kv_copy_blocks(_dev(self.k_scales), _dev(self.v_scales), _dev(pairs),
@@ -223,11 +295,14 @@ class Q8Cache:
 def paged_cache_write_q8(k_new, v_new, cache: "Q8Cache", slot_mapping, stream=None) -> None:
     """Quantize k_new, v_new [T, Hkv, D] (f32 or bf16) to 8-bit codes with one
     scale per row and scatter them to their slots."""
+    torch = _torch()
     NB, Hkv, bs, D = cache.shape
     T = k_new.shape[0]
-    if (tuple(k_new.shape) != (T, Hkv, D) or v_new.shape != k_new.shape
-            or tuple(slot_mapping.shape) != (T,) or v_new.dtype != k_new.dtype):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_cache_write_q8: shape or dtype mismatch")
+    _expect(k_new, "k_new", (torch.float32, torch.bfloat16), (T, Hkv, D))
+    _expect(v_new, "v_new", k_new.dtype, (T, Hkv, D))
+    _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
+    _one_gpu("paged_cache_write_q8", k_new, v_new, cache.k_codes, cache.v_codes,
+             cache.k_scales, cache.v_scales, slot_mapping)
     check(load().paged_cache_write_q8(
         _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes),
         _dev(cache.k_scales), _dev(cache.v_scales), _dev(slot_mapping), T, NB, Hkv, D, bs,
@@ -238,14 +313,18 @@ def paged_attention_decode_q8(out, q, cache: "Q8Cache", block_tables, context_le
                               partition_tokens=0, workspace=None, lse=None,
                               stream=None) -> None:
     """paged_attention_decode over a cache of 8-bit codes; q bf16 [B, nq, Hq, D]."""
-    import torch
-
+    torch = _torch()
+    _expect(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        _fail("paged_attention_decode_q8: q must be [B, nq, Hq, D]")
     B, nq, Hq, D = q.shape
     NB, Hkv, bs, Dk = cache.shape
-    max_blocks = block_tables.shape[1]
-    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
-            or tuple(context_lens.shape) != (B,) or q.dtype != torch.bfloat16):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode_q8: shape mismatch")
+    if Dk != D:
+        _fail(f"paged_attention_decode_q8: head dim {D} of q, {Dk} of the cache")
+    max_blocks = _check_attention_io("paged_attention_decode_q8", out, lse, block_tables,
+                                     context_lens, B, nq, Hq, D)
+    _one_gpu("paged_attention_decode_q8", out, q, cache.k_codes, cache.v_codes,
+             cache.k_scales, cache.v_scales, block_tables, context_lens, workspace, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode_q8(
         _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.k_scales),
@@ -277,6 +356,8 @@ class Q3Cache:
     def copy_blocks(self, pairs, stream=None) -> None:
         NB, Hkv, bs, D = self.shape
         n = pairs.shape[0]
+        _expect(pairs, "pairs", _torch().int32, (n, 2))
+        _one_gpu("Q3Cache.copy_blocks", self.k_codes, pairs)
         check(load().paged_kv_copy_blocks(_dev(self.k_codes), _dev(self.v_codes), _dev(pairs), n,
                                           NB, Hkv, D // 2, bs, _lib.PKV_I8, _stream(stream)))
         check(load().paged_kv_copy_blocks(_dev(self.k_scales), _dev(self.v_scales), _dev(pairs),
@@ -286,11 +367,14 @@ class Q3Cache:
 def paged_cache_write_q3(k_new, v_new, cache: "Q3Cache", slot_mapping, stream=None) -> None:
     """Quantize k_new, v_new [T, Hkv, D] (f32 or bf16) to 3-bit codes with one
     scale per row and scatter them to their slots."""
+    torch = _torch()
     NB, Hkv, bs, D = cache.shape
     T = k_new.shape[0]
-    if (tuple(k_new.shape) != (T, Hkv, D) or v_new.shape != k_new.shape
-            or tuple(slot_mapping.shape) != (T,) or v_new.dtype != k_new.dtype):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_cache_write_q3: shape or dtype mismatch")
+    _expect(k_new, "k_new", (torch.float32, torch.bfloat16), (T, Hkv, D))
+    _expect(v_new, "v_new", k_new.dtype, (T, Hkv, D))
+    _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
+    _one_gpu("paged_cache_write_q3", k_new, v_new, cache.k_codes, cache.v_codes,
+             cache.k_scales, cache.v_scales, slot_mapping)
     check(load().paged_cache_write_q3(
         _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes),
         _dev(cache.k_scales), _dev(cache.v_scales), _dev(slot_mapping), T, NB, Hkv, D, bs,
@@ -301,14 +385,18 @@ def paged_attention_decode_q3(out, q, cache: "Q3Cache", block_tables, context_le
                               partition_tokens=0, workspace=None, lse=None,
                               stream=None) -> None:
     """paged_attention_decode over a cache of 3-bit codes; q bf16 [B, nq, Hq, D]."""
-    import torch
-
+    torch = _torch()
+    _expect(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        _fail("paged_attention_decode_q3: q must be [B, nq, Hq, D]")
     B, nq, Hq, D = q.shape
     NB, Hkv, bs, Dk = cache.shape
-    max_blocks = block_tables.shape[1]
-    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
-            or tuple(context_lens.shape) != (B,) or q.dtype != torch.bfloat16):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode_q3: shape mismatch")
+    if Dk != D:
+        _fail(f"paged_attention_decode_q3: head dim {D} of q, {Dk} of the cache")
+    max_blocks = _check_attention_io("paged_attention_decode_q3", out, lse, block_tables,
+                                     context_lens, B, nq, Hq, D)
+    _one_gpu("paged_attention_decode_q3", out, q, cache.k_codes, cache.v_codes,
+             cache.k_scales, cache.v_scales, block_tables, context_lens, workspace, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode_q3(
         _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.k_scales),
@@ -325,16 +413,28 @@ def paged_attention_workspace_size(B, nq, Hq, Hkv, D, max_blocks, block_size,
     return out.value
 
 
+def _check_decode_args(call, out, q, k_cache, v_cache, block_tables, context_lens, lse) -> int:
+    torch = _torch()
+    _expect(k_cache, "k_cache", (torch.float32, torch.bfloat16))
+    if k_cache.dim() != 4 or q.dim() != 4:
+        _fail(f"{call}: caches [num_blocks, Hkv, block_size, D] and q [B, nq, Hq, D] expected")
+    _expect(v_cache, "v_cache", k_cache.dtype, k_cache.shape)
+    _expect(q, "q", k_cache.dtype)
+    B, nq, Hq, D = q.shape
+    if k_cache.shape[3] != D:
+        _fail(f"{call}: head dim {D} of q, {k_cache.shape[3]} of the caches")
+    return _check_attention_io(call, out, lse, block_tables, context_lens, B, nq, Hq, D)
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                            partition_tokens=0, workspace=None, lse=None, stream=None) -> None:
     """out fp32 [B, nq, Hq, D]; q [B, nq, Hq, D]; tables int32 [B, max_blocks]."""
+    max_blocks = _check_decode_args("paged_attention_decode", out, q, k_cache, v_cache,
+                                    block_tables, context_lens, lse)
     B, nq, Hq, D = q.shape
-    NB, Hkv, bs, Dk = k_cache.shape
-    max_blocks = block_tables.shape[1]
-    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
-            or tuple(context_lens.shape) != (B,) or q.dtype != k_cache.dtype
-            or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode: shape mismatch")
+    NB, Hkv, bs, _ = k_cache.shape
+    _one_gpu("paged_attention_decode", out, q, k_cache, v_cache, block_tables, context_lens,
+             workspace, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode(
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,
@@ -403,14 +503,18 @@ def paged_attention_decode_shared(out, q, k_cache, v_cache, block_tables, contex
 
     device_groups: groups.to_device(...) (seq_prefix, group_start, members,
     group_tokens as device int32 tensors)."""
+    max_blocks = _check_decode_args("paged_attention_decode_shared", out, q, k_cache, v_cache,
+                                    block_tables, context_lens, lse)
     B, nq, Hq, D = q.shape
-    NB, Hkv, bs, Dk = k_cache.shape
-    max_blocks = block_tables.shape[1]
-    if (Dk != D or tuple(out.shape) != (B, nq, Hq, D) or block_tables.shape[0] != B
-            or tuple(context_lens.shape) != (B,) or q.dtype != k_cache.dtype
-            or v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype):
-        raise InvalidArgument(_lib.PKV_EINVAL, "paged_attention_decode_shared: shape mismatch")
+    NB, Hkv, bs, _ = k_cache.shape
     seq_prefix, group_start, members, group_tokens = device_groups
+    i32 = _torch().int32
+    _expect(seq_prefix, "seq_prefix", i32, (B,))
+    _expect(group_start, "group_start", i32, (groups.n_groups + 1,))
+    _expect(members, "members", i32, (max(groups.n_members, 1),))
+    _expect(group_tokens, "group_tokens", i32, (max(groups.n_groups, 1),))
+    _one_gpu("paged_attention_decode_shared", out, q, k_cache, v_cache, block_tables,
+             context_lens, seq_prefix, group_start, members, group_tokens, workspace, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode_shared(
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,

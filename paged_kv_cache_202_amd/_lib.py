@@ -52,6 +52,7 @@ PROTOTYPES = {
     "paged_kv_block_tables": (c_int, [c_void_p, P_i64, c_i32, c_i32, P_i32, P_i32]),
     "paged_kv_stats": (c_int, [c_void_p, ctypes.POINTER(Stats)]),
     "paged_kv_validate": (c_int, [c_void_p]),
+    "paged_kv_check_slots": (c_int, [P_i32, c_i32, c_i64, P_i32]),
     "paged_cache_write": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                   c_i32, c_i32, c_i32, c_i32, c_int, c_void_p]),
     "paged_kv_copy_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32,

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-SOURCES = ["pool.cpp", "groups.cpp", "cache_ops.hip", "decode.hip", "verify_inst.hip",
+SOURCES = ["pool.cpp", "groups.cpp", "checks.cpp", "cache_ops.hip", "decode.hip", "verify_inst.hip",
            "shared_inst.hip"] + [
     f"decode_inst_{dt}_d{d}.hip" for dt in ("f32", "bf16") for d in (64, 128, 256)] + [
     f"decode_inst_mfma_d{d}.hip" for d in (64, 128, 256)]
@@ -37,6 +37,9 @@ def hipcc() -> str:
 def _flags(src: str) -> list[str]:
     flags = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall",
              "-Wno-unused-function"]
+    if os.environ.get("PKV_DEBUG_SLOTS") == "1":
+        # debug build: cache writes refuse slot mappings that repeat a slot
+        flags.append("-DPKV_DEBUG_SLOTS")
     if src.endswith(".hip"):
         # packed fp32 instructions stay disabled on this target
         flags += ["-x", "hip", f"--offload-arch={ARCH}",

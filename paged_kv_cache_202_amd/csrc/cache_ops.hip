@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 #include "pagedkv.h"
 #include "status.h"
@@ -130,6 +131,29 @@ int elem_bytes(int dtype) {
 
 using pkv::fail;
 
+#ifdef PKV_DEBUG_SLOTS
+// Debug builds only: refuse a slot mapping that names one slot twice (see
+// paged_kv_check_slots). The mapping is copied to the host and the stream
+// waited for, which a production write must not do.
+static int debug_check_slots(const int32_t *slot_mapping, int32_t T, int64_t num_slots,
+                             hipStream_t stream) {
+  std::vector<int32_t> host(T);
+  hipError_t e = hipMemcpyAsync(host.data(), slot_mapping, sizeof(int32_t) * (size_t)T,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(PKV_EHIP, "slot check copy: %s", hipGetErrorString(e));
+  return paged_kv_check_slots(host.data(), T, num_slots, nullptr);
+}
+#define PKV_CHECK_SLOTS(slots, T, n, stream) \
+  do {                                                                          \
+    if (int rc_ = debug_check_slots(slots, T, n, (hipStream_t)(stream))) return rc_; \
+  } while (0)
+#else
+#define PKV_CHECK_SLOTS(slots, T, n, stream) \
+  do {                                       \
+  } while (0)
+#endif
+
 extern "C" int paged_cache_write(const void *k_new, const void *v_new, void *k_cache,
                                  void *v_cache, const int32_t *slot_mapping, int32_t T,
                                  int32_t num_blocks, int32_t Hkv, int32_t D,
@@ -145,6 +169,7 @@ extern "C" int paged_cache_write(const void *k_new, const void *v_new, void *k_c
     return fail(PKV_EINVAL, "NULL pointer");
   for (const void *p : {k_new, v_new, (const void *)k_cache, (const void *)v_cache})
     if ((uintptr_t)p % 16) return fail(PKV_EINVAL, "K/V pointers must be 16-byte aligned");
+  PKV_CHECK_SLOTS(slot_mapping, T, (int64_t)num_blocks * block_size, stream);
   const int32_t vpr = D * es / 16;
   const int64_t total = (int64_t)T * Hkv * vpr;
   const int64_t want = (total + 255) / 256;
@@ -198,6 +223,7 @@ static int cache_write_q(const void *k_new, const void *v_new, int8_t *k_codes, 
     return fail(PKV_EINVAL, "NULL pointer");
   const int64_t rows = (int64_t)T * Hkv;
   const int64_t num_slots = (int64_t)num_blocks * block_size;
+  PKV_CHECK_SLOTS(slot_mapping, T, num_slots, stream);
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   hipStream_t s = (hipStream_t)stream;
 #define PKV_Q(d)                                                                            \

@@ -144,3 +144,169 @@ def test_low_bit_and_chunk_host_checks_need_no_gpu():
     assert lib.paged_attention_decode(fake, fake, fake, fake, fake, 4, fake, 2, 64, 32, 8, 128,
                                       16, 8, 0.1, _lib.PKV_BF16, 0, None, 0, None, None) \
         == _lib.PKV_EINVAL
+
+
+# ------------------------------------------------------------ binding checks
+# The kernels read raw memory: a float64 or bf16 output, a short lse, an
+# int64 index array (read as pairs of int32 words) or a tensor on another
+# device would be read or written out of bounds. The binding refuses them
+# before any library call, so these run on CPU tensors.
+
+def _decode_args(torch, **over):
+    B, nq, Hq, Hkv, D, NB, bs, mb = 2, 1, 8, 2, 64, 6, 16, 3
+    a = dict(out=torch.empty(B, nq, Hq, D), q=torch.empty(B, nq, Hq, D, dtype=torch.bfloat16),
+             k_cache=torch.empty(NB, Hkv, bs, D, dtype=torch.bfloat16),
+             v_cache=torch.empty(NB, Hkv, bs, D, dtype=torch.bfloat16),
+             block_tables=torch.zeros(B, mb, dtype=torch.int32),
+             context_lens=torch.ones(B, dtype=torch.int32), scale=0.125,
+             lse=torch.empty(B, nq, Hq))
+    a.update(over)
+    return a
+
+
+BAD_DECODE = {
+    "out bf16": lambda t: dict(out=t.empty(2, 1, 8, 64, dtype=t.bfloat16)),
+    "out float64": lambda t: dict(out=t.empty(2, 1, 8, 64, dtype=t.float64)),
+    "out short": lambda t: dict(out=t.empty(2, 1, 4, 64)),
+    "lse short": lambda t: dict(lse=t.empty(2, 1, 4)),
+    "lse bf16": lambda t: dict(lse=t.empty(2, 1, 8, dtype=t.bfloat16)),
+    "tables int64": lambda t: dict(block_tables=t.zeros(2, 3, dtype=t.int64)),
+    "tables 1-d": lambda t: dict(block_tables=t.zeros(6, dtype=t.int32)),
+    "lens int64": lambda t: dict(context_lens=t.ones(2, dtype=t.int64)),
+    "lens short": lambda t: dict(context_lens=t.ones(1, dtype=t.int32)),
+    "q f32 over bf16 caches": lambda t: dict(q=t.empty(2, 1, 8, 64)),
+    "v_cache f32": lambda t: dict(v_cache=t.empty(6, 2, 16, 64)),
+    "caches f16": lambda t: dict(k_cache=t.empty(6, 2, 16, 64, dtype=t.float16),
+                                 v_cache=t.empty(6, 2, 16, 64, dtype=t.float16)),
+    "head dims differ": lambda t: dict(q=t.empty(2, 1, 8, 128, dtype=t.bfloat16),
+                                       out=t.empty(2, 1, 8, 128)),
+}
+
+
+@pytest.mark.parametrize("case", list(BAD_DECODE))
+def test_decode_binding_refuses(case):
+    torch = pytest.importorskip("torch")
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.paged_attention_decode(**_decode_args(torch, **BAD_DECODE[case](torch)))
+
+
+def test_decode_binding_refuses_host_tensors():
+    """Right types and shapes, but not on the GPU."""
+    torch = pytest.importorskip("torch")
+    with pytest.raises(pkv.InvalidArgument, match="on the GPU"):
+        pkv.paged_attention_decode(**_decode_args(torch))
+
+
+def test_cache_write_and_copy_bindings_refuse():
+    torch = pytest.importorskip("torch")
+    kc = torch.empty(6, 2, 16, 64, dtype=torch.bfloat16)
+    k = torch.empty(3, 2, 64, dtype=torch.bfloat16)
+    good = torch.zeros(3, dtype=torch.int32)
+    for slots in (torch.zeros(3, dtype=torch.int64), torch.zeros(4, dtype=torch.int32)):
+        with pytest.raises(pkv.InvalidArgument, match="slot_mapping"):
+            pkv.paged_cache_write(k, k, kc, kc, slots)
+    with pytest.raises(pkv.InvalidArgument, match="k_new"):
+        pkv.paged_cache_write(k.float(), k, kc, kc, good)
+    with pytest.raises(pkv.InvalidArgument, match="on the GPU"):
+        pkv.paged_cache_write(k, k, kc, kc, good)
+    for pairs in (torch.zeros(2, 2, dtype=torch.int64), torch.zeros(2, 3, dtype=torch.int32)):
+        with pytest.raises(pkv.InvalidArgument, match="pairs"):
+            pkv.paged_kv_copy_blocks(kc, kc, pairs)
+    with pytest.raises(pkv.InvalidArgument, match="v_cache"):
+        pkv.paged_kv_copy_blocks(kc, kc.float(), torch.zeros(2, 2, dtype=torch.int32))
+
+
+def test_code_cache_bindings_refuse():
+    torch = pytest.importorskip("torch")
+
+    class HostQ8:  # the shape of a Q8Cache, in host memory
+        k_codes = v_codes = torch.empty(6, 2, 16, 64, dtype=torch.int8)
+        k_scales = v_scales = torch.empty(6, 2, 16)
+        shape = (6, 2, 16, 64)
+
+    k = torch.empty(3, 2, 64)
+    with pytest.raises(pkv.InvalidArgument, match="slot_mapping"):
+        pkv.paged_cache_write_q8(k, k, HostQ8, torch.zeros(3, dtype=torch.int64))
+    with pytest.raises(pkv.InvalidArgument, match="v_new"):
+        pkv.paged_cache_write_q8(k, k.bfloat16(), HostQ8, torch.zeros(3, dtype=torch.int32))
+    a = _decode_args(torch)
+    for over in (dict(lse=torch.empty(2, 1, 7)), dict(context_lens=torch.ones(2, dtype=torch.int64)),
+                 dict(q=torch.empty(2, 1, 8, 64))):
+        b = dict(a, **over)
+        with pytest.raises(pkv.InvalidArgument):
+            pkv.paged_attention_decode_q8(b["out"], b["q"], HostQ8, b["block_tables"],
+                                          b["context_lens"], 0.125, lse=b["lse"])
+
+
+def test_slot_check_finds_repeated_slots():
+    """Reading of the duplicate-slot case: two tokens of one write naming the
+    same slot is a caller error; the host check names the later token."""
+    lib = pkv.load()
+    import numpy as np
+
+    def run(slots, n):
+        a = np.asarray(slots, np.int32)
+        dup = ctypes.c_int32(99)
+        rc = lib.paged_kv_check_slots(a.ctypes.data_as(_lib.P_i32), len(a), n, ctypes.byref(dup))
+        return rc, dup.value
+
+    assert run([], 10) == (_lib.PKV_OK, -1)
+    assert run([3, 1, 2, 0], 4) == (_lib.PKV_OK, -1)
+    assert run([5, -1, -1, 7, 9, 9], 9) == (_lib.PKV_OK, -1)  # skipped slots may repeat
+    assert run([4, 1, 4, 2, 1], 8) == (_lib.PKV_EINVAL, 2)
+    assert run([0, 6, 2, 6], 8) == (_lib.PKV_EINVAL, 3)
+    assert b"token 3 writes slot 6" in lib.paged_kv_last_error()
+    assert lib.paged_kv_check_slots(None, 2, 8, None) == _lib.PKV_EINVAL
+    with pytest.raises(pkv.InvalidArgument):
+        pkv.paged_kv_check_slots([1, 1], 4)
+
+
+def test_allocator_slot_mappings_never_repeat():
+    """Every batch the allocator emits -- with forks, copies and truncates --
+    passes the duplicate-slot check."""
+    import random
+
+    import numpy as np
+
+    rnd = random.Random(5)
+    pool = pkv.PagedKVPool(64, 4, initial_free_stack=np.random.default_rng(5).permutation(64))
+    ids = []
+    for step in range(200):
+        if not ids or rnd.random() < 0.15:
+            ids.append(len(ids) + 1000 * step)
+            pool.seq_create(ids[-1])
+        elif rnd.random() < 0.2:
+            s = rnd.choice(ids)
+            ids.append(s + 7_000_000 + step)
+            pool.fork(s, ids[-1], rnd.randint(0, pool.seq_length(s)))
+        elif rnd.random() < 0.2:
+            s = rnd.choice(ids)
+            pool.truncate(s, rnd.randint(0, pool.seq_length(s)))
+        members = [rnd.choice(ids) for _ in range(rnd.randint(1, 6))]
+        try:
+            slots, _ = pool.alloc_batch(members, [rnd.randint(0, 6) for _ in members])
+        except MemoryError:
+            for s in ids[: len(ids) // 2]:
+                pool.free(s)
+            ids = ids[len(ids) // 2:]
+            continue
+        pkv.paged_kv_check_slots(slots, 64 * 4)
+
+
+def test_debug_slot_check_compiles():
+    """The debug build's cache write (PKV_DEBUG_SLOTS) compiles for gfx950."""
+    from paged_kv_cache_202_amd import build as b
+
+    try:
+        hipcc = b.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not available")
+    import tempfile
+
+    src = "cache_ops.hip"
+    with tempfile.TemporaryDirectory() as d:
+        cmd = [hipcc] + b._flags(src) + ["-DPKV_DEBUG_SLOTS", "-c",
+                                          os.path.join(b.CSRC, src), "-o",
+                                          os.path.join(d, "cache_ops.o")]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-3000:]
