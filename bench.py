@@ -217,6 +217,7 @@ class Workload:
         self.d_q = q.to(dev)
         self.tables_host = tables
         self.out = torch.empty((B, nq, Hq, D), dtype=torch.float32, device=dev)
+        self.lse = None  # an optional [B, nq, Hq] float32 output (the parity tests set it)
         self.scale = 1.0 / math.sqrt(D)
         self.part = w.partition_tokens
         ws = pkv.paged_attention_workspace_size(B, nq, Hq, Hkv, D, self.max_blocks, bs,
@@ -237,11 +238,13 @@ class Workload:
         r = i % self.rotate
         if self.q8:
             self.decode_q(self.out, self.d_q, self.qc[r], self.d_tables, self.d_lens,
-                          self.scale, partition_tokens=self.part, workspace=self.ws)
+                          self.scale, partition_tokens=self.part, workspace=self.ws,
+                          lse=self.lse)
             return
         self.pkv.paged_attention_decode(self.out, self.d_q, self.kc[r], self.vc[r],
                                         self.d_tables, self.d_lens, self.scale,
-                                        partition_tokens=self.part, workspace=self.ws)
+                                        partition_tokens=self.part, workspace=self.ws,
+                                        lse=self.lse)
 
     def step(self, i: int) -> None:
         self.cache_write(i)
@@ -332,6 +335,7 @@ class PrefixVerifyWorkload:
         self.d_lens = torch.from_numpy(clens).to(dev)
         self.d_q = self.host_q.to(dev)
         self.out = torch.empty((B, K, Hq, D), dtype=torch.float32, device=dev)
+        self.lse = None  # an optional [B, K, Hq] float32 output (the parity tests set it)
         self.scale = 1.0 / math.sqrt(D)
         self.part = w.partition_tokens
         ws = pkv.paged_attention_workspace_size(B, K, Hq, Hkv, D, self.max_blocks, bs, self.part)
@@ -359,11 +363,11 @@ class PrefixVerifyWorkload:
                                                    self.d_tables, self.d_lens, self.scale,
                                                    self.groups, self.d_groups,
                                                    partition_tokens=self.part,
-                                                   workspace=self.ws)
+                                                   workspace=self.ws, lse=self.lse)
             return
         self.pkv.paged_attention_decode(self.out, self.d_q, self.kc, self.vc, self.d_tables,
                                         self.d_lens, self.scale, partition_tokens=self.part,
-                                        workspace=self.ws)
+                                        workspace=self.ws, lse=self.lse)
 
     def step(self, i: int) -> None:
         self.cache_write(i)

@@ -4,8 +4,8 @@ The GPU side is bench.py's own setup (library allocator, cache-write kernel,
 the timed step: cache write of the new tokens then attention). The oracle
 side builds its own allocator state and host pool from the same synthetic
 inputs and walks the block tables in float64 (C oracle, OpenMP). Slots and
-tables must match bit for bit; every output row must be within max-abs 1e-2
-(bf16 caches).
+tables must match bit for bit; every output and lse must be within max-abs
+1e-2 (bf16 caches) and within a tight bound that a dropped tile would break.
 """
 
 import os
@@ -19,6 +19,7 @@ import bench
 from oracle import attention as oatt
 from oracle import native
 from oracle.pool import PagedPool
+from scenario import TIGHT
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +54,13 @@ def oracle_side(wk):
             np.array(tables, np.int32), np.array(lens, np.int32), kp, vp)
 
 
+# Tight bounds on out and lse beside the 1e-2 contract bound (see
+# tests/scenario.py: far below what one dropped or repeated 16-token tile
+# moves at these sizes).
+BOUND = {"llama3_8b_b32_8k": TIGHT["decode"], "llama3_8b_varlen_b256": TIGHT["decode"],
+         "llama33_70b_b4_128k": TIGHT["decode_128k"]}
+
+
 @pytest.mark.parametrize("name", ["llama3_8b_b32_8k", "llama3_8b_varlen_b256",
                                   "llama33_70b_b4_128k"])
 def test_full_size_workload(name, device):
@@ -63,13 +71,19 @@ def test_full_size_workload(name, device):
     assert np.array_equal(wk.step_slots, step_slots)
     assert np.array_equal(wk.tables_host, tables)
     assert np.array_equal(wk.lens, lens)
+    wk.lse = torch.full((wk.B, wk.nq, wk.Hq), float("nan"), dtype=torch.float32, device=device)
     wk.step(0)  # the timed step: new-token cache write, then attention
     torch.cuda.synchronize()
     out = wk.out.cpu().numpy()
+    lse = wk.lse.cpu().numpy()
     q = wk.host_q.view(torch.int16).numpy().view(np.uint16)
-    ref, _ = native.attention(q, "bf16", kp, vp, "bf16", tables, lens, wk.scale, wk.bs,
-                              threads=min(16, len(os.sched_getaffinity(0))))
+    ref, ref_lse = native.attention(q, "bf16", kp, vp, "bf16", tables, lens, wk.scale, wk.bs,
+                                    threads=min(16, len(os.sched_getaffinity(0))))
     err = np.abs(out - ref).max()
-    print(f"  {name}: max-abs error {err:.3e} over {out.size} outputs", flush=True)
-    assert np.isfinite(out).all()
-    assert err <= 1e-2
+    lerr = np.abs(lse - ref_lse).max()
+    out_bound, lse_bound = BOUND[name]
+    print(f"  {name}: max-abs error out {err:.3e}, lse {lerr:.3e} over {out.size} outputs "
+          f"(tight bounds {out_bound:.0e}, {lse_bound:.0e})", flush=True)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert err <= 1e-2 and lerr <= 1e-2  # the contract
+    assert err <= out_bound and lerr <= lse_bound

@@ -17,8 +17,16 @@ import bench
 from oracle import attention as oatt
 from oracle import native
 from oracle.pool import PagedPool
+from scenario import TIGHT
 
 pytestmark = pytest.mark.gpu
+
+# Tight bounds on out and lse beside the 1e-2 contract bound (see
+# tests/scenario.py): the multi-query tiles round the softmax weights to bf16
+# for the p.v product, so out errors sit near 4e-4 here; one dropped or
+# repeated 16-token tile of these ~2.5K-token contexts moves out by >= 3e-3
+# and lse by >= 4e-3.
+OUT_BOUND, LSE_BOUND = TIGHT["multi_query"]
 
 
 def bits(t):
@@ -62,14 +70,20 @@ def test_prefix_share_verify(prefix, expect_copies, device):
         vp[dst] = vp[src]
     oatt.cache_write(kp, vp, bits(wk.k_suf), bits(wk.v_suf), suf_slots, bs)
     oatt.cache_write(kp, vp, bits(wk.k_dft), bits(wk.v_dft), dft_slots, bs)
+    wk.lse = torch.full((B, K, wk.Hq), float("nan"), dtype=torch.float32, device=device)
     wk.step(0)  # the timed step: draft cache write, then verify attention
     torch.cuda.synchronize()
     out = wk.out.cpu().numpy()
-    ref, _ = native.attention(bits(wk.host_q), "bf16", kp, vp, "bf16", np.array(tables, np.int32),
-                              np.array(lens, np.int32), wk.scale, bs,
-                              threads=min(16, len(os.sched_getaffinity(0))))
+    lse = wk.lse.cpu().numpy()
+    ref, ref_lse = native.attention(bits(wk.host_q), "bf16", kp, vp, "bf16",
+                                    np.array(tables, np.int32), np.array(lens, np.int32),
+                                    wk.scale, bs, threads=min(16, len(os.sched_getaffinity(0))))
     err = np.abs(out - ref).max()
-    print(f"  max-abs error {err:.3e} over {out.size} outputs", flush=True)
-    assert np.isfinite(out).all() and err <= 1e-2
+    lerr = np.abs(lse - ref_lse).max()
+    print(f"  max-abs error out {err:.3e}, lse {lerr:.3e} over {out.size} outputs "
+          f"(tight bounds {OUT_BOUND:.0e}, {LSE_BOUND:.0e})", flush=True)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert err <= 1e-2 and lerr <= 1e-2  # the contract
+    assert err <= OUT_BOUND and lerr <= LSE_BOUND
     # 128 (or 129) shared blocks + each sequence's private blocks: 2240 either way
     assert wk.pool.stats()["allocated_blocks"] == 2240
