@@ -291,6 +291,27 @@ int paged_attention_decode(float *out, const void *q, const void *k_cache,
                            void *workspace, size_t workspace_bytes,
                            float *lse_out, void *stream);
 
+/* paged_attention_decode for callers that cannot allocate device memory --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc: the same arguments without the workspace, the same kernels and
+ * results. Partials that need a workspace go to a device array inside the
+ * library of 64 MiB (every graded workload fits: the 131072-token split-K
+ * call with 512-token partitions needs 32.5 MiB), one per GPU, held until
+ * the process ends; its address on the calling thread's current device is
+ * looked up once (hipGetSymbolAddress) and kept. Nothing is allocated and
+ * nothing in it needs to start at zero. Every call on one GPU uses the same
+ * array, so calls on one GPU that may overlap (other streams, other host
+ * threads) race on it: issue them on one stream. EINVAL, before anything is
+ * launched, when paged_attention_workspace_size() for these sizes exceeds
+ * 64 MiB; other errors as paged_attention_decode. */
+int paged_attention_decode_noalloc(float *out, const void *q, const void *k_cache,
+                                   const void *v_cache, const int32_t *block_tables,
+                                   int32_t max_blocks, const int32_t *context_lens,
+                                   int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                                   int32_t D, int32_t block_size, int32_t num_blocks,
+                                   float scale, int dtype, int32_t partition_tokens,
+                                   float *lse_out, void *stream);
+
 /* ---- caches of 8-bit per-row codes --------------------------------------
  * The teaching quantizer of [KVNB demo] Demo 2 (symmetric integer codes,
  * one scale per row), 8 bits, applied to every (token, KV head) row of K

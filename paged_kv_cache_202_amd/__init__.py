@@ -24,7 +24,7 @@ __all__ = [
     "PrefixGroups", "paged_kv_prefix_groups", "paged_attention_shared_workspace_size",
     "paged_attention_decode_shared", "Q8Cache", "paged_cache_write_q8",
     "paged_attention_decode_q8", "Q3Cache", "paged_cache_write_q3", "paged_attention_decode_q3",
-    "paged_kv_check_slots",
+    "paged_kv_check_slots", "paged_attention_decode_noalloc",
 ]
 
 
@@ -440,6 +440,22 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,
         _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB, float(scale), dtype_code(k_cache),
         int(partition_tokens), _dev(workspace), ws_bytes, _dev(lse), _stream(stream)))
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   partition_tokens=0, lse=None, stream=None) -> None:
+    """paged_attention_decode without a workspace: partials in the library's
+    own per-GPU scratch array (calls on one GPU must not overlap)."""
+    max_blocks = _check_decode_args("paged_attention_decode_noalloc", out, q, k_cache, v_cache,
+                                    block_tables, context_lens, lse)
+    B, nq, Hq, D = q.shape
+    NB, Hkv, bs, _ = k_cache.shape
+    _one_gpu("paged_attention_decode_noalloc", out, q, k_cache, v_cache, block_tables,
+             context_lens, lse)
+    check(load().paged_attention_decode_noalloc(
+        _dev(out), _dev(q), _dev(k_cache), _dev(v_cache), _dev(block_tables), max_blocks,
+        _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB, float(scale), dtype_code(k_cache),
+        int(partition_tokens), _dev(lse), _stream(stream)))
 
 
 # ---------------------------------------------------------------- shared prefixes

@@ -63,6 +63,10 @@ PROTOTYPES = {
                                        c_i32, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                        c_i32, c_i32, c_float, c_int, c_i32, c_void_p,
                                        c_size_t, c_void_p, c_void_p]),
+    "paged_attention_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_i32, c_void_p, c_i32, c_i32, c_i32,
+                                               c_i32, c_i32, c_i32, c_i32, c_float, c_int,
+                                               c_i32, c_void_p, c_void_p]),
     "paged_cache_write_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                      c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                      c_int, c_void_p]),

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 #include <limits>
+#include <mutex>
 
 #include "decode_kernel.h"
 #include "verify_mfma.h"
@@ -618,6 +619,63 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks,
                      context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype, part,
                      workspace, workspace_bytes, lse_out, stream);
+}
+
+// ---------------------------------------------------------------------------
+// paged_attention_decode for callers that cannot allocate: the partials live
+// in a file-scope device array instead of a caller workspace. Each GPU the
+// library runs on holds its own copy until the process ends; its address on
+// a device is asked for once, with that device current, and kept.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the calling thread's current device.
+static int scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_EINVAL, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PKV_EHIP, "address of the scratch array: %s", hipGetErrorString(e));
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return PKV_OK;
+}
+
+extern "C" int paged_attention_decode_noalloc(float *out, const void *q, const void *k_cache,
+                                              const void *v_cache, const int32_t *block_tables,
+                                              int32_t max_blocks, const int32_t *context_lens,
+                                              int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
+                                              int32_t D, int32_t bs, int32_t num_blocks,
+                                              float scale, int dtype, int32_t part,
+                                              float *lse_out, void *stream) {
+  if (!elem_bytes(dtype))
+    return fail(PKV_EINVAL, "unsupported dtype %d", dtype);
+  size_t need = 0;
+  if (int rc = paged_attention_workspace_size(B, nq, Hq, Hkv, D, max_blocks, bs, part, &need))
+    return rc;
+  if (need > kScratchBytes)
+    return fail(PKV_EINVAL,
+                "this call needs %zu bytes of partials; the no-allocation entry point holds "
+                "%zu (pass a workspace to paged_attention_decode instead)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  if (need)
+    if (int rc = scratch_address(&ws)) return rc;
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks,
+                     context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype, part, ws,
+                     need ? kScratchBytes : 0, lse_out, stream);
 }
 
 extern "C" int paged_attention_decode_q3(float *out, const void *q, const uint8_t *k_codes,
