@@ -60,7 +60,7 @@ struct ShareArgs {
   int32_t prefix_part;  // tokens per prefix partition (multiple of 16)
 };
 
-template <int D>
+template <int D, int W = 1>
 struct PrefixGeo {
   static constexpr int NC = D / 32;                // A-operand chunks per lane (16 B each)
   static constexpr int NCB = D / 16;               // column blocks of P V
@@ -68,17 +68,23 @@ struct PrefixGeo {
   static constexpr int kTileBytes = 2 * kHalf;     // K then V
   static constexpr int kLoads = kTileBytes / 1024; // 1 KiB gathers per tile
   static constexpr int kRowChunks = D / 8;         // 16-byte chunks per V token row
-  // tiles in the ring (64 KiB at most): all but one are in flight while the
-  // oldest is read, so the workgroup keeps up to 56 KiB of gathers going
-  static constexpr int kSlots = kTileBytes <= 8192 ? 8 : 65536 / kTileBytes;
-  static_assert(kSlots >= 3 && (kSlots & (kSlots - 1)) == 0, "ring of 4 or 8 slots");
+  // tiles in the ring: 128 KiB for workgroups of eight wavefronts (their
+  // registers allow one workgroup per CU, so the LDS would idle otherwise),
+  // 64 KiB else, at most 16 tiles
+  static constexpr int kRingBytes = W >= 8 ? 131072 : 65536;
+  static constexpr int kSlots =
+      kRingBytes / kTileBytes > 16 ? 16 : kRingBytes / kTileBytes;
+  static_assert(kSlots >= 4 && (kSlots & (kSlots - 1)) == 0, "ring of 4, 8 or 16 slots");
 };
 
-// XOR swizzle of the 16-byte chunks of V token row t: the sixteen rows of a
-// tile put any given chunk in different bank groups.
+// XOR swizzle of the 16-byte chunks of V token row t. A transposing read of
+// a 16-lane group names 32 bytes (a chunk pair) of each of four consecutive
+// tokens; XOR-ing with 2 t moves the four tokens' pairs to four different
+// 32-byte bank ranges (and eight consecutive tokens to all sixteen chunks of
+// a row), where XOR-ing with t would leave tokens t and t ^ 1 on one range.
 template <int D>
 __device__ __forceinline__ int v_swizzle(int t) {
-  return t & (PrefixGeo<D>::kRowChunks - 1);
+  return (2 * t) & (PrefixGeo<D>::kRowChunks - 1);
 }
 
 // One tile's MFMA operands from an LDS slot, with one wait for all of them.
@@ -287,6 +293,84 @@ __device__ __forceinline__ void read_v2_128(uint2 (&v)[2][8], const PKV_LDS char
       : "memory");
 }
 
+// K halves and V halves on their own for the other head dims, so that a
+// trip's K can be read for its score products while the V of the trip
+// before is still to come: D = 64 (two tiles a trip, 4 KiB apart) and
+// D = 256 (one tile a trip).
+__device__ __forceinline__ void read_k2_64(u32x4_t (&k)[2][2], const PKV_LDS char *kp) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:4096\n\t"
+      "ds_read_b128 %3, %4 offset:5120\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1])
+      : "v"(kp)
+      : "memory");
+}
+
+__device__ __forceinline__ void read_v2_64(uint2 (&v)[2][4], const PKV_LDS char *const (&va)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %10 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:4096\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[1][0]),
+        "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
+      : "memory");
+}
+
+__device__ __forceinline__ void read_k_256(u32x4_t (&k)[8], const PKV_LDS char *kp) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),
+        "=&v"(k[6]), "=&v"(k[7])
+      : "v"(kp)
+      : "memory");
+}
+
+__device__ __forceinline__ void read_v_256(uint2 (&v)[16], const PKV_LDS char *const (&va)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %17\n\t"
+      "ds_read_b64_tr_b16 %2, %18\n\t"
+      "ds_read_b64_tr_b16 %3, %19\n\t"
+      "ds_read_b64_tr_b16 %4, %20\n\t"
+      "ds_read_b64_tr_b16 %5, %21\n\t"
+      "ds_read_b64_tr_b16 %6, %22\n\t"
+      "ds_read_b64_tr_b16 %7, %23\n\t"
+      "ds_read_b64_tr_b16 %8, %24\n\t"
+      "ds_read_b64_tr_b16 %9, %25\n\t"
+      "ds_read_b64_tr_b16 %10, %26\n\t"
+      "ds_read_b64_tr_b16 %11, %27\n\t"
+      "ds_read_b64_tr_b16 %12, %28\n\t"
+      "ds_read_b64_tr_b16 %13, %29\n\t"
+      "ds_read_b64_tr_b16 %14, %30\n\t"
+      "ds_read_b64_tr_b16 %15, %31\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]),
+        "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
+        "v"(va[7]), "v"(va[8]), "v"(va[9]), "v"(va[10]), "v"(va[11]), "v"(va[12]),
+        "v"(va[13]), "v"(va[14]), "v"(va[15])
+      : "memory");
+}
+
 // Where the query rows of a workgroup come from.
 enum class RowSource {
   kSharedGroups,  // stacked rows of a sharing group's members over their common prefix
@@ -295,7 +379,7 @@ enum class RowSource {
 
 template <int D, int W, int RT, RowSource SRC>
 __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareArgs &s) {
-  using Gp = PrefixGeo<D>;
+  using Gp = PrefixGeo<D, W>;
   constexpr int NC = Gp::NC, NCB = Gp::NCB, kSlots = Gp::kSlots;
   constexpr int TT = D <= 128 ? 2 : 1;  // 16-token tiles per trip
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
@@ -421,13 +505,18 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
     const int t = pos / (D * 2), cp = (pos % (D * 2)) / 16;
     return t * (D * 2) + (cp ^ v_swizzle<D>(t)) * 16;
   };
+  // bytes of one block (all KV heads) and this KV head's offset inside it
+  const size_t blk_bytes = (size_t)a.Hkv * a.bs * (D * 2);
+  const size_t head_off = (size_t)h * a.bs * (D * 2);
+  const bool bs16 = a.bs == kTile;  // a block is one tile: no offset inside it
   auto stage = [&](int slot, int k, int blk) {
     const int t0 = t_begin + k * kTile;
     if (blk < 0 || blk >= a.num_blocks) {
       bad = 1;
       blk = 0;
     }
-    const size_t tile = (((size_t)blk * a.Hkv + h) * a.bs + (size_t)(t0 % a.bs)) * (D * 2);
+    const size_t tile = (size_t)(uint32_t)blk * blk_bytes + head_off +
+                        (bs16 ? 0 : (size_t)(t0 % a.bs) * (D * 2));
     PKV_LDS char *dst = ring + slot * Gp::kTileBytes;
 #pragma unroll
     for (int i = 0; i < (Gp::kLoads + W - 1) / W; ++i) {
@@ -468,6 +557,20 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
   }
   float scale_log2 = a.scale_log2;  // waited for here, not inside the loop
   settle_s(scale_log2);
+  if (scale_log2 < 0.f) {
+    // q.k x scale = (-q).k x (-scale): negating bf16 queries is exact, and a
+    // positive scale lets the largest raw score stand for the largest scaled one
+    scale_log2 = -scale_log2;
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        qb[r][c].x ^= 0x80008000u;
+        qb[r][c].y ^= 0x80008000u;
+        qb[r][c].z ^= 0x80008000u;
+        qb[r][c].w ^= 0x80008000u;
+      }
+  }
 
   // keys of this partition visible to row ln of tile r
   int lim_p[RT];
@@ -490,59 +593,51 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
       stage(kn % kSlots, min(kn, n_tiles - 1), __builtin_amdgcn_readlane(tblv, kn & 63));
     }
   };
-
-  // prologue: trips 0 .. kTrips - 2 in flight
+  // this lane's LDS read addresses inside slot 0: its K chunks, and the V
+  // chunk of each column block (a trip adds its slot's offset)
+  const PKV_LDS char *k_rd = ring + lane * 16;
+  const PKV_LDS char *v_rd[NCB];
 #pragma unroll
-  for (int j = 0; j < kTrips - 1; ++j)
+  for (int cb = 0; cb < NCB; ++cb) v_rd[cb] = ring + v_addr[cb];
+
+  // Trips go in windows of kWin with one barrier each: within a window the
+  // wavefronts drift apart, so that while some read LDS others run the
+  // matrix cores or the softmax, instead of all doing the same in step.
+  constexpr int kWin = kTrips >= 8 ? 2 : 1;
+  // prologue: trips 0 .. kTrips - kWin - 1 in flight
+#pragma unroll
+  for (int j = 0; j < kTrips - kWin; ++j)
     if (j < n_trips) stage_trip(j);
   for (int j = 0; j < n_trips; ++j) {
-    // this wavefront's gathers of trip j have landed (the later ones, up to
-    // kTrips - 2 trips, may not)
-    const int ahead = min(n_trips - 1 - j, kTrips - 2);
-    static_for<kTrips - 1>([&](auto ac) {
-      constexpr int A = decltype(ac)::value;
-      if (ahead == A) wait_vmcnt<A * TT * kPerWave>();
-    });
-    // ... and so have everyone's; everyone is done reading trip j - 1, whose
-    // slots take trip j + kTrips - 1
-    __builtin_amdgcn_s_barrier();
-    if (j + kTrips - 1 < n_trips) stage_trip(j + kTrips - 1);
-    const PKV_LDS char *kt = ring + ((TT * j) % kSlots) * Gp::kTileBytes;
+    if (j % kWin == 0) {
+      // this wavefront's gathers of trips j .. j + kWin - 1 have landed (the
+      // later ones, up to kTrips - 2 kWin trips, may not) ...
+      const int ahead = max(0, min(n_trips - j - kWin, kTrips - 2 * kWin));
+      static_for<kTrips - 2 * kWin + 1>([&](auto ac) {
+        constexpr int A = decltype(ac)::value;
+        if (ahead == A) wait_vmcnt<A * TT * kPerWave>();
+      });
+      // ... and so have everyone's; everyone is done reading the window
+      // before, whose slots take the trips kTrips - kWin ahead
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int u = 0; u < kWin; ++u)
+        if (j + kTrips - kWin + u < n_trips) stage_trip(j + kTrips - kWin + u);
+    }
+    const int so = ((TT * j) % kSlots) * Gp::kTileBytes;  // the trip's slot
     const int t0 = t_begin + TT * j * kTile;
 
+    // the K half of the trip's tiles; V is read after the softmax
     u32x4_t kr[TT][NC];
-    uint2 vb[TT][NCB];
-    constexpr bool kSplitReads = D == 128 && TT == 2;
-    const PKV_LDS char *va[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) va[cb] = kt + v_addr[cb];
-    if constexpr (kSplitReads)
-      read_k2_128(kr, kt + lane * 16);
-    else if constexpr (TT == 2)
-      read_kv2<D>(kr, vb, kt + lane * 16, va);
+    if constexpr (D == 128)
+      read_k2_128(kr, k_rd + so);
+    else if constexpr (D == 64)
+      read_k2_64(kr, k_rd + so);
     else
-      read_kv<D>(kr[0], vb[0], kt + lane * 16, va);
-    auto zero_tail = [&]() {
-      if (t0 + TT * kTile <= t_end) return;
-      // the last trip: V of tokens past the partition (stale slots past a
-      // context's end, or the repeated last tile) is zeroed, since a zero
-      // weight times a non-finite value would still poison the product
-#pragma unroll
-      for (int u = 0; u < TT; ++u) {
-        const int tk = t0 + u * kTile + 4 * lg;
-        const unsigned xm = (tk < t_end ? 0xffffu : 0u) | (tk + 1 < t_end ? 0xffff0000u : 0u);
-        const unsigned ym = (tk + 2 < t_end ? 0xffffu : 0u) | (tk + 3 < t_end ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          vb[u][cb].x &= xm;
-          vb[u][cb].y &= ym;
-        }
-      }
-    };
-    if constexpr (!kSplitReads) zero_tail();
+      read_k_256(kr[0], k_rd + so);
 
-    // S^T = K Q^T per tile and row tile: sv[u][r][e] = score of row ln with
-    // token t0 + 16 u + 4 lg + e
+    // S^T = K Q^T per tile and row tile: sv[u][r][e] = q.k of row ln with
+    // token t0 + 16 u + 4 lg + e (unscaled; the scale enters the exponent)
     f32x4_t sv[TT][RT];
 #pragma unroll
     for (int u = 0; u < TT; ++u)
@@ -557,63 +652,81 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
           sv[u][r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8_t, kr[u][c]), __builtin_bit_cast(bf16x8_t, qb[r][c]),
               sv[u][r], 0, 0, 0);
+
     uint2 pa[TT][RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      float sc[TT][4];
-      bool need = false;
-      if (__all(t0 + TT * kTile <= lim_p[r])) {
-        // every row of the tile sees all of the trip's tokens: no masks
+      if (!__all(t0 + TT * kTile <= lim_p[r])) {
+        // tokens a row does not see (causal, or past the partition) score -inf
 #pragma unroll
         for (int u = 0; u < TT; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[u][e] = sv[u][r][e] * scale_log2;
-            need |= sc[u][e] > m_row[r] + kLazyLog2;
-          }
-      } else {
-#pragma unroll
-        for (int u = 0; u < TT; ++u)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool vis = t0 + 16 * u + 4 * lg + e < lim_p[r];
-            sc[u][e] = vis ? sv[u][r][e] * scale_log2 : kNegInf;
-            need |= sc[u][e] > m_row[r] + kLazyLog2;
-          }
+          for (int e = 0; e < 4; ++e)
+            if (t0 + 16 * u + 4 * lg + e >= lim_p[r]) sv[u][r][e] = kNegInf;
       }
-      if (__any(need)) {
-        // row ln's scores are spread over the four lane groups
-        float tmax = kNegInf;
+      // the lazy maximum: raised only when a score passes it by kLazyLog2;
+      // scale_log2 > 0 (a negative scale was moved into the query), so the
+      // largest raw score gives the largest scaled one
+      float rmax = kNegInf;
 #pragma unroll
-        for (int u = 0; u < TT; ++u)
-          tmax = fmaxf(tmax, fmaxf(fmaxf(sc[u][0], sc[u][1]), fmaxf(sc[u][2], sc[u][3])));
-        tmax = fmaxf(tmax, exact_xor<16>(tmax));
-        tmax = fmaxf(tmax, exact_xor<32>(tmax));
-        const float mn = fmaxf(m_row[r], tmax);
+      for (int u = 0; u < TT; ++u)
+        rmax = fmaxf(rmax, fmaxf(fmaxf(sv[u][r][0], sv[u][r][1]), fmaxf(sv[u][r][2], sv[u][r][3])));
+      const float tmax = rmax * scale_log2;
+      if (__any(tmax > m_row[r] + kLazyLog2)) {
+        // row ln's scores are spread over the four lane groups
+        float gmax = fmaxf(tmax, exact_xor<16>(tmax));
+        gmax = fmaxf(gmax, exact_xor<32>(gmax));
+        const float mn = fmaxf(m_row[r], gmax);
         const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row[r] - mn);
         m_row[r] = mn;
         l_part[r] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) o[r][cb] *= alpha;
       }
-      // a masked score (-inf) gives exp2(-inf) = 0; the maximum is floored so
-      // that a row with no visible key yet (maximum -inf) gives 0 too, not NaN
-      const float m_sub = fmaxf(m_row[r], -3.0e38f);
+      // weights exp2(s * scale_log2 - m): a masked score (-inf) gives 0, and
+      // the maximum is floored so that a row with no visible key yet (maximum
+      // -inf) gives 0 too, not NaN
+      const float neg_m = -fmaxf(m_row[r], -3.0e38f);
 #pragma unroll
       for (int u = 0; u < TT; ++u) {
         float pw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pw[e] = __builtin_amdgcn_exp2f(sc[u][e] - m_sub);
+          pw[e] = __builtin_amdgcn_exp2f(fmaf(sv[u][r][e], scale_log2, neg_m));
           l_part[r] += pw[e];
         }
         pa[u][r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
       }
     }
 
-    if constexpr (kSplitReads) {
-      read_v2_128(vb, va);
-      zero_tail();
+    // the V half, read transposed
+    uint2 vb[TT][NCB];
+    {
+      const PKV_LDS char *va[NCB];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) va[cb] = v_rd[cb] + so;
+      if constexpr (D == 128)
+        read_v2_128(vb, va);
+      else if constexpr (D == 64)
+        read_v2_64(vb, va);
+      else
+        read_v_256(vb[0], va);
+    }
+    if (t0 + TT * kTile > t_end) {
+      // the last trip: V of tokens past the partition (stale slots past a
+      // context's end, or the repeated last tile) is zeroed, since a zero
+      // weight times a non-finite value would still poison the product
+#pragma unroll
+      for (int u = 0; u < TT; ++u) {
+        const int tk = t0 + u * kTile + 4 * lg;
+        const unsigned xm = (tk < t_end ? 0xffffu : 0u) | (tk + 1 < t_end ? 0xffff0000u : 0u);
+        const unsigned ym = (tk + 2 < t_end ? 0xffffu : 0u) | (tk + 3 < t_end ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          vb[u][cb].x &= xm;
+          vb[u][cb].y &= ym;
+        }
+      }
     }
 
     // O^T += V^T P^T: A operand V[token][dim cb * 16 + ln], B operand
@@ -659,7 +772,7 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
 }
 
 template <int D, int W, int RT>
-__global__ void __launch_bounds__(W * 64)
+__global__ void __launch_bounds__(W * 64, W >= 4 ? 2 : 1)
 prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   mfma_rows_body<D, W, RT, RowSource::kSharedGroups>(a, s);
 }
@@ -667,7 +780,7 @@ prefix_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
 // Chunked prefill: grid (KV partitions, Hkv, B x chunks); s carries only
 // chunks and prefix_part (the partition length).
 template <int D, int W, int RT>
-__global__ void __launch_bounds__(W * 64)
+__global__ void __launch_bounds__(W * 64, W >= 4 ? 2 : 1)
 chunk_mfma_kernel(const DecodeArgs a, const ShareArgs s) {
   mfma_rows_body<D, W, RT, RowSource::kChunk>(a, s);
 }
