@@ -273,7 +273,8 @@ class PrefixVerifyWorkload:
     call (query i of K sees the first L - K + i + 1 tokens).
     """
 
-    def __init__(self, name: str, device, prefix: int | None = None, share: bool = True):
+    def __init__(self, name: str, device, prefix: int | None = None, share: bool = True,
+                 rotate: int = 1):
         import torch
 
         import paged_kv_cache_202_amd as pkv
@@ -351,23 +352,32 @@ class PrefixVerifyWorkload:
             ws = max(ws, pkv.paged_attention_shared_workspace_size(
                 B, K, Hq, Hkv, D, self.max_blocks, bs, self.groups, self.part))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev) if ws else None
-        self.rotate = 1
+        # pool copies used in turn (same contents, same tables): with two, the
+        # working sets of successive calls (2 x 150 MB at the C5 sizes) do not
+        # fit the 256 MB last-level cache, so repeats are read from HBM
+        self.rotate = max(1, rotate)
+        self.kcs = [self.kc] + [self.kc.clone() for _ in range(self.rotate - 1)]
+        self.vcs = [self.vc] + [self.vc.clone() for _ in range(self.rotate - 1)]
         torch.cuda.synchronize()
 
     def cache_write(self, i: int) -> None:
-        self.pkv.paged_cache_write(self.k_step, self.v_step, self.kc, self.vc, self.d_step_slots)
+        r = i % self.rotate
+        self.pkv.paged_cache_write(self.k_step, self.v_step, self.kcs[r], self.vcs[r],
+                                   self.d_step_slots)
 
     def attend(self, i: int) -> None:
+        r = i % self.rotate
         if self.share:
-            self.pkv.paged_attention_decode_shared(self.out, self.d_q, self.kc, self.vc,
+            self.pkv.paged_attention_decode_shared(self.out, self.d_q, self.kcs[r], self.vcs[r],
                                                    self.d_tables, self.d_lens, self.scale,
                                                    self.groups, self.d_groups,
                                                    partition_tokens=self.part,
                                                    workspace=self.ws, lse=self.lse)
             return
-        self.pkv.paged_attention_decode(self.out, self.d_q, self.kc, self.vc, self.d_tables,
-                                        self.d_lens, self.scale, partition_tokens=self.part,
-                                        workspace=self.ws, lse=self.lse)
+        self.pkv.paged_attention_decode(self.out, self.d_q, self.kcs[r], self.vcs[r],
+                                        self.d_tables, self.d_lens, self.scale,
+                                        partition_tokens=self.part, workspace=self.ws,
+                                        lse=self.lse)
 
     def step(self, i: int) -> None:
         self.cache_write(i)
@@ -578,7 +588,8 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe, dev)
     if args.workload.startswith("prefix_share"):
-        wk = PrefixVerifyWorkload(args.workload, dev, share=not args.no_share)
+        wk = PrefixVerifyWorkload(args.workload, dev, share=not args.no_share,
+                                  rotate=args.rotate)
     else:
         wk = Workload(args.workload, args.rotate, dev)
     log(f"[bench] workload {args.workload} ready; max_blocks {wk.max_blocks}")

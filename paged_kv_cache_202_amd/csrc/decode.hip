@@ -14,6 +14,7 @@
 #include "decode_kernel.h"
 #include "verify_mfma.h"
 #include "shared_prefix.h"
+#include "group_decode.h"
 #include "decode_mfma.h"
 #include "pagedkv.h"
 #include "status.h"
@@ -755,6 +756,11 @@ int share_plan(int32_t G, int32_t nq, int32_t Hkv, int32_t D, int32_t n_groups,
 
 }  // namespace
 
+// Tokens past the longest shared prefix up to which the one-pass kernel
+// serves a batch: its workgroups stream their members' own tokens alone, so
+// long private rests go to the partitioned kernels instead.
+constexpr int64_t kOnePassRest = 4096;
+
 static size_t shared_workspace_need(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t D,
                                     int64_t max_ctx, int32_t part, const SharePlan &sp) {
   const Plan pl = plan_launch(B, Hkv, max_ctx, part, false);
@@ -809,6 +815,47 @@ extern "C" int paged_attention_decode_shared(
   SharePlan sp;
   if (int rc = share_plan(G, nq, Hkv, D, n_groups, max_members, max_prefix, &sp)) return rc;
   const int64_t max_ctx = (int64_t)max_blocks * bs;
+
+  // Every sequence in a group, and little past the prefixes: one pass per
+  // (KV head, a few members) over the shared prefix and each member's own
+  // tokens, merged on chip -- no prefix partials, no reduce launch.
+  if (D <= 128 && n_members == B && max_ctx <= (int64_t)max_prefix + kOnePassRest) {
+    const int32_t mpt = kVerifyRows / sp.rpm;
+    const int64_t wg2 = (int64_t)Hkv * n_groups * ((max_members + 2 * mpt - 1) / (2 * mpt));
+    const int32_t RT = wg2 >= kResidentWaves / 8 ? 2 : 1;
+    const int32_t chunks = (max_members + RT * mpt - 1) / (RT * mpt);
+    GroupLauncher one = pick_group(D, RT);
+    if (!one) return fail(PKV_EINVAL, "no one-pass kernel for D=%d", D);
+    if ((int64_t)n_groups * chunks > 65535) return fail(PKV_EINVAL, "too many groups for one launch");
+    DecodeArgs a{};
+    a.out = out;
+    a.lse = lse_out;
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.tables = block_tables;
+    a.lens = context_lens;
+    a.B = B;
+    a.max_blocks = max_blocks;
+    a.nq = nq;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.bs = bs;
+    a.num_blocks = num_blocks;
+    a.scale_log2 = scale * kLog2e;
+    ShareArgs sh{};
+    sh.group_start = group_start;
+    sh.members = members;
+    sh.group_tokens = group_tokens;
+    sh.n_groups = n_groups;
+    sh.n_members = n_members;
+    sh.chunks = chunks;
+    sh.rpm = sp.rpm;
+    one(a, sh, dim3(Hkv, n_groups * chunks), (hipStream_t)stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PKV_EHIP, "one-pass launch: %s", hipGetErrorString(e));
+    return PKV_OK;
+  }
 
   // the rest of every context: the ordinary kernels, never the stream
   const bool mfma = use_mfma(dtype, nq, G);

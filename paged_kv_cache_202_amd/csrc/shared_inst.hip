@@ -1,5 +1,6 @@
 // Instantiations of the MFMA row-tile kernels (bf16 caches): the shared-prefix
 // kernel and the chunked-prefill kernel.
+#include "group_decode.h"
 #include "shared_prefix.h"
 
 namespace pkv {
@@ -38,6 +39,17 @@ PrefixLauncher pick_rows_kernel(int D, int W, int RT) {
 
 PrefixLauncher pick_prefix(int D, int W, int RT, bool chunk) {
   return chunk ? pick_rows_kernel<true>(D, W, RT) : pick_rows_kernel<false>(D, W, RT);
+}
+
+template <int D, int RT>
+void launch_group(const DecodeArgs &a, const ShareArgs &s, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((group_mfma_kernel<D, RT>), grid, dim3(512), 0, st, a, s);
+}
+
+GroupLauncher pick_group(int D, int RT) {
+  if (D == 64) return RT == 2 ? &launch_group<64, 2> : RT == 1 ? &launch_group<64, 1> : nullptr;
+  if (D == 128) return RT == 2 ? &launch_group<128, 2> : RT == 1 ? &launch_group<128, 1> : nullptr;
+  return nullptr;
 }
 
 }  // namespace decode
