@@ -122,8 +122,11 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
   constexpr int TPL = Gg::TPL, RB = Gg::RB, kSlots = Gg::kSlots;
   constexpr int ROWS = RT * 16;
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
+  // rows padded by four floats: the 16 rows one wavefront writes at once
+  // then start in 16 different bank groups instead of one
+  constexpr int kAccPitch = D + 4;
   struct Merge {
-    float acc[W][ROWS][D];
+    float acc[W][ROWS][kAccPitch];
     float m[W][ROWS];
     float l[W][ROWS];
   };
