@@ -44,6 +44,9 @@ def kernel_sources(workload: str) -> list:
 
     csrc = "paged_kv_cache_202_amd/csrc/"
     w = WORKLOADS[workload]
+    if w.shared_prefix:  # the one-pass shared-prefix kernel
+        return [csrc + "decode_kernel.h", csrc + "verify_mfma.h", csrc + "shared_prefix.h",
+                csrc + "group_decode.h", csrc + "shared_inst.hip", csrc + "decode.hip"]
     if w.kv_codes or mfma_decode(w.dtype, w.queries_per_seq, w.head_dim, w.partition_tokens):
         return [csrc + "decode_kernel.h", csrc + "verify_mfma.h", csrc + "decode_mfma.h",
                 csrc + "decode_inst_mfma_d128.hip", csrc + "decode.hip"]
@@ -67,10 +70,33 @@ def sources_sha256(workload: str) -> str:
     return h.hexdigest()
 
 
+def profile_path(workload: str) -> str:
+    """The committed counter summary of a workload's attention call, named for
+    its dominant kernel."""
+    from synth.workloads import WORKLOADS
+
+    kernel = "group_mfma_kernel" if WORKLOADS[workload].shared_prefix else "decode"
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}.json")
+
+
+def prefix_unique_bytes(w) -> int:
+    """Minimum bytes of one shared-prefix attention call: the shared prefix's
+    K/V once per KV head, each sequence's private tokens (suffix and drafts)
+    once, q read, fp32 out written, tables and lengths read."""
+    B, nq = w.batch, w.queries_per_seq
+    L = w.shared_prefix + w.unique_suffix + nq
+    lens = np.full(B, L, dtype=np.int64)
+    logical = algorithmic_bytes(B, nq, w.q_heads, w.kv_heads, w.head_dim, w.esize, lens,
+                                -(-L // w.block_size))
+    kv_logical = 2 * w.kv_heads * w.head_dim * w.esize * int(lens.sum())
+    kv_unique = 2 * w.kv_heads * w.head_dim * w.esize * (w.shared_prefix + B * (L - w.shared_prefix))
+    return logical - kv_logical + kv_unique
+
+
 def profiled_traffic(workload: str):
     """HBM bytes per attention call from the committed rocprofv3 counter summary,
     or None when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}.json")
+    path = profile_path(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -489,6 +515,47 @@ def _counter_per_dispatch(d: str, counter: str, kernel_re: str):
     return statistics.mean(per.values()), len(per)
 
 
+def merge_sq_counters(args) -> int:
+    """Add one rocprofv3 pass of SQ counters (LDS use, bank conflicts, wave
+    residency, instruction mix: whichever the pass holds) to the workload's
+    committed summary, with the command that took them. SQ_WAVE_CYCLES is
+    read as counting 4-cycle units (per shader engine), SQ_BUSY_CYCLES as
+    cycles; the machine has 32 shader engines of 32 SIMDs."""
+    path = profile_path(args.workload)
+    with open(path) as f:
+        out = json.load(f)
+    rows = [r for r in _csv_rows(args.sq_dir, "counter_collection.csv")
+            if re.search(args.kernel_regex, r["Kernel_Name"])]
+    per = {}
+    for r in rows:
+        per.setdefault(r["Dispatch_Id"], {}).setdefault(r["Counter_Name"], 0.0)
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"/{args.kernel_regex}/ matches no dispatch in {args.sq_dir}")
+    names = sorted(next(iter(per.values())))
+    avg = {c: sum(d[c] for d in per.values()) / len(per) for c in names}
+    derived = {}
+    if "SQ_WAVE_CYCLES" in avg and "SQ_BUSY_CYCLES" in avg:
+        derived["resident_waves_per_simd"] = 4 * avg["SQ_WAVE_CYCLES"] / avg["SQ_BUSY_CYCLES"] / 32
+    if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_INSTS_LDS" in avg:
+        derived["bank_conflict_cycles_per_lds_instruction"] = (avg["SQ_LDS_BANK_CONFLICT"] /
+                                                               avg["SQ_INSTS_LDS"])
+    if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg:
+        derived["bank_conflict_share_of_lds_active"] = (avg["SQ_LDS_BANK_CONFLICT"] /
+                                                        avg["SQ_LDS_IDX_ACTIVE"])
+    if "SQ_INSTS_VALU" in avg and "SQ_WAVES" in avg:
+        w = avg["SQ_WAVES"]
+        derived["per_wave"] = {c[len("SQ_INSTS_"):].lower(): avg[c] / w
+                               for c in names if c.startswith("SQ_INSTS_")}
+    key = args.sq_key or "sq_counters"
+    out[key] = {"counters_per_dispatch": avg, "dispatches": len(per), "derived": derived,
+                "command": args.sq_command or ""}
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out[key], indent=1))
+    return 0
+
+
 def summarize_profile(args) -> int:
     """Condense rocprofv3 output into profiles/decode_<workload>.json: the
     kernel's average duration (--kernel-trace --stats), its HBM bytes per
@@ -496,6 +563,8 @@ def summarize_profile(args) -> int:
     read for a plain copy of known size (--copy-probe), and a hash of the
     kernel sources they were taken on."""
     kre = args.kernel_regex
+    if args.sq_dir and not args.trace_dir:
+        return merge_sq_counters(args)
     stats = [r for r in _csv_rows(args.trace_dir, "kernel_stats.csv") if re.search(kre, r["Name"])]
     if len(stats) != 1:
         raise SystemExit(f"/{kre}/ matches {len(stats)} kernels in the trace")
@@ -511,7 +580,10 @@ def summarize_profile(args) -> int:
     from synth import workloads as wl
 
     w = WORKLOADS[args.workload]
-    if w.context is None:  # the seeded lengths, drawn as the workload draws them
+    if w.shared_prefix:
+        lens = np.full(w.batch, w.shared_prefix + w.unique_suffix + w.queries_per_seq,
+                       dtype=np.int64)
+    elif w.context is None:  # the seeded lengths, drawn as the workload draws them
         rng = np.random.default_rng(w.rng_seed)
         wl.free_stack_permutation(rng, w.num_blocks)
         lens = wl.draw_lengths(rng, w).astype(np.int64)
@@ -533,12 +605,16 @@ def summarize_profile(args) -> int:
         "fetch_bytes_per_launch": fetch * 1024 * ffac,
         "write_bytes_per_launch": write * 1024 * wfac,
         "traffic_bytes_per_launch": fetch * 1024 * ffac + write * 1024 * wfac,
-        "algorithmic_bytes_per_launch": algorithmic_bytes(
+        "algorithmic_bytes_per_launch": prefix_unique_bytes(w) if w.shared_prefix else
+        algorithmic_bytes(
             w.batch, w.queries_per_seq, w.q_heads, w.kv_heads, w.head_dim, w.esize, lens,
             -(-int(lens.max()) // w.block_size),
             kv_row_bytes={8: w.head_dim + 4, 3: w.head_dim // 2 + 4}.get(w.kv_codes)),
     }
-    path = os.path.join(ROOT, "profiles", f"decode_{args.workload}.json")
+    if w.shared_prefix:
+        out["algorithmic_bytes_note"] = ("unique bytes: every shared block once per KV head, "
+                                         "each sequence's private tokens once")
+    path = profile_path(args.workload)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
@@ -570,6 +646,10 @@ def main() -> int:
     ap.add_argument("--copy-fetch-dir")
     ap.add_argument("--copy-write-dir")
     ap.add_argument("--copy-mib", type=int, default=512)
+    ap.add_argument("--sq-dir", help="with --summarize-profile and no --trace-dir: merge this "
+                                     "rocprofv3 --pmc pass of SQ counters into the summary")
+    ap.add_argument("--sq-key", help="name of the merged section (default sq_counters)")
+    ap.add_argument("--sq-command", help="the rocprofv3 command that took the pass")
     args = ap.parse_args()
     if args.summarize_profile:
         return summarize_profile(args)

@@ -109,6 +109,8 @@ __device__ __forceinline__ void read_group_tile(u32x4_t (&k)[D / 32], uint2 (&v)
   }
 }
 
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
 // Most members a workgroup holds (RT = 2 row tiles of 16 one-row members).
 constexpr int kGroupMaxMembers = 32;
 
@@ -121,6 +123,11 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
   constexpr int NL = Gg::NL, KCH = Gg::KCH, NC = Gg::NC, NCB = Gg::NCB, CPT = Gg::CPT;
   constexpr int TPL = Gg::TPL, RB = Gg::RB, kSlots = Gg::kSlots;
   constexpr int ROWS = RT * 16;
+  // two row tiles: O^T += V^T P^T for both at once on v_mfma_f32_32x32x16_bf16
+  // (32 dims x 32 rows a product: four per tile at D = 128, not sixteen
+  // 16x16x16 products)
+  constexpr bool kWide = RT == 2;
+  constexpr int NB32 = D / 32;  // 32-dim blocks
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   // rows padded by four floats: the 16 rows one wavefront writes at once
   // then start in 16 different bank groups instead of one
@@ -286,7 +293,22 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
     for (int c = 0; c < KCH; ++c) ka[c] = row + 16 * ((KCH * lg + c) ^ (t % CPT));
   }
   const PKV_LDS char *va[NCB];
-  {
+  if constexpr (kWide) {
+    // the 32x32x16 A operand V^T of 32-dim block b: lane l holds dim
+    // 32 b + l % 32 of tokens 8 (l / 32) .. + 7, from two transposing reads
+    // (half h of the tokens: read 2 b + h); in them lane s of 16-lane group
+    // G names dims 4 (s % 4) .. + 3 of dims 32 b + 16 (G % 2) .. of token
+    // 8 (G / 2) + 4 h + s / 4
+#pragma unroll
+    for (int b = 0; b < NB32; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 8 * (lg >> 1) + 4 * h + (ln >> 2);
+        const PKV_LDS char *row = ring + Gg::kHalf + (t / TPL) * 1024 + (t % TPL) * RB;
+        const int c = 2 * (2 * b + (lg & 1)) + ((ln >> 1) & 1);
+        va[2 * b + h] = row + 16 * (c ^ ((2 * t) % CPT)) + 8 * (ln & 1);
+      }
+  } else {
     // lane s of group lg names dims 4 (s % 4) .. + 3 of column block cb of
     // token 4 lg + s / 4: byte 32 cb + 8 (s % 4) of its row, chunk-swizzled
     const int t = 4 * lg + (ln >> 2);
@@ -315,11 +337,23 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
     for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(vt + voff[i], dst + (NL + i) * 1024);
   };
 
+  // O^T: per row tile and 16-dim column block (16x16 layout: lane holds row
+  // ln, dims 4 lg .. + 3), or, two row tiles, per 32-dim block (32x32
+  // layout: lane l holds row tile (l / 16) % 2, row l % 16, and in register
+  // i dim 8 (i / 4) + 4 (l / 32) + i % 4 of the block)
   f32x4_t o[RT][NCB];
+  f32x16_t ow[NB32];
+  if constexpr (kWide) {
 #pragma unroll
-  for (int r = 0; r < RT; ++r)
+    for (int b = 0; b < NB32; ++b)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) o[r][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 16; ++i) ow[b][i] = 0.f;
+  } else {
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) o[r][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   float m_row[RT], l_part[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
@@ -368,26 +402,17 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
       read_group_tile<D, SLOT * Gg::kTileBytes>(kr, vt, ka, va);
       const int code = __builtin_amdgcn_readlane(codev, j & 63);
       const int mcur = (code >> 26) - 1, kcur = code & ((1 << 26) - 1);
-      if (j + kSlots < n_mine) {  // the slot is free again: refill it
-        const int jn = j + kSlots;
-        if ((jn & 63) == 0) {  // next window of tiles (drains the ring once)
-          tblv = window(jn >> 6, codev);
-          settle_v(tblv);
-          settle_v(codev);
-        }
-        stage_j(jn);
-      }
       const int t0 = kcur * kTile;
       if (mcur >= 0 && t0 + kTile > mem_len[mcur]) {
         // the member's last tile: slots past its length may hold stale bits
         // (even NaN), zeroed so that a zero weight cannot meet them
-        const int Lm = mem_len[mcur], tv = t0 + 4 * lg;
-        const uint32_t m01 = (tv < Lm ? 0xffffu : 0u) | (tv + 1 < Lm ? 0xffff0000u : 0u);
-        const uint32_t m23 = (tv + 2 < Lm ? 0xffffu : 0u) | (tv + 3 < Lm ? 0xffff0000u : 0u);
+        const int Lm = mem_len[mcur];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          vt[cb].x &= m01;
-          vt[cb].y &= m23;
+          // the tokens this lane's V elements come from
+          const int tv = kWide ? t0 + 8 * (lg >> 1) + 4 * (cb & 1) : t0 + 4 * lg;
+          vt[cb].x &= (tv < Lm ? 0xffffu : 0u) | (tv + 1 < Lm ? 0xffff0000u : 0u);
+          vt[cb].y &= (tv + 2 < Lm ? 0xffffu : 0u) | (tv + 3 < Lm ? 0xffff0000u : 0u);
         }
       }
       // S^T = K Q^T per row tile (one row tile: in two chains of half the
@@ -407,6 +432,9 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
         sv[r] = acc[0];
         if constexpr (NCH == 2) sv[r] += acc[1];
       }
+      uint2 pb[RT];     // each row tile's weights, bf16
+      float alpha[RT];  // each row tile's rescale of this lane's row
+      bool rescale = false;
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         // wavefront-uniform: the prefix's tile (or the member's own tile, its
@@ -421,16 +449,20 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
         }
         const float tmax =
             fmaxf(fmaxf(sv[r][0], sv[r][1]), fmaxf(sv[r][2], sv[r][3])) * scale_log2;
+        alpha[r] = 1.f;
         if (__any(tmax > m_row[r] + kLazyLog2)) {
           // row ln's scores are spread over the four lane groups
           float gmax = fmaxf(tmax, exact_xor<16>(tmax));
           gmax = fmaxf(gmax, exact_xor<32>(gmax));
           const float mn = fmaxf(m_row[r], gmax);
-          const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row[r] - mn);
+          alpha[r] = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row[r] - mn);
           m_row[r] = mn;
-          l_part[r] *= alpha;
+          l_part[r] *= alpha[r];
+          rescale = true;
+          if constexpr (!kWide) {
 #pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) o[r][cb] *= alpha;
+            for (int cb = 0; cb < NCB; ++cb) o[r][cb] *= alpha[r];
+          }
         }
         // a masked score gives exp2(-inf) = 0; the floored maximum keeps a
         // row with no visible key yet at 0, not NaN
@@ -441,12 +473,48 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
           pw[e] = __builtin_amdgcn_exp2f(fmaf(sv[r][e], scale_log2, neg_m));
           l_part[r] += pw[e];
         }
-        const uint2 pb = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
+        pb[r] = make_uint2(pack_bf16(pw[0], pw[1]), pack_bf16(pw[2], pw[3]));
+        if constexpr (!kWide) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(i16x4_t, vt[cb]), __builtin_bit_cast(i16x4_t, pb), o[r][cb], 0,
-              0, 0);
+          for (int cb = 0; cb < NCB; ++cb)
+            o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(i16x4_t, vt[cb]), __builtin_bit_cast(i16x4_t, pb[r]),
+                o[r][cb], 0, 0, 0);
+        }
+      }
+      if constexpr (kWide) {
+        if (rescale) {
+          // lane l's accumulator rows belong to row tile (l / 16) % 2
+          const float al = (lane & 16) ? alpha[1] : alpha[0];
+#pragma unroll
+          for (int b = 0; b < NB32; ++b) ow[b] *= al;
+        }
+        // P^T of both row tiles as the B operand: lane l takes row tile
+        // (l / 16) % 2's row l % 16, tokens 8 (l / 32) .. + 7. Row tile 0's
+        // weights sit in every lane (tokens 4 lg ..), so the swap of 16-lane
+        // rows gives, per dword, the low tokens (first result) and the high
+        // tokens (second result)
+        const auto sx = __builtin_amdgcn_permlane16_swap(pb[0].x, pb[1].x, false, false);
+        const auto sy = __builtin_amdgcn_permlane16_swap(pb[0].y, pb[1].y, false, false);
+        const uint4 pp = make_uint4(sx[0], sy[0], sx[1], sy[1]);
+#pragma unroll
+        for (int b = 0; b < NB32; ++b) {
+          const uint4 va4 = make_uint4(vt[2 * b].x, vt[2 * b].y, vt[2 * b + 1].x, vt[2 * b + 1].y);
+          ow[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, va4),
+                                                         __builtin_bit_cast(bf16x8_t, pp),
+                                                         ow[b], 0, 0, 0);
+        }
+      }
+      // the slot is free again: refill it, after this tile's products are
+      // issued, so that the gathers' issue overlaps the matrix core's work
+      if (j + kSlots < n_mine) {
+        const int jn = j + kSlots;
+        if ((jn & 63) == 0) {  // next window of tiles (drains the ring once)
+          tblv = window(jn >> 6, codev);
+          settle_v(tblv);
+          settle_v(codev);
+        }
+        stage_j(jn);
       }
     };
     // unrolled by the ring depth: tile j sits in slot j % kSlots
@@ -465,13 +533,26 @@ __global__ void __launch_bounds__(512, 2) group_mfma_kernel(const DecodeArgs a, 
   }
   bad = __builtin_amdgcn_readfirstlane(bad);
   __syncthreads();  // the partials overwrite the rings
+  if constexpr (kWide) {
+    float *dst = sm.mg.acc[wave][lane & 31] + 4 * (lane >> 5);
+#pragma unroll
+    for (int b = 0; b < NB32; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4 *>(dst + 32 * b + 8 * q) = make_float4(
+            ow[b][4 * q], ow[b][4 * q + 1], ow[b][4 * q + 2], ow[b][4 * q + 3]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      float *dst = sm.mg.acc[wave][r * 16 + ln];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
+            make_float4(o[r][cb][0], o[r][cb][1], o[r][cb][2], o[r][cb][3]);
+    }
+  }
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    float *dst = sm.mg.acc[wave][r * 16 + ln];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
-          make_float4(o[r][cb][0], o[r][cb][1], o[r][cb][2], o[r][cb][3]);
     if (lg == 0) {
       sm.mg.m[wave][r * 16 + ln] = m_row[r];
       sm.mg.l[wave][r * 16 + ln] = l_part[r];
