@@ -89,6 +89,18 @@ __device__ __forceinline__ int code_k_lane_offset(int lane, int i) {
   return i * 1024 + tl * RB + 16 * ((lane % Gc::CPT) ^ (t % Gc::CPT));
 }
 
+// This lane's byte offset inside a tile's bf16 V rows for the gather of
+// load row i: lane l fetches chunk (l % CPT) ^ (2 t % CPT) of token t =
+// i * TPL + l / CPT, so that LDS position p of token t holds chunk
+// p ^ (2 t % CPT). The four tokens one transposing read names (rows a
+// multiple of the bank width apart) then fall on different banks.
+template <int RB>
+__device__ __forceinline__ int bf16_v_lane_offset(int lane, int i) {
+  using Gc = CodeGeo<RB>;
+  const int tl = lane / Gc::CPT, t = i * Gc::TPL + tl;
+  return i * 1024 + tl * RB + 16 * ((lane % Gc::CPT) ^ ((2 * t) % Gc::CPT));
+}
+
 // One tile's operands from an LDS slot, with one wait for all of them.
 // K: this lane's KCH chunks (token l % 16, chunks KCH (l / 16) .. + KCH - 1,
 // at LDS offsets ka[c]); V: NV transposing reads at va + 32 j; scales: the
@@ -163,52 +175,54 @@ __device__ __forceinline__ void read_codes<256>(u32x4_t (&k)[4], uint2 (&v)[8], 
 }
 
 // bf16 tiles: KCH K chunks (as for codes) and D / 16 transposing 16-bit V
-// reads at va + 32 cb (ds_read_b64_tr_b16: in each 16-lane group lane i
-// receives element i % 4 of the 4 named by lanes i / 4 + 4 u, u = 0..3).
+// reads, column block cb at va[cb] (ds_read_b64_tr_b16: in each 16-lane
+// group lane i receives element i % 4 of the 4 named by lanes i / 4 + 4 u,
+// u = 0..3).
 template <int RB>
 __device__ __forceinline__ void read_bf16(u32x4_t (&k)[CodeGeo<RB>::KCH],
                                           uint2 (&v)[RB / 32],
                                           const PKV_LDS char *const (&ka)[CodeGeo<RB>::KCH],
-                                          const PKV_LDS char *va);
+                                          const PKV_LDS char *const (&va)[RB / 32]);
 
 template <>
 __device__ __forceinline__ void read_bf16<128>(u32x4_t (&k)[2], uint2 (&v)[4],
                                                const PKV_LDS char *const (&ka)[2],
-                                               const PKV_LDS char *va) {
+                                               const PKV_LDS char *const (&va)[4]) {
   asm volatile(
       "ds_read_b128 %0, %6\n\t"
       "ds_read_b128 %1, %7\n\t"
       "ds_read_b64_tr_b16 %2, %8\n\t"
-      "ds_read_b64_tr_b16 %3, %8 offset:32\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
-      "ds_read_b64_tr_b16 %5, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %3, %9\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %11\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
-      : "v"(ka[0]), "v"(ka[1]), "v"(va)
+      : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])
       : "memory");
 }
 
 template <>
 __device__ __forceinline__ void read_bf16<256>(u32x4_t (&k)[4], uint2 (&v)[8],
                                                const PKV_LDS char *const (&ka)[4],
-                                               const PKV_LDS char *va) {
+                                               const PKV_LDS char *const (&va)[8]) {
   asm volatile(
       "ds_read_b128 %0, %12\n\t"
       "ds_read_b128 %1, %13\n\t"
       "ds_read_b128 %2, %14\n\t"
       "ds_read_b128 %3, %15\n\t"
       "ds_read_b64_tr_b16 %4, %16\n\t"
-      "ds_read_b64_tr_b16 %5, %16 offset:32\n\t"
-      "ds_read_b64_tr_b16 %6, %16 offset:64\n\t"
-      "ds_read_b64_tr_b16 %7, %16 offset:96\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
-      "ds_read_b64_tr_b16 %9, %16 offset:160\n\t"
-      "ds_read_b64_tr_b16 %10, %16 offset:192\n\t"
-      "ds_read_b64_tr_b16 %11, %16 offset:224\n\t"
+      "ds_read_b64_tr_b16 %5, %17\n\t"
+      "ds_read_b64_tr_b16 %6, %18\n\t"
+      "ds_read_b64_tr_b16 %7, %19\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %21\n\t"
+      "ds_read_b64_tr_b16 %10, %22\n\t"
+      "ds_read_b64_tr_b16 %11, %23\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(v[0]), "=&v"(v[1]),
         "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va)
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7])
       : "memory");
 }
 
@@ -486,9 +500,12 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
     const char *kbase = (const char *)a.kc;
     const char *vbase = (const char *)a.vc;
-    int koff[NL];
+    int koff[NL], voff[NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) koff[i] = code_k_lane_offset<RB>(lane, i);
+    for (int i = 0; i < NL; ++i) {
+      koff[i] = code_k_lane_offset<RB>(lane, i);
+      voff[i] = kBf ? bf16_v_lane_offset<RB>(lane, i) : i * 1024 + lane * 16;
+    }
     int bad = 0;
     // gather the tile at logical token t0 (from block blk) into a ring slot,
     // in TileRing::stage's order: the scales (codes), the K rows (chunks
@@ -505,12 +522,12 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         gather_lds4<kKvNonTemporal>((const char *)((lane & 16) ? a.vs : a.ks) + so,
                                     dst + Ring::kCodeBytes);
       }
-      const char *kp = kbase + rowi * RB, *vp = vbase + rowi * RB + lane * 16;
+      const char *kp = kbase + rowi * RB, *vp = vbase + rowi * RB;
 #pragma unroll
       for (int i = 0; i < NL; ++i) gather_lds16<kKvNonTemporal>(kp + koff[i], dst + i * 1024);
 #pragma unroll
       for (int i = 0; i < NL; ++i)
-        gather_lds16<kKvNonTemporal>(vp + i * 1024, dst + (NL + i) * 1024);
+        gather_lds16<kKvNonTemporal>(vp + voff[i], dst + (NL + i) * 1024);
     };
 
     const int wstart = indep ? t_begin : t_begin + wave * kTile;  // this wavefront's first tile
@@ -582,11 +599,21 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       // V, codes: lane s of group lg names token 4 lg + (s / 2) % 4, bytes
       // 16 ((s / 2) / 4) + 8 (s % 2) .. + 7 of each 32-byte column pair; bf16:
       // token 4 lg + s / 4, dims 4 (s % 4) .. + 3 of each 16-dim column block
+      // cb (bytes 32 cb + 8 (s % 4), whose 16-byte chunk c sits at position
+      // c ^ (2 t % CPT)), one address per column block
       const PKV_LDS char *va;
+      const PKV_LDS char *vab[Gc::NV];
       {
         const int u = kBf ? ln >> 2 : ln >> 1, t = 4 * lg + (u & 3);
         const int col = kBf ? 8 * (ln & 3) : 16 * (u >> 2) + 8 * (ln & 1);
-        va = ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB + col;
+        const PKV_LDS char *row =
+            ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB;
+        va = row + col;
+#pragma unroll
+        for (int cb = 0; cb < Gc::NV; ++cb) {
+          const int c = 2 * cb + ((ln >> 1) & 1);
+          vab[cb] = row + 16 * (c ^ ((2 * t) % Gc::CPT)) + 8 * (ln & 1);
+        }
       }
       const PKV_LDS char *sa = ring_base + Ring::kCodeBytes + 16 * lg;
 #pragma unroll
@@ -609,9 +636,12 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
           const PKV_LDS char *kas[KCH];
 #pragma unroll
           for (int c = 0; c < KCH; ++c) kas[c] = ka[c] + so;
-          if constexpr (kBf)
-            read_bf16<RB>(kr, vt, kas, va + so);
-          else
+          if constexpr (kBf) {
+            const PKV_LDS char *vas[Gc::NV];
+#pragma unroll
+            for (int cb = 0; cb < Gc::NV; ++cb) vas[cb] = vab[cb] + so;
+            read_bf16<RB>(kr, vt, kas, vas);
+          } else
             read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
         }
         if (k + kSlots < n_tiles) {  // the slot is free again: refill it
