@@ -470,7 +470,50 @@ def cpu_baseline(wk: Workload, budget_s: float = 20.0) -> dict:
     return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"float64 C oracle walking block tables token by token, OpenMP over "
                       f"rows; {n_seq} of {wk.B} sequences (all {wk.Hq} heads, full context), "
-                      f"median of 3 runs of {med:.2f}s; rows {len(rows)} of {rows_total}"}
+                      f"median of 3 runs of {med:.2f}s; rows {len(rows)} of {rows_total}",
+            "python_oracle_small": python_oracle_c1()}
+
+
+def python_oracle_c1() -> dict:
+    """The pure-Python float64 oracle timed on the small fp32 configuration
+    (4 sequences of 6, 9, 17 and 33 tokens, 4 query heads over 2 KV heads,
+    head dim 64): its cost per token is that of a walk over block tables one
+    token at a time, which only the small case can afford."""
+    from oracle import attention as oatt
+    from oracle.pool import PagedPool
+    from synth import workloads as wl
+
+    w = wl.WORKLOADS["tiny_f32"]
+    rng = np.random.default_rng(w.rng_seed)
+    stack = wl.free_stack_permutation(rng, w.num_blocks)
+    lens = wl.draw_lengths(rng, w)
+    root = wl.root_seed(rng)
+    pool = PagedPool(w.num_blocks, w.block_size, stack.tolist())
+    slots = []
+    for b, n in enumerate(lens.tolist()):
+        pool.create(b)
+        slots += pool.append(b, n)[0]
+    tables, clens = pool.block_tables(range(w.batch), -(-int(lens.max()) // w.block_size))
+    T = int(lens.sum())
+    shape = (w.num_blocks, w.kv_heads, w.block_size, w.head_dim)
+    kp = np.zeros(shape, np.float32)
+    vp = np.zeros(shape, np.float32)
+    k = wl.cast(wl.normal_array(root, 0, (T, w.kv_heads, w.head_dim)), "f32")
+    v = wl.cast(wl.normal_array(root, 1, (T, w.kv_heads, w.head_dim)), "f32")
+    q = wl.cast(wl.normal_array(root, 2, (w.batch, 1, w.q_heads, w.head_dim)), "f32")
+    oatt.cache_write(kp, vp, k, v, slots, w.block_size)
+    scale = 1.0 / math.sqrt(w.head_dim)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oatt.attention(q, "f32", kp, vp, "f32", tables, clens, scale, w.block_size)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": w.batch / med, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": med,
+            "sample": "pure-Python float64 oracle, whole small fp32 batch (4 sequences, "
+                      "lengths 6/9/17/33, 4 query heads, 2 KV heads, head dim 64), "
+                      "median of 3 runs"}
 
 
 def copy_probe(mib: int, dev) -> int:
@@ -490,6 +533,45 @@ def copy_probe(mib: int, dev) -> int:
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": 2 * n * block, "copy_probe_bytes_written": 2 * n * block,
                       "launches": 3}), flush=True)
+    return 0
+
+
+def read_probe(mib: int, dev) -> int:
+    """Read ceilings of this machine: a buffer of `mib` MiB (well past the 256 MB
+    last-level cache) read as 4 KiB chunks -- the K (or V) run of one
+    16-token, 128-dim bf16 tile -- in sequence and in a seeded random order,
+    with the decode kernels' loads: to registers (plain and non-temporal; four
+    workgroups of eight wavefronts a CU) and through the non-temporal
+    direct-to-LDS rings (one workgroup a CU, 16 KiB in flight a wavefront).
+    Prints one JSON line; each figure is the median of 5 timed launches."""
+    import torch
+
+    import paged_kv_cache_202_amd as pkv
+
+    chunk = 4096
+    n = mib * (1 << 20) // chunk
+    buf = torch.randint(0, 256, (n * chunk,), dtype=torch.uint8, device=dev)
+    orders = {"sequential": torch.arange(n, dtype=torch.int32, device=dev),
+              "random": torch.from_numpy(np.random.default_rng(20260801).permutation(n)
+                                         .astype(np.int32)).to(dev)}
+    modes = {"registers": (0, 1024), "registers_nt": (1, 1024), "lds_rings_nt": (2, 256)}
+    out = {"read_probe_bytes": n * chunk, "chunk_bytes": chunk}
+    for oname, order in orders.items():
+        for mname, (mode, n_wg) in modes.items():
+            sink = torch.zeros(n_wg, dtype=torch.int32, device=dev)
+            pkv.paged_kv_read_probe(buf, order, sink, chunk, mode)
+            times = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                pkv.paged_kv_read_probe(buf, order, sink, chunk, mode)
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) * 1e-3)
+            gbs = n * chunk / statistics.median(times) / 1e9
+            out[f"{oname}_{mname}_GBs"] = gbs
+            log(f"[bench] read probe {oname:10s} {mname:13s} {gbs:7.0f} GB/s")
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -636,6 +718,9 @@ def main() -> int:
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run paged_kv_copy_blocks over MIB MiB of K and of V (a plain "
                          "copy of known size, to calibrate HBM byte counters), then exit")
+    ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
+                    help="only measure read ceilings over MIB MiB (sequential and random 4 KiB "
+                         "chunks, with the decode kernels' loads), then exit")
     ap.add_argument("--summarize-profile", action="store_true",
                     help="no GPU work: condense rocprofv3 output (the --*-dir options) into "
                          "profiles/decode_<workload>.json")
@@ -667,6 +752,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.copy_probe:
         return copy_probe(args.copy_probe, dev)
+    if args.read_probe:
+        return read_probe(args.read_probe, dev)
     if args.workload.startswith("prefix_share"):
         wk = PrefixVerifyWorkload(args.workload, dev, share=not args.no_share,
                                   rotate=args.rotate)

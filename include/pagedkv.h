@@ -444,6 +444,28 @@ int paged_attention_decode_shared(
     int32_t n_members, int32_t max_members, int32_t max_prefix,
     void *workspace, size_t workspace_bytes, float *lse_out, void *stream);
 
+/* ======================================================================
+ * Measurement aid (not part of the attention path)
+ * ====================================================================== */
+
+/* Read n_chunks chunks of chunk_bytes bytes (1, 2, 4 or 8 KiB) from the
+ * device buffer buf (buf_bytes long, 16-byte aligned): chunk k at byte
+ * order[k] * chunk_bytes (order: device int32; an entry at or past
+ * buf_bytes / chunk_bytes reads the last whole chunk). n_wg workgroups of
+ * eight wavefronts; wavefront w of workgroup x takes chunks x * 8 + w,
+ * + 8 n_wg, ... Each lane loads 16 bytes per 1 KiB, as the decode kernels
+ * load K/V rows: mode 0 into registers, mode 1 into registers with
+ * non-temporal loads, mode 2 with the non-temporal direct-to-LDS gathers
+ * into two-slot rings that the decode kernels use, read back from LDS.
+ * sink (device, n_wg uint32) receives each workgroup's XOR of every
+ * 32-bit word it read. With order = 0, 1, 2, ... it measures a sequential
+ * read stream; with a random permutation, the reads of a cache whose blocks
+ * came from a shuffled free list. Returns PKV_EINVAL for sizes or a mode out
+ * of range, PKV_EHIP if the launch fails. */
+int paged_kv_read_probe(const void *buf, size_t buf_bytes, const int32_t *order,
+                        int32_t n_chunks, int32_t chunk_bytes, int mode, int32_t n_wg,
+                        uint32_t *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
     UnknownSequence, PKV_BF16, PKV_F32, check, load)
 
 __all__ = [
-    "PagedKVPool", "paged_cache_write", "paged_kv_copy_blocks",
+    "paged_kv_read_probe", "PagedKVPool", "paged_cache_write", "paged_kv_copy_blocks",
     "paged_attention_workspace_size", "paged_attention_decode", "dtype_code",
     "PrefixGroups", "paged_kv_prefix_groups", "paged_attention_shared_workspace_size",
     "paged_attention_decode_shared", "Q8Cache", "paged_cache_write_q8",
@@ -542,3 +542,20 @@ def paged_attention_decode_shared(out, q, k_cache, v_cache, block_tables, contex
 
 def default_scale(head_dim: int) -> float:
     return 1.0 / math.sqrt(head_dim)
+
+
+def paged_kv_read_probe(buf, order, sink, chunk_bytes: int = 4096, mode: int = 2,
+                        stream=None) -> None:
+    """Measurement aid (paged_kv_read_probe): read chunks of `buf` (a uint8
+    device tensor) in the order of `order` (int32 chunk indices) with the
+    decode kernels' load pattern; `sink` (uint32 or int32, one per
+    workgroup) receives each workgroup's XOR of the words it read."""
+    torch = _torch()
+    _expect(buf, "buf", torch.uint8)
+    _expect(order, "order", torch.int32)
+    _expect(sink, "sink", (torch.int32, torch.uint32) if hasattr(torch, "uint32") else torch.int32)
+    _one_gpu("paged_kv_read_probe", buf, order, sink)
+    check(load().paged_kv_read_probe(
+        ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.c_void_p(order.data_ptr()),
+        order.numel(), int(chunk_bytes), int(mode), sink.numel(),
+        ctypes.c_void_p(sink.data_ptr()), _stream(stream)))

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
 SOURCES = ["pool.cpp", "groups.cpp", "checks.cpp", "cache_ops.hip", "decode.hip", "verify_inst.hip",
-           "shared_inst.hip"] + [
+           "shared_inst.hip", "probe.hip"] + [
     f"decode_inst_{dt}_d{d}.hip" for dt in ("f32", "bf16") for d in (64, 128, 256)] + [
     f"decode_inst_mfma_d{d}.hip" for d in (64, 128, 256)]
 ARCH = "gfx950"

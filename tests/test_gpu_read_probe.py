@@ -1,0 +1,35 @@
+"""The read probe (a measurement aid) reads exactly the chunks it is given.
+
+Every mode and chunk size: the XOR over the workgroups' sinks equals the XOR
+of every 32-bit word of the chunks named by `order`, computed on the host.
+An order entry past the buffer reads its last chunk (so a chunk named twice
+cancels out of the XOR)."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_202_amd as pkv
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("chunk", [1024, 4096, 8192])
+def test_probe_reads_named_chunks(device, mode, chunk):
+    rng = np.random.default_rng(7 + mode + chunk)
+    n_buf = (2 << 20) // chunk
+    host = rng.integers(0, 256, n_buf * chunk, dtype=np.uint8)
+    buf = torch.from_numpy(host).to(device)
+    words = host.view(np.uint32).reshape(n_buf, chunk // 4)
+    order = rng.permutation(n_buf)[: n_buf - 5].astype(np.int32)
+    order = np.concatenate([order, np.array([n_buf + 3, 2**31 - 1], np.int32)])  # past the end
+    n_wg = 37
+    sink = torch.zeros(n_wg, dtype=torch.int32, device=device)
+    pkv.paged_kv_read_probe(buf, torch.from_numpy(order).to(device), sink, chunk, mode)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    clamped = np.minimum(order.astype(np.int64), n_buf - 1)
+    want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(words[clamped], axis=1))
+    print(f"mode {mode} chunk {chunk}: xor {got:#010x} (host {want:#010x})", flush=True)
+    assert got == want
