@@ -44,6 +44,10 @@ def kernel_sources(workload: str) -> list:
 
     csrc = "paged_kv_cache_202_amd/csrc/"
     w = WORKLOADS[workload]
+    if w.dtype == "bf16" and w.group * w.queries_per_seq > 16 and not w.shared_prefix:
+        # the chunked-prefill row-tile kernel
+        return [csrc + "decode_kernel.h", csrc + "verify_mfma.h", csrc + "shared_prefix.h",
+                csrc + "shared_inst.hip", csrc + "decode.hip"]
     if w.shared_prefix:  # the one-pass shared-prefix kernel
         return [csrc + "decode_kernel.h", csrc + "verify_mfma.h", csrc + "shared_prefix.h",
                 csrc + "group_decode.h", csrc + "shared_inst.hip", csrc + "decode.hip"]
@@ -75,7 +79,13 @@ def profile_path(workload: str) -> str:
     its dominant kernel."""
     from synth.workloads import WORKLOADS
 
-    kernel = "group_mfma_kernel" if WORKLOADS[workload].shared_prefix else "decode"
+    w = WORKLOADS[workload]
+    if w.shared_prefix:
+        kernel = "group_mfma_kernel"
+    elif w.dtype == "bf16" and w.group * w.queries_per_seq > 16:  # a prefill chunk
+        kernel = "chunk_mfma_kernel"
+    else:
+        kernel = "decode"
     return os.path.join(ROOT, "profiles", f"{kernel}_{workload}.json")
 
 

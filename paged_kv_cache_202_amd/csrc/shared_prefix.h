@@ -381,7 +381,9 @@ template <int D, int W, int RT, RowSource SRC>
 __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareArgs &s) {
   using Gp = PrefixGeo<D, W>;
   constexpr int NC = Gp::NC, NCB = Gp::NCB, kSlots = Gp::kSlots;
-  constexpr int TT = D <= 128 ? 2 : 1;  // 16-token tiles per trip
+  // 16-token tiles per trip: at D = 128 four (a longer run of products
+  // between softmax steps), two at D = 64, one at D = 256
+  constexpr int TT = D == 128 ? 4 : D == 64 ? 2 : 1;
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   __shared__ u32x4_t sm_ring[kSlots * Gp::kTileBytes / 16];
 
@@ -629,9 +631,12 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
 
     // the K half of the trip's tiles; V is read after the softmax
     u32x4_t kr[TT][NC];
-    if constexpr (D == 128)
-      read_k2_128(kr, k_rd + so);
-    else if constexpr (D == 64)
+    if constexpr (D == 128) {
+      // tile pairs, 16 KiB apart in the ring
+#pragma unroll
+      for (int pp = 0; pp < TT / 2; ++pp)
+        read_k2_128(*reinterpret_cast<u32x4_t(*)[2][NC]>(&kr[2 * pp][0]), k_rd + so + pp * 16384);
+    } else if constexpr (D == 64)
       read_k2_64(kr, k_rd + so);
     else
       read_k_256(kr[0], k_rd + so);
@@ -705,9 +710,15 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
       const PKV_LDS char *va[NCB];
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) va[cb] = v_rd[cb] + so;
-      if constexpr (D == 128)
-        read_v2_128(vb, va);
-      else if constexpr (D == 64)
+      if constexpr (D == 128) {
+#pragma unroll
+        for (int pp = 0; pp < TT / 2; ++pp) {
+          const PKV_LDS char *vp[NCB];
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb) vp[cb] = va[cb] + pp * 16384;
+          read_v2_128(*reinterpret_cast<uint2(*)[2][NCB]>(&vb[2 * pp][0]), vp);
+        }
+      } else if constexpr (D == 64)
         read_v2_64(vb, va);
       else
         read_v_256(vb[0], va);
@@ -737,12 +748,16 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
-        if constexpr (TT == 2) {
-          const u32x4_t va2 = {vb[0][cb].x, vb[0][cb].y, vb[1][cb].x, vb[1][cb].y};
-          const u32x4_t pb2 = {pa[0][r].x, pa[0][r].y, pa[1][r].x, pa[1][r].y};
-          o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8_t, va2), __builtin_bit_cast(bf16x8_t, pb2), o[r][cb], 0,
-              0, 0);
+        if constexpr (TT >= 2) {
+          // two tiles' tokens per product (k = 32)
+#pragma unroll
+          for (int u = 0; u < TT; u += 2) {
+            const u32x4_t va2 = {vb[u][cb].x, vb[u][cb].y, vb[u + 1][cb].x, vb[u + 1][cb].y};
+            const u32x4_t pb2 = {pa[u][r].x, pa[u][r].y, pa[u + 1][r].x, pa[u + 1][r].y};
+            o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, va2), __builtin_bit_cast(bf16x8_t, pb2), o[r][cb],
+                0, 0, 0);
+          }
         } else {
           o[r][cb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
               __builtin_bit_cast(i16x4_t, vb[0][cb]), __builtin_bit_cast(i16x4_t, pa[0][r]),
