@@ -248,49 +248,65 @@ __device__ __forceinline__ void read_kv2<128>(u32x4_t (&k)[2][4], uint2 (&v)[2][
 // do not all read LDS at once after the trip's barrier and then all wait on
 // the matrix core (chunked prefill 4 x 512 rows at 8K: 384.7 -> 368.9 us;
 // reading each tile's K right before its products instead: 384.1 us).
+// K of a tile pair at kp + OFF (tiles 8 KiB apart), with one wait.
+template <int OFF>
 __device__ __forceinline__ void read_k2_128(u32x4_t (&k)[2][4], const PKV_LDS char *kp) {
+  static_assert(OFF >= 0 && OFF + 11264 < 65536, "LDS immediate offsets are 16 bits");
   asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %8 offset:1024\n\t"
-      "ds_read_b128 %2, %8 offset:2048\n\t"
-      "ds_read_b128 %3, %8 offset:3072\n\t"
-      "ds_read_b128 %4, %8 offset:8192\n\t"
-      "ds_read_b128 %5, %8 offset:9216\n\t"
-      "ds_read_b128 %6, %8 offset:10240\n\t"
-      "ds_read_b128 %7, %8 offset:11264\n\t"
+      "ds_read_b128 %0, %8 offset:%9\n\t"
+      "ds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\t"
+      "ds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\t"
+      "ds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\t"
+      "ds_read_b128 %7, %8 offset:%16\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[0][2]), "=&v"(k[0][3]), "=&v"(k[1][0]),
         "=&v"(k[1][1]), "=&v"(k[1][2]), "=&v"(k[1][3])
-      : "v"(kp)
+      : "v"(kp), "i"(OFF), "i"(OFF + 1024), "i"(OFF + 2048), "i"(OFF + 3072), "i"(OFF + 8192),
+        "i"(OFF + 9216), "i"(OFF + 10240), "i"(OFF + 11264)
       : "memory");
 }
 
+// V of a tile pair, transposed: column block cb at va[cb] + OFF and + OFF +
+// 8 KiB, with one wait.
+template <int OFF>
 __device__ __forceinline__ void read_v2_128(uint2 (&v)[2][8], const PKV_LDS char *const (&va)[8]) {
+  static_assert(OFF >= 0 && OFF + 8192 < 65536, "LDS immediate offsets are 16 bits");
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %17\n\t"
-      "ds_read_b64_tr_b16 %2, %18\n\t"
-      "ds_read_b64_tr_b16 %3, %19\n\t"
-      "ds_read_b64_tr_b16 %4, %20\n\t"
-      "ds_read_b64_tr_b16 %5, %21\n\t"
-      "ds_read_b64_tr_b16 %6, %22\n\t"
-      "ds_read_b64_tr_b16 %7, %23\n\t"
-      "ds_read_b64_tr_b16 %8, %16 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %9, %17 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %10, %18 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %11, %19 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %12, %20 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %13, %21 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %14, %22 offset:8192\n\t"
-      "ds_read_b64_tr_b16 %15, %23 offset:8192\n\t"
+      "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+      "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]), "=&v"(v[0][4]),
         "=&v"(v[0][5]), "=&v"(v[0][6]), "=&v"(v[0][7]), "=&v"(v[1][0]), "=&v"(v[1][1]),
         "=&v"(v[1][2]), "=&v"(v[1][3]), "=&v"(v[1][4]), "=&v"(v[1][5]), "=&v"(v[1][6]),
         "=&v"(v[1][7])
       : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]),
-        "v"(va[7])
+        "v"(va[7]), "i"(OFF), "i"(OFF + 8192)
       : "memory");
+}
+
+// The largest of three floats in one instruction (fmaxf would first quiet
+// each operand: one more instruction per value).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // K halves and V halves on their own for the other head dims, so that a
@@ -600,7 +616,8 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
   const PKV_LDS char *k_rd = ring + lane * 16;
   const PKV_LDS char *v_rd[NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) v_rd[cb] = ring + v_addr[cb];
+  for (int cb = 0; cb < NCB; ++cb)
+    v_rd[cb] = ring + v_addr[cb] - (D == 128 ? Gp::kHalf : 0);  // D = 128: kHalf in the offset
 
   // Trips go in windows of kWin with one barrier each: within a window the
   // wavefronts drift apart, so that while some read LDS others run the
@@ -633,9 +650,10 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
     u32x4_t kr[TT][NC];
     if constexpr (D == 128) {
       // tile pairs, 16 KiB apart in the ring
-#pragma unroll
-      for (int pp = 0; pp < TT / 2; ++pp)
-        read_k2_128(*reinterpret_cast<u32x4_t(*)[2][NC]>(&kr[2 * pp][0]), k_rd + so + pp * 16384);
+      static_for<TT / 2>([&](auto pc) {
+        constexpr int pp = decltype(pc)::value;
+        read_k2_128<pp * 16384>(*reinterpret_cast<u32x4_t(*)[2][NC]>(&kr[2 * pp][0]), k_rd + so);
+      });
     } else if constexpr (D == 64)
       read_k2_64(kr, k_rd + so);
     else
@@ -662,20 +680,33 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
       if (!__all(t0 + TT * kTile <= lim_p[r])) {
-        // tokens a row does not see (causal, or past the partition) score -inf
+        // tokens a row does not see (causal, or past the partition) score
+        // -inf: token t0 + 16 u + 4 lg + e, compared as 16 u + e against the
+        // lane's bound (constants in the compares)
+        const int d = lim_p[r] - t0 - 4 * lg;
 #pragma unroll
         for (int u = 0; u < TT; ++u)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (t0 + 16 * u + 4 * lg + e >= lim_p[r]) sv[u][r][e] = kNegInf;
+            if (16 * u + e >= d) sv[u][r][e] = kNegInf;
       }
       // the lazy maximum: raised only when a score passes it by kLazyLog2;
       // scale_log2 > 0 (a negative scale was moved into the query), so the
       // largest raw score gives the largest scaled one
-      float rmax = kNegInf;
+      float rmax;
+      if constexpr (TT == 4) {
+        const float a0 = max3f(sv[0][r][0], sv[0][r][1], sv[0][r][2]);
+        const float a1 = max3f(sv[0][r][3], sv[1][r][0], sv[1][r][1]);
+        const float a2 = max3f(sv[1][r][2], sv[1][r][3], sv[2][r][0]);
+        const float a3 = max3f(sv[2][r][1], sv[2][r][2], sv[2][r][3]);
+        const float a4 = max3f(sv[3][r][0], sv[3][r][1], sv[3][r][2]);
+        rmax = max3f(max3f(a0, a1, a2), max3f(a3, a4, sv[3][r][3]), a0);
+      } else {
+        rmax = kNegInf;
 #pragma unroll
-      for (int u = 0; u < TT; ++u)
-        rmax = fmaxf(rmax, fmaxf(fmaxf(sv[u][r][0], sv[u][r][1]), fmaxf(sv[u][r][2], sv[u][r][3])));
+        for (int u = 0; u < TT; ++u)
+          rmax = fmaxf(rmax, fmaxf(fmaxf(sv[u][r][0], sv[u][r][1]), fmaxf(sv[u][r][2], sv[u][r][3])));
+      }
       const float tmax = rmax * scale_log2;
       if (__any(tmax > m_row[r] + kLazyLog2)) {
         // row ln's scores are spread over the four lane groups
@@ -711,13 +742,12 @@ __device__ __forceinline__ void mfma_rows_body(const DecodeArgs &a, const ShareA
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) va[cb] = v_rd[cb] + so;
       if constexpr (D == 128) {
-#pragma unroll
-        for (int pp = 0; pp < TT / 2; ++pp) {
-          const PKV_LDS char *vp[NCB];
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb) vp[cb] = va[cb] + pp * 16384;
-          read_v2_128(*reinterpret_cast<uint2(*)[2][NCB]>(&vb[2 * pp][0]), vp);
-        }
+        // the V half sits kHalf into each slot: part of the immediate offset
+        static_for<TT / 2>([&](auto pc) {
+          constexpr int pp = decltype(pc)::value;
+          read_v2_128<Gp::kHalf + pp * 16384>(*reinterpret_cast<uint2(*)[2][NCB]>(&vb[2 * pp][0]),
+                                              va);
+        });
       } else if constexpr (D == 64)
         read_v2_64(vb, va);
       else
