@@ -641,7 +641,8 @@ def merge_sq_counters(args) -> int:
                                for c in names if c.startswith("SQ_INSTS_")}
     key = args.sq_key or "sq_counters"
     out[key] = {"counters_per_dispatch": avg, "dispatches": len(per), "derived": derived,
-                "command": args.sq_command or ""}
+                "command": args.sq_command or "",
+                "kernel_sources_sha256": sources_sha256(args.workload)}
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out[key], indent=1))
@@ -707,6 +708,11 @@ def summarize_profile(args) -> int:
         out["algorithmic_bytes_note"] = ("unique bytes: every shared block once per KV head, "
                                          "each sequence's private tokens once")
     path = profile_path(args.workload)
+    if os.path.exists(path):  # SQ counter passes merged earlier keep their own commands
+        with open(path) as f:
+            old = json.load(f)
+        out.update({k: v for k, v in old.items()
+                    if isinstance(v, dict) and "counters_per_dispatch" in v})
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))

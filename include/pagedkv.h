@@ -222,7 +222,9 @@ int paged_kv_check_slots(const int32_t *slots, int32_t T, int64_t num_slots,
 /* Copy-on-write device copy: for each of the n pairs (device array), copy
  * block src -> dst in both pools (all Hkv * block_size * D elements). Pairs
  * with an id outside [0, num_blocks) are skipped. Must run before the cache
- * write of the same step, on the same stream. */
+ * write of the same step, on the same stream. v_cache may be NULL: then only
+ * k_cache is copied (a single-pool array, such as the scales of an 8-bit or
+ * 3-bit cache). */
 int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_t *pairs,
                          int32_t n, int32_t num_blocks, int32_t Hkv, int32_t D,
                          int32_t block_size, int dtype, void *stream);
@@ -317,18 +319,24 @@ int paged_attention_decode_noalloc(float *out, const void *q, const void *k_cach
  * one scale per row), 8 bits, applied to every (token, KV head) row of K
  * and of V as it is written: scale = max |x| / 127 (1 for a row of zeros),
  * code = clip(round-half-even(x / scale), -127, 127), computed in float64;
- * the scale is stored as float32. Such a cache is four device arrays:
- *   k_codes, v_codes:   int8    [num_blocks, Hkv, block_size, D]
- *   k_scales, v_scales: float32 [num_blocks, Hkv, block_size]
- * (D + 4 bytes per token and head instead of 2 D for bf16). */
+ * the scale is stored as float32. Such a cache is three device arrays:
+ *   k_codes, v_codes: int8    [num_blocks, Hkv, block_size, D]
+ *   scales:           float32 [num_blocks, Hkv, 2, block_size]
+ * where scales[b, h, 0, :] are the K rows' scales and scales[b, h, 1, :]
+ * the V rows' (D + 4 bytes per token and head instead of 2 D for bf16).
+ * K and V scales sit side by side so that one (block, KV head) reads one
+ * contiguous 2 * block_size * 4 bytes: a single 128-byte line at
+ * block_size 16 when the array is 128-byte aligned (any array from the HIP
+ * allocator is). */
 
 /* Quantize and scatter T new rows: k_new, v_new device `dtype` (f32 or
  * bf16) [T, Hkv, D]; slot_mapping as in paged_cache_write (-1 or out of
  * range: skipped). D in {64, 128, 256}. Asynchronous on `stream`.
  * Copy-on-write for such a cache: paged_kv_copy_blocks on the codes
- * (dtype PKV_I8) and on the scales (dtype PKV_F32, D = 1). */
+ * (dtype PKV_I8) and on the scales alone (k_cache = scales, v_cache NULL,
+ * dtype PKV_F32, Hkv as the cache's, D = 2). */
 int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
-                         int8_t *v_codes, float *k_scales, float *v_scales,
+                         int8_t *v_codes, float *scales,
                          const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
                          int32_t Hkv, int32_t D, int32_t block_size, int dtype,
                          void *stream);
@@ -339,11 +347,11 @@ int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
  * [B, nq, Hq, D]; out, lse, tables, lengths, partition_tokens and workspace
  * as there (paged_attention_workspace_size gives the size; -1 is taken as 0
  * here). Rows per KV head: G * nq rounded up to a power of two <= 16 (one
- * matrix-core wavefront holds them all). Scale arrays 16-byte aligned.
+ * matrix-core wavefront holds them all). The scale array 16-byte aligned.
  * Host-checked as paged_attention_decode -> EINVAL. */
 int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
-                              const int8_t *v_codes, const float *k_scales,
-                              const float *v_scales, const int32_t *block_tables,
+                              const int8_t *v_codes, const float *scales,
+                              const int32_t *block_tables,
                               int32_t max_blocks, const int32_t *context_lens,
                               int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
                               int32_t D, int32_t block_size, int32_t num_blocks,
@@ -357,19 +365,19 @@ int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
  * Codes are stored two per byte as code + 8 (dim 2 i in the low nibble of
  * byte i): half a byte per element, byte-aligned for the decode kernels
  * (the pages' 3 bits per element would not give whole bytes per lane):
- *   k_codes, v_codes:   uint8   [num_blocks, Hkv, block_size, D / 2]
- *   k_scales, v_scales: float32 [num_blocks, Hkv, block_size]
+ *   k_codes, v_codes: uint8   [num_blocks, Hkv, block_size, D / 2]
+ *   scales:           float32 [num_blocks, Hkv, 2, block_size] (as above)
  * D in {128, 256}. paged_cache_write_q3 / paged_attention_decode_q3 are the
  * 8-bit calls' counterparts (same arguments, errors and copy-on-write: codes
  * as PKV_I8 with D / 2 bytes per row). */
 int paged_cache_write_q3(const void *k_new, const void *v_new, uint8_t *k_codes,
-                         uint8_t *v_codes, float *k_scales, float *v_scales,
+                         uint8_t *v_codes, float *scales,
                          const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
                          int32_t Hkv, int32_t D, int32_t block_size, int dtype,
                          void *stream);
 int paged_attention_decode_q3(float *out, const void *q, const uint8_t *k_codes,
-                              const uint8_t *v_codes, const float *k_scales,
-                              const float *v_scales, const int32_t *block_tables,
+                              const uint8_t *v_codes, const float *scales,
+                              const int32_t *block_tables,
                               int32_t max_blocks, const int32_t *context_lens,
                               int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
                               int32_t D, int32_t block_size, int32_t num_blocks,

@@ -263,9 +263,43 @@ def paged_kv_copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
                                       D, bs, dtype_code(k_cache), _stream(stream)))
 
 
-class Q8Cache:
-    """A paged cache of 8-bit per-row codes: int8 codes [NB, Hkv, bs, D] and
-    float32 scales [NB, Hkv, bs], for K and for V (device tensors)."""
+class _CodeCache:
+    """What the 8-bit and 3-bit caches share: one float32 scale array
+    [NB, Hkv, 2, bs] holding each (block, KV head)'s K row scales (index 0)
+    beside its V row scales (index 1), so that one (block, head) reads one
+    contiguous run; k_scales and v_scales are views of it."""
+
+    def _init_scales(self, num_blocks, Hkv, block_size, device):
+        import torch
+
+        self.scales = torch.ones((num_blocks, Hkv, 2, block_size), dtype=torch.float32,
+                                 device=device)
+
+    @property
+    def k_scales(self):
+        """K row scales [NB, Hkv, bs] (a view of `scales`)."""
+        return self.scales[:, :, 0]
+
+    @property
+    def v_scales(self):
+        """V row scales [NB, Hkv, bs] (a view of `scales`)."""
+        return self.scales[:, :, 1]
+
+    def _copy_blocks(self, name, code_row_bytes, pairs, stream) -> None:
+        NB, Hkv, bs, _ = self.shape
+        n = pairs.shape[0]
+        _expect(pairs, "pairs", _torch().int32, (n, 2))
+        _one_gpu(name, self.k_codes, pairs)
+        check(load().paged_kv_copy_blocks(_dev(self.k_codes), _dev(self.v_codes), _dev(pairs), n,
+                                          NB, Hkv, code_row_bytes, bs, _lib.PKV_I8,
+                                          _stream(stream)))
+        check(load().paged_kv_copy_blocks(_dev(self.scales), None, _dev(pairs), n, NB, Hkv, 2,
+                                          bs, PKV_F32, _stream(stream)))
+
+
+class Q8Cache(_CodeCache):
+    """A paged cache of 8-bit per-row codes: int8 codes [NB, Hkv, bs, D] for
+    K and for V, and the float32 scales [NB, Hkv, 2, bs] (device tensors)."""
 
     def __init__(self, num_blocks, Hkv, block_size, D, device):
         import torch
@@ -273,8 +307,7 @@ class Q8Cache:
         shape = (num_blocks, Hkv, block_size, D)
         self.k_codes = torch.zeros(shape, dtype=torch.int8, device=device)
         self.v_codes = torch.zeros(shape, dtype=torch.int8, device=device)
-        self.k_scales = torch.ones(shape[:3], dtype=torch.float32, device=device)
-        self.v_scales = torch.ones(shape[:3], dtype=torch.float32, device=device)
+        self._init_scales(num_blocks, Hkv, block_size, device)
 
     @property
     def shape(self):
@@ -282,14 +315,7 @@ class Q8Cache:
 
     def copy_blocks(self, pairs, stream=None) -> None:
         """Copy-on-write of whole blocks: codes and scales."""
-        NB, Hkv, bs, D = self.shape
-        n = pairs.shape[0]
-        _expect(pairs, "pairs", _torch().int32, (n, 2))
-        _one_gpu("Q8Cache.copy_blocks", self.k_codes, pairs)
-        check(load().paged_kv_copy_blocks(_dev(self.k_codes), _dev(self.v_codes), _dev(pairs), n,
-                                          NB, Hkv, D, bs, _lib.PKV_I8, _stream(stream)))
-        check(load().paged_kv_copy_blocks(_dev(self.k_scales), _dev(self.v_scales), _dev(pairs),
-                                          n, NB, Hkv, 1, bs, PKV_F32, _stream(stream)))
+        self._copy_blocks("Q8Cache.copy_blocks", self.shape[3], pairs, stream)
 
 
 def paged_cache_write_q8(k_new, v_new, cache: "Q8Cache", slot_mapping, stream=None) -> None:
@@ -302,11 +328,10 @@ def paged_cache_write_q8(k_new, v_new, cache: "Q8Cache", slot_mapping, stream=No
     _expect(v_new, "v_new", k_new.dtype, (T, Hkv, D))
     _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
     _one_gpu("paged_cache_write_q8", k_new, v_new, cache.k_codes, cache.v_codes,
-             cache.k_scales, cache.v_scales, slot_mapping)
+             cache.scales, slot_mapping)
     check(load().paged_cache_write_q8(
-        _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes),
-        _dev(cache.k_scales), _dev(cache.v_scales), _dev(slot_mapping), T, NB, Hkv, D, bs,
-        dtype_code(k_new), _stream(stream)))
+        _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.scales),
+        _dev(slot_mapping), T, NB, Hkv, D, bs, dtype_code(k_new), _stream(stream)))
 
 
 def paged_attention_decode_q8(out, q, cache: "Q8Cache", block_tables, context_lens, scale,
@@ -324,19 +349,19 @@ def paged_attention_decode_q8(out, q, cache: "Q8Cache", block_tables, context_le
     max_blocks = _check_attention_io("paged_attention_decode_q8", out, lse, block_tables,
                                      context_lens, B, nq, Hq, D)
     _one_gpu("paged_attention_decode_q8", out, q, cache.k_codes, cache.v_codes,
-             cache.k_scales, cache.v_scales, block_tables, context_lens, workspace, lse)
+             cache.scales, block_tables, context_lens, workspace, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode_q8(
-        _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.k_scales),
-        _dev(cache.v_scales), _dev(block_tables), max_blocks, _dev(context_lens), B, nq, Hq,
-        Hkv, D, bs, NB, float(scale), int(partition_tokens), _dev(workspace), ws_bytes,
-        _dev(lse), _stream(stream)))
+        _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.scales),
+        _dev(block_tables), max_blocks, _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB,
+        float(scale), int(partition_tokens), _dev(workspace), ws_bytes, _dev(lse),
+        _stream(stream)))
 
 
-class Q3Cache:
+class Q3Cache(_CodeCache):
     """A paged cache of 3-bit per-row codes, two per byte (code + 8, even dim
-    in the low nibble): codes uint8 [NB, Hkv, bs, D / 2] and float32 scales
-    [NB, Hkv, bs], for K and for V (device tensors)."""
+    in the low nibble): codes uint8 [NB, Hkv, bs, D / 2] for K and for V, and
+    the float32 scales [NB, Hkv, 2, bs] (device tensors)."""
 
     def __init__(self, num_blocks, Hkv, block_size, D, device):
         import torch
@@ -345,8 +370,7 @@ class Q3Cache:
         self.D = D
         self.k_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
         self.v_codes = torch.zeros(shape, dtype=torch.uint8, device=device)
-        self.k_scales = torch.ones(shape[:3], dtype=torch.float32, device=device)
-        self.v_scales = torch.ones(shape[:3], dtype=torch.float32, device=device)
+        self._init_scales(num_blocks, Hkv, block_size, device)
 
     @property
     def shape(self):
@@ -354,14 +378,8 @@ class Q3Cache:
         return tuple(self.k_codes.shape[:3]) + (self.D,)
 
     def copy_blocks(self, pairs, stream=None) -> None:
-        NB, Hkv, bs, D = self.shape
-        n = pairs.shape[0]
-        _expect(pairs, "pairs", _torch().int32, (n, 2))
-        _one_gpu("Q3Cache.copy_blocks", self.k_codes, pairs)
-        check(load().paged_kv_copy_blocks(_dev(self.k_codes), _dev(self.v_codes), _dev(pairs), n,
-                                          NB, Hkv, D // 2, bs, _lib.PKV_I8, _stream(stream)))
-        check(load().paged_kv_copy_blocks(_dev(self.k_scales), _dev(self.v_scales), _dev(pairs),
-                                          n, NB, Hkv, 1, bs, PKV_F32, _stream(stream)))
+        """Copy-on-write of whole blocks: codes and scales."""
+        self._copy_blocks("Q3Cache.copy_blocks", self.D // 2, pairs, stream)
 
 
 def paged_cache_write_q3(k_new, v_new, cache: "Q3Cache", slot_mapping, stream=None) -> None:
@@ -374,11 +392,10 @@ def paged_cache_write_q3(k_new, v_new, cache: "Q3Cache", slot_mapping, stream=No
     _expect(v_new, "v_new", k_new.dtype, (T, Hkv, D))
     _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
     _one_gpu("paged_cache_write_q3", k_new, v_new, cache.k_codes, cache.v_codes,
-             cache.k_scales, cache.v_scales, slot_mapping)
+             cache.scales, slot_mapping)
     check(load().paged_cache_write_q3(
-        _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes),
-        _dev(cache.k_scales), _dev(cache.v_scales), _dev(slot_mapping), T, NB, Hkv, D, bs,
-        dtype_code(k_new), _stream(stream)))
+        _dev(k_new), _dev(v_new), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.scales),
+        _dev(slot_mapping), T, NB, Hkv, D, bs, dtype_code(k_new), _stream(stream)))
 
 
 def paged_attention_decode_q3(out, q, cache: "Q3Cache", block_tables, context_lens, scale,
@@ -396,13 +413,13 @@ def paged_attention_decode_q3(out, q, cache: "Q3Cache", block_tables, context_le
     max_blocks = _check_attention_io("paged_attention_decode_q3", out, lse, block_tables,
                                      context_lens, B, nq, Hq, D)
     _one_gpu("paged_attention_decode_q3", out, q, cache.k_codes, cache.v_codes,
-             cache.k_scales, cache.v_scales, block_tables, context_lens, workspace, lse)
+             cache.scales, block_tables, context_lens, workspace, lse)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(load().paged_attention_decode_q3(
-        _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.k_scales),
-        _dev(cache.v_scales), _dev(block_tables), max_blocks, _dev(context_lens), B, nq, Hq,
-        Hkv, D, bs, NB, float(scale), int(partition_tokens), _dev(workspace), ws_bytes,
-        _dev(lse), _stream(stream)))
+        _dev(out), _dev(q), _dev(cache.k_codes), _dev(cache.v_codes), _dev(cache.scales),
+        _dev(block_tables), max_blocks, _dev(context_lens), B, nq, Hq, Hkv, D, bs, NB,
+        float(scale), int(partition_tokens), _dev(workspace), ws_bytes, _dev(lse),
+        _stream(stream)))
 
 
 def paged_attention_workspace_size(B, nq, Hq, Hkv, D, max_blocks, block_size,

@@ -70,17 +70,17 @@ PROTOTYPES = {
                                                c_i32, c_i32, c_i32, c_i32, c_float, c_int,
                                                c_i32, c_void_p, c_void_p]),
     "paged_cache_write_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                     c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                      c_int, c_void_p]),
     "paged_attention_decode_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                          c_void_p, c_void_p, c_i32, c_void_p, c_i32, c_i32,
+                                          c_void_p, c_i32, c_void_p, c_i32, c_i32,
                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_float, c_i32,
                                           c_void_p, c_size_t, c_void_p, c_void_p]),
     "paged_cache_write_q3": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                     c_void_p, c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
+                                     c_void_p, c_i32, c_i32, c_i32, c_i32, c_i32,
                                      c_int, c_void_p]),
     "paged_attention_decode_q3": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
-                                          c_void_p, c_void_p, c_i32, c_void_p, c_i32, c_i32,
+                                          c_void_p, c_i32, c_void_p, c_i32, c_i32,
                                           c_i32, c_i32, c_i32, c_i32, c_i32, c_float, c_i32,
                                           c_void_p, c_size_t, c_void_p, c_void_p]),
     "paged_kv_prefix_groups": (c_int, [P_i32, c_i32, P_i32, c_i32, c_i32, c_i32, c_i32, c_i32,

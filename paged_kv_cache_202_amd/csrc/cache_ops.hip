@@ -43,22 +43,20 @@ cache_write_kernel(const uint4 *__restrict__ k_new, const uint4 *__restrict__ v_
   }
 }
 
-// blockIdx.y = pair index; threads stride over the block's 16-byte vectors.
+// blockIdx.y = pair index, blockIdx.z = pool (0: k_cache, 1: v_cache);
+// threads stride over the block's 16-byte vectors.
 __global__ void __launch_bounds__(256)
 copy_blocks_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
                    const pkv_cow_t *__restrict__ pairs, int64_t vec_per_block,
                    int32_t num_blocks) {
   const pkv_cow_t pr = pairs[blockIdx.y];
   if (pr.src < 0 || pr.src >= num_blocks || pr.dst < 0 || pr.dst >= num_blocks) return;
-  const uint4 *ks = k_cache + (int64_t)pr.src * vec_per_block;
-  const uint4 *vs = v_cache + (int64_t)pr.src * vec_per_block;
-  uint4 *kd = k_cache + (int64_t)pr.dst * vec_per_block;
-  uint4 *vd = v_cache + (int64_t)pr.dst * vec_per_block;
+  uint4 *pool = blockIdx.z ? v_cache : k_cache;
+  const uint4 *src = pool + (int64_t)pr.src * vec_per_block;
+  uint4 *dst = pool + (int64_t)pr.dst * vec_per_block;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < vec_per_block;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
-  }
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
 }
 
 // Per-row integer codes of the course page's teaching quantizer (project
@@ -66,15 +64,15 @@ copy_blocks_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
 // new (token, KV head) row x of D values, limit = 2^(BITS-1) - 1, scale =
 // max |x| / limit (1 for a row of zeros), code = clip(round-half-even(x /
 // scale), -limit, limit), in float64 as the page computes; the scale is
-// stored as float32. 8-bit codes are stored as int8; 3-bit codes two per
-// byte, code + 8, even dim in the low nibble. One wavefront per row: each
-// lane holds D / 64 consecutive elements.
+// stored as float32 in the scale row [blk, h, K = 0 / V = 1, :] beside the
+// other's. 8-bit codes are stored as int8; 3-bit codes two per byte, code +
+// 8, even dim in the low nibble. One wavefront per row: each lane holds
+// D / 64 consecutive elements.
 template <int D, int BITS, typename T>
 __global__ void __launch_bounds__(256)
 cache_write_q_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
                      int8_t *__restrict__ k_codes, int8_t *__restrict__ v_codes,
-                     float *__restrict__ k_scales, float *__restrict__ v_scales,
-                     const int32_t *__restrict__ slots, int64_t rows, int32_t Hkv, int32_t bs,
+                     float *__restrict__ scales, const int32_t *__restrict__ slots, int64_t rows, int32_t Hkv, int32_t bs,
                      int64_t num_slots) {
   constexpr int EPL = D / 64;
   constexpr double kLimit = (1 << (BITS - 1)) - 1;
@@ -87,7 +85,7 @@ cache_write_q_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
   const int64_t s = slots[t];
   if (s < 0 || s >= num_slots) return;
   const int64_t blk = s / bs, off = s - blk * bs;
-  const int64_t dst = (blk * Hkv + h) * bs + off;  // row of the code and scale pools
+  const int64_t dst = (blk * Hkv + h) * bs + off;  // row of the code pools
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const T *src = (which ? v_new : k_new) + row * D + lane * EPL;
@@ -119,7 +117,7 @@ cache_write_q_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
       for (int e = 0; e < EPL; e += 2)
         codes[e / 2] = (uint8_t)((c[e] + 8) | ((c[e + 1] + 8) << 4));
     }
-    if (lane == 0) (which ? v_scales : k_scales)[dst] = (float)scale;
+    if (lane == 0) scales[((blk * Hkv + h) * 2 + which) * bs + off] = (float)scale;
   }
 }
 
@@ -194,13 +192,14 @@ extern "C" int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_
   const int64_t block_bytes = (int64_t)Hkv * block_size * D * es;
   if (block_bytes % 16) return fail(PKV_EINVAL, "block bytes must be a multiple of 16");
   if (n == 0) return PKV_OK;
-  if (!k_cache || !v_cache || !pairs) return fail(PKV_EINVAL, "NULL pointer");
+  if (!k_cache || !pairs) return fail(PKV_EINVAL, "NULL pointer");
   if ((uintptr_t)k_cache % 16 || (uintptr_t)v_cache % 16)
     return fail(PKV_EINVAL, "K/V pools must be 16-byte aligned");
   const int64_t vpb = block_bytes / 16;
   int gx = (int)((vpb + 255) / 256);
   if (gx > 64) gx = 64;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, n), dim3(256), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(gx, n, v_cache ? 2 : 1), dim3(256), 0,
+                     (hipStream_t)stream,
                      (uint4 *)k_cache, (uint4 *)v_cache, pairs, vpb, num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PKV_EHIP, "block copy launch: %s", hipGetErrorString(e));
@@ -209,7 +208,7 @@ extern "C" int paged_kv_copy_blocks(void *k_cache, void *v_cache, const pkv_cow_
 
 template <int BITS>
 static int cache_write_q(const void *k_new, const void *v_new, int8_t *k_codes, int8_t *v_codes,
-                         float *k_scales, float *v_scales, const int32_t *slot_mapping, int32_t T,
+                         float *scales, const int32_t *slot_mapping, int32_t T,
                          int32_t num_blocks, int32_t Hkv, int32_t D, int32_t block_size,
                          int dtype, void *stream) {
   if (dtype != PKV_F32 && dtype != PKV_BF16)
@@ -219,7 +218,7 @@ static int cache_write_q(const void *k_new, const void *v_new, int8_t *k_codes, 
   if (D != 128 && D != 256 && (BITS == 3 || D != 64))
     return fail(PKV_EINVAL, "head dim %d unsupported for %d-bit codes", D, BITS);
   if (T == 0) return PKV_OK;
-  if (!k_new || !v_new || !k_codes || !v_codes || !k_scales || !v_scales || !slot_mapping)
+  if (!k_new || !v_new || !k_codes || !v_codes || !scales || !slot_mapping)
     return fail(PKV_EINVAL, "NULL pointer");
   const int64_t rows = (int64_t)T * Hkv;
   const int64_t num_slots = (int64_t)num_blocks * block_size;
@@ -232,13 +231,11 @@ static int cache_write_q(const void *k_new, const void *v_new, int8_t *k_codes, 
       if (dtype == PKV_BF16)                                                                \
         hipLaunchKernelGGL((cache_write_q_kernel<d, BITS, uint16_t>), grid, block, 0, s,     \
                            (const uint16_t *)k_new, (const uint16_t *)v_new, k_codes,        \
-                           v_codes, k_scales, v_scales, slot_mapping, rows, Hkv, block_size, \
-                           num_slots);                                                      \
+                           v_codes, scales, slot_mapping, rows, Hkv, block_size, num_slots); \
       else                                                                                  \
         hipLaunchKernelGGL((cache_write_q_kernel<d, BITS, float>), grid, block, 0, s,        \
                            (const float *)k_new, (const float *)v_new, k_codes, v_codes,     \
-                           k_scales, v_scales, slot_mapping, rows, Hkv, block_size,          \
-                           num_slots);                                                      \
+                           scales, slot_mapping, rows, Hkv, block_size, num_slots);          \
     }                                                                                       \
   }
   PKV_Q(64) PKV_Q(128) PKV_Q(256)
@@ -249,20 +246,19 @@ static int cache_write_q(const void *k_new, const void *v_new, int8_t *k_codes, 
 }
 
 extern "C" int paged_cache_write_q8(const void *k_new, const void *v_new, int8_t *k_codes,
-                                    int8_t *v_codes, float *k_scales, float *v_scales,
+                                    int8_t *v_codes, float *scales,
                                     const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
                                     int32_t Hkv, int32_t D, int32_t block_size, int dtype,
                                     void *stream) {
-  return cache_write_q<8>(k_new, v_new, k_codes, v_codes, k_scales, v_scales, slot_mapping, T,
-                          num_blocks, Hkv, D, block_size, dtype, stream);
+  return cache_write_q<8>(k_new, v_new, k_codes, v_codes, scales, slot_mapping, T, num_blocks,
+                          Hkv, D, block_size, dtype, stream);
 }
 
 extern "C" int paged_cache_write_q3(const void *k_new, const void *v_new, uint8_t *k_codes,
-                                    uint8_t *v_codes, float *k_scales, float *v_scales,
+                                    uint8_t *v_codes, float *scales,
                                     const int32_t *slot_mapping, int32_t T, int32_t num_blocks,
                                     int32_t Hkv, int32_t D, int32_t block_size, int dtype,
                                     void *stream) {
-  return cache_write_q<3>(k_new, v_new, (int8_t *)k_codes, (int8_t *)v_codes, k_scales,
-                          v_scales, slot_mapping, T, num_blocks, Hkv, D, block_size, dtype,
-                          stream);
+  return cache_write_q<3>(k_new, v_new, (int8_t *)k_codes, (int8_t *)v_codes, scales,
+                          slot_mapping, T, num_blocks, Hkv, D, block_size, dtype, stream);
 }

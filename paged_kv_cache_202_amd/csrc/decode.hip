@@ -472,10 +472,11 @@ static int chunk_attention(float *out, const void *q, const void *k_cache, const
   return PKV_OK;
 }
 
-// The attention call for fp32 and bf16 caches (ks = vs = nullptr) and for
-// caches of int8 codes (dtype PKV_I8, bf16 queries, per-row scales ks, vs).
+// The attention call for fp32 and bf16 caches (scales = nullptr) and for
+// caches of codes (dtype PKV_I8 or kCodes3, bf16 queries, per-row scales
+// [num_blocks, Hkv, 2, bs]).
 static int decode_impl(float *out, const void *q, const void *k_cache, const void *v_cache,
-                       const float *ks, const float *vs, const int32_t *block_tables,
+                       const float *scales, const int32_t *block_tables,
                        int32_t max_blocks, const int32_t *context_lens, int32_t B, int32_t nq,
                        int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t num_blocks,
                        float scale, int dtype, int32_t part, void *workspace,
@@ -560,8 +561,7 @@ static int decode_impl(float *out, const void *q, const void *k_cache, const voi
   a.num_parts = NP;
   a.slices = S;
   a.scale_log2 = scale * kLog2e;
-  a.ks = ks;
-  a.vs = vs;
+  a.scales = scales;
   a.parts_per_wg = ppw;
   StreamArgs sa{};
   size_t need = 0;
@@ -617,7 +617,7 @@ extern "C" int paged_attention_decode(float *out, const void *q, const void *k_c
   if (!elem_bytes(dtype))
     return fail(PKV_EINVAL, "unsupported dtype %d (int8 codes: paged_attention_decode_q8)",
                 dtype);
-  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks,
+  return decode_impl(out, q, k_cache, v_cache, nullptr, block_tables, max_blocks,
                      context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype, part,
                      workspace, workspace_bytes, lse_out, stream);
 }
@@ -674,40 +674,38 @@ extern "C" int paged_attention_decode_noalloc(float *out, const void *q, const v
   void *ws = nullptr;
   if (need)
     if (int rc = scratch_address(&ws)) return rc;
-  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, block_tables, max_blocks,
+  return decode_impl(out, q, k_cache, v_cache, nullptr, block_tables, max_blocks,
                      context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, dtype, part, ws,
                      need ? kScratchBytes : 0, lse_out, stream);
 }
 
 extern "C" int paged_attention_decode_q3(float *out, const void *q, const uint8_t *k_codes,
-                                         const uint8_t *v_codes, const float *k_scales,
-                                         const float *v_scales, const int32_t *block_tables,
+                                         const uint8_t *v_codes, const float *scales,
+                                         const int32_t *block_tables,
                                          int32_t max_blocks, const int32_t *context_lens,
                                          int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
                                          int32_t D, int32_t bs, int32_t num_blocks, float scale,
                                          int32_t part, void *workspace, size_t workspace_bytes,
                                          float *lse_out, void *stream) {
-  if (!k_scales || !v_scales) return fail(PKV_EINVAL, "NULL pointer");
-  if ((uintptr_t)k_scales % 16 || (uintptr_t)v_scales % 16)
-    return fail(PKV_EINVAL, "scale arrays must be 16-byte aligned");
+  if (!scales) return fail(PKV_EINVAL, "NULL pointer");
+  if ((uintptr_t)scales % 16) return fail(PKV_EINVAL, "the scale array must be 16-byte aligned");
   if (D != 128 && D != 256) return fail(PKV_EINVAL, "head dim %d unsupported for 3-bit codes", D);
-  return decode_impl(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, max_blocks,
+  return decode_impl(out, q, k_codes, v_codes, scales, block_tables, max_blocks,
                      context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, kCodes3, part,
                      workspace, workspace_bytes, lse_out, stream);
 }
 
 extern "C" int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
-                                         const int8_t *v_codes, const float *k_scales,
-                                         const float *v_scales, const int32_t *block_tables,
+                                         const int8_t *v_codes, const float *scales,
+                                         const int32_t *block_tables,
                                          int32_t max_blocks, const int32_t *context_lens,
                                          int32_t B, int32_t nq, int32_t Hq, int32_t Hkv,
                                          int32_t D, int32_t bs, int32_t num_blocks, float scale,
                                          int32_t part, void *workspace, size_t workspace_bytes,
                                          float *lse_out, void *stream) {
-  if (!k_scales || !v_scales) return fail(PKV_EINVAL, "NULL pointer");
-  if ((uintptr_t)k_scales % 16 || (uintptr_t)v_scales % 16)
-    return fail(PKV_EINVAL, "scale arrays must be 16-byte aligned");
-  return decode_impl(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, max_blocks,
+  if (!scales) return fail(PKV_EINVAL, "NULL pointer");
+  if ((uintptr_t)scales % 16) return fail(PKV_EINVAL, "the scale array must be 16-byte aligned");
+  return decode_impl(out, q, k_codes, v_codes, scales, block_tables, max_blocks,
                      context_lens, B, nq, Hq, Hkv, D, bs, num_blocks, scale, PKV_I8, part,
                      workspace, workspace_bytes, lse_out, stream);
 }

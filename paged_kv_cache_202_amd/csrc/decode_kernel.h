@@ -230,10 +230,9 @@ struct DecodeArgs {
   int32_t part_base;
   int32_t prefix_part;
   // Caches of codes only (the matrix-core code kernel; else nullptr): the
-  // float32 scale of each (block, KV head, slot) row of K and of V,
-  // [num_blocks, Hkv, bs].
-  const float *ks;
-  const float *vs;
+  // float32 scale of each (block, KV head, slot) row, K and V side by side,
+  // [num_blocks, Hkv, 2 (K, V), bs].
+  const float *scales;
   // MFMA decode kernel only: > 0 makes its wavefronts independent, each
   // streaming a run of this many consecutive partitions through its ring and
   // writing the run's partials into its first partition's slot (the reduce

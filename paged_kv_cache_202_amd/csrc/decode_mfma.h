@@ -506,6 +506,9 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       koff[i] = code_k_lane_offset<RB>(lane, i);
       voff[i] = kBf ? bf16_v_lane_offset<RB>(lane, i) : i * 1024 + lane * 16;
     }
+    // scales: lanes 0-15 the K rows' of the tile's 16 tokens, lanes 16-31 the
+    // V rows' (lanes 32-63 repeat them), one contiguous run per (block, head)
+    const int32_t soff = (lane & 16 ? a.bs : 0) + (lane & 15);
     int bad = 0;
     // gather the tile at logical token t0 (from block blk) into a ring slot,
     // in TileRing::stage's order: the scales (codes), the K rows (chunks
@@ -518,8 +521,8 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       const size_t rowi = ((size_t)blk * a.Hkv + g) * a.bs + (size_t)(t0 % a.bs);
       PKV_LDS char *dst = ring.base + slot * Ring::kTileBytes;
       if constexpr (!kBf) {
-        const size_t so = rowi * 4 + (size_t)(lane & 15) * 4;
-        gather_lds4<kKvNonTemporal>((const char *)((lane & 16) ? a.vs : a.ks) + so,
+        const size_t srow = ((size_t)blk * a.Hkv + g) * 2 * a.bs + (size_t)(t0 % a.bs);
+        gather_lds4<kKvNonTemporal>((const char *)(a.scales + srow + soff),
                                     dst + Ring::kCodeBytes);
       }
       const char *kp = kbase + rowi * RB, *vp = vbase + rowi * RB;

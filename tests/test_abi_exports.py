@@ -61,6 +61,12 @@ def test_host_argument_checks_need_no_gpu():
     assert lib.paged_cache_write(None, None, None, None, None, 3, 4, 8, 128, 16, 1, None) \
         == _lib.PKV_EINVAL  # NULL pointers
     assert lib.paged_kv_copy_blocks(None, None, None, 0, 4, 8, 128, 16, 1, None) == _lib.PKV_OK
+    fake = ctypes.c_void_p(256)
+    # one pool (v_cache NULL) is allowed, a missing k_cache is not
+    assert lib.paged_kv_copy_blocks(None, fake, fake, 1, 4, 8, 2, 16, 0, None) \
+        == _lib.PKV_EINVAL
+    assert lib.paged_kv_copy_blocks(fake, ctypes.c_void_p(264), fake, 1, 4, 8, 2, 16, 0, None) \
+        == _lib.PKV_EINVAL  # v_cache not 16-byte aligned
     assert lib.paged_attention_decode(None, None, None, None, None, 4, None, 2, 1, 32, 8, 128,
                                       16, 64, ctypes.c_float(0.1), 1, 0, None, 0, None,
                                       None) == _lib.PKV_EINVAL
@@ -109,18 +115,20 @@ def test_low_bit_and_chunk_host_checks_need_no_gpu():
     lib = pkv.load()
     fake = ctypes.c_void_p(256)
     # cache write of 8-bit codes
-    assert lib.paged_cache_write_q8(None, None, None, None, None, None, None, 0, 4, 8, 128, 16,
+    assert lib.paged_cache_write_q8(None, None, None, None, None, None, 0, 4, 8, 128, 16,
                                     _lib.PKV_BF16, None) == _lib.PKV_OK  # nothing to write
-    assert lib.paged_cache_write_q8(fake, fake, fake, fake, fake, fake, fake, 3, 4, 8, 96, 16,
+    assert lib.paged_cache_write_q8(fake, fake, fake, fake, fake, fake, 3, 4, 8, 96, 16,
                                     _lib.PKV_BF16, None) == _lib.PKV_EINVAL  # head dim
-    assert lib.paged_cache_write_q8(fake, fake, fake, fake, fake, fake, fake, 3, 4, 8, 128, 16,
+    assert lib.paged_cache_write_q8(fake, fake, fake, fake, fake, fake, 3, 4, 8, 128, 16,
                                     _lib.PKV_I8, None) == _lib.PKV_EINVAL  # rows are f32/bf16
-    assert lib.paged_cache_write_q8(fake, fake, fake, fake, None, fake, fake, 3, 4, 8, 128, 16,
+    assert lib.paged_cache_write_q8(fake, fake, fake, fake, None, fake, 3, 4, 8, 128, 16,
                                     _lib.PKV_BF16, None) == _lib.PKV_EINVAL  # NULL scales
+    assert lib.paged_cache_write_q3(fake, fake, fake, fake, fake, fake, 3, 4, 8, 64, 16,
+                                    _lib.PKV_BF16, None) == _lib.PKV_EINVAL  # head dim
     # decode over 8-bit codes
 
     def q8(scales=fake, nq=1, Hq=32, part=0, D=128):
-        return lib.paged_attention_decode_q8(fake, fake, fake, fake, scales, scales, fake, 4,
+        return lib.paged_attention_decode_q8(fake, fake, fake, fake, scales, fake, 4,
                                              fake, 2, nq, Hq, 8, D, 16, 8, 0.1, part, None, 0,
                                              None, None)
     assert q8(scales=None) == _lib.PKV_EINVAL
@@ -221,7 +229,7 @@ def test_code_cache_bindings_refuse():
 
     class HostQ8:  # the shape of a Q8Cache, in host memory
         k_codes = v_codes = torch.empty(6, 2, 16, 64, dtype=torch.int8)
-        k_scales = v_scales = torch.empty(6, 2, 16)
+        scales = torch.empty(6, 2, 2, 16)
         shape = (6, 2, 16, 64)
 
     k = torch.empty(3, 2, 64)

@@ -169,6 +169,33 @@ def test_cache_write_zero_rows_and_skipped_slots(device):
     assert kc[0, 0, 1, 5] == -127 and ks[0, 0, 1] == np.float32(3.0 / 127)
     assert (cache.v_codes.cpu().numpy()[0, :, :2] == 127).all()
     assert (ks[0, :, 2:] == 7.0).all() and (ks[1] == 7.0).all()  # -1 and out of range skipped
+    # K and V scales sit side by side per (block, KV head)
+    sc = cache.scales.cpu().numpy()
+    assert np.array_equal(sc[:, :, 0].view(np.uint32), ks.view(np.uint32))
+    assert (sc[0, :, 1, :2] == np.float32(1.0 / 127)).all()  # V rows of ones
+
+
+@pytest.mark.parametrize("bits", [8, 3])
+def test_code_cache_copy_blocks(bits, device):
+    """Copy-on-write of a code cache: the codes of K and V and the block's
+    whole scale run move from src to dst; pairs naming a block outside the
+    pool are skipped; every other block is left alone."""
+    print(f"code cache copy_blocks: {bits} bits", flush=True)
+    NB, Hkv, bs, D = 6, 2, 16, 128
+    cache = (pkv.Q8Cache if bits == 8 else pkv.Q3Cache)(NB, Hkv, bs, D, device)
+    g = torch.Generator().manual_seed(11)
+    for t in (cache.k_codes, cache.v_codes):
+        t.copy_(torch.randint(0, 256, t.shape, generator=g, dtype=torch.uint8).view(t.dtype))
+    cache.scales.copy_(torch.rand(cache.scales.shape, generator=g))
+    before = [t.cpu().numpy().copy() for t in (cache.k_codes, cache.v_codes, cache.scales)]
+    pairs = torch.tensor([[1, 4], [2, 5], [0, NB], [-1, 3]], dtype=torch.int32, device=device)
+    cache.copy_blocks(pairs)
+    torch.cuda.synchronize()
+    after = [t.cpu().numpy() for t in (cache.k_codes, cache.v_codes, cache.scales)]
+    for b, a in zip(before, after):
+        want = b.copy()
+        want[4], want[5] = b[1], b[2]
+        assert np.array_equal(a.view(np.uint8), want.view(np.uint8))
 
 
 CASES = [
