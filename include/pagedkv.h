@@ -362,9 +362,13 @@ int paged_attention_decode_q8(float *out, const void *q, const int8_t *k_codes,
 /* ---- caches of 3-bit per-row codes --------------------------------------
  * The same quantizer with 3 bits ([KVNB demo] Demo 2; the 3-bit storage
  * scenario of [KVNB s8]): limit 3, scale = max |x| / 3, code in [-3, 3].
- * Codes are stored two per byte as code + 8 (dim 2 i in the low nibble of
- * byte i): half a byte per element, byte-aligned for the decode kernels
- * (the pages' 3 bits per element would not give whole bytes per lane):
+ * Codes are stored two per byte (dim 2 i in the low nibble of byte i), each
+ * as its 4-bit float e2m1 bits (sign, 2 exponent bits with bias 1, 1
+ * mantissa bit), which hold every code exactly: 0 -> 0x0, 1 -> 0x2,
+ * 2 -> 0x4, 3 -> 0x5, and bit 3 set for -1, -2, -3 (0xA, 0xC, 0xD). Half a
+ * byte per element, byte-aligned for the decode kernels (the pages' 3 bits
+ * per element would not give whole bytes per lane), and a native operand
+ * of the gfx950 matrix cores:
  *   k_codes, v_codes: uint8   [num_blocks, Hkv, block_size, D / 2]
  *   scales:           float32 [num_blocks, Hkv, 2, block_size] (as above)
  * D in {128, 256}. paged_cache_write_q3 / paged_attention_decode_q3 are the

@@ -359,9 +359,9 @@ def paged_attention_decode_q8(out, q, cache: "Q8Cache", block_tables, context_le
 
 
 class Q3Cache(_CodeCache):
-    """A paged cache of 3-bit per-row codes, two per byte (code + 8, even dim
-    in the low nibble): codes uint8 [NB, Hkv, bs, D / 2] for K and for V, and
-    the float32 scales [NB, Hkv, 2, bs] (device tensors)."""
+    """A paged cache of 3-bit per-row codes, two per byte as 4-bit float e2m1
+    bits (even dim in the low nibble): codes uint8 [NB, Hkv, bs, D / 2] for K
+    and for V, and the float32 scales [NB, Hkv, 2, bs] (device tensors)."""
 
     def __init__(self, num_blocks, Hkv, block_size, D, device):
         import torch

@@ -65,9 +65,17 @@ copy_blocks_kernel(uint4 *__restrict__ k_cache, uint4 *__restrict__ v_cache,
 // max |x| / limit (1 for a row of zeros), code = clip(round-half-even(x /
 // scale), -limit, limit), in float64 as the page computes; the scale is
 // stored as float32 in the scale row [blk, h, K = 0 / V = 1, :] beside the
-// other's. 8-bit codes are stored as int8; 3-bit codes two per byte, code +
-// 8, even dim in the low nibble. One wavefront per row: each lane holds
-// D / 64 consecutive elements.
+// other's. 8-bit codes are stored as int8; 3-bit codes two per byte as the
+// 4-bit float e2m1 (sign, 2 exponent bits, 1 mantissa bit), which holds
+// every code in [-3, 3] exactly, even dim in the low nibble. One wavefront
+// per row: each lane holds D / 64 consecutive elements.
+// e2m1 bits of an integer code in [-3, 3]: 0, 1, 2, 3 are 0x0, 0x2, 0x4,
+// 0x5 (1 = 2^0, 2 = 2^1, 3 = 1.5 x 2^1); bit 3 is the sign (0 stays +0).
+__device__ __forceinline__ uint32_t e2m1_code(int c) {
+  const int m = c < 0 ? -c : c;
+  return (c < 0 ? 8u : 0u) | (m == 3 ? 5u : 2u * (uint32_t)m);
+}
+
 template <int D, int BITS, typename T>
 __global__ void __launch_bounds__(256)
 cache_write_q_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
@@ -115,7 +123,7 @@ cache_write_q_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
       uint8_t *codes = (uint8_t *)(which ? v_codes : k_codes) + dst * (D / 2) + lane * (EPL / 2);
 #pragma unroll
       for (int e = 0; e < EPL; e += 2)
-        codes[e / 2] = (uint8_t)((c[e] + 8) | ((c[e + 1] + 8) << 4));
+        codes[e / 2] = (uint8_t)(e2m1_code(c[e]) | (e2m1_code(c[e + 1]) << 4));
     }
     if (lane == 0) scales[((blk * Hkv + h) * 2 + which) * bs + off] = (float)scale;
   }

@@ -17,11 +17,14 @@
 // 128 FMAs), and at 16 lanes per SIMD that costs about as long as the
 // tile's HBM traffic. Here both products run on MFMA and the VALU only
 // widens codes and runs the softmax:
-//   * S^T = K Q^T with v_mfma_f32_16x16x32 (bf16, or f16 for codes): A = a
-//     token's row (lane l: token l % 16, a quarter of the row; codes widened
-//     to fp16 in registers), B = the query rows (row l % 16, the same
-//     quarter). The output leaves lane l the scores of row l % 16 for
-//     tokens 4 (l / 16) .. + 3.
+//   * S^T = K Q^T with v_mfma_f32_16x16x32 (bf16, or f16 for 8-bit codes):
+//     A = a token's row (lane l: token l % 16, a quarter of the row; 8-bit
+//     codes widened to fp16 in registers), B = the query rows (row l % 16,
+//     the same quarter). The output leaves lane l the scores of row l % 16
+//     for tokens 4 (l / 16) .. + 3. 3-bit codes are stored as fp4 (e2m1)
+//     and enter v_mfma_scale_f32_16x16x128_f8f6f4 as they are read (A, no
+//     widening at all); the query is its B operand as two fp8 (e4m3) pieces
+//     hi + lo, exact for bf16 queries (mfma_fp4_fp8 gives the k order).
 //   * those four weights (times their tokens' V scales for codes) are the
 //     B operand of O^T += V^T P^T as they stand. Its A operand (4 tokens x
 //     1 dim per lane) comes from the gfx950 transposing LDS reads: for
@@ -35,17 +38,16 @@
 //     V repeated: 16 significant bits per weight, so results move by no
 //     more than fp32 rounding across partitionings. In a context's last
 //     tile, V slots past its end (stale bits, maybe NaN) are zeroed.
-//   * codes widen exactly: (code ^ 0x80) in the low byte of fp16 0x64xx is
-//     1152 + code (8 bits); the offsets are removed once per score
+//   * 8-bit codes widen exactly: (code ^ 0x80) in the low byte of fp16
+//     0x64xx is 1152 + code; the offsets are removed once per score
 //     (1152 x sum q) and once per output (1152 x the sum of the fp16
-//     weights used). A stored nibble (code + 8) there is 1032 + code, and
-//     one packed fp16 add takes it to the code itself: next to codes of at
-//     most 3 an offset of 1032 would cancel too many bits of the fp32 sums.
-//   * 3-bit codes, two per byte (dim 2 i in the low nibble of byte i): the
-//     same tile scheme on rows of D / 2 bytes. A K word (8 dims) widens
-//     low nibbles then high nibbles, so the query's dims are taken in that
-//     order too; a transposed V byte gives two dims (2 c, 2 c + 1), so one
-//     read feeds four output column blocks whose rows interleave.
+//     weights used).
+//   * 3-bit codes, two e2m1 nibbles per byte (dim 2 i in the low nibble of
+//     byte i): the same tile scheme on rows of D / 2 bytes. A transposed V
+//     byte (one token) gives two dims (2 c, 2 c + 1) as exact fp16 in one
+//     v_cvt_scalef32_pk_f16_fp4; the even and the odd dims of four tokens
+//     then form the A operands of two output column blocks whose rows
+//     interleave.
 //   * up to 16 query rows (G x query tokens) per wavefront at no extra MFMA
 //     work; the staging, ring, lazy softmax and partials are the partition
 //     kernel's. K rows are stored in the LDS ring with their 16-byte chunks
@@ -230,23 +232,29 @@ __device__ __forceinline__ void read_bf16<256>(u32x4_t (&k)[4], uint2 (&v)[8],
 __device__ __forceinline__ uint2 codes_f16x4(uint32_t w) {
   return make_uint2(codes_f16_lo(w), codes_f16_hi(w));
 }
-// Four nibble codes u (the low or high nibbles of a word, masked into byte
-// positions) as four fp16 values 1024 + u.
-__device__ __forceinline__ uint2 nibbles_f16x4(uint32_t n) {
-  return make_uint2(__builtin_amdgcn_perm(0x64646464u, n, 0x04010400u),
-                    __builtin_amdgcn_perm(0x64646464u, n, 0x04030402u));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// S^T += K Q^T over 128 dims with 3-bit codes: A = 32 fp4 (e2m1) codes per
+// lane as stored (u32x4), B = 32 fp8 (e4m3) query values per lane, block
+// scales 1 (E8M0 127); row (A) and column (B) = lane % 16. The products'
+// k index as measured on gfx950: lane group g of A holds k = 32 g + i in
+// its nibble i (even i in the low nibble of a byte); lane group g of B holds
+// k = 16 g + j in its byte j < 16 and k = 64 + 16 g + (j - 16) in byte
+// j >= 16.
+__device__ __forceinline__ c32x4_t mfma_fp4_fp8(u32x4_t a, const uint32_t (&b)[8], c32x4_t c) {
+  const i32x8_t av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8_t bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3],
+                      (int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, 127, 0, 127);
 }
-// The same as the codes themselves (stored nibble - 8), exactly: with
-// offsets as large as 1032 next to codes of at most 3 the fp32 sums would
-// cancel away too many bits.
-__device__ __forceinline__ uint2 nibble_codes_f16x4(uint32_t n) {
-  const uint2 u = nibbles_f16x4(n);
-  const f16x2_t off = {(_Float16)-1032.f, (_Float16)-1032.f};
-  return make_uint2(__builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u.x) + off),
-                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, u.y) + off));
+
+// Four fp32 values as the low (word_hi false) or high half of fp8 (e4m3,
+// round to nearest even) bytes 0..3 of a word.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  const uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
-__device__ __forceinline__ uint32_t low_nibbles(uint32_t w) { return w & 0x0f0f0f0fu; }
-__device__ __forceinline__ uint32_t high_nibbles(uint32_t w) { return (w >> 4) & 0x0f0f0f0fu; }
 
 template <int DT, int D, int RW, int kWaves, bool kStream>
 __global__ void __launch_bounds__(kWaves * 64)
@@ -443,9 +451,76 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     const int rr = row0 + ln, qi = rr / G;
     const bool row_live = ln < RW && qi < nq;
     uint32_t qb[NC][4];
+    uint32_t qp[KCH][2][8];  // 3-bit codes: the query as fp8 pieces hi + lo
     float qcorr, qfac;
     int lim;  // keys visible to row ln
-    {
+    if constexpr (kNib) {
+      // B operand of the fp4 x fp8 products: for product c (the lane's K
+      // chunk c), byte j of this lane's 32 is dim 32 (KCH (2 (j / 16) +
+      // lg / 2) + c) + 16 (lg % 2) + j % 16 -- the dim that the fp4 code it
+      // meets belongs to. Each dim scaled by 2^-e (the row's largest entry
+      // in [2^7, 2^8)) and split into e4m3 pieces hi = rne(x), lo = rne(x -
+      // hi): a bf16 value has 8 significant bits and e4m3 4, so hi + lo is
+      // x exactly unless x sits more than 10 binades below the row maximum
+      // (then within 2^-10 absolute, 2^-18 of the maximum).
+      float x[KCH][2][16];
+      if (row_live) {
+        const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
+        const uint16_t *qrow = (const uint16_t *)a.q + row * D;
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                qrow + 32 * (KCH * (2 * h + lg / 2) + c) + 16 * (lg % 2));
+            const uint4 t[2] = {src[0], src[1]};
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const uint32_t wv[4] = {t[u].x, t[u].y, t[u].z, t[u].w};
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                x[c][h][8 * u + 2 * v] = bf16_lo(wv[v]);
+                x[c][h][8 * u + 2 * v + 1] = bf16_hi(wv[v]);
+              }
+            }
+          }
+      } else {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) x[c][h][t] = 0.f;
+      }
+      float mx = 0.f;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) mx = fmaxf(mx, fabsf(x[c][h][t]));
+      mx = fmaxf(mx, exact_xor<16>(mx));
+      mx = fmaxf(mx, exact_xor<32>(mx));
+      int ex = 0;
+      frexpf(mx, &ex);
+      const int e = mx == 0.f ? 0 : ex - 8;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {  // word m: bytes 4 m .. 4 m + 3
+          const float *xs = &x[c][m / 4][4 * (m % 4)];
+          const float v0 = ldexpf(xs[0], -e), v1 = ldexpf(xs[1], -e);
+          const float v2 = ldexpf(xs[2], -e), v3 = ldexpf(xs[3], -e);
+          const uint32_t hw = fp8x4(v0, v1, v2, v3);
+          const f32x2_t d01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hw, false);
+          const f32x2_t d23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hw, true);
+          qp[c][0][m] = hw;
+          qp[c][1][m] = fp8x4(v0 - d01.x, v1 - d01.y, v2 - d23.x, v3 - d23.y);
+        }
+      qcorr = 0.f;
+      qfac = ldexpf(1.f, e) * a.scale_log2;
+      lim = row_live ? L - nq + qi + 1 : 0;
+    } else {
       uint32_t w[D / 8];  // bf16 pairs: dims 2 j, 2 j + 1 of the quarter
       if (row_live) {
         const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
@@ -481,10 +556,8 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       for (int c = 0; c < NC && !kBf; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1) for 8-bit
-          // codes; low nibbles (dims 0, 2, 4, 6) then high ones for 3-bit
-          const int d0 = kNib ? 8 * c + (j < 2 ? 4 * j : 4 * (j - 2) + 1) : 8 * c + 2 * j;
-          const int d1 = kNib ? d0 + 2 : d0 + 1;
+          // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1)
+          const int d0 = 8 * c + 2 * j, d1 = d0 + 1;
           const _Float16 lo = (_Float16)ldexpf(qdim(d0), -e);
           const _Float16 hi = (_Float16)ldexpf(qdim(d1), -e);
           sum += (float)lo + (float)hi;
@@ -658,8 +731,15 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 
         // S^T = K Q^T: s[e] = row ln . token 4 lg + e (codes with offsets)
         c32x4_t s = c32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kNib) {  // the fp4 codes as stored, the query's fp8 pieces
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
+          for (int c = 0; c < KCH; ++c) {
+            s = mfma_fp4_fp8(kr[c], qp[c][0], s);
+            s = mfma_fp4_fp8(kr[c], qp[c][1], s);
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < NC && !kNib; ++c) {
           if constexpr (kBf) {
             const u32x4_t bv = {qb[c][0], qb[c][1], qb[c][2], qb[c][3]};
             s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kr[c]),
@@ -668,13 +748,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
             continue;
           }
           u32x4_t av;
-          if constexpr (kNib) {  // one word: 8 dims, low nibbles first
-            const u32x4_t kw = kr[c / 4];
-            const uint32_t wd = kw[c % 4];
-            const uint2 lo = nibble_codes_f16x4(low_nibbles(wd));
-            const uint2 hi = nibble_codes_f16x4(high_nibbles(wd));
-            av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
-          } else {  // two words: 8 dims in order
+          {  // two words: 8 dims in order
             const u32x4_t kw = kr[c / 2];
             const uint2 lo = codes_f16x4(kw[2 * (c % 2)]), hi = codes_f16x4(kw[2 * (c % 2) + 1]);
             av = u32x4_t{lo.x, lo.y, hi.x, hi.y};
@@ -758,14 +832,22 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
           if constexpr (kNib) {  // bytes 32 j + ln and 32 j + 16 + ln: four dims
-            const uint32_t x = vt[j].x, y = vt[j].y;
-            const uint32_t nib[4] = {low_nibbles(x), high_nibbles(x), low_nibbles(y),
-                                     high_nibbles(y)};
+            const uint32_t xy[2] = {vt[j].x, vt[j].y};
 #pragma unroll
-            for (int n = 0; n < 4; ++n)
-              o[4 * j + n] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                  __builtin_bit_cast(h16x4_t, nibble_codes_f16x4(nib[n])), pb, o[4 * j + n],
-                  0, 0, 0);
+            for (int hh = 0; hh < 2; ++hh) {
+              // byte u = token 4 lg + u: its two e2m1 codes (even dim low)
+              // as exact fp16, then the even dims and the odd dims of the
+              // four tokens as two A operands
+              const f16x2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 0);
+              const f16x2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 1);
+              const f16x2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 2);
+              const f16x2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 3);
+              const h16x4_t ev = {c0.x, c1.x, c2.x, c3.x}, od = {c0.y, c1.y, c2.y, c3.y};
+              o[4 * j + 2 * hh] =
+                  __builtin_amdgcn_mfma_f32_16x16x16f16(ev, pb, o[4 * j + 2 * hh], 0, 0, 0);
+              o[4 * j + 2 * hh + 1] =
+                  __builtin_amdgcn_mfma_f32_16x16x16f16(od, pb, o[4 * j + 2 * hh + 1], 0, 0, 0);
+            }
           } else {  // dims 32 j + ln and 32 j + 16 + ln
             o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
                 __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].x)), pb, o[2 * j], 0, 0, 0);

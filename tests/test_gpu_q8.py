@@ -35,10 +35,29 @@ def host_bits(t):
     return t.numpy()
 
 
+# The 4-bit float e2m1 (sign, 2 exponent bits with bias 1, 1 mantissa bit;
+# exponent 0 is subnormal: 0.5 x mantissa), by nibble. The 3-bit cache stores
+# each code in [-3, 3] as its e2m1 bits; a nibble the quantizer never writes
+# (-0, a half, +-4, +-6) decodes to a value no code equals (100 for the
+# non-integers and -0).
+E2M1_AS_CODE = np.array([0, 100, 1, 100, 2, 3, 4, 6, 100, 100, -1, 100, -2, -3, -4, -6],
+                        np.int16)
+
+
+def test_e2m1_table_is_the_format():
+    """Pin the decoding table to the e2m1 definition itself."""
+    for n in range(16):
+        s, e, m = n >> 3, (n >> 1) & 3, n & 1
+        v = (0.5 * m) if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+        v = -v if s else v
+        want = int(v) if v == int(v) and not (s and v == 0) else 100
+        assert E2M1_AS_CODE[n] == want, n
+
+
 def unpack3(codes):
-    """int8 codes of a 3-bit cache's bytes (code + 8, even dim low nibble)."""
-    lo = (codes & 0xF).astype(np.int16) - 8
-    hi = (codes >> 4).astype(np.int16) - 8
+    """int8 codes of a 3-bit cache's bytes (e2m1 nibbles, even dim low)."""
+    lo = E2M1_AS_CODE[codes & 0xF]
+    hi = E2M1_AS_CODE[codes >> 4]
     return np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (-1,)).astype(np.int8)
 
 
@@ -93,9 +112,9 @@ class Q8Case:
                                                                  device)
         self.cache.k_scales.fill_(float("nan"))
         self.cache.v_scales.fill_(float("nan"))
-        # codes the quantizer never writes: -128, or nibbles 0 (code -8)
-        self.cache.k_codes.fill_(-128 if bits == 8 else 0)
-        self.cache.v_codes.fill_(-128 if bits == 8 else 0)
+        # codes the quantizer never writes: -128, or e2m1 nibbles -6
+        self.cache.k_codes.fill_(-128 if bits == 8 else 0xFF)
+        self.cache.v_codes.fill_(-128 if bits == 8 else 0xFF)
         write = pkv.paged_cache_write_q8 if bits == 8 else pkv.paged_cache_write_q3
         write(self.k_new.to(device), self.v_new.to(device), self.cache,
               torch.from_numpy(lslots).to(device))
@@ -150,7 +169,7 @@ def test_cache_write_codes_bit_exact(in_dtype, D, bits, device):
         w = want.transpose(0, 2, 1)[live].view(np.uint32)
         assert np.array_equal(g, w)
     # slots nobody wrote keep their fill
-    assert (kc.transpose(0, 2, 1, 3)[~live] == (-128 if bits == 8 else -8)).all()
+    assert (kc.transpose(0, 2, 1, 3)[~live] == (-128 if bits == 8 else -6)).all()
     assert np.isnan(ks.transpose(0, 2, 1)[~live]).all()
 
 
