@@ -249,6 +249,17 @@ __device__ __forceinline__ c32x4_t mfma_fp4_fp8(u32x4_t a, const uint32_t (&b)[8
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, 127, 0, 127);
 }
 
+// a * b, except that the result is 0 whenever a or b is 0, even against an
+// infinite or NaN other factor (the rule of v_mul_legacy_f32); otherwise the
+// ordinary rounded product. The compiler's hazard checks do not look into
+// inline assembly, and `a` is a v_exp_f32 result here: a vector read of a
+// transcendental's result needs one wait state, hence the s_nop.
+__device__ __forceinline__ float mul_zero_wins(float a, float b) {
+  float r;
+  asm("s_nop 0\n\tv_mul_legacy_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Four fp32 values as the low (word_hi false) or high half of fp8 (e4m3,
 // round to nearest even) bytes 0..3 of a word.
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
@@ -765,7 +776,8 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool vis = t0 + 4 * lg + e < lim;
-          sc[e] = vis ? (kBf ? s[e] * qfac : (s[e] - qcorr) * (kss[e] * qfac)) : kNegInf;
+          const float sq = kOffset != 0.f ? s[e] - qcorr : s[e];
+          sc[e] = vis ? (kBf ? s[e] * qfac : sq * (kss[e] * qfac)) : kNegInf;
           need |= sc[e] > m_row + kLazyLog2;
         }
         if (__any(need)) {  // raise the running maximum of row ln
@@ -786,10 +798,11 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);
+          const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);  // 0 when masked
           l_part += pw;
-          // the V scale of a masked token may be stale: never multiplied
-          pv[e] = sc[e] == kNegInf ? 0.f : kBf ? pw : pw * vss[e];
+          // the V scale of a masked token may be stale (even NaN): its zero
+          // weight wins the product
+          pv[e] = kBf ? pw : mul_zero_wins(pw, vss[e]);
         }
         if constexpr (kBf) {
           // O^T += V^T P^T with bf16 weights; in a context's last tile the

@@ -301,12 +301,11 @@ __device__ __forceinline__ void read_v2_128(uint2 (&v)[2][8], const PKV_LDS char
       : "memory");
 }
 
-// The largest of three floats in one instruction (fmaxf would first quiet
-// each operand: one more instruction per value).
+// The largest of three floats (the compiler forms v_max3_f32; inline
+// assembly here would hide from its hazard checks that the operands come
+// straight from the matrix cores).
 __device__ __forceinline__ float max3f(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 
 // K halves and V halves on their own for the other head dims, so that a
