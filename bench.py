@@ -635,6 +635,9 @@ def merge_sq_counters(args) -> int:
     if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_LDS_IDX_ACTIVE" in avg:
         derived["bank_conflict_share_of_lds_active"] = (avg["SQ_LDS_BANK_CONFLICT"] /
                                                         avg["SQ_LDS_IDX_ACTIVE"])
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        derived["share_of_mfma_busy_with_valu_coexecuting"] = (
+            avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"])
     if "SQ_INSTS_VALU" in avg and "SQ_WAVES" in avg:
         w = avg["SQ_WAVES"]
         derived["per_wave"] = {c[len("SQ_INSTS_"):].lower(): avg[c] / w
