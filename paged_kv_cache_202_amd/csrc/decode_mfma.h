@@ -503,6 +503,16 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) x[c][h][t] = 0.f;
       }
+      // a negative scale moves into the query (negation is exact), so that
+      // the factor qfac below is positive
+      if (a.scale_log2 < 0.f) {
+#pragma unroll
+        for (int c = 0; c < KCH; ++c)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) x[c][h][t] = -x[c][h][t];
+      }
       float mx = 0.f;
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
@@ -529,7 +539,9 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
           qp[c][1][m] = fp8x4(v0 - d01.x, v1 - d01.y, v2 - d23.x, v3 - d23.y);
         }
       qcorr = 0.f;
-      qfac = ldexpf(1.f, e) * a.scale_log2;
+      // at least 1e-30: a masked raw score (-inf) times it stays -inf, and
+      // with scale 0 every visible weight is still exp2(0) = 1
+      qfac = fmaxf(ldexpf(1.f, e) * fabsf(a.scale_log2), 1e-30f);
       lim = row_live ? L - nq + qi + 1 : 0;
     } else {
       uint32_t w[D / 8];  // bf16 pairs: dims 2 j, 2 j + 1 of the quarter
@@ -547,11 +559,14 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         for (int j = 0; j < D / 8; ++j) w[j] = 0u;
       }
       auto qdim = [&](int d) { return d % 2 ? bf16_hi(w[d / 2]) : bf16_lo(w[d / 2]); };
+      // a negative scale moves into the query (negation is exact), so that
+      // the factor qfac below is positive
+      const bool neg = a.scale_log2 < 0.f;
       if constexpr (kBf) {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) qb[c][j] = w[4 * c + j];
+          for (int j = 0; j < 4; ++j) qb[c][j] = w[4 * c + j] ^ (neg ? 0x80008000u : 0u);
       }
       float mx = 0.f;
 #pragma unroll
@@ -569,15 +584,16 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         for (int j = 0; j < 4; ++j) {
           // MFMA c, k = 2 j, 2 j + 1: dims 8 c + (2 j, 2 j + 1)
           const int d0 = 8 * c + 2 * j, d1 = d0 + 1;
-          const _Float16 lo = (_Float16)ldexpf(qdim(d0), -e);
-          const _Float16 hi = (_Float16)ldexpf(qdim(d1), -e);
+          const float sg = neg ? -1.f : 1.f;
+          const _Float16 lo = (_Float16)(sg * ldexpf(qdim(d0), -e));
+          const _Float16 hi = (_Float16)(sg * ldexpf(qdim(d1), -e));
           sum += (float)lo + (float)hi;
           qb[c][j] = __builtin_bit_cast(uint32_t, f16x2_t{lo, hi});
         }
       sum += exact_xor<16>(sum);
       sum += exact_xor<32>(sum);
       qcorr = kOffset * sum;
-      qfac = ldexpf(1.f, e) * a.scale_log2;
+      qfac = fmaxf(ldexpf(1.f, e) * fabsf(a.scale_log2), 1e-30f);  // as above
       lim = row_live ? L - nq + qi + 1 : 0;
     }
 
@@ -631,6 +647,10 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) o[cb] = c32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_row = kNegInf, l_part = 0.f, w_part = 0.f;
+    // the raw score (before the factor qfac > 0) past which the running
+    // maximum is raised: (m_row + kLazyLog2) / qfac
+    const float rqfac = 1.f / qfac;
+    float thr = kNegInf;
 
     // The partial of partition pp, or in stream mode of segment id pp,
     // straight from the registers (independent wavefronts).
@@ -771,22 +791,25 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         const int t0 = tile_t0(k);
         const float kss[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
         const float vss[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
-        float sc[4];
+        // raw scores rs = score / qfac: the maximum test against thr, the
+        // scaling inside the exponent's fma
+        float rs[4];
         bool need = false;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool vis = t0 + 4 * lg + e < lim;
           const float sq = kOffset != 0.f ? s[e] - qcorr : s[e];
-          sc[e] = vis ? (kBf ? s[e] * qfac : sq * (kss[e] * qfac)) : kNegInf;
-          need |= sc[e] > m_row + kLazyLog2;
+          rs[e] = vis ? (kBf ? s[e] : sq * kss[e]) : kNegInf;
+          need |= rs[e] > thr;
         }
         if (__any(need)) {  // raise the running maximum of row ln
-          float tmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+          float tmax = fmaxf(fmaxf(rs[0], rs[1]), fmaxf(rs[2], rs[3]));
           tmax = fmaxf(tmax, exact_xor<16>(tmax));
-          tmax = fmaxf(tmax, exact_xor<32>(tmax));
+          tmax = fmaxf(tmax, exact_xor<32>(tmax)) * qfac;
           const float mn = fmaxf(m_row, tmax);
           const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_row - mn);
           m_row = mn;
+          thr = (mn + kLazyLog2) * rqfac;
           l_part *= alpha;
           w_part *= alpha;
 #pragma unroll
@@ -798,7 +821,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float pw = __builtin_amdgcn_exp2f(sc[e] - m_sub);  // 0 when masked
+          const float pw = __builtin_amdgcn_exp2f(fmaf(rs[e], qfac, -m_sub));  // 0 when masked
           l_part += pw;
           // the V scale of a masked token may be stale (even NaN): its zero
           // weight wins the product

@@ -167,6 +167,16 @@ def test_placement_invariance_is_bitwise(device):
     assert np.array_equal(oa, ob) and np.array_equal(la, lb)
 
 
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+@pytest.mark.parametrize("part", [0, -1])
+def test_negative_and_zero_scale(device, scale, part):
+    """A negative scale (the matrix-core kernel moves its sign into the
+    query) and scale 0 (every visible key weighs the same; lse = log of the
+    count), bf16 on the split plan and on the stream plan."""
+    case = Case((1, 17, 250, 1000), 32, 8, 128, 16, "bf16", seed=7, device=device, scale=scale)
+    check_case(case, part)
+
+
 def test_single_token_context_returns_its_value(device):
     case = Case((1, 1, 1), 8, 2, 128, 16, "bf16", seed=3, stack_seed=3)
     out, _ = case.run_gpu()

@@ -250,6 +250,24 @@ def test_q8_attention_matches_oracle(ci, bits, device):
 
 
 @pytest.mark.parametrize("bits", [8, 3])
+@pytest.mark.parametrize("scale", [-0.09, 0.0])
+def test_q8_negative_and_zero_scale(scale, bits, device):
+    """A negative scale (the kernel moves its sign into the query) and scale 0
+    (every visible key weighs the same; lse = log of the count), on the split
+    plan and on the stream plan."""
+    print(f"{bits}-bit attention, scale {scale}", flush=True)
+    c = Q8Case((1, 17, 250, 1000), 32, 8, 128, nq=1, seed=77, device=device, bits=bits)
+    c.scale = scale
+    ref, ref_lse = c.run_oracle()
+    for part in (0, -1):
+        out, lse = c.run_gpu(part)
+        err = np.abs(out - ref).max()
+        print(f"  partition {part}: max-abs error {err:.3e}", flush=True)
+        assert np.isfinite(out).all() and err <= 1e-2
+        assert np.abs(lse - ref_lse).max() <= 1e-2
+
+
+@pytest.mark.parametrize("bits", [8, 3])
 def test_q8_many_partitions_per_workgroup(bits, device):
     """2 sequences x 8 KV heads x 256 partitions of 16 tokens: one wavefront
     streams a run of two consecutive partitions as one partial."""
