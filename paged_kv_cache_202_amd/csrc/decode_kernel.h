@@ -372,6 +372,23 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"i"(VM) : "memory");
 }
 
+// Wait until at most ahead * L vector-memory operations are pending, for a
+// wavefront-uniform ahead in [0, S) of a ring of S slots. `steady` must be
+// ahead == S - 1 (a full ring ahead), given as its own condition: tested
+// first, the common case costs one compare and branch; tested as a value of
+// ahead, the compiler folds it into a search over all S cases.
+template <int S, int L>
+__device__ __forceinline__ void wait_ahead(bool steady, int ahead) {
+  if (steady) {
+    wait_vmcnt<(S - 1) * L>();
+    return;
+  }
+  static_for<S - 1>([&](auto ac) {
+    constexpr int A = decltype(ac)::value;
+    if (ahead == A) wait_vmcnt<A * L>();
+  });
+}
+
 // ---------------------------------------------------------------------------
 // Per-wavefront ring of LDS slots that K/V tiles are gathered into with
 // direct-to-LDS loads (global_load_lds_dwordx4: lane i's 16 bytes land at

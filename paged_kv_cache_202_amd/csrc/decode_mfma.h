@@ -731,10 +731,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       for (int k = 0; k < n_tiles; ++k) {
         const int slot = k & (kSlots - 1);
         const int ahead = min(n_tiles - 1 - k, kSlots - 1);
-        static_for<kSlots>([&](auto ac) {
-          constexpr int A = decltype(ac)::value;
-          if (ahead == A) wait_vmcnt<A * Ring::kLoads>();
-        });
+        wait_ahead<kSlots, Ring::kLoads>(k + kSlots <= n_tiles, ahead);
         u32x4_t kr[KCH];
         uint2 vt[NV];
         float4 ksc = make_float4(1.f, 1.f, 1.f, 1.f), vsc = ksc;
