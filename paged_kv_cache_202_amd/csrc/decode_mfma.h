@@ -43,11 +43,11 @@
 //     (1152 x sum q) and once per output (1152 x the sum of the fp16
 //     weights used).
 //   * 3-bit codes, two e2m1 nibbles per byte (dim 2 i in the low nibble of
-//     byte i): the same tile scheme on rows of D / 2 bytes. A transposed V
-//     byte (one token) gives two dims (2 c, 2 c + 1) as exact fp16 in one
-//     v_cvt_scalef32_pk_f16_fp4; the even and the odd dims of four tokens
-//     then form the A operands of two output column blocks whose rows
-//     interleave.
+//     byte i): the same tile scheme on rows of D / 2 bytes. V comes from the
+//     4-bit transposing read ds_read_b64_tr_b4, arranged so that each byte
+//     of the result holds two consecutive tokens of one dim: one
+//     v_cvt_scalef32_pk_f16_fp4 per byte gives the A operand as exact fp16,
+//     with no rearranging (read_nib_codes).
 //   * up to 16 query rows (G x query tokens) per wavefront at no extra MFMA
 //     work; the staging, ring, lazy softmax and partials are the partition
 //     kernel's. K rows are stored in the LDS ring with their 16-byte chunks
@@ -173,6 +173,59 @@ __device__ __forceinline__ void read_codes<256>(u32x4_t (&k)[4], uint2 (&v)[8], 
         "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
         "=&v"(ks), "=&v"(vs)
       : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va), "v"(sa)
+      : "memory");
+}
+
+// 3-bit tiles (rows of RB = D / 2 bytes of e2m1 nibbles): as read_codes, but
+// V by 4-bit transposing reads, ds_read_b64_tr_b4. In each 16-lane group
+// lane i receives nibble i of the 8-byte word each lane u of the group
+// names, at nibble position u (measured on gfx950 with an in-bounds read of
+// tagged words). Lane u names token 4 (l / 16) + u % 4 and the 16-dim block
+// u / 4 of each 64-dim run (read h: run h, at va + 32 h), so byte 2 b of the
+// result holds that lane's dim of block b for tokens 0 and 1 of its four,
+// byte 2 b + 1 for tokens 2 and 3.
+template <int RB>
+__device__ __forceinline__ void read_nib_codes(u32x4_t (&k)[CodeGeo<RB>::KCH],
+                                               uint2 (&v)[CodeGeo<RB>::NV], float4 &ks,
+                                               float4 &vs,
+                                               const PKV_LDS char *const (&ka)[CodeGeo<RB>::KCH],
+                                               const PKV_LDS char *va, const PKV_LDS char *sa);
+
+template <>
+__device__ __forceinline__ void read_nib_codes<64>(u32x4_t (&k)[1], uint2 (&v)[2], float4 &ks,
+                                                   float4 &vs, const PKV_LDS char *const (&ka)[1],
+                                                   const PKV_LDS char *va,
+                                                   const PKV_LDS char *sa) {
+  asm volatile(
+      "ds_read_b128 %0, %5\n\t"
+      "ds_read_b64_tr_b4 %1, %6\n\t"
+      "ds_read_b64_tr_b4 %2, %6 offset:32\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "ds_read_b128 %4, %7 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(ks), "=&v"(vs)
+      : "v"(ka[0]), "v"(va), "v"(sa)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void read_nib_codes<128>(u32x4_t (&k)[2], uint2 (&v)[4], float4 &ks,
+                                                    float4 &vs, const PKV_LDS char *const (&ka)[2],
+                                                    const PKV_LDS char *va,
+                                                    const PKV_LDS char *sa) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b64_tr_b4 %2, %10\n\t"
+      "ds_read_b64_tr_b4 %3, %10 offset:32\n\t"
+      "ds_read_b64_tr_b4 %4, %10 offset:64\n\t"
+      "ds_read_b64_tr_b4 %5, %10 offset:96\n\t"
+      "ds_read_b128 %6, %11\n\t"
+      "ds_read_b128 %7, %11 offset:64\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]),
+        "=&v"(ks), "=&v"(vs)
+      : "v"(ka[0]), "v"(ka[1]), "v"(va), "v"(sa)
       : "memory");
 }
 
@@ -665,22 +718,10 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         const size_t row = ((size_t)b * nq + qi) * a.Hq + g * G + (rr % G);
         const size_t pi = kStream ? (size_t)pp * RW + ln : row * a.num_parts + a.part_base + pp;
         float *dst = a.part_acc + pi * D;
-        if constexpr (kNib) {
 #pragma unroll
-          for (int jh = 0; jh < NCB / 2; ++jh) {
-            const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
-            float *q8 = dst + 32 * jh + 8 * lg;
-            *reinterpret_cast<float4 *>(q8) =
-                make_float4(lo[0] + off, hi[0] + off, lo[1] + off, hi[1] + off);
-            *reinterpret_cast<float4 *>(q8 + 4) =
-                make_float4(lo[2] + off, hi[2] + off, lo[3] + off, hi[3] + off);
-          }
-        } else {
-#pragma unroll
-          for (int cb = 0; cb < NCB; ++cb)
-            *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
-                make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
-        }
+        for (int cb = 0; cb < NCB; ++cb)
+          *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
+              make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
         if (lg == 0) {
           a.part_m[pi] = bad ? __builtin_nanf("") : m_row;
           a.part_l[pi] = lt;
@@ -711,8 +752,10 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       const PKV_LDS char *va;
       const PKV_LDS char *vab[Gc::NV];
       {
-        const int u = kBf ? ln >> 2 : ln >> 1, t = 4 * lg + (u & 3);
-        const int col = kBf ? 8 * (ln & 3) : 16 * (u >> 2) + 8 * (ln & 1);
+        // 3-bit: lane s names token 4 lg + s % 4, the 8-byte word s / 4 of
+        // each 32-byte run (read_nib_codes)
+        const int u = kBf ? ln >> 2 : kNib ? ln : ln >> 1, t = 4 * lg + (u & 3);
+        const int col = kBf ? 8 * (ln & 3) : kNib ? 8 * (ln >> 2) : 16 * (u >> 2) + 8 * (ln & 1);
         const PKV_LDS char *row =
             ring_base + NL * 1024 + (t / Gc::TPL) * 1024 + (t % Gc::TPL) * RB;
         va = row + col;
@@ -746,7 +789,10 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
             for (int cb = 0; cb < Gc::NV; ++cb) vas[cb] = vab[cb] + so;
             read_bf16<RB>(kr, vt, kas, vas);
           } else
-            read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
+            if constexpr (kNib)
+              read_nib_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
+            else
+              read_codes<RB>(kr, vt, ksc, vsc, kas, va + so, sa + so);
         }
         if (k + kSlots < n_tiles) {  // the slot is free again: refill it
           const int kn = k + kSlots;
@@ -864,23 +910,20 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         // O^T += V^T P^T: A = V[tokens 4 lg .. + 3][one dim per lane]
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
-          if constexpr (kNib) {  // bytes 32 j + ln and 32 j + 16 + ln: four dims
+          if constexpr (kNib) {  // read j: 16-dim blocks 4 j .. 4 j + 3
             const uint32_t xy[2] = {vt[j].x, vt[j].y};
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              // byte u = token 4 lg + u: its two e2m1 codes (even dim low)
-              // as exact fp16, then the even dims and the odd dims of the
-              // four tokens as two A operands
-              const f16x2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 0);
-              const f16x2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 1);
-              const f16x2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 2);
-              const f16x2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(xy[hh], 1.f, 3);
-              const h16x4_t ev = {c0.x, c1.x, c2.x, c3.x}, od = {c0.y, c1.y, c2.y, c3.y};
-              o[4 * j + 2 * hh] =
-                  __builtin_amdgcn_mfma_f32_16x16x16f16(ev, pb, o[4 * j + 2 * hh], 0, 0, 0);
-              o[4 * j + 2 * hh + 1] =
-                  __builtin_amdgcn_mfma_f32_16x16x16f16(od, pb, o[4 * j + 2 * hh + 1], 0, 0, 0);
-            }
+            static_for<4>([&](auto bc) {
+              // bytes 2 bb and 2 bb + 1 of the read: tokens (0, 1) and (2, 3)
+              // of this lane's four, its dim of block 4 j + bb, exact fp16
+              constexpr int bb = decltype(bc)::value;
+              const uint32_t w = xy[bb >> 1];
+              const f16x2_t c01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.f, 2 * (bb & 1));
+              const f16x2_t c23 =
+                  __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.f, 2 * (bb & 1) + 1);
+              const h16x4_t av = {c01.x, c01.y, c23.x, c23.y};
+              o[4 * j + bb] =
+                  __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, o[4 * j + bb], 0, 0, 0);
+            });
           } else {  // dims 32 j + ln and 32 j + 16 + ln
             o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(
                 __builtin_bit_cast(h16x4_t, codes_f16x4(vt[j].x)), pb, o[2 * j], 0, 0, 0);
@@ -912,24 +955,10 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     __syncthreads();  // the partials overwrite the other wavefronts' rings
     if (ln < RW) {
       float *dst = sm.mg.acc[wave][ln];
-      if constexpr (kNib) {
-        // block 4 j + 2 h + n holds dim 64 j + 32 h + 2 m + n (m = 4 lg + e):
-        // the two nibble blocks interleave into 8 consecutive dims
 #pragma unroll
-        for (int jh = 0; jh < NCB / 2; ++jh) {
-          const c32x4_t lo = o[2 * jh], hi = o[2 * jh + 1];
-          float *q8 = dst + 32 * jh + 8 * lg;
-          *reinterpret_cast<float4 *>(q8) =
-              make_float4(lo[0] + off, hi[0] + off, lo[1] + off, hi[1] + off);
-          *reinterpret_cast<float4 *>(q8 + 4) =
-              make_float4(lo[2] + off, hi[2] + off, lo[3] + off, hi[3] + off);
-        }
-      } else {
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
-              make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
-      }
+      for (int cb = 0; cb < NCB; ++cb)
+        *reinterpret_cast<float4 *>(dst + 16 * cb + 4 * lg) =
+            make_float4(o[cb][0] + off, o[cb][1] + off, o[cb][2] + off, o[cb][3] + off);
       if (lg == 0) {
         sm.mg.m[wave][ln] = m_row;
         sm.mg.l[wave][ln] = l_part;
