@@ -546,10 +546,11 @@ def copy_probe(mib: int, dev) -> int:
     return 0
 
 
-def read_probe(mib: int, dev) -> int:
+def read_probe(mib: int, dev, chunk: int = 4096) -> int:
     """Read ceilings of this machine: a buffer of `mib` MiB (well past the 256 MB
-    last-level cache) read as 4 KiB chunks -- the K (or V) run of one
-    16-token, 128-dim bf16 tile -- in sequence and in a seeded random order,
+    last-level cache) read as `chunk`-byte chunks -- 4 KiB: the K (or V) run
+    of one 16-token, 128-dim bf16 tile; 1 KiB: the same for 3-bit codes;
+    2 KiB: 8-bit codes -- in sequence and in a seeded random order,
     with the decode kernels' loads: to registers (plain and non-temporal; four
     workgroups of eight wavefronts a CU) and through the non-temporal
     direct-to-LDS rings (one workgroup a CU, 16 KiB in flight a wavefront).
@@ -558,7 +559,6 @@ def read_probe(mib: int, dev) -> int:
 
     import paged_kv_cache_202_amd as pkv
 
-    chunk = 4096
     n = mib * (1 << 20) // chunk
     buf = torch.randint(0, 256, (n * chunk,), dtype=torch.uint8, device=dev)
     orders = {"sequential": torch.arange(n, dtype=torch.int32, device=dev),
@@ -738,8 +738,10 @@ def main() -> int:
                     help="only run paged_kv_copy_blocks over MIB MiB of K and of V (a plain "
                          "copy of known size, to calibrate HBM byte counters), then exit")
     ap.add_argument("--read-probe", type=int, default=0, metavar="MIB",
-                    help="only measure read ceilings over MIB MiB (sequential and random 4 KiB "
+                    help="only measure read ceilings over MIB MiB (sequential and random "
                          "chunks, with the decode kernels' loads), then exit")
+    ap.add_argument("--read-probe-chunk", type=int, default=4096, choices=(1024, 2048, 4096),
+                    help="chunk bytes of --read-probe")
     ap.add_argument("--summarize-profile", action="store_true",
                     help="no GPU work: condense rocprofv3 output (the --*-dir options) into "
                          "profiles/decode_<workload>.json")
@@ -772,7 +774,7 @@ def main() -> int:
     if args.copy_probe:
         return copy_probe(args.copy_probe, dev)
     if args.read_probe:
-        return read_probe(args.read_probe, dev)
+        return read_probe(args.read_probe, dev, args.read_probe_chunk)
     if args.workload.startswith("prefix_share"):
         wk = PrefixVerifyWorkload(args.workload, dev, share=not args.no_share,
                                   rotate=args.rotate)
