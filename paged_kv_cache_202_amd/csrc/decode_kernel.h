@@ -399,7 +399,7 @@ __device__ __forceinline__ void wait_ahead(bool steady, int ahead) {
 // barrier; the compiler cannot track which LDS bytes a pending DMA writes,
 // so the read-back and its waits are written out here.
 // ---------------------------------------------------------------------------
-template <int NL, bool SC = false>
+template <int NL, bool SC = false, int kRowBudget = 16384>
 struct TileRing {
   static constexpr int kCodeBytes = 2 * NL * 1024;
   // with per-row scales (code caches), after the K and V rows: the tile's 16
@@ -408,9 +408,9 @@ struct TileRing {
   // lane mask could be split by the compiler into several instructions,
   // which would break the counting of loads in flight)
   static constexpr int kTileBytes = kCodeBytes + (SC ? 256 : 0);
-  // at least one tile, else as many as fit 16 KiB of rows: two tiles of a
-  // D = 128 bf16 head, four of a D = 64 one
-  static constexpr int kSlots = kCodeBytes >= 16384 ? 1 : 16384 / kCodeBytes;
+  // at least one tile, else as many as fit the budget of rows (16 KiB: two
+  // tiles of a D = 128 bf16 head, four of a D = 64 one)
+  static constexpr int kSlots = kCodeBytes >= kRowBudget ? 1 : kRowBudget / kCodeBytes;
   static constexpr int kBytes = kSlots * kTileBytes;  // per wavefront
   static constexpr int kLoads = 2 * NL + (SC ? 1 : 0);  // DMA instructions per tile
   static_assert((kSlots & (kSlots - 1)) == 0, "slot count must be a power of two");

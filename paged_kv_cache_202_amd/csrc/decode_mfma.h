@@ -320,6 +320,14 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)w, true);
 }
 
+// K/V rows in flight per wavefront: 4 KiB, at least one tile (two 3-bit
+// tiles at D = 128, one 8-bit or bf16 tile). Random 16-token tiles of a
+// paged cache came back faster with fewer of them outstanding: per call on
+// the 8K batch, 3-bit codes 55.1 us at 16 KiB, 53.4 at 8, 51.1 at 4, 60 at
+// 2; 8-bit codes 93.0 / 90.1 / 89.3; the 128K split-K call 339.5 us at
+// 16 KiB, 326.8 at 4; bf16 the same at one tile as at two.
+constexpr int kMfmaRingBudget = 4096;
+
 template <int DT, int D, int RW, int kWaves, bool kStream>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
@@ -333,7 +341,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
   constexpr float kOffset = DT == PKV_I8 ? 1152.f : 0.f;  // fp16 form = offset + code
   constexpr float kNegInf = -std::numeric_limits<float>::infinity();
   constexpr int kStride = kWaves * kTile;  // tokens between a wavefront's tiles
-  using Ring = TileRing<NL, !kBf>;
+  using Ring = TileRing<NL, !kBf, kMfmaRingBudget>;
   constexpr int kSlots = Ring::kSlots;
   static_assert(DT == PKV_BF16 || DT == PKV_I8 || DT == kCodes3, "bf16, 8-bit or 3-bit codes");
   static_assert(!kBf || NV == NCB, "one transposing read per bf16 column block");
@@ -1006,7 +1014,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
 template <int DT, int D, int RW, int W>
 void launch_mfma(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
   constexpr int RB = DT == PKV_BF16 ? 2 * D : DT == kCodes3 ? D / 2 : D;
-  static_assert(W * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16>::kBytes <= 163840,
+  static_assert(W * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16, kMfmaRingBudget>::kBytes <= 163840,
                 "LDS of the rings");
   hipLaunchKernelGGL((decode_mfma_kernel<DT, D, RW, W, false>), grid, dim3(W * 64), 0, s, a,
                      sa);
@@ -1027,7 +1035,7 @@ constexpr int kMfmaStreamSegCost = 2;
 template <int DT, int D, int RW>
 void launch_mfma_stream(const DecodeArgs &a, const StreamArgs &sa, dim3 grid, hipStream_t s) {
   constexpr int RB = DT == PKV_BF16 ? 2 * D : DT == kCodes3 ? D / 2 : D;
-  static_assert(8 * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16>::kBytes >=
+  static_assert(8 * TileRing<CodeGeo<RB>::NL, DT != PKV_BF16, kMfmaRingBudget>::kBytes >=
                     (kMfmaStreamSeqs + 1 + 512) * 4,
                 "the slot prefix fits the rings' LDS");
   hipLaunchKernelGGL((decode_mfma_kernel<DT, D, RW, 8, true>), grid, dim3(8 * 64), 0, s, a,

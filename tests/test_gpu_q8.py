@@ -229,6 +229,9 @@ CASES = [
     ((1, 15, 16, 17, 100, 333, 2049, 700), 32, 8, 128, 1, -1),
     ((5, 64, 129, 700, 1025, 3), 16, 8, 64, 1, -1),
     (tuple(range(1, 300, 11)), 8, 2, 128, 1, -1),
+    # 4096-token partitions: the many-wavefront workgroup split, ragged last tile
+    ((8192, 5000), 32, 8, 128, 1, 4096),
+    ((4500, 4200), 32, 8, 128, 4, 4096),    # 16 rows per wavefront
 ]
 
 
