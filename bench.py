@@ -553,7 +553,8 @@ def read_probe(mib: int, dev, chunk: int = 4096) -> int:
     2 KiB: 8-bit codes -- in sequence and in a seeded random order,
     with the decode kernels' loads: to registers (plain and non-temporal; four
     workgroups of eight wavefronts a CU) and through the non-temporal
-    direct-to-LDS rings (one workgroup a CU, 16 KiB in flight a wavefront).
+    direct-to-LDS rings (one workgroup a CU; 16, 8 and 4 KiB in flight a
+    wavefront, as far as a ring holds one chunk).
     Prints one JSON line; each figure is the median of 5 timed launches."""
     import torch
 
@@ -564,17 +565,21 @@ def read_probe(mib: int, dev, chunk: int = 4096) -> int:
     orders = {"sequential": torch.arange(n, dtype=torch.int32, device=dev),
               "random": torch.from_numpy(np.random.default_rng(20260801).permutation(n)
                                          .astype(np.int32)).to(dev)}
-    modes = {"registers": (0, 1024), "registers_nt": (1, 1024), "lds_rings_nt": (2, 256)}
+    modes = {"registers": (0, 1024, 16384), "registers_nt": (1, 1024, 16384),
+             "lds_rings_nt": (2, 256, 16384)}
+    for ring in (8192, 4096):
+        if ring >= chunk:
+            modes[f"lds_rings_nt_{ring // 1024}k"] = (2, 256, ring)
     out = {"read_probe_bytes": n * chunk, "chunk_bytes": chunk}
     for oname, order in orders.items():
-        for mname, (mode, n_wg) in modes.items():
+        for mname, (mode, n_wg, ring) in modes.items():
             sink = torch.zeros(n_wg, dtype=torch.int32, device=dev)
-            pkv.paged_kv_read_probe(buf, order, sink, chunk, mode)
+            pkv.paged_kv_read_probe(buf, order, sink, chunk, mode, ring)
             times = []
             for _ in range(5):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record()
-                pkv.paged_kv_read_probe(buf, order, sink, chunk, mode)
+                pkv.paged_kv_read_probe(buf, order, sink, chunk, mode, ring)
                 b.record()
                 torch.cuda.synchronize()
                 times.append(a.elapsed_time(b) * 1e-3)

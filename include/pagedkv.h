@@ -468,15 +468,17 @@ int paged_attention_decode_shared(
  * + 8 n_wg, ... Each lane loads 16 bytes per 1 KiB, as the decode kernels
  * load K/V rows: mode 0 into registers, mode 1 into registers with
  * non-temporal loads, mode 2 with the non-temporal direct-to-LDS gathers
- * into two-slot rings that the decode kernels use, read back from LDS.
- * sink (device, n_wg uint32) receives each workgroup's XOR of every
+ * the decode kernels use into a ring of ring_bytes (4, 8 or 16 KiB, at
+ * least one chunk; ignored by modes 0 and 1) per wavefront, read back from
+ * LDS: ring_bytes is what each wavefront keeps in flight. sink (device,
+ * n_wg uint32) receives each workgroup's XOR of every
  * 32-bit word it read. With order = 0, 1, 2, ... it measures a sequential
  * read stream; with a random permutation, the reads of a cache whose blocks
  * came from a shuffled free list. Returns PKV_EINVAL for sizes or a mode out
  * of range, PKV_EHIP if the launch fails. */
 int paged_kv_read_probe(const void *buf, size_t buf_bytes, const int32_t *order,
-                        int32_t n_chunks, int32_t chunk_bytes, int mode, int32_t n_wg,
-                        uint32_t *sink, void *stream);
+                        int32_t n_chunks, int32_t chunk_bytes, int mode, int32_t ring_bytes,
+                        int32_t n_wg, uint32_t *sink, void *stream);
 
 #ifdef __cplusplus
 }

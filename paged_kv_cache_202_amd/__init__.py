@@ -562,11 +562,12 @@ def default_scale(head_dim: int) -> float:
 
 
 def paged_kv_read_probe(buf, order, sink, chunk_bytes: int = 4096, mode: int = 2,
-                        stream=None) -> None:
+                        ring_bytes: int = 16384, stream=None) -> None:
     """Measurement aid (paged_kv_read_probe): read chunks of `buf` (a uint8
     device tensor) in the order of `order` (int32 chunk indices) with the
     decode kernels' load pattern; `sink` (uint32 or int32, one per
-    workgroup) receives each workgroup's XOR of the words it read."""
+    workgroup) receives each workgroup's XOR of the words it read. In LDS
+    mode (2) each wavefront keeps `ring_bytes` (4, 8 or 16 KiB) in flight."""
     torch = _torch()
     _expect(buf, "buf", torch.uint8)
     _expect(order, "order", torch.int32)
@@ -574,5 +575,5 @@ def paged_kv_read_probe(buf, order, sink, chunk_bytes: int = 4096, mode: int = 2
     _one_gpu("paged_kv_read_probe", buf, order, sink)
     check(load().paged_kv_read_probe(
         ctypes.c_void_p(buf.data_ptr()), buf.numel(), ctypes.c_void_p(order.data_ptr()),
-        order.numel(), int(chunk_bytes), int(mode), sink.numel(),
+        order.numel(), int(chunk_bytes), int(mode), int(ring_bytes), sink.numel(),
         ctypes.c_void_p(sink.data_ptr()), _stream(stream)))

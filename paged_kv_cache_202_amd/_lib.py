@@ -54,7 +54,7 @@ PROTOTYPES = {
     "paged_kv_validate": (c_int, [c_void_p]),
     "paged_kv_check_slots": (c_int, [P_i32, c_i32, c_i64, P_i32]),
     "paged_kv_read_probe": (c_int, [c_void_p, c_size_t, c_void_p, c_i32, c_i32, c_int, c_i32,
-                                    c_void_p, c_void_p]),
+                                    c_i32, c_void_p, c_void_p]),
     "paged_cache_write": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i32,
                                   c_i32, c_i32, c_i32, c_i32, c_int, c_void_p]),
     "paged_kv_copy_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_i32, c_i32, c_i32,

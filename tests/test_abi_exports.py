@@ -71,6 +71,13 @@ def test_host_argument_checks_need_no_gpu():
                                       16, 64, ctypes.c_float(0.1), 1, 0, None, 0, None,
                                       None) == _lib.PKV_EINVAL
     assert b"NULL" in lib.paged_kv_last_error()
+    # the read probe: a ring of another size, or one that cannot hold a chunk
+    sink = ctypes.c_void_p(512)
+    assert lib.paged_kv_read_probe(fake, 1 << 20, fake, 4, 4096, 2, 12288, 1, sink, None) \
+        == _lib.PKV_EINVAL
+    assert lib.paged_kv_read_probe(fake, 1 << 20, fake, 4, 8192, 2, 4096, 1, sink, None) \
+        == _lib.PKV_EINVAL
+    assert b"cannot hold" in lib.paged_kv_last_error()
 
 
 def test_workspace_grows_with_partitions():

@@ -14,9 +14,12 @@ import paged_kv_cache_202_amd as pkv
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("mode,ring", [(0, 16384), (1, 16384), (2, 16384), (2, 8192),
+                                       (2, 4096)])
 @pytest.mark.parametrize("chunk", [1024, 4096, 8192])
-def test_probe_reads_named_chunks(device, mode, chunk):
+def test_probe_reads_named_chunks(device, mode, ring, chunk):
+    if ring < chunk:
+        pytest.skip("a ring holds at least one chunk")
     rng = np.random.default_rng(7 + mode + chunk)
     n_buf = (2 << 20) // chunk
     host = rng.integers(0, 256, n_buf * chunk, dtype=np.uint8)
@@ -26,10 +29,10 @@ def test_probe_reads_named_chunks(device, mode, chunk):
     order = np.concatenate([order, np.array([n_buf + 3, 2**31 - 1], np.int32)])  # past the end
     n_wg = 37
     sink = torch.zeros(n_wg, dtype=torch.int32, device=device)
-    pkv.paged_kv_read_probe(buf, torch.from_numpy(order).to(device), sink, chunk, mode)
+    pkv.paged_kv_read_probe(buf, torch.from_numpy(order).to(device), sink, chunk, mode, ring)
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     clamped = np.minimum(order.astype(np.int64), n_buf - 1)
     want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(words[clamped], axis=1))
-    print(f"mode {mode} chunk {chunk}: xor {got:#010x} (host {want:#010x})", flush=True)
+    print(f"mode {mode} ring {ring} chunk {chunk}: xor {got:#010x} (host {want:#010x})", flush=True)
     assert got == want
