@@ -1026,8 +1026,10 @@ constexpr int kMfmaStreamSeqs = 4096;
 // Slots without work at the head of each unit in stream mode: what a
 // segment's start costs (query load, block-id window, ring fill: a few
 // dependent memory latencies) in the time of one 16-token tile of a
-// wavefront (about 2.6 us on the 8K decode batch).
-constexpr int kMfmaStreamSegCost = 2;
+// wavefront. Measured on the variable-length batch of 256: bf16 283.3 us
+// at 2, 281.7 at 3, 283.8 at 4; over 8-bit codes 157 us at 2 to 6 alike
+// (166 at 0).
+constexpr int kMfmaStreamSegCost = 3;
 
 // Stream mode over bf16 caches or caches of codes (eight independent
 // wavefronts per workgroup, grid.x = sa.n_waves / 8), then the merge of its
