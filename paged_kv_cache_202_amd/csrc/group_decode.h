@@ -61,11 +61,7 @@ struct GroupGeo {
   static constexpr int NCB = D / 16;            // 16-dim output column blocks
   static constexpr int kHalf = kTile * RB;      // bytes of K (or V) of a tile
   static constexpr int kTileBytes = 2 * kHalf;
-#ifdef PKV_GSLOTS
-  static constexpr int kSlots = PKV_GSLOTS;
-#else
   static constexpr int kSlots = kTileBytes >= 8192 ? 2 : 4;  // 16 KiB a wavefront
-#endif
   static_assert(KCH == NC, "one 16-byte K chunk per q.k MFMA");
 };
 
