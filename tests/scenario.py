@@ -160,4 +160,11 @@ TIGHT = {
     "decode": (1e-4, 1e-4),       # one query token, contexts up to 8K
     "decode_128k": (1e-5, 1e-5),  # one query token over 131072-token contexts
     "multi_query": (1e-3, 1e-4),  # bf16 weights in the MFMA p.v product, ~2.5K
+    # caches of codes: the p.v product takes each weight as fp16 rounded toward
+    # zero (relative error below 2^-10), which averages out over a long
+    # context (3.4e-5 measured at 8K) but not over the few dominant weights of
+    # a short one (4e-4 in the variable-length batch); rows of contexts of at
+    # least 4096 tokens, and shorter ones
+    "codes_long": (2e-4, 1e-4),
+    "codes_short": (1e-3, 1e-4),
 }

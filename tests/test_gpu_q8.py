@@ -23,6 +23,7 @@ from oracle import native
 from oracle import quant
 from oracle.attention import widen
 from oracle.pool import PagedPool
+from scenario import TIGHT
 from synth import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -326,9 +327,11 @@ def test_q8_full_size_sampled(name, bits, device):
     tables, lens = opool.block_tables(range(wk.B), wk.max_blocks)
     tables, lens = np.array(tables, np.int32), np.array(lens, np.int32)
     assert np.array_equal(wk.tables_host, tables)
+    wk.lse = torch.full((wk.B, wk.nq, wk.Hq), float("nan"), dtype=torch.float32, device=device)
     wk.step(0)
     torch.cuda.synchronize()
     out = wk.out.cpu().numpy()
+    lse = wk.lse.cpu().numpy().reshape(-1)
     # the oracle quantizes the rows of a few sequences only (for the
     # variable-length batch also the longest and the last one)
     seqs = [0, 9, 20, 31] if wk.B == 32 else sorted({0, 9, 100, int(np.argmax(wk.lens)),
@@ -354,9 +357,18 @@ def test_q8_full_size_sampled(name, bits, device):
         for blk in tables[b][:-(-int(lens[b]) // wk.bs)]:
             assert np.array_equal(gk[blk], kc[blk]) and np.array_equal(gks[blk], ks[blk])
     rows = np.concatenate([np.arange(b * wk.Hq, (b + 1) * wk.Hq) for b in seqs]).astype(np.int64)
-    ref, _ = native.attention_q8(host_bits(wk.host_q), "bf16", kc, vc, ks, vs, tables, lens,
-                                 wk.scale, wk.bs, rows=rows,
-                                 threads=min(16, len(os.sched_getaffinity(0))))
-    err = np.abs(out.reshape(-1, wk.D)[rows] - ref).max()
-    print(f"  max-abs error {err:.3e} over {len(rows)} rows", flush=True)
-    assert np.isfinite(out).all() and err <= 1e-2
+    ref, ref_lse = native.attention_q8(host_bits(wk.host_q), "bf16", kc, vc, ks, vs, tables,
+                                       lens, wk.scale, wk.bs, rows=rows,
+                                       threads=min(16, len(os.sched_getaffinity(0))))
+    d_out = np.abs(out.reshape(-1, wk.D)[rows] - ref).max(axis=1)
+    d_lse = np.abs(lse[rows] - ref_lse)
+    err, lerr = d_out.max(), d_lse.max()
+    print(f"  max-abs error out {err:.3e}, lse {lerr:.3e} over {len(rows)} rows", flush=True)
+    assert np.isfinite(out).all() and err <= 1e-2 and lerr <= 1e-2
+    # the tight bounds, by the row's context length (one dropped or repeated
+    # tile would break them: tests/test_parity_bounds.py)
+    long_row = np.asarray(wk.lens)[rows // wk.Hq] >= 4096
+    for sel, key in ((long_row, "codes_long"), (~long_row, "codes_short")):
+        if sel.any():
+            ob, lb = TIGHT[key]
+            assert d_out[sel].max() <= ob and d_lse[sel].max() <= lb, key

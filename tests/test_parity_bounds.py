@@ -58,6 +58,10 @@ def smallest_tile_effect(n, G, D=128, units=2, seed=0):
     ("decode_128k", 131072, 8, 5),
     # prefix sharing + 4-draft verify: 2564-token contexts, shortest row 2561
     ("multi_query", 2561, 4, 3),
+    # caches of codes: rows of contexts of at least 4096 tokens, and the
+    # longest context below that
+    ("codes_long", 8192, 4, 5),
+    ("codes_short", 4095, 4, 2),
 ])
 def test_tight_bound_sees_one_tile(name, n, G, margin):
     out_bound, lse_bound = TIGHT[name]
