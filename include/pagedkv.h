@@ -102,6 +102,8 @@ typedef struct {
  * every slot fits an int32. *out receives the handle. */
 int paged_kv_pool_create(int32_t total_blocks, int32_t block_size,
                          const int32_t *initial_free_stack, pkv_pool **out);
+/* Free the pool and every sequence in it (NULL is a no-op); the handle is
+ * invalid afterwards. */
 void paged_kv_pool_destroy(pkv_pool *pool);
 
 /* Register an empty sequence. EEXIST if the id is taken. */
@@ -144,15 +146,20 @@ int paged_kv_fork(pkv_pool *pool, int64_t parent, int64_t child,
                   int32_t prefix_tokens);
 
 /* Release a sequence: drop one reference per table entry in table order;
- * blocks reaching zero go on top of the free stack ([KVNB s5] release). */
+ * blocks reaching zero go on top of the free stack ([KVNB s5] release).
+ * ENOENT (pool unchanged) if the id is unknown. */
 int paged_kv_free(pkv_pool *pool, int64_t seq_id);
 
 /* Shorten a sequence to new_length (0 <= new_length <= length): table
  * entries past ceil(new_length / block_size) are released in table order; a
  * kept partial block that is shared stays shared, so the next append copies
- * it. (Rollback of rejected speculative tokens.) */
+ * it. (Rollback of rejected speculative tokens.) ENOENT if the id is
+ * unknown, EINVAL if new_length is outside [0, length]; the pool is then
+ * unchanged. */
 int paged_kv_truncate(pkv_pool *pool, int64_t seq_id, int32_t new_length);
 
+/* The sequence's length in *len; ENOENT if the id is unknown, EINVAL if len
+ * is NULL. */
 int paged_kv_seq_length(const pkv_pool *pool, int64_t seq_id, int32_t *len);
 
 /* Number of live sequences in *n_out, and (when ids_out is not NULL) their
