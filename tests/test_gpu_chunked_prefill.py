@@ -48,6 +48,21 @@ def test_chunk_matches_oracle(ci, device):
     assert np.abs(lse - ref_lse).max() <= 1e-2
 
 
+@pytest.mark.parametrize("bs", [32, 64])
+def test_chunk_larger_blocks(bs, device):
+    """Blocks of 32 and 64 tokens: the row-tile kernel's tiles start inside
+    blocks, chunk and cached prefix alike."""
+    print(f"chunked prefill, block size {bs}", flush=True)
+    case = Case((700, 1300), 32, 8, 128, bs, "bf16", nq=96, seed=950 + bs, stack_seed=bs,
+                device=device, partition_tokens=0)
+    out, lse = case.run_gpu()
+    ref, ref_lse = case.run_oracle()
+    err = np.abs(out - ref).max()
+    print(f"  max-abs error {err:.3e}", flush=True)
+    assert np.isfinite(out).all() and err <= tolerance("bf16")
+    assert np.abs(lse - ref_lse).max() <= 1e-2
+
+
 def test_rows_without_keys_and_bad_tables_give_nan(device):
     """A sequence shorter than its chunk, and one whose table points outside
     the pool, produce NaN rows; the others are unaffected."""

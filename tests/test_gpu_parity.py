@@ -107,6 +107,30 @@ def test_decode_matches_oracle(device, ci):
     check_case(case, part)
 
 
+# Blocks of 32 and 64 tokens: a 16-token tile then starts inside its block
+# (the kernels look the block up by t / block_size and gather from offset
+# t % block_size in it); each kernel family of the single-query and verify
+# paths once.
+BIG_BLOCK_CASES = [
+    # lens, Hq, Hkv, D, block_size, dtype, nq, partition
+    ((1, 17, 250, 1000), 32, 8, 128, 32, "bf16", 1, 0),    # matrix-core decode kernel
+    ((5000, 4100), 32, 8, 128, 64, "bf16", 1, 4096),        # its 8-wavefront workgroups
+    ((515, 47, 2000, 33), 32, 8, 128, 32, "bf16", 1, -1),   # its stream mode
+    ((31, 480, 1000), 8, 2, 256, 64, "bf16", 1, 0),         # VALU kernel, D = 256
+    ((6, 9, 17, 33, 300), 4, 2, 64, 32, "f32", 1, 48),      # fp32, partitions across blocks
+    ((90, 600, 47), 32, 8, 128, 32, "bf16", 4, 0),          # 4-draft verify tile
+]
+
+
+@pytest.mark.parametrize("ci", range(len(BIG_BLOCK_CASES)))
+def test_larger_blocks(device, ci):
+    lens, Hq, Hkv, D, bs, dtype, nq, part = BIG_BLOCK_CASES[ci]
+    say(f"block size {bs}: lens {lens} Hq {Hq} Hkv {Hkv} D {D} {dtype} nq {nq} part {part}")
+    case = Case(lens, Hq, Hkv, D, bs, dtype, nq=nq, seed=700 + ci, stack_seed=ci,
+                partition_tokens=part)
+    check_case(case, part)
+
+
 def test_partition_sizes_agree(device):
     case = Case((3000, 1234), 32, 8, 128, 16, "bf16", seed=77, stack_seed=4)
     runs = [case.run_gpu(p) for p in (0, 512, 256, 128, 64, 16, 3008, -1)]

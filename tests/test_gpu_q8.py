@@ -272,6 +272,23 @@ def test_q8_negative_and_zero_scale(scale, bits, device):
 
 
 @pytest.mark.parametrize("bits", [8, 3])
+@pytest.mark.parametrize("bs", [32, 64])
+def test_q8_larger_blocks(bs, bits, device):
+    """Blocks of 32 and 64 tokens: tiles (and their rows' scales) start
+    inside a block; the split plan and the stream plan."""
+    print(f"{bits}-bit attention, block size {bs}", flush=True)
+    c = Q8Case((1, 17, 250, 1000, 2100), 32, 8, 128, bs=bs, seed=40 + bs, device=device,
+               bits=bits)
+    ref, ref_lse = c.run_oracle()
+    for part in (0, -1):
+        out, lse = c.run_gpu(part)
+        err = np.abs(out - ref).max()
+        print(f"  partition {part}: max-abs error {err:.3e}", flush=True)
+        assert np.isfinite(out).all() and err <= 1e-2
+        assert np.abs(lse - ref_lse).max() <= 1e-2
+
+
+@pytest.mark.parametrize("bits", [8, 3])
 def test_q8_many_partitions_per_workgroup(bits, device):
     """2 sequences x 8 KV heads x 256 partitions of 16 tokens: one wavefront
     streams a run of two consecutive partitions as one partial."""

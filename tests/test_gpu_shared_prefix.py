@@ -193,6 +193,25 @@ def test_shared_prefix_matches_oracle(ci, device):
     assert np.abs(out - plain).max() <= tolerance("bf16")
 
 
+@pytest.mark.parametrize("bs,nq", [(32, 4), (64, 1)])
+def test_shared_prefix_larger_blocks(bs, nq, device):
+    """Blocks of 32 and 64 tokens: the prefix's tiles and the members' own
+    tiles start inside blocks; the one-pass kernel and the plain path agree
+    with the oracle."""
+    print(f"shared prefix, block size {bs}, nq {nq}", flush=True)
+    c = ShareCase([(320, [20, 35, 70, 1, 48, 16]), (256, [9, 40, 33])], [100, 17], 32, 8, 128,
+                  nq, bs=bs, seed=60 + bs, device=device)
+    out, lse = c.run(shared=True, partition_tokens=0)
+    ref, ref_lse = c.oracle()
+    err, err_lse = np.abs(out - ref).max(), np.abs(lse - ref_lse).max()
+    print(f"  groups {c.groups.n_groups}; max-abs {err:.3e}, lse {err_lse:.3e}", flush=True)
+    assert c.groups.n_groups == 2
+    assert np.isfinite(out).all() and err <= tolerance("bf16")
+    assert np.isfinite(lse).all() and err_lse <= tolerance("bf16")
+    plain, _ = c.run(shared=False, partition_tokens=0)
+    assert np.abs(out - plain).max() <= tolerance("bf16")
+
+
 def test_no_groups_is_plain_decode(device):
     c = ShareCase([(256, [10, 20])], [30], 32, 8, 128, 4, seed=11, device=device)
     out, _ = c.run(shared=True, min_tokens=10**6)  # no group qualifies
