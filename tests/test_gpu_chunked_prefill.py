@@ -30,6 +30,10 @@ CASES = [
     ((999,), 32, 8, 128, 77, 16),         # 16-token partitions, odd chunk
     ((300, 18), 32, 32, 128, 17, 0),      # G = 1, 17 rows: a 1-row second tile
     ((777,), 32, 8, 64, 200, -1),         # -1 asks for the library's choice here
+    # one KV head (multi-query attention): more than 16 rows per KV head even
+    # for one query token, so decode itself runs on the row-tile kernel
+    ((600, 2100, 1), 32, 1, 128, 1, 0),   # G = 32, one query token, a 1-token context
+    ((1500, 90), 64, 1, 64, 3, 0),        # G = 64, three query tokens
 ]
 
 
