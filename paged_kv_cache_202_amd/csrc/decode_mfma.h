@@ -515,6 +515,19 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       t_end = min(L, t_begin + ppw * a.part_tokens);
     }
 
+    // this wavefront's tiles of [t_begin, t_end), and lane i's block id of
+    // its tile i, loaded ahead of the query so that the two loads' latencies
+    // overlap instead of adding up
+    const int wstart = indep ? t_begin : t_begin + wave * kTile;  // this wavefront's first tile
+    const int wstride = indep ? kTile : kStride;                   // and the step between its tiles
+    const int n_tiles = wstart < t_end ? (t_end - wstart + wstride - 1) / wstride : 0;
+    auto tile_t0 = [&](int k) { return wstart + k * wstride; };
+    const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
+    auto table_window = [&](int w) {
+      return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
+    };
+    const int tblv0 = n_tiles > 0 ? table_window(0) : 0;
+
     // ---- this lane's query row ln as the B operand of the q.k MFMAs: the
     //      lane's quarter of the dims (lg * D / 4 ..), 8 per MFMA; bf16 as is
     //      for bf16 K, else fp16 in the order the K codes widen, scaled by 2^-e
@@ -658,7 +671,6 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
       lim = row_live ? L - nq + qi + 1 : 0;
     }
 
-    const int32_t *trow = a.tables + (size_t)b * a.max_blocks;
     const char *kbase = (const char *)a.kc;
     const char *vbase = (const char *)a.vc;
     int koff[NL], voff[NL];
@@ -694,13 +706,6 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
         gather_lds16<kKvNonTemporal>(vp + voff[i], dst + (NL + i) * 1024);
     };
 
-    const int wstart = indep ? t_begin : t_begin + wave * kTile;  // this wavefront's first tile
-    const int wstride = indep ? kTile : kStride;                   // and the step between its tiles
-    const int n_tiles = wstart < t_end ? (t_end - wstart + wstride - 1) / wstride : 0;
-    auto tile_t0 = [&](int k) { return wstart + k * wstride; };
-    auto table_window = [&](int w) {
-      return trow[tile_t0(min(64 * w + lane, n_tiles - 1)) / a.bs];
-    };
 
     // O^T accumulators, offsets included: o[cb][e] = O^T[m = 4 lg + e][row ln]
     // of column block cb (8-bit: dim 16 cb + m; 3-bit: see the merge below)
@@ -738,7 +743,7 @@ decode_mfma_kernel(const DecodeArgs a, const StreamArgs sa) {
     };
 
     if (n_tiles > 0) {
-      int tblv = table_window(0);
+      int tblv = tblv0;
       settle_v(tblv);
       auto table_at = [&](int k) { return __builtin_amdgcn_readlane(tblv, k & 63); };
       Ring ring;
